@@ -1,0 +1,348 @@
+/*
+ * fp8_oracle.c -- plain, slow, CPU reference of the FP8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product
+ * path (the HIP library and its Python binding) never calls it, and the two
+ * share no source, header, table or helper.
+ *
+ * Every routine is the written-out definition of what it computes: no
+ * blocking, no fusion, no reordering beyond what the definition states.
+ * Floating point that the method performs in fp32 is done here in fp32 with
+ * IEEE round-to-nearest-even (x86-64 SSE, no contraction: build with
+ * -ffp-contract=off and without fast-math); sums are carried in fp64.
+ *
+ * Sources (the web pages of the AstrAI repository by ViperEkura):
+ *   [CMP]  compare view 3e57cc8...main (split diff), file hunks named below
+ *   [LOG1] commit log at 3e57cc8 (astrai/extension)
+ *   [LOG4] author commit search (benchmark commit messages)
+ * plus the OCP 8-bit floating point specification (E4M3 / E5M2) for the
+ * bit encodings, which the pages name but do not spell out.
+ *
+ * Parity pins: every exported function is pinned by a CPU test (see the
+ * test module headers); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define FMT_E4M3 0
+#define FMT_E5M2 1
+
+/* Format constants of the OCP definition.  The maxima 448 and 57344 are the
+ * ones [CMP] astrai/extension/fp8.py prints in its FP8_MAX table. */
+static int fmt_mbits(int fmt) { return fmt == FMT_E5M2 ? 2 : 3; }
+static int fmt_bias(int fmt) { return fmt == FMT_E5M2 ? 15 : 7; }
+double orc_fmt_max(int fmt) { return fmt == FMT_E5M2 ? 57344.0 : 448.0; }
+static uint8_t fmt_max_code(int fmt) { return fmt == FMT_E5M2 ? 0x7B : 0x7E; }
+
+/* ------------------------------------------------------------------------
+ * fp8 decode: byte -> exact value (OCP definition).
+ * E4M3: bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN.
+ * E5M2: bias 15, 2 mantissa bits, exponent field 31 is inf (mantissa 0) or
+ * NaN (mantissa != 0).
+ * ---------------------------------------------------------------------- */
+float orc_decode(uint8_t byte, int fmt)
+{
+    const int mbits = fmt_mbits(fmt);
+    const int bias = fmt_bias(fmt);
+    const int sign = byte >> 7;
+    const int expf = (byte & 0x7F) >> mbits;
+    const int mant = byte & ((1 << mbits) - 1);
+    double v;
+    if (fmt == FMT_E4M3 && (byte & 0x7F) == 0x7F) return NAN;
+    if (fmt == FMT_E5M2 && expf == 31) {
+        if (mant) return NAN;
+        return sign ? -INFINITY : INFINITY;
+    }
+    if (expf == 0)
+        v = ldexp((double)mant, 1 - bias - mbits); /* subnormal */
+    else
+        v = ldexp((double)((1 << mbits) + mant), expf - bias - mbits);
+    return (float)(sign ? -v : v);
+}
+
+/* ------------------------------------------------------------------------
+ * fp8 encode: fp32 -> byte, round to nearest with ties to even, saturating
+ * to the largest finite value ("satfinite").  [CMP] quantize.cuh, cvt_fp8 /
+ * cvt_fp8x2: the kernel converts with round-nearest-even and satfinite.
+ *
+ * Method: find the spacing q of representable values around |v| (the
+ * subnormal spacing below the smallest normal), round |v|/q to the nearest
+ * integer with ties to even (nearbyint in the default rounding mode), and
+ * rebuild the bit fields from the rounded value.  Any |v| >= max (including
+ * infinity) saturates.  NaN maps to the NaN code S.1111111 with the sign
+ * kept (the pages never feed NaN; this choice is documented, not pinned).
+ * ---------------------------------------------------------------------- */
+uint8_t orc_encode(float v, int fmt)
+{
+    const int mbits = fmt_mbits(fmt);
+    const int bias = fmt_bias(fmt);
+    const int e_min = 1 - bias; /* exponent of the smallest normal */
+    const double fmax = orc_fmt_max(fmt);
+    uint32_t bits;
+    memcpy(&bits, &v, sizeof bits);
+    const uint8_t sign = (bits >> 31) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;
+    const double a = fabs((double)v);
+    if (a >= fmax) return sign | fmt_max_code(fmt);
+    if (a == 0.0) return sign;
+    int e = ilogb(a);
+    if (e < e_min) e = e_min;
+    const double q = ldexp(1.0, e - mbits);
+    const double n = nearbyint(a / q); /* a / q is exact: q is a power of 2 */
+    double r = n * q;
+    if (r > fmax) r = fmax; /* unreachable for a < fmax; kept as a guard */
+    if (r == 0.0) return sign;
+    const int er = ilogb(r);
+    if (er < e_min) {
+        const int mant = (int)(r / ldexp(1.0, e_min - mbits));
+        return sign | (uint8_t)mant;
+    }
+    const int mant = (int)(r / ldexp(1.0, er - mbits)) - (1 << mbits);
+    return sign | (uint8_t)(((er + bias) << mbits) | mant);
+}
+
+/* Encode an fp32 array (used by the exhaustive pin). */
+void orc_encode_array(const float* v, int64_t n, int fmt, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_encode(v[i], fmt);
+}
+
+/* Encode every fp32 bit pattern in [first, first + n) (exhaustive pin). */
+void orc_encode_bits_range(uint32_t first, int64_t n, int fmt, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t b = first + (uint32_t)i;
+        float f;
+        memcpy(&f, &b, sizeof f);
+        out[i] = orc_encode(f, fmt);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * bf16 helpers.  A bf16 value is the upper half of an fp32 bit pattern, so
+ * widening is exact.  Narrowing from fp64 rounds ONCE to nearest-even
+ * (bias 127, 7 stored mantissa bits, subnormal spacing 2^-133, overflow to
+ * infinity), with no intermediate fp32 rounding.
+ * ---------------------------------------------------------------------- */
+float orc_bf16_to_f32(uint16_t h)
+{
+    const uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+uint16_t orc_bf16_from_f64(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    if (isnan(v)) return sign | 0x7FC0;
+    const double a = fabs(v);
+    if (isinf(a)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    int e = ilogb(a);
+    if (e < -126) e = -126;
+    const double q = ldexp(1.0, e - 7);
+    const double n = nearbyint(a / q);
+    const double r = n * q;
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;
+    const int er = ilogb(r);
+    if (er < -126) return sign | (uint16_t)(r / ldexp(1.0, -133));
+    const int mant = (int)(r / ldexp(1.0, er - 7)) - 128;
+    return sign | (uint16_t)(((er + 127) << 7) | mant);
+}
+
+void orc_bf16_from_f64_array(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_f64(v[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * amax: max |x_i| over the raw (pre-quantization) bf16 values, as fp32.
+ * [CMP] quantize.cuh, fp8_quantize_kernel: the running max takes fabsf of
+ * the unscaled input; [LOG1] records the bug where the quantized max was
+ * used instead.  NaN inputs are skipped (fmaxf semantics); an all-zero or
+ * empty tensor gives 0.
+ * ---------------------------------------------------------------------- */
+float orc_amax(const uint16_t* x, int64_t n)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        const float a = fabsf(orc_bf16_to_f32(x[i]));
+        if (a > m) m = a; /* a NaN compares false and is skipped */
+    }
+    return m;
+}
+
+/* ------------------------------------------------------------------------
+ * Scale from an amax peak.  [CMP] astrai/extension/fp8.py,
+ * FP8Recipe.scale_from_history, and quantize.cuh publish_amax: the scale is
+ * the quantization step (peak / FP8_MAX) / 2^margin, clamped below at
+ * 1e-12, computed as two IEEE fp32 divisions.
+ * ---------------------------------------------------------------------- */
+float orc_scale_from_peak(float peak, int fmt, int margin)
+{
+    const float fmax = (float)orc_fmt_max(fmt);
+    const float pow2 = ldexpf(1.0f, margin);
+    const float t = peak / fmax;
+    const float s = t / pow2;
+    return s > 1e-12f ? s : 1e-12f;
+}
+
+/* The multiplier a quantize applies: the fp32 reciprocal of the step.
+ * [CMP] fp8.py passes scale.reciprocal() to quantize, and the kernel
+ * multiplies each element by it. */
+float orc_multiplier(float s) { return 1.0f / s; }
+
+/* ------------------------------------------------------------------------
+ * Quantize: q_i = encode(fp32(x_i * m)), m = fp32(1 / s).
+ * [CMP] quantize.cuh, fp8_quantize_kernel (multiply, then convert).
+ * ---------------------------------------------------------------------- */
+void orc_quantize(const uint16_t* x, int64_t n, int fmt, float s, uint8_t* out)
+{
+    const float m = orc_multiplier(s);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const float prod = orc_bf16_to_f32(x[i]) * m;
+        out[i] = orc_encode(prod, fmt);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Scaled GEMM.  [CMP] ops/fp8.py mm_fp8 and csrc/kernels/fp8/common.h
+ * (operand layout tags, batch strides where 0 broadcasts) and epilogue.cuh
+ * (accumulate, apply the combined scale, add the bias, round once to bf16).
+ *
+ *   out[b,i,j] = bf16( (sum_k A[b,i,k] * B[b,k,j]) * fp32(sa*sb) + bias[j] )
+ *
+ * A is M x K: stored [M][K] with row stride lda (trans_a = 0) or [K][M]
+ * (trans_a = 1).  B is K x N: stored [K][N] (trans_b = 0) or [N][K]
+ * (trans_b = 1, the nn.Linear weight).  The sum, the scale product and the
+ * bias add are carried in fp64; the result rounds once to bf16.
+ * out is contiguous [batch][M][N].
+ * ---------------------------------------------------------------------- */
+static float g_dec[2][256];
+static int g_dec_ready = 0;
+
+static void dec_tables(void)
+{
+    if (g_dec_ready) return;
+    for (int f = 0; f < 2; ++f)
+        for (int c = 0; c < 256; ++c) g_dec[f][c] = orc_decode((uint8_t)c, f);
+    g_dec_ready = 1;
+}
+
+static double gemm_one(const uint8_t* A, const uint8_t* B, int fmt, int trans_a,
+                       int trans_b, int64_t K, int64_t lda, int64_t ldb,
+                       int64_t b, int64_t i, int64_t j, int64_t stride_a,
+                       int64_t stride_b)
+{
+    const uint8_t* Ab = A + b * stride_a;
+    const uint8_t* Bb = B + b * stride_b;
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        const uint8_t ca = trans_a ? Ab[k * lda + i] : Ab[i * lda + k];
+        const uint8_t cb = trans_b ? Bb[j * ldb + k] : Bb[k * ldb + j];
+        acc += (double)g_dec[fmt][ca] * (double)g_dec[fmt][cb];
+    }
+    return acc;
+}
+
+static uint16_t epilogue_one(double acc, float s, const uint16_t* bias, int64_t j)
+{
+    double y = acc * (double)s;
+    if (bias) y += (double)orc_bf16_to_f32(bias[j]);
+    return orc_bf16_from_f64(y);
+}
+
+void orc_gemm(const uint8_t* A, const uint8_t* B, int fmt, int trans_a, int trans_b,
+              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+              int64_t batch, int64_t stride_a, int64_t stride_b, float sa, float sb,
+              const uint16_t* bias, uint16_t* out)
+{
+    dec_tables();
+    const float s = sa * sb; /* fp32 product of the two steps */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t j = 0; j < N; ++j) {
+                const double acc = gemm_one(A, B, fmt, trans_a, trans_b, K, lda, ldb,
+                                            b, i, j, stride_a, stride_b);
+                out[(b * M + i) * N + j] = epilogue_one(acc, s, bias, j);
+            }
+}
+
+/* The same definition evaluated only at listed output coordinates, for
+ * parity at sizes where the full product is too slow on the CPU.  Also
+ * returns sum_k |A*B| * |s| per sample (the scale of the fp32 rounding
+ * error a correct kernel may carry), in absdot (nullable). */
+void orc_gemm_sampled(const uint8_t* A, const uint8_t* B, int fmt, int trans_a,
+                      int trans_b, int64_t K, int64_t lda, int64_t ldb,
+                      int64_t stride_a, int64_t stride_b, float sa, float sb,
+                      const uint16_t* bias, int64_t n_samples, const int64_t* sb_idx,
+                      const int64_t* si_idx, const int64_t* sj_idx, uint16_t* out,
+                      double* absdot)
+{
+    dec_tables();
+    const float s = sa * sb;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_samples; ++t) {
+        const double acc = gemm_one(A, B, fmt, trans_a, trans_b, K, lda, ldb, sb_idx[t],
+                                    si_idx[t], sj_idx[t], stride_a, stride_b);
+        out[t] = epilogue_one(acc, s, bias, sj_idx[t]);
+        if (absdot) {
+            const uint8_t* Ab = A + sb_idx[t] * stride_a;
+            const uint8_t* Bb = B + sb_idx[t] * stride_b;
+            double m = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t ca = trans_a ? Ab[k * lda + si_idx[t]] : Ab[si_idx[t] * lda + k];
+                const uint8_t cb = trans_b ? Bb[sj_idx[t] * ldb + k] : Bb[k * ldb + sj_idx[t]];
+                m += fabs((double)g_dec[fmt][ca] * (double)g_dec[fmt][cb]);
+            }
+            absdot[t] = m * fabs((double)s);
+        }
+    }
+}
+
+/* Sum of |A*B| * |s| for every output (same indexing as orc_gemm), used to
+ * bound the fp32 accumulation error a correct kernel may carry. */
+void orc_gemm_absdot(const uint8_t* A, const uint8_t* B, int fmt, int trans_a, int trans_b,
+                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                     int64_t batch, int64_t stride_a, int64_t stride_b, float sa, float sb,
+                     double* out)
+{
+    dec_tables();
+    const float s = sa * sb;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t j = 0; j < N; ++j) {
+                const uint8_t* Ab = A + b * stride_a;
+                const uint8_t* Bb = B + b * stride_b;
+                double m = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const uint8_t ca = trans_a ? Ab[k * lda + i] : Ab[i * lda + k];
+                    const uint8_t cb = trans_b ? Bb[j * ldb + k] : Bb[k * ldb + j];
+                    m += fabs((double)g_dec[fmt][ca] * (double)g_dec[fmt][cb]);
+                }
+                out[(b * M + i) * N + j] = m * fabs((double)s);
+            }
+}
+
+/* ------------------------------------------------------------------------
+ * Bias gradient: db[j] = bf16( sum_m g[m, j] ), the column sum of the bf16
+ * output gradient, carried in fp64 and rounded once.  [CMP] fp8.py,
+ * _LinearFp8.backward (grad_b is the sum of g over rows, cast to bf16).
+ * ---------------------------------------------------------------------- */
+void orc_colsum(const uint16_t* g, int64_t M, int64_t N, uint16_t* db)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j) {
+        double acc = 0.0;
+        for (int64_t m = 0; m < M; ++m) acc += (double)orc_bf16_to_f32(g[m * N + j]);
+        db[j] = orc_bf16_from_f64(acc);
+    }
+}

@@ -1,0 +1,314 @@
+"""Benchmark of the FP8 linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the fp8 linear layer forward + backward at M = N = K = 4096 with delayed
+scaling (history 16, margin 0) in the HYBRID format (E4M3 forward, E5M2
+gradients), through the library's entry points in the order fp8_linear_fwd
+and fp8_linear_bwd issue them:
+  quantize x, w (E4M3, fused amax, in-kernel ring fold)  -> NT GEMM + bias
+  quantize g (E5M2, fold), w, x (E5M2, forward steps)    -> NN GEMM (dX),
+  TN GEMM (dW), column sum (bias gradient).
+The step is driven through fp8_quantize / fp8_mm / fp8_colsum so that HIP
+events can bracket each GEMM launch inside the timed region; before timing,
+its outputs are checked to be bit-identical to fp8_linear_fwd / _bwd.
+
+value = GEMM flops of the step (3 x 2 x 4096^3) / measured step time, in
+TFLOP/s: the fp8 GEMM rate the layer delivers with its quantize overhead
+included.  Components of the metric are reported beside it: the 4096^3 NT
+GEMM alone, the 64 x 8192 x 2048 NT GEMM (TFLOP/s and HBM GB/s) and the
+delayed-scaling quantize of a bf16 [8192, 8192] tensor (GB/s), each with
+operands rotated over > 256 MB so that the MALL cannot serve them.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+E4M3, E5M2 = 0, 1
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--size", type=int, default=4096)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-components", action="store_true")
+    return p.parse_args()
+
+
+class Layer:
+    """Device state of one fp8 linear layer at M = N = K = size."""
+
+    def __init__(self, f, torch, size, seed0=600):
+        import workloads as wl
+        M = N = K = size
+        self.M, self.N, self.K = M, N, K
+        dev = "cuda"
+
+        def up(h):
+            return torch.from_numpy(h.view(np.int16)).to(dev)
+
+        self.x = up(wl.normal_bf16((M, K), 1.0, seed0 + 1))
+        self.w = up(wl.normal_bf16((N, K), 0.02, seed0 + 2))
+        self.bias = up(wl.normal_bf16((N,), 0.1, seed0 + 3))
+        self.g = up(wl.normal_bf16((M, N), 1e-3, seed0 + 4))
+        u8 = dict(dtype=torch.uint8, device=dev)
+        i16 = dict(dtype=torch.int16, device=dev)
+        self.x8 = torch.empty(M * K, **u8)
+        self.w8 = torch.empty(N * K, **u8)
+        self.g8 = torch.empty(M * N, **u8)
+        self.x8b = torch.empty(M * K, **u8)
+        self.w8b = torch.empty(N * K, **u8)
+        self.out = torch.empty(M * N, **i16)
+        self.dx = torch.empty(M * K, **i16)
+        self.dw = torch.empty(N * K, **i16)
+        self.db = torch.empty(N, **i16)
+        self.sfwd = torch.zeros(2, dtype=torch.float32, device=dev)
+        self.sg = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.cs_ws = torch.empty(f.fp8_colsum_workspace(M, N), **u8)
+        self.rx, self.rw, self.rg = f.Ring(16), f.Ring(16), f.Ring(16)
+
+    def seed(self, f):
+        """First use of each ring: measure-only fold of the current tensor."""
+        f.fp8_quantize(self.w, E4M3, ring=self.rw)
+        f.fp8_quantize(self.x, E4M3, ring=self.rx)
+        f.fp8_quantize(self.g, E5M2, ring=self.rg)
+        for r in (self.rx, self.rw, self.rg):
+            r.initialized = True
+
+    def step(self, f, ev=None):
+        M, N, K = self.M, self.N, self.K
+        sx, sw = self.sfwd[0:1], self.sfwd[1:2]
+        # forward (E4M3): quantize with the ring's step, fold amax, NT GEMM
+        f.fp8_quantize(self.x, E4M3, scale=self.rx.scale, out=self.x8, ring=self.rx,
+                       scale_used=sx)
+        f.fp8_quantize(self.w, E4M3, scale=self.rw.scale, out=self.w8, ring=self.rw,
+                       scale_used=sw)
+        if ev:
+            ev[0][0].record()
+        f.fp8_mm(self.x8, self.w8, E4M3, 0, 1, M, N, K, K, K, 1, 0, 0, sx, sw, self.bias,
+                 self.out)
+        if ev:
+            ev[0][1].record()
+        # backward (E5M2): g with its ring, x and w with the forward steps
+        f.fp8_quantize(self.g, E5M2, scale=self.rg.scale, out=self.g8, ring=self.rg,
+                       scale_used=self.sg)
+        f.fp8_quantize(self.w, E5M2, scale=sw, out=self.w8b)
+        if ev:
+            ev[1][0].record()
+        f.fp8_mm(self.g8, self.w8b, E5M2, 0, 0, M, K, N, N, K, 1, 0, 0, self.sg, sw, None,
+                 self.dx)
+        if ev:
+            ev[1][1].record()
+        f.fp8_quantize(self.x, E5M2, scale=sx, out=self.x8b)
+        if ev:
+            ev[2][0].record()
+        f.fp8_mm(self.g8, self.x8b, E5M2, 1, 0, N, K, M, N, K, 1, 0, 0, self.sg, sx, None,
+                 self.dw)
+        if ev:
+            ev[2][1].record()
+        f.fp8_colsum(self.g, M, N, self.db, self.cs_ws)
+        for r in (self.rx, self.rw, self.rg):
+            r.idx = (r.idx + 1) % r.len
+
+
+def check_against_linear_entry_points(f, torch):
+    """The benchmark step and fp8_linear_fwd / _bwd give identical bits."""
+    ref = Layer(f, torch, 256, seed0=900)
+    ref.seed(f)
+    ref.step(f)
+    rx, rw, rg = f.Ring(16), f.Ring(16), f.Ring(16)
+    m = 256
+    fws = torch.zeros(f.fp8_linear_fwd_workspace(m, m, m), dtype=torch.uint8, device="cuda")
+    bws = torch.zeros(f.fp8_linear_bwd_workspace(m, m, m), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(2, dtype=torch.float32, device="cuda")
+    out = torch.empty(m * m, dtype=torch.int16, device="cuda")
+    dx, dw = torch.empty_like(out), torch.empty_like(out)
+    db = torch.empty(m, dtype=torch.int16, device="cuda")
+    f.fp8_linear_fwd(ref.x, ref.w, ref.bias, m, m, m, E4M3, False, 0, rx, rw, fws, sc, out)
+    f.fp8_linear_bwd(ref.g, ref.x, ref.w, m, m, m, E5M2, False, 0, sc, rg, bws, None, dx, dw, db)
+    torch.cuda.synchronize()
+    for a, b in ((out, ref.out), (dx, ref.dx), (dw, ref.dw), (db, ref.db)):
+        if not torch.equal(a, b):
+            raise SystemExit("benchmark step differs from fp8_linear_fwd/bwd")
+
+
+def time_kernel(torch, launch, n, rotate=1):
+    """Average duration (ms) of `launch(i)` over n launches, HIP events."""
+    for i in range(3):
+        launch(i % rotate)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        launch(i % rotate)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def components(f, torch):
+    """Per-kernel figures for the parts of the metric (HBM-cold operands)."""
+    import workloads as wl
+    res = {}
+    dev = "cuda"
+    # 4096^3 NT GEMM + bias, pre-quantized E4M3
+    n = 4096
+    a8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+    b8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+    s = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
+    bias = torch.zeros(n, dtype=torch.int16, device=dev)
+    out = torch.empty(n * n, dtype=torch.int16, device=dev)
+    ms = time_kernel(torch, lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s,
+                                                bias, out), 50)
+    res["gemm_nt_4096"] = dict(us=round(ms * 1e3, 2),
+                               tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
+    del a8, b8, out
+    # 64 x 8192 x 2048 NT, weight rotated over 32 copies (537 MB)
+    M, N, K = 64, 8192, 2048
+    d = wl.smallm()
+    rot = 32
+    xs = torch.randint(0, 120, (M * K,), dtype=torch.uint8, device=dev)
+    ws = [torch.randint(0, 120, (N * K,), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    outs = [torch.empty(M * N, dtype=torch.int16, device=dev) for _ in range(rot)]
+    ms = time_kernel(torch, lambda i: f.fp8_mm(xs, ws[i], E4M3, 0, 1, M, N, K, K, K, 1, 0, 0, s,
+                                                s, None, outs[i]), 64, rotate=rot)
+    byts = M * K + N * K + 2 * M * N
+    res["gemm_nt_64x8192x2048"] = dict(us=round(ms * 1e3, 2),
+                                       tflops=round(2 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                                       gbs=round(byts / (ms * 1e-3) / 1e9, 1),
+                                       hbm_frac=round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+    del ws, outs, d
+    # delayed-scaling quantize of bf16 [8192, 8192] (fold on), 3 buffer sets
+    n = 8192 * 8192
+    rot = 3
+    xs = [torch.randn(n, device=dev).to(torch.bfloat16).view(torch.int16) for _ in range(rot)]
+    qs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(rot)]
+    rings = [f.Ring(16) for _ in range(rot)]
+    for i in range(rot):
+        f.fp8_quantize(xs[i], E4M3, ring=rings[i])
+    ms = time_kernel(torch, lambda i: f.fp8_quantize(xs[i], E4M3, scale=rings[i].scale,
+                                                      out=qs[i], ring=rings[i]), 30, rotate=rot)
+    res["quantize_8192x8192"] = dict(us=round(ms * 1e3, 2),
+                                     gbs=round(3 * n / (ms * 1e-3) / 1e9, 1),
+                                     hbm_frac=round(3 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+    return res
+
+
+def cpu_baseline(size):
+    """The CPU oracle timed on a bounded sample of the step: every quantize
+    of the step on a 256-row slice and the three GEMMs on 32 output rows
+    each, scaled to the whole step."""
+    import workloads as wl
+    from oracle import oracle as orc
+    M = N = K = size
+    rows = 256
+    grow = 32
+    x = wl.normal_bf16((rows, K), 1.0, 601)
+    w = wl.normal_bf16((N, K), 0.02, 602)
+    g = wl.normal_bf16((rows, N), 1e-3, 604)
+    t0 = time.perf_counter()
+    x8 = orc.quantize(x, E4M3, 0.01)
+    w8s = orc.quantize(w[:rows], E4M3, 1e-4)
+    orc.quantize(g, E5M2, 1e-7)
+    orc.quantize(w[:rows], E5M2, 1e-4)
+    orc.quantize(x, E5M2, 0.01)
+    orc.colsum(g, rows, N)
+    tq = time.perf_counter() - t0
+    w8 = orc.quantize(w, E4M3, 1e-4)
+    t0 = time.perf_counter()
+    orc.gemm(x8[:grow], w8, E4M3, False, True, grow, N, K, 0.01, 1e-4, None)
+    tg = time.perf_counter() - t0
+    del w8s
+    # scale: quantizes and colsum touch 5 tensors of M*K-ish elements + g for
+    # colsum; each GEMM of the step has M (= N) output rows
+    t_step = tq * (M / rows) + 3 * tg * (M / grow)
+    flops = 3 * 2.0 * M * N * K
+    return dict(value=round(flops / t_step / 1e12, 6), unit="TFLOP/s",
+                cores=int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()),
+                kind="oracle",
+                sample=(f"oracle quantize x5 + colsum on {rows} of {M} rows and the NT GEMM "
+                        f"on {grow} of {M} output rows (K={K}, N={N}), scaled to the full "
+                        f"step (3 GEMMs); measured {tq + tg:.1f} s, projected step "
+                        f"{t_step:.1f} s"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import fp8_tensor_scaled_amd as f
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    size = args.size
+    layer = Layer(f, torch, size)
+    check_against_linear_entry_points(f, torch)
+    layer.seed(f)
+    for _ in range(args.warmup):
+        layer.step(f)
+    torch.cuda.synchronize()
+    names = ["gemm_nt_fwd", "gemm_nn_dx", "gemm_tn_dw"]
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.step(f, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gemm_flops = 2.0 * size ** 3
+    kern = {}
+    for j, nm in enumerate(names):
+        dur = float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+        kern[nm] = dict(us=round(dur * 1e3, 2), tflops=round(gemm_flops / (dur * 1e-3) / 1e12, 1))
+    dom = max(names, key=lambda k: kern[k]["us"])
+    achieved = kern[dom]["tflops"]
+    value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": "FP8 GEMM TFLOP/s @4096^3 & 64x8192x2048 (E4M3, bf16 out); quantize GB/s",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (e4m3 fwd / e5m2 bwd) x fp8 -> fp32 acc -> bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"fp8 linear layer fwd+bwd, M=N=K={size}, delayed scaling "
+                                "(history 16), HYBRID e4m3/e5m2, bias; value = 3 GEMM flops / "
+                                "step time"),
+                   "M": size, "N": size, "K": size},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None},
+        "kernels": kern,
+    }
+    if not args.no_components:
+        line["components"] = components(f, torch)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(size)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

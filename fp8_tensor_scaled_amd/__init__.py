@@ -1,0 +1,223 @@
+"""Python binding of libfp8lin.so, the gfx950 FP8 linear layer.
+
+Argument marshalling only: every function below passes device pointers,
+sizes and the current HIP stream to the C entry point of the same name
+(declared in include/fp8lin.h) and turns a non-OK status into an exception.
+All arithmetic runs in the library's HIP kernels; there is no fallback.
+torch is used for device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "FMT_MAX", "Ring", "library_path", "fp8_quantize",
+    "fp8_scale_ring_finalize", "fp8_mm", "fp8_colsum", "fp8_colsum_workspace",
+    "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
+    "fp8_linear_bwd_workspace", "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset",
+    "EXPORTED_SYMBOLS",
+]
+
+E4M3 = 0
+E5M2 = 1
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
+
+EXPORTED_SYMBOLS = (
+    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_scale_ring_finalize",
+    "fp8_mm", "fp8_colsum_workspace", "fp8_colsum", "fp8_linear_fwd_workspace",
+    "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
+    "fp8_linear_bwd_workspace", "fp8_linear_bwd", "fp8_last_error", "fp8_version",
+)
+
+
+class _RingC(ctypes.Structure):
+    _fields_ = [("state", ctypes.c_void_p), ("len", ctypes.c_int32), ("idx", ctypes.c_int32),
+                ("initialized", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m fp8_tensor_scaled_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F, S = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                         ctypes.c_size_t)
+    R = ctypes.POINTER(_RingC)
+    sig = {
+        "fp8_ring_state_floats": (I64, [I32]),
+        "fp8_format_max": (F, [I32]),
+        "fp8_quantize": (I32, [P, I64, I32, P, P, R, I32, P, P]),
+        "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
+        "fp8_mm": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P,
+                         P, P]),
+        "fp8_colsum_workspace": (S, [I64, I64]),
+        "fp8_colsum": (I32, [P, I64, I64, P, P, S, P]),
+        "fp8_linear_fwd_workspace": (S, [I64, I64, I64]),
+        "fp8_linear_fwd_x8_offset": (S, [I64, I64, I64]),
+        "fp8_linear_fwd_w8_offset": (S, [I64, I64, I64]),
+        "fp8_linear_fwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, R, R, P, S, P, P, P]),
+        "fp8_linear_bwd_workspace": (S, [I64, I64, I64]),
+        "fp8_linear_bwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, P, R, P, S, P, P, P, P,
+                                 P]),
+        "fp8_last_error": (ctypes.c_char_p, []),
+        "fp8_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int, what: str) -> None:
+    if status == 0:
+        return
+    msg = _lib.fp8_last_error().decode(errors="replace")
+    if status == 1:
+        raise ValueError(f"{what}: {msg}")
+    raise RuntimeError(f"{what} failed (status {status}): {msg}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    """HIP stream handle: torch's current stream by default, an int handle
+    as given (0 = the null stream), or a torch.cuda.Stream."""
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Ring:
+    """Delayed-scaling state of one operand: the device buffer
+    [hist len | scale | legacy | amax | done] (zero-filled) and the host-side
+    slot index / initialized flag the linear calls maintain."""
+
+    def __init__(self, length: int = 16, device="cuda"):
+        n = int(_lib.fp8_ring_state_floats(length))
+        if n <= 0:
+            raise ValueError(f"bad ring length {length}")
+        self.state = torch.zeros(n, dtype=torch.float32, device=device)
+        self.c = _RingC(self.state.data_ptr(), length, 0, 0, 0)
+
+    @property
+    def len(self) -> int:
+        return self.c.len
+
+    @property
+    def idx(self) -> int:
+        return self.c.idx
+
+    @idx.setter
+    def idx(self, v: int) -> None:
+        self.c.idx = int(v)
+
+    @property
+    def initialized(self) -> bool:
+        return bool(self.c.initialized)
+
+    @initialized.setter
+    def initialized(self, v: bool) -> None:
+        self.c.initialized = int(bool(v))
+
+    @property
+    def hist(self) -> torch.Tensor:
+        return self.state[: self.len]
+
+    @property
+    def scale(self) -> torch.Tensor:
+        return self.state[self.len: self.len + 1]
+
+
+def _ring_ref(r: Ring | None):
+    return None if r is None else ctypes.byref(r.c)
+
+
+def fp8_quantize(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, ring: Ring | None = None, margin: int = 0,
+                 scale_used: torch.Tensor | None = None, stream=None) -> None:
+    """bf16 x -> fp8 codes in ``out`` (uint8, same numel); see fp8lin.h."""
+    st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
+                           margin, _ptr(scale_used), _stream(stream))
+    _check(st, "fp8_quantize")
+
+
+def fp8_scale_ring_finalize(ring: Ring, fmt: int, amax: torch.Tensor, margin: int = 0,
+                            stream=None) -> None:
+    st = _lib.fp8_scale_ring_finalize(_ring_ref(ring), fmt, _ptr(amax), margin, _stream(stream))
+    _check(st, "fp8_scale_ring_finalize")
+
+
+def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt: int, trans_a: int, trans_b: int, m: int,
+           n: int, k: int, lda: int, ldb: int, batch: int, stride_a: int, stride_b: int,
+           scale_a: torch.Tensor, scale_b: torch.Tensor, bias: torch.Tensor | None,
+           out: torch.Tensor, stream=None) -> None:
+    st = _lib.fp8_mm(_ptr(a), _ptr(b), fmt, trans_a, trans_b, m, n, k, lda, ldb, batch,
+                     stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias), _ptr(out),
+                     _stream(stream))
+    _check(st, "fp8_mm")
+
+
+def fp8_colsum_workspace(m: int, n: int) -> int:
+    return int(_lib.fp8_colsum_workspace(m, n))
+
+
+def fp8_colsum(g: torch.Tensor, m: int, n: int, db: torch.Tensor, workspace: torch.Tensor,
+               stream=None) -> None:
+    st = _lib.fp8_colsum(_ptr(g), m, n, _ptr(db), _ptr(workspace), workspace.numel(),
+                         _stream(stream))
+    _check(st, "fp8_colsum")
+
+
+def fp8_linear_fwd_workspace(M: int, N: int, K: int) -> int:
+    return int(_lib.fp8_linear_fwd_workspace(M, N, K))
+
+
+def fp8_linear_fwd_x8_offset(M: int, N: int, K: int) -> int:
+    return int(_lib.fp8_linear_fwd_x8_offset(M, N, K))
+
+
+def fp8_linear_fwd_w8_offset(M: int, N: int, K: int) -> int:
+    return int(_lib.fp8_linear_fwd_w8_offset(M, N, K))
+
+
+def fp8_linear_bwd_workspace(M: int, N: int, K: int) -> int:
+    return int(_lib.fp8_linear_bwd_workspace(M, N, K))
+
+
+def fp8_linear_fwd(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x: Ring | None,
+                   ring_w: Ring | None, workspace: torch.Tensor, scales_out: torch.Tensor,
+                   out: torch.Tensor, stream=None) -> None:
+    st = _lib.fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, fmt, int(dynamic), margin,
+                             _ring_ref(ring_x), _ring_ref(ring_w), _ptr(workspace),
+                             workspace.numel(), _ptr(scales_out), _ptr(out), _stream(stream))
+    _check(st, "fp8_linear_fwd")
+
+
+def fp8_linear_bwd(g, x, w, M, N, K, fmt, dynamic, margin, scales_fwd, ring_g: Ring | None,
+                   workspace: torch.Tensor, scales_out, dx, dw, db, stream=None) -> None:
+    st = _lib.fp8_linear_bwd(_ptr(g), _ptr(x), _ptr(w), M, N, K, fmt, int(dynamic), margin,
+                             _ptr(scales_fwd), _ring_ref(ring_g), _ptr(workspace),
+                             workspace.numel(), _ptr(scales_out), _ptr(dx), _ptr(dw), _ptr(db),
+                             _stream(stream))
+    _check(st, "fp8_linear_bwd")

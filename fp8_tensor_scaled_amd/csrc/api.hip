@@ -1,0 +1,459 @@
+// C ABI of the fp8 linear layer: argument validation, workspace layout and
+// the linear-layer orchestration.  Declarations and contracts: fp8lin.h.
+//
+// Orchestration follows AstrAI compare view 3e57cc8...main,
+// astrai/extension/fp8.py: fp8_linear_forward (seed the rings on first use,
+// snapshot the scales, quantize with the in-kernel fold, GEMM with the
+// snapshots, advance) and _LinearFp8.backward (the gradient ring likewise,
+// forward scales reused, operands re-quantized in the backward format).
+// Unlike the pages' current backward, which transposes the operands while
+// quantizing and runs NT products, dX and dW run directly as NN and TN
+// products (the layouts of the pages' removed fused backward binding).
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fp8lin.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp8_status_t fail(fp8_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fp8_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(FP8_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// gfx950 check, cached per device.
+fp8_status_t check_device() {
+    static int cached[64];  // 0 unknown, 1 ok, 2 unsupported
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev >= 0 && dev < 64 && cached[dev] == 1) return FP8_OK;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) cached[dev] = ok ? 1 : 2;
+    if (!ok)
+        return fail(FP8_EUNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                    dev, prop.gcnArchName);
+    return FP8_OK;
+}
+
+bool fmt_ok(fp8_fmt_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+
+fp8_status_t check_ring(const fp8_ring_t* r, const char* name) {
+    if (!r) return fail(FP8_EINVAL, "%s: ring is NULL", name);
+    if (!r->state) return fail(FP8_EINVAL, "%s: ring state is NULL", name);
+    if (r->len < 1 || r->len > 4096)
+        return fail(FP8_EINVAL, "%s: ring len %d outside [1, 4096]", name, r->len);
+    if (r->idx < 0 || r->idx >= r->len)
+        return fail(FP8_EINVAL, "%s: ring idx %d outside [0, %d)", name, r->idx, r->len);
+    return FP8_OK;
+}
+
+float pow2f(int32_t margin) { return ldexpf(1.0f, margin); }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace layouts.  Control block (256 B, zero-once, self-cleaning):
+// three length-1 scratch rings of 5 floats each, at float offsets 0, 8, 16.
+constexpr size_t kCtrl = 256;
+constexpr int kScratchRingLen = 1;
+float* scratch_ring(void* ws, int i) { return static_cast<float*>(ws) + 8 * i; }
+
+struct FwdLayout {
+    size_t x8, w8, total;
+};
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K) {
+    FwdLayout l;
+    l.x8 = kCtrl;
+    l.w8 = align256(l.x8 + (size_t)M * K);
+    l.total = align256(l.w8 + (size_t)N * K);
+    return l;
+}
+
+struct BwdLayout {
+    size_t g8, x8, w8, colsum, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
+    BwdLayout l;
+    l.g8 = kCtrl;
+    l.x8 = align256(l.g8 + (size_t)M * N);
+    l.w8 = align256(l.x8 + (size_t)M * K);
+    l.colsum = align256(l.w8 + (size_t)N * K);
+    l.total = align256(l.colsum + fp8lin::colsum_workspace(M, N));
+    return l;
+}
+
+fp8_status_t do_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+                         uint8_t* out, float* ring_state, int32_t len, int32_t idx,
+                         int32_t margin, float* scale_used, hipStream_t stream) {
+    fp8lin::QuantLaunch q;
+    q.x = x;
+    q.numel = numel;
+    q.fmt = fmt;
+    q.scale = scale;
+    q.out = out;
+    q.ring_state = ring_state;
+    q.ring_len = len;
+    q.ring_idx = idx;
+    q.pow2_margin = pow2f(margin);
+    q.scale_used = scale_used;
+    hipError_t e = fp8lin::launch_quantize(q, stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return FP8_OK;
+}
+
+fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, int tb,
+                     int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
+                     const float* sa, const float* sb, const uint16_t* bias, uint16_t* out,
+                     hipStream_t stream) {
+    fp8lin::GemmLaunch g;
+    g.a = a;
+    g.b = b;
+    g.fmt = fmt;
+    g.trans_a = ta;
+    g.trans_b = tb;
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.batch = 1;
+    g.scale_a = sa;
+    g.scale_b = sb;
+    g.bias = bias;
+    g.out = out;
+    hipError_t e = fp8lin::launch_gemm(g, stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fp8_ring_state_floats(int32_t len) { return len < 1 ? 0 : (int64_t)len + 4; }
+
+float fp8_format_max(fp8_fmt_t fmt) {
+    return fmt == FP8_E4M3 ? 448.0f : fmt == FP8_E5M2 ? 57344.0f : 0.0f;
+}
+
+const char* fp8_last_error(void) { return g_err; }
+
+const char* fp8_version(void) { return "fp8lin 0.1 (gfx950)"; }
+
+fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+                          uint8_t* out, const fp8_ring_t* ring, int32_t margin,
+                          float* scale_used, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_quantize: unsupported fp8 format %d", fmt);
+    if (numel < 0) return fail(FP8_EINVAL, "fp8_quantize: numel %lld < 0", (long long)numel);
+    if (numel > 0 && !x) return fail(FP8_EINVAL, "fp8_quantize: x is NULL");
+    if (numel == 0 && !ring) return FP8_OK;  // nothing to convert, nothing to fold
+    if (!out && !ring) return fail(FP8_EINVAL, "fp8_quantize: neither out nor ring given");
+    if (out && !scale) return fail(FP8_EINVAL, "fp8_quantize: scale is NULL");
+    if (ring) {
+        fp8_status_t st = check_ring(ring, "fp8_quantize");
+        if (st) return st;
+    }
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_quantize: margin %d outside [0, 64]", margin);
+    if (!out && scale_used)
+        return fail(FP8_EINVAL, "fp8_quantize: scale_used needs a quantizing call");
+    fp8_status_t st = check_device();
+    if (st) return st;
+    return do_quantize(x, numel, fmt, out ? scale : nullptr, out, ring ? ring->state : nullptr,
+                       ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, stream);
+}
+
+fp8_status_t fp8_scale_ring_finalize(const fp8_ring_t* ring, fp8_fmt_t fmt, const float* amax,
+                                     int32_t margin, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt))
+        return fail(FP8_EINVAL, "fp8_scale_ring_finalize: unsupported fp8 format %d", fmt);
+    fp8_status_t st = check_ring(ring, "fp8_scale_ring_finalize");
+    if (st) return st;
+    if (!amax) return fail(FP8_EINVAL, "fp8_scale_ring_finalize: amax is NULL");
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_scale_ring_finalize: margin %d outside [0, 64]", margin);
+    st = check_device();
+    if (st) return st;
+    hipError_t e = fp8lin::launch_ring_finalize(ring->state, ring->len, ring->idx, fmt,
+                                                pow2f(margin), amax, stream);
+    if (e != hipSuccess) return hip_fail(e, "ring finalize launch");
+    return FP8_OK;
+}
+
+fp8_status_t fp8_mm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t trans_a,
+                    int32_t trans_b, int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
+                    int64_t batch, int64_t stride_a, int64_t stride_b, const float* scale_a,
+                    const float* scale_b, const uint16_t* bias, uint16_t* out,
+                    hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_mm: unsupported fp8 format %d", fmt);
+    if (!a || !b || !out || !scale_a || !scale_b)
+        return fail(FP8_EINVAL, "fp8_mm: NULL operand, output or scale");
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return fail(FP8_EINVAL, "fp8_mm: trans flags must be 0 or 1");
+    if (m < 1 || n < 1 || k < 1)
+        return fail(FP8_EINVAL, "fp8_mm: m, n, k must be >= 1 (got %lld, %lld, %lld)",
+                    (long long)m, (long long)n, (long long)k);
+    if (batch < 1 || batch > 65535)
+        return fail(FP8_EINVAL, "fp8_mm: batch %lld outside [1, 65535]", (long long)batch);
+    const int64_t a_cols = trans_a ? m : k, b_cols = trans_b ? k : n;
+    if (lda < a_cols)
+        return fail(FP8_EINVAL, "fp8_mm: lda %lld < %lld", (long long)lda, (long long)a_cols);
+    if (ldb < b_cols)
+        return fail(FP8_EINVAL, "fp8_mm: ldb %lld < %lld", (long long)ldb, (long long)b_cols);
+    if (batch > 1 && (stride_a < 0 || stride_b < 0))
+        return fail(FP8_EINVAL, "fp8_mm: negative batch stride");
+    if ((double)m * (double)n * (double)batch >= 1099511627776.0)
+        return fail(FP8_EINVAL, "fp8_mm: output too large");
+    fp8_status_t st = check_device();
+    if (st) return st;
+    fp8lin::GemmLaunch g;
+    g.a = a;
+    g.b = b;
+    g.fmt = fmt;
+    g.trans_a = trans_a;
+    g.trans_b = trans_b;
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.batch = batch;
+    g.stride_a = stride_a;
+    g.stride_b = stride_b;
+    g.scale_a = scale_a;
+    g.scale_b = scale_b;
+    g.bias = bias;
+    g.out = out;
+    hipError_t e = fp8lin::launch_gemm(g, stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return FP8_OK;
+}
+
+size_t fp8_colsum_workspace(int64_t m, int64_t n) {
+    if (m < 1 || n < 1) return 0;
+    return fp8lin::colsum_workspace(m, n);
+}
+
+fp8_status_t fp8_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!g || !db || !workspace) return fail(FP8_EINVAL, "fp8_colsum: NULL pointer");
+    if (m < 1 || n < 1) return fail(FP8_EINVAL, "fp8_colsum: m, n must be >= 1");
+    if (workspace_bytes < fp8lin::colsum_workspace(m, n))
+        return fail(FP8_EINVAL, "fp8_colsum: workspace %zu < %zu bytes", workspace_bytes,
+                    fp8lin::colsum_workspace(m, n));
+    fp8_status_t st = check_device();
+    if (st) return st;
+    hipError_t e = fp8lin::launch_colsum(g, m, n, db, workspace, stream);
+    if (e != hipSuccess) return hip_fail(e, "colsum launch");
+    return FP8_OK;
+}
+
+size_t fp8_linear_fwd_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return fwd_layout(M, N, K).total;
+}
+size_t fp8_linear_fwd_x8_offset(int64_t M, int64_t N, int64_t K) {
+    return fwd_layout(M, N, K).x8;
+}
+size_t fp8_linear_fwd_w8_offset(int64_t M, int64_t N, int64_t K) {
+    return fwd_layout(M, N, K).w8;
+}
+
+fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t* bias,
+                            int64_t M, int64_t N, int64_t K, fp8_fmt_t fmt, int32_t dynamic,
+                            int32_t margin, fp8_ring_t* ring_x, fp8_ring_t* ring_w,
+                            void* workspace, size_t workspace_bytes, float* scales_out,
+                            uint16_t* out, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_linear_fwd: unsupported fp8 format %d", fmt);
+    if (!x || !w || !out || !workspace || !scales_out)
+        return fail(FP8_EINVAL, "fp8_linear_fwd: NULL pointer argument");
+    if (M < 1 || N < 1 || K < 1) return fail(FP8_EINVAL, "fp8_linear_fwd: M, N, K must be >= 1");
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_linear_fwd: margin %d outside [0, 64]", margin);
+    if (!dynamic) {
+        fp8_status_t st = check_ring(ring_x, "fp8_linear_fwd ring_x");
+        if (st) return st;
+        st = check_ring(ring_w, "fp8_linear_fwd ring_w");
+        if (st) return st;
+        if (ring_x->state == ring_w->state)
+            return fail(FP8_EINVAL, "fp8_linear_fwd: ring_x and ring_w share a state buffer");
+    }
+    const FwdLayout L = fwd_layout(M, N, K);
+    if (workspace_bytes < L.total)
+        return fail(FP8_EINVAL, "fp8_linear_fwd: workspace %zu < %zu bytes", workspace_bytes,
+                    L.total);
+    fp8_status_t st = check_device();
+    if (st) return st;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* x8 = ws + L.x8;
+    uint8_t* w8 = ws + L.w8;
+    float* sx = scales_out;
+    float* sw = scales_out + 1;
+    if (dynamic) {
+        // Current-amax scaling: measure into a length-1 scratch ring, then
+        // quantize with the scale it published.
+        float* rx = scratch_ring(workspace, 0);
+        float* rw = scratch_ring(workspace, 1);
+        if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0, margin,
+                              nullptr, stream)))
+            return st;
+        if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0, margin,
+                              nullptr, stream)))
+            return st;
+        if ((st = do_quantize(x, M * K, fmt, rx + kScratchRingLen, x8, nullptr, 0, 0, margin, sx,
+                              stream)))
+            return st;
+        if ((st = do_quantize(w, N * K, fmt, rw + kScratchRingLen, w8, nullptr, 0, 0, margin, sw,
+                              stream)))
+            return st;
+    } else {
+        if (!ring_w->initialized) {
+            if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, ring_w->state, ring_w->len,
+                                  ring_w->idx, margin, nullptr, stream)))
+                return st;
+            ring_w->initialized = 1;
+        }
+        if (!ring_x->initialized) {
+            if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, ring_x->state, ring_x->len,
+                                  ring_x->idx, margin, nullptr, stream)))
+                return st;
+            ring_x->initialized = 1;
+        }
+        // Each quantize reads the ring's published step (its snapshot goes
+        // to scales_out) before its own last workgroup folds the new amax.
+        if ((st = do_quantize(x, M * K, fmt, ring_x->state + ring_x->len, x8, ring_x->state,
+                              ring_x->len, ring_x->idx, margin, sx, stream)))
+            return st;
+        if ((st = do_quantize(w, N * K, fmt, ring_w->state + ring_w->len, w8, ring_w->state,
+                              ring_w->len, ring_w->idx, margin, sw, stream)))
+            return st;
+    }
+    if ((st = do_gemm(x8, w8, fmt, 0, 1, M, N, K, K, K, sx, sw, bias, out, stream))) return st;
+    if (!dynamic) {
+        ring_x->idx = (ring_x->idx + 1) % ring_x->len;
+        ring_w->idx = (ring_w->idx + 1) % ring_w->len;
+    }
+    return FP8_OK;
+}
+
+size_t fp8_linear_bwd_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return bwd_layout(M, N, K).total;
+}
+
+fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t* w, int64_t M,
+                            int64_t N, int64_t K, fp8_fmt_t fmt, int32_t dynamic,
+                            int32_t margin, const float* scales_fwd, fp8_ring_t* ring_g,
+                            void* workspace, size_t workspace_bytes, float* scales_out,
+                            uint16_t* dx, uint16_t* dw, uint16_t* db, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_linear_bwd: unsupported fp8 format %d", fmt);
+    if (!g || !workspace) return fail(FP8_EINVAL, "fp8_linear_bwd: NULL g or workspace");
+    if (dx && !w) return fail(FP8_EINVAL, "fp8_linear_bwd: dx needs w");
+    if (dw && !x) return fail(FP8_EINVAL, "fp8_linear_bwd: dw needs x");
+    if (M < 1 || N < 1 || K < 1) return fail(FP8_EINVAL, "fp8_linear_bwd: M, N, K must be >= 1");
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_linear_bwd: margin %d outside [0, 64]", margin);
+    if (!dynamic) {
+        if (!scales_fwd)
+            return fail(FP8_EINVAL, "fp8_linear_bwd: delayed scaling needs scales_fwd");
+        fp8_status_t st = check_ring(ring_g, "fp8_linear_bwd ring_g");
+        if (st) return st;
+    }
+    const BwdLayout L = bwd_layout(M, N, K);
+    if (workspace_bytes < L.total)
+        return fail(FP8_EINVAL, "fp8_linear_bwd: workspace %zu < %zu bytes", workspace_bytes,
+                    L.total);
+    fp8_status_t st = check_device();
+    if (st) return st;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* g8 = ws + L.g8;
+    uint8_t* x8 = ws + L.x8;
+    uint8_t* w8 = ws + L.w8;
+    // Scales used: in scales_out when given, else in the control block.
+    float* sc = scales_out ? scales_out : scratch_ring(workspace, 3);
+    float* sg = sc;
+    const float* sx;
+    const float* sw;
+    if (dynamic) {
+        float* rg = scratch_ring(workspace, 0);
+        float* rx = scratch_ring(workspace, 1);
+        float* rw = scratch_ring(workspace, 2);
+        if ((st = do_quantize(g, M * N, fmt, nullptr, nullptr, rg, kScratchRingLen, 0, margin,
+                              nullptr, stream)))
+            return st;
+        if ((st = do_quantize(g, M * N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0, margin, sg,
+                              stream)))
+            return st;
+        if (dw) {
+            if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0,
+                                  margin, nullptr, stream)))
+                return st;
+        }
+        if (dx) {
+            if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0,
+                                  margin, nullptr, stream)))
+                return st;
+        }
+        sx = rx + kScratchRingLen;
+        sw = rw + kScratchRingLen;
+    } else {
+        if (!ring_g->initialized) {
+            if ((st = do_quantize(g, M * N, fmt, nullptr, nullptr, ring_g->state, ring_g->len,
+                                  ring_g->idx, margin, nullptr, stream)))
+                return st;
+            ring_g->initialized = 1;
+        }
+        if ((st = do_quantize(g, M * N, fmt, ring_g->state + ring_g->len, g8, ring_g->state,
+                              ring_g->len, ring_g->idx, margin, sg, stream)))
+            return st;
+        sx = scales_fwd;
+        sw = scales_fwd + 1;
+    }
+    if (dx) {
+        if ((st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
+                              scales_out ? scales_out + 2 : nullptr, stream)))
+            return st;
+        // dX[M][K] = g8[M][N] . w8[N][K]  (NN)
+        if ((st = do_gemm(g8, w8, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx, stream)))
+            return st;
+    }
+    if (dw) {
+        if ((st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
+                              scales_out ? scales_out + 1 : nullptr, stream)))
+            return st;
+        // dW[N][K] = g8^T . x8: A = g8 stored [M][N] (k-major rows of m), B = x8 [M][K]  (TN)
+        if ((st = do_gemm(g8, x8, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw, stream)))
+            return st;
+    }
+    if (db) {
+        hipError_t e = fp8lin::launch_colsum(g, M, N, db, ws + L.colsum, stream);
+        if (e != hipSuccess) return hip_fail(e, "colsum launch");
+    }
+    if (!dynamic) ring_g->idx = (ring_g->idx + 1) % ring_g->len;
+    return FP8_OK;
+}
+
+}  // extern "C"

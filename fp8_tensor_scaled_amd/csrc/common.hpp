@@ -1,0 +1,91 @@
+// Device helpers shared by the fp8 linear-layer kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// Largest finite value of each OCP format.
+template <int FMT>
+__device__ __forceinline__ constexpr float fmt_max() {
+    return FMT ? 57344.0f : 448.0f;
+}
+
+// bf16 bit pattern -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Saturating clamp to +-max that keeps NaN, so the hardware conversion that
+// follows rounds to nearest even within range and never overflows.
+template <int FMT>
+__device__ __forceinline__ float sat(float v) {
+    const float c = __builtin_amdgcn_fmed3f(v, -fmt_max<FMT>(), fmt_max<FMT>());
+    return v != v ? v : c;
+}
+
+// Four fp32 -> four fp8 codes packed little-endian in one dword.
+// v_cvt_pk_{fp8,bf8}_f32 round to nearest even on gfx950 (OCP encodings).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    int w;
+    if constexpr (FMT) {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<FMT>(a), sat<FMT>(b), 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<FMT>(c), sat<FMT>(d), w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(sat<FMT>(a), sat<FMT>(b), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(sat<FMT>(c), sat<FMT>(d), w, true);
+    }
+    return (uint32_t)w;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint8_t cvt1(float a) {
+    int w;
+    if constexpr (FMT)
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<FMT>(a), 0.0f, 0, false);
+    else
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(sat<FMT>(a), 0.0f, 0, false);
+    return (uint8_t)(w & 0xff);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// One fp8 MFMA: D(16x16, fp32) += X(16x128) . Y(16x128)^T.
+// Lane l holds row l%16 of X and of Y, bytes k = 32*(l/16) .. +31; the
+// result row 4*(l/16)+i, column l%16 sits in register i.
+template <int FMT>
+__device__ __forceinline__ v4f mfma16x16x128(const v8i& x, const v8i& y, v4f acc) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc, FMT, FMT, 0, 0, 0, 0);
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,111 @@
+// Scaled fp8 GEMM: out = bf16(acc * fp32(sa*sb) + bias), fp32 accumulation.
+//
+// Method (AstrAI compare view 3e57cc8...main: astrai/extension/ops/fp8.py
+// mm_fp8; csrc/kernels/fp8/common.h operand layout tags and batch strides;
+// csrc/kernels/fp8/gemm/epilogue.cuh bias + single bf16 rounding).
+//
+// This file holds the dispatcher and the general kernel, which accepts any
+// layout, size, stride and alignment: every lane gathers its MFMA operand
+// bytes one by one (zero outside the matrix) and each wave owns a 16x16
+// output tile.  It is the correctness fallback for shapes the tiled kernels
+// do not take; the tiled kernels live in gemm_tiled.hip.
+
+#include "common.hpp"
+#include "gemm_tiled.hpp"
+#include "internal.hpp"
+
+namespace fp8lin {
+
+struct GenericParams {
+    const uint8_t* a;
+    const uint8_t* b;
+    const float* sa;
+    const float* sb;
+    const uint16_t* bias;
+    uint16_t* out;
+    int64_t m, n, k, lda, ldb;
+    int64_t stride_a, stride_b;
+    int trans_a, trans_b;
+};
+
+constexpr int kGenThreads = 256;  // 4 waves, 2x2 grid of 16x16 tiles
+
+template <int FMT>
+__global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GenericParams p) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int64_t bz = blockIdx.z;
+    const int64_t col0 = (int64_t)blockIdx.x * 32 + (wave % 2) * 16;
+    const uint8_t* A = p.a + bz * p.stride_a;
+    const uint8_t* B = p.b + bz * p.stride_b;
+    const float s = (*p.sa) * (*p.sb);
+    const int64_t bc = col0 + lane % 16;  // this lane's column of B
+    const int kq = 32 * (lane / 16);
+    for (int64_t by = blockIdx.y; by * 32 < p.m; by += gridDim.y) {
+    const int64_t row0 = by * 32 + (wave / 2) * 16;
+    const int64_t ar = row0 + lane % 16;  // this lane's row of A
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t k0 = 0; k0 < p.k; k0 += 128) {
+        union {
+            v8i v;
+            uint8_t b[32];
+        } xa, xb;
+#pragma unroll 4
+        for (int j = 0; j < 32; ++j) {
+            const int64_t kk = k0 + kq + j;
+            uint8_t va = 0, vb = 0;
+            if (kk < p.k) {
+                if (ar < p.m) va = p.trans_a ? A[kk * p.lda + ar] : A[ar * p.lda + kk];
+                if (bc < p.n) vb = p.trans_b ? B[bc * p.ldb + kk] : B[kk * p.ldb + bc];
+            }
+            xa.b[j] = va;
+            xb.b[j] = vb;
+        }
+        acc = mfma16x16x128<FMT>(xa.v, xb.v, acc);
+    }
+    const int64_t oc = col0 + lane % 16;
+    if (oc < p.n) {
+        const float bias = p.bias ? bf16_to_f32(p.bias[oc]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t orow = row0 + 4 * (lane / 16) + i;
+            if (orow < p.m)
+                p.out[(bz * p.m + orow) * p.n + oc] = f32_to_bf16(fmaf(acc[i], s, bias));
+        }
+    }
+    }
+}
+
+static hipError_t launch_generic(const GemmLaunch& g, hipStream_t stream) {
+    GenericParams p{};
+    p.a = g.a;
+    p.b = g.b;
+    p.sa = g.scale_a;
+    p.sb = g.scale_b;
+    p.bias = g.bias;
+    p.out = g.out;
+    p.m = g.m;
+    p.n = g.n;
+    p.k = g.k;
+    p.lda = g.lda;
+    p.ldb = g.ldb;
+    p.stride_a = g.batch > 1 ? g.stride_a : 0;
+    p.stride_b = g.batch > 1 ? g.stride_b : 0;
+    p.trans_a = g.trans_a;
+    p.trans_b = g.trans_b;
+    const int64_t gy = (g.m + 31) / 32;
+    const dim3 grid((unsigned)((g.n + 31) / 32), (unsigned)(gy < 65535 ? gy : 65535),
+                    (unsigned)g.batch);
+    if (g.fmt == 0)
+        hipLaunchKernelGGL(gemm_generic_kernel<0>, grid, dim3(kGenThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(gemm_generic_kernel<1>, grid, dim3(kGenThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream) {
+    if (gemm_tiled_supported(g)) return launch_gemm_tiled(g, stream);
+    return launch_generic(g, stream);
+}
+
+}  // namespace fp8lin

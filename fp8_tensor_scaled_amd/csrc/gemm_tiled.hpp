@@ -1,0 +1,15 @@
+// LDS-tiled fp8 MFMA GEMM kernels (declarations).
+#pragma once
+
+#include "internal.hpp"
+
+namespace fp8lin {
+
+// True when the tiled kernels take this problem: 16-byte aligned operand
+// bases, leading dimensions and batch strides; k a multiple of 16 for a
+// k-contiguous operand; m (n) a multiple of 16 for an m- (n-) contiguous
+// A (B).  Everything else runs on the general kernel.
+bool gemm_tiled_supported(const GemmLaunch& g);
+hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream);
+
+}  // namespace fp8lin

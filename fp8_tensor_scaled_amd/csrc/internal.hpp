@@ -1,0 +1,48 @@
+// Host-side declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+// Everything a quantize launch needs (plain values, no ownership).
+struct QuantLaunch {
+    const uint16_t* x = nullptr;
+    int64_t numel = 0;
+    int fmt = 0;
+    const float* scale = nullptr;  // step s (device); m = 1/s
+    uint8_t* out = nullptr;        // null: measure only
+    float* ring_state = nullptr;   // null: no fold
+    int32_t ring_len = 0;
+    int32_t ring_idx = 0;
+    float pow2_margin = 1.0f;
+    float* scale_used = nullptr;
+};
+hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
+
+hipError_t launch_ring_finalize(float* state, int32_t len, int32_t idx, int fmt,
+                                float pow2_margin, const float* amax, hipStream_t stream);
+
+// GEMM problem in the C-ABI's terms.
+struct GemmLaunch {
+    const uint8_t* a = nullptr;
+    const uint8_t* b = nullptr;
+    int fmt = 0;
+    int trans_a = 0, trans_b = 0;
+    int64_t m = 0, n = 0, k = 0, lda = 0, ldb = 0;
+    int64_t batch = 1, stride_a = 0, stride_b = 0;
+    const float* scale_a = nullptr;
+    const float* scale_b = nullptr;
+    const uint16_t* bias = nullptr;
+    uint16_t* out = nullptr;
+};
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
+
+// Column sum (bias gradient).
+size_t colsum_workspace(int64_t m, int64_t n);
+hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, void* ws,
+                         hipStream_t stream);
+
+}  // namespace fp8lin

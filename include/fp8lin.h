@@ -1,0 +1,256 @@
+/*
+ * fp8lin.h -- C ABI of the FP8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer has two stages (AstrAI web pages by ViperEkura; "compare view
+ * 3e57cc8...main" is the split diff of the fp8 extension, "author commit
+ * search" the benchmark commit log):
+ *   1. quantize: amax of the raw bf16 values, a per-tensor scale derived
+ *      from it (current amax, or the max over a history ring of previous
+ *      amaxes), and a saturating round-to-nearest-even cast to OCP E4M3 or
+ *      E5M2;
+ *   2. scaled GEMM: fp8 x fp8 with fp32 accumulation in the forward NT,
+ *      the dX NN and the dW TN layouts (plus batched / broadcast operands),
+ *      dequantized by the product of the two steps, with a fused bf16 bias
+ *      and bf16 output; and the bias gradient (column sum of the output
+ *      gradient).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless its comment says
+ *     "host".  bf16 tensors are passed as uint16_t bit patterns, fp8 tensors
+ *     as uint8_t codes; matrices are row-major.
+ *   - A "scale" is the quantization STEP s (dequantization multiplier):
+ *     fp8 code q represents q * s.  A quantize multiplies each element by
+ *     the fp32 reciprocal 1.0f / s.
+ *   - The caller owns all memory and the stream.  No entry point allocates,
+ *     frees, or synchronizes; every call only enqueues kernels on `stream`
+ *     (NULL = the default stream) and returns.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     bad argument returns FP8_EINVAL (or FP8_EUNSUPPORTED for a device
+ *     that is not gfx950) and enqueues nothing; a failed launch returns
+ *     FP8_EHIP.  fp8_last_error() then describes the failure.  Errors that
+ *     only the device could see (a bad device pointer) surface as HIP
+ *     errors on the stream.
+ *   - Calls that share a ring or a workspace must be ordered (same stream,
+ *     or synchronized); the library never locks.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* fp8 formats (compare view: csrc/kernels/fp8/common.h, FP8Format).
+ * E4M3: OCP e4m3fn, no infinities, largest finite 448, NaN S.1111.111.
+ * E5M2: OCP e5m2, largest finite 57344, infinities and NaNs. */
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_fmt_t;
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_EINVAL = 1,      /* bad argument; nothing was enqueued */
+    FP8_EUNSUPPORTED = 2, /* current device is not gfx950 */
+    FP8_EHIP = 3          /* a HIP call or launch failed */
+} fp8_status_t;
+
+/* Delayed-scaling state of one operand (compare view: astrai/extension/
+ * fp8.py, _ScaleRing; csrc/kernels/fp8/quantize.cuh, publish_amax).
+ *
+ * `state` is a device buffer of len + 4 fp32 words:
+ *     [ hist[0..len) | scale | legacy | amax | done ]
+ * hist  : amax history window;
+ * scale : the published step for the next use;
+ * legacy: unused (kept so the buffer layout matches the pages' ring);
+ * amax, done: kernel scratch (running amax as fp32 bits, block counter as
+ *        uint32 bits) that every fold leaves at zero again.
+ * The caller zero-fills `state` once when the ring is created.
+ * `len`, `idx`, `initialized` live on the host: `idx` is the slot the next
+ * fold writes; `initialized` = 0 makes the linear calls seed the ring from
+ * the current tensor before using it.  fp8_quantize and
+ * fp8_scale_ring_finalize read the struct and never change it;
+ * fp8_linear_fwd / fp8_linear_bwd seed (set initialized = 1) and advance
+ * idx = (idx + 1) % len after enqueueing their work. */
+typedef struct fp8_ring {
+    float* state;        /* device, len + 4 floats */
+    int32_t len;         /* history length, 1 <= len <= 4096 */
+    int32_t idx;         /* 0 <= idx < len */
+    int32_t initialized; /* host flag for the linear calls */
+    int32_t reserved;
+} fp8_ring_t;
+
+/* Number of fp32 words of a ring state buffer with history length len. */
+int64_t fp8_ring_state_floats(int32_t len);
+
+/* Largest finite value of a format (448 or 57344); 0 for a bad format. */
+float fp8_format_max(fp8_fmt_t fmt);
+
+/* ---------------------------------------------------------------------
+ * fp8_quantize -- bf16 -> fp8 with fused amax and optional ring fold.
+ * (compare view: quantize.cuh fp8_quantize_kernel and publish_amax;
+ *  astrai/extension/ops/fp8.py quantize)
+ *
+ *   out[i] = encode_fmt( fp32( x[i] * (1.0f / *scale) ) )
+ *
+ * encode_fmt rounds to nearest, ties to even, and saturates: any value
+ * beyond the format's largest finite value (infinity included) becomes
+ * +-max.  NaN inputs produce a NaN code.
+ *
+ * x         : bf16 [numel]; any 2-byte alignment (16-byte alignment of x and
+ *             out takes the vector path).
+ * numel     : >= 0.
+ * scale     : fp32 step s > 0, read once per workgroup before any fold
+ *             publishes; may alias ring->state + ring->len.  Required when
+ *             out != NULL, ignored otherwise.
+ * out       : fp8 [numel], or NULL for a measure-only pass (amax + fold).
+ * ring      : host pointer, nullable.  When set, the launch's last
+ *             workgroup folds amax = max_i |x[i]| over the raw bf16 values
+ *             (NaN skipped; 0 for numel == 0) into hist[ring->idx] and
+ *             publishes scale = max(max(hist) / FMAX / 2^margin, 1e-12f)
+ *             (two IEEE fp32 divisions) into the ring's scale slot.
+ *             A length-1 ring therefore yields dynamic (current-amax)
+ *             scaling: measure-only into it, then quantize with
+ *             scale = ring->state + 1.
+ * margin    : 0 <= margin <= 64, used by the fold only.
+ * scale_used: nullable fp32 [1]; receives *scale as this launch read it
+ *             (the snapshot a later GEMM must dequantize with).
+ * Either out or ring must be non-NULL, except that an empty call
+ * (numel == 0) without a ring does nothing and returns FP8_OK.
+ * ------------------------------------------------------------------- */
+fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt,
+                          const float* scale, uint8_t* out, const fp8_ring_t* ring,
+                          int32_t margin, float* scale_used, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * fp8_scale_ring_finalize -- fold an externally measured amax.
+ * (compare view: publish_amax's last-block step, as a standalone launch)
+ *
+ *   hist[ring->idx] = *amax;
+ *   scale = max(max(hist) / FMAX / 2^margin, 1e-12f)
+ *
+ * ring : host pointer, required.  amax: fp32 [1] (device), >= 0.
+ * Typical use: an amax reduced elsewhere (e.g. a MAX all-reduce across
+ * data-parallel ranks of per-rank measure-only passes).
+ * ------------------------------------------------------------------- */
+fp8_status_t fp8_scale_ring_finalize(const fp8_ring_t* ring, fp8_fmt_t fmt,
+                                     const float* amax, int32_t margin,
+                                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * fp8_mm -- scaled fp8 GEMM with fp32 accumulation and bf16 output.
+ * (compare view: astrai/extension/ops/fp8.py mm_fp8; csrc/kernels/fp8/
+ *  common.h FP8Params and layout tags; gemm/epilogue.cuh)
+ *
+ *   out[b][i][j] = bf16_rne( sum_k A_b[i][k] * B_b[k][j] * fp32(sa * sb)
+ *                            + bias[j] )
+ *
+ * A_b is m x k, stored at a + b * stride_a as
+ *     trans_a == 0: [m][k] rows of stride lda (>= k)
+ *     trans_a == 1: [k][m] rows of stride lda (>= m)
+ * B_b is k x n, stored at b + b * stride_b as
+ *     trans_b == 0: [k][n] rows of stride ldb (>= n)
+ *     trans_b == 1: [n][k] rows of stride ldb (>= k)  (nn.Linear weight)
+ * The linear layer uses NT (0,1) forward, NN (0,0) for dX and TN (1,0)
+ * for dW; TT (1,1) is accepted too.
+ * stride_a / stride_b: element strides between batches; 0 broadcasts the
+ *     operand over the batch.  Ignored when batch == 1.
+ * m, n, k >= 1 (k == 0 is rejected); batch >= 1; m*n*batch < 2^40.
+ * scale_a, scale_b: fp32 [1] steps of A and B (device).
+ * bias: bf16 [n] or NULL.  out: bf16 [batch][m][n], contiguous.
+ * Both operands use the same fp8 format.  Accumulation is fp32 in an
+ * unspecified order; the epilogue computes acc * s + bias in fp32 and
+ * rounds once to bf16.
+ * ------------------------------------------------------------------- */
+fp8_status_t fp8_mm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t trans_a,
+                    int32_t trans_b, int64_t m, int64_t n, int64_t k, int64_t lda,
+                    int64_t ldb, int64_t batch, int64_t stride_a, int64_t stride_b,
+                    const float* scale_a, const float* scale_b, const uint16_t* bias,
+                    uint16_t* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * fp8_colsum -- bias gradient db[j] = bf16( sum_i g[i][j] ), g bf16 [m][n].
+ * (compare view: astrai/extension/fp8.py _LinearFp8.backward, grad_b)
+ * fp32 accumulation in a fixed order (deterministic).  workspace: device
+ * scratch of fp8_colsum_workspace(m, n) bytes (no initialization needed).
+ * ------------------------------------------------------------------- */
+size_t fp8_colsum_workspace(int64_t m, int64_t n);
+fp8_status_t fp8_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * fp8_linear_fwd -- out[M][N] = x[M][K] w[N][K]^T * (sx*sw) + bias
+ * (compare view: astrai/extension/fp8.py fp8_linear_forward)
+ *
+ * dynamic != 0: sx, sw are derived from the current amax of x and w
+ *     (measure-only pass into length-1 scratch rings, then quantize).
+ *     ring_x / ring_w are ignored (may be NULL).
+ * dynamic == 0 (delayed): ring_x and ring_w (host pointers, required) are
+ *     seeded from the current tensors when not initialized; the scale in
+ *     each ring is snapshotted by the quantize that reads it, the quantize
+ *     folds the current amax and publishes the next scale, the GEMM
+ *     dequantizes with the snapshots, and both rings advance.
+ * workspace: device scratch of fp8_linear_fwd_workspace(M, N, K) bytes; its
+ *     first 256 bytes are control slots that must be zero before the first
+ *     use and that every call leaves at zero (allocate zeroed, then reuse).
+ *     It receives x8 [M][K] and w8 [N][K] (fmt codes) at
+ *     fp8_linear_fwd_x8_offset / _w8_offset.
+ * scales_out: fp32 [2] (device) receives the steps used, [sx, sw]; the
+ *     delayed backward reuses them.
+ * bias: bf16 [N] or NULL.  out: bf16 [M][N].  M, N, K >= 1.
+ * ------------------------------------------------------------------- */
+size_t fp8_linear_fwd_workspace(int64_t M, int64_t N, int64_t K);
+size_t fp8_linear_fwd_x8_offset(int64_t M, int64_t N, int64_t K);
+size_t fp8_linear_fwd_w8_offset(int64_t M, int64_t N, int64_t K);
+fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t* bias,
+                            int64_t M, int64_t N, int64_t K, fp8_fmt_t fmt,
+                            int32_t dynamic, int32_t margin, fp8_ring_t* ring_x,
+                            fp8_ring_t* ring_w, void* workspace, size_t workspace_bytes,
+                            float* scales_out, uint16_t* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * fp8_linear_bwd -- gradients of the linear layer in the backward format.
+ * (compare view: astrai/extension/fp8.py _LinearFp8.backward; the removed
+ *  linear_backward_fp8 binding in csrc/kernels/fp8/ops.cu for the NN / TN
+ *  layouts)
+ *
+ *   dx[M][K] = g8 . w8b        * fp32(sg*sw)   (NN)
+ *   dw[N][K] = g8^T . x8b      * fp32(sg*sx)   (TN)
+ *   db[N]    = bf16( sum_m g[m][:] )
+ * g bf16 [M][N], x bf16 [M][K], w bf16 [N][K]; g8, x8b, w8b are g, x, w
+ * quantized in `fmt` (the backward format, E5M2 under HYBRID).
+ *
+ * dynamic == 0 (delayed): sg is ring_g's scale (seeded from g when not
+ *     initialized), snapshotted while the g quantize folds amax(g) and
+ *     publishes the next scale; ring_g advances.  sx, sw are the forward's
+ *     steps, scales_fwd = [sx, sw] (device fp32 [2], required).
+ * dynamic != 0: sg, sx, sw are measured now from g, x, w in `fmt`;
+ *     scales_fwd and ring_g are ignored.
+ * dx, dw, db: each NULL to skip that gradient (x8b is only made for dw,
+ *     w8b only for dx).
+ * workspace: fp8_linear_bwd_workspace(M, N, K) bytes, same zero-once
+ *     contract as the forward's.
+ * scales_out: nullable fp32 [3] receives [sg, sx, sw].
+ * ------------------------------------------------------------------- */
+size_t fp8_linear_bwd_workspace(int64_t M, int64_t N, int64_t K);
+fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t* w,
+                            int64_t M, int64_t N, int64_t K, fp8_fmt_t fmt,
+                            int32_t dynamic, int32_t margin, const float* scales_fwd,
+                            fp8_ring_t* ring_g, void* workspace, size_t workspace_bytes,
+                            float* scales_out, uint16_t* dx, uint16_t* dw, uint16_t* db,
+                            hipStream_t stream);
+
+/* Message of the last non-OK status returned on the calling thread
+ * (thread-local; "" if none). */
+const char* fp8_last_error(void);
+
+/* Library version string. */
+const char* fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

@@ -1,0 +1,143 @@
+"""Host-only checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/fp8lin.h declares, and rejects bad arguments before
+touching a device."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8lin.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(fp8_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def f():
+    import fp8_tensor_scaled_amd as f
+    return f
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fp8_quantize", "fp8_scale_ring_finalize", "fp8_mm", "fp8_linear_fwd",
+              "fp8_linear_bwd", "fp8_colsum", "fp8_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(f):
+    out = subprocess.run(["nm", "-D", "--defined-only", f.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    assert set(f.EXPORTED_SYMBOLS) == set(declared_functions())
+
+
+def test_pure_helpers(f):
+    lib = f._lib
+    assert lib.fp8_ring_state_floats(16) == 20
+    assert lib.fp8_ring_state_floats(0) == 0
+    assert lib.fp8_format_max(0) == 448.0 and lib.fp8_format_max(1) == 57344.0
+    assert lib.fp8_format_max(7) == 0.0
+    assert f.fp8_linear_fwd_workspace(0, 1, 1) == 0
+    M, N, K = 2048, 4096, 1024
+    assert f.fp8_linear_fwd_workspace(M, N, K) >= 256 + M * K + N * K
+    assert f.fp8_linear_fwd_x8_offset(M, N, K) % 256 == 0
+    assert f.fp8_linear_fwd_w8_offset(M, N, K) >= f.fp8_linear_fwd_x8_offset(M, N, K) + M * K
+    assert f.fp8_linear_bwd_workspace(M, N, K) >= 256 + M * N + M * K + N * K
+    assert b"gfx950" in lib.fp8_version()
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)  # never dereferenced: validation fails first
+
+
+def _err(lib):
+    return lib.fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, 10, 0, FAKE, FAKE, None, 0, None, None), "x is NULL"),
+    ((FAKE, 10, 2, FAKE, FAKE, None, 0, None, None), "format"),
+    ((FAKE, -1, 0, FAKE, FAKE, None, 0, None, None), "numel"),
+    ((FAKE, 10, 0, None, None, None, 0, None, None), "neither"),
+    ((FAKE, 10, 0, None, FAKE, None, 0, None, None), "scale is NULL"),
+    ((FAKE, 10, 0, FAKE, FAKE, None, 65, None, None), "margin"),
+])
+def test_quantize_validation(f, args, needle):
+    st = f._lib.fp8_quantize(*args)
+    assert st == 1 and needle in _err(f._lib)
+
+
+def test_ring_validation(f):
+    lib = f._lib
+    r = f._RingC(0x1000, 16, 16, 0, 0)
+    st = lib.fp8_quantize(FAKE, 10, 0, None, None, ctypes.byref(r), 0, None, None)
+    assert st == 1 and "idx" in _err(lib)
+    r = f._RingC(0x1000, 0, 0, 0, 0)
+    st = lib.fp8_scale_ring_finalize(ctypes.byref(r), 0, FAKE, 0, None)
+    assert st == 1 and "len" in _err(lib)
+    r = f._RingC(None, 4, 0, 0, 0)
+    st = lib.fp8_scale_ring_finalize(ctypes.byref(r), 0, FAKE, 0, None)
+    assert st == 1 and "state" in _err(lib)
+
+
+def mm(lib, **kw):
+    a = dict(a=FAKE, b=FAKE, fmt=0, ta=0, tb=1, m=64, n=64, k=64, lda=64, ldb=64, batch=1,
+             sta=0, stb=0, sa=FAKE, sb=FAKE, bias=None, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.fp8_mm(*a.values())
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(fmt=5), "format"),
+    (dict(a=None), "NULL"),
+    (dict(sa=None), "NULL"),
+    (dict(ta=2), "trans"),
+    (dict(k=0), ">= 1"),
+    (dict(batch=0), "batch"),
+    (dict(batch=70000), "batch"),
+    (dict(lda=32), "lda"),
+    (dict(tb=0, ldb=63), "ldb"),
+    (dict(batch=2, sta=-1), "stride"),
+])
+def test_mm_validation(f, kw, needle):
+    st = mm(f._lib, **kw)
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
+def test_valid_call_without_gpu_reports_hip_error(f):
+    """With valid arguments and no device, the call fails in the device
+    check (status FP8_EHIP or FP8_EUNSUPPORTED) and enqueues nothing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = mm(f._lib)
+    assert st in (2, 3)
+
+
+def test_linear_validation(f):
+    lib = f._lib
+    st = lib.fp8_linear_fwd(FAKE, FAKE, None, 32, 32, 32, 0, 0, 0, None, None, FAKE, 1 << 20,
+                            FAKE, FAKE, None)
+    assert st == 1 and "ring" in _err(lib)
+    st = lib.fp8_linear_fwd(FAKE, FAKE, None, 32, 32, 32, 0, 1, 0, None, None, FAKE, 16, FAKE,
+                            FAKE, None)
+    assert st == 1 and "workspace" in _err(lib)
+    st = lib.fp8_linear_bwd(FAKE, FAKE, FAKE, 32, 32, 32, 1, 0, 0, None, None, FAKE, 1 << 20,
+                            None, FAKE, FAKE, FAKE, None)
+    assert st == 1 and "scales_fwd" in _err(lib)
+    st = lib.fp8_linear_bwd(FAKE, None, FAKE, 32, 32, 32, 1, 1, 0, None, None, FAKE, 1 << 20,
+                            None, FAKE, FAKE, FAKE, None)
+    assert st == 1 and "dw needs x" in _err(lib)
+    st = lib.fp8_colsum(FAKE, 10, 10, FAKE, FAKE, 4, None)
+    assert st == 1 and "workspace" in _err(lib)

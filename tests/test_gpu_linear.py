@@ -1,0 +1,164 @@
+"""GPU parity of the linear-layer entry points against the CPU oracle.
+
+linear256: dynamic-scaling E4M3 forward at 256^3 (full output compare).
+train: delayed-scaling HYBRID forward + backward over four steps with the
+input scaled 1, 4, 0.25, 2 -- scales, rings and fp8 operands bit-exact every
+step, GEMM outputs at sampled coordinates, bias gradient in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_util import check_gemm, from_dev_bf16, from_dev_u8, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_tensor_scaled_amd as f
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return f
+
+
+class Fwd:
+    def __init__(self, lib, M, N, K):
+        self.ws = torch.zeros(lib.fp8_linear_fwd_workspace(M, N, K), dtype=torch.uint8,
+                              device="cuda")
+        self.x8_off = lib.fp8_linear_fwd_x8_offset(M, N, K)
+        self.w8_off = lib.fp8_linear_fwd_w8_offset(M, N, K)
+        self.scales = torch.zeros(2, dtype=torch.float32, device="cuda")
+        self.out = torch.empty(M * N, dtype=torch.int16, device="cuda")
+        self.M, self.N, self.K = M, N, K
+
+    def x8(self):
+        return from_dev_u8(self.ws[self.x8_off: self.x8_off + self.M * self.K])
+
+    def w8(self):
+        return from_dev_u8(self.ws[self.w8_off: self.w8_off + self.N * self.K])
+
+
+def test_linear256_dynamic_forward(lib, orc):
+    d = wl.linear256()
+    M, N, K = d["M"], d["N"], d["K"]
+    f = Fwd(lib, M, N, K)
+    for rep in range(2):  # the workspace's scratch slots re-arm themselves
+        lib.fp8_linear_fwd(to_dev_bf16(d["x"]), to_dev_bf16(d["w"]), to_dev_bf16(d["bias"]),
+                           M, N, K, E4M3, True, 0, None, None, f.ws, f.scales, f.out)
+        torch.cuda.synchronize()
+        ref = orc.linear_fwd(d["x"], d["w"], d["bias"], M, N, K, E4M3, True)
+        sc = f.scales.cpu().numpy()
+        assert sc[0] == ref.sx and sc[1] == ref.sw
+        assert np.array_equal(f.x8(), ref.x8.ravel())
+        assert np.array_equal(f.w8(), ref.w8.ravel())
+        absdot = orc.gemm_absdot(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
+        check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, "linear256")
+
+
+def _samples(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    return (np.zeros(n, np.int64), rng.integers(0, M, n), rng.integers(0, N, n))
+
+
+def test_train_delayed_hybrid_four_steps(lib, orc):
+    d = wl.train()
+    M, N, K = d["M"], d["N"], d["K"]
+    f = Fwd(lib, M, N, K)
+    bws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    rx, rw, rg = lib.Ring(16), lib.Ring(16), lib.Ring(16)
+    ox, ow, og = orc.Ring(16), orc.Ring(16), orc.Ring(16)
+    wd, bd = to_dev_bf16(d["w"]), to_dev_bf16(d["bias"])
+    dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    db = torch.empty(N, dtype=torch.int16, device="cuda")
+    sb = torch.zeros(3, dtype=torch.float32, device="cuda")
+    for t in range(4):
+        xd, gd = to_dev_bf16(d["x"][t]), to_dev_bf16(d["g"][t])
+        lib.fp8_linear_fwd(xd, wd, bd, M, N, K, E4M3, False, 0, rx, rw, f.ws, f.scales, f.out)
+        lib.fp8_linear_bwd(gd, xd, wd, M, N, K, E5M2, False, 0, f.scales, rg, bws, sb, dx, dw,
+                           db)
+        torch.cuda.synchronize()
+        rf = orc.linear_fwd(d["x"][t], d["w"], d["bias"], M, N, K, E4M3, False, ox, ow)
+        rb = orc.linear_bwd(d["g"][t], d["x"][t], d["w"], M, N, K, E5M2, False, rf.sx, rf.sw,
+                            og)
+        # scales, rings and fp8 operands: bit-exact
+        sc = f.scales.cpu().numpy()
+        assert (sc[0], sc[1]) == (rf.sx, rf.sw), t
+        sbh = sb.cpu().numpy()
+        assert (sbh[0], sbh[1], sbh[2]) == (rb.sg, rb.sx, rb.sw), t
+        for gr, orr in ((rx, ox), (rw, ow), (rg, og)):
+            assert np.array_equal(gr.state.cpu().numpy(), orr.state()), t
+            assert gr.idx == orr.idx and gr.initialized == orr.initialized
+        assert np.array_equal(f.x8(), rf.x8.ravel())
+        assert np.array_equal(f.w8(), rf.w8.ravel())
+        g8 = from_dev_u8(bws[256: 256 + M * N])
+        assert np.array_equal(g8, rb.g8.ravel())
+        # GEMM outputs at sampled coordinates
+        s = _samples(M, N, 2000, t)
+        ref, ad = orc.gemm_sampled(rf.x8, rf.w8, E4M3, False, True, M, N, K, rf.sx, rf.sw,
+                                   d["bias"], s)
+        check_gemm(from_dev_bf16(f.out).reshape(M, N)[s[1], s[2]], ref, ad, K, f"fwd {t}")
+        w8b = orc.quantize(d["w"], E5M2, rb.sw)
+        x8b = orc.quantize(d["x"][t], E5M2, rb.sx)
+        s = _samples(M, K, 2000, 10 + t)
+        ref, ad = orc.gemm_sampled(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw, None,
+                                   s)
+        check_gemm(from_dev_bf16(dx).reshape(M, K)[s[1], s[2]], ref, ad, N, f"dX {t}")
+        s = _samples(N, K, 2000, 20 + t)
+        ref, ad = orc.gemm_sampled(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx, None,
+                                   s)
+        check_gemm(from_dev_bf16(dw).reshape(N, K)[s[1], s[2]], ref, ad, M, f"dW {t}")
+        absg = np.abs(wl.bf16_bits_to_f32(d["g"][t]).astype(np.float64)).sum(0)
+        check_gemm(from_dev_bf16(db), rb.db, absg, M, f"db {t}")
+
+
+@pytest.mark.parametrize("dynamic", [True, False])
+def test_backward_masks_and_dynamic_small(lib, orc, dynamic):
+    M, N, K = 96, 80, 112
+    x = wl.normal_bf16((M, K), 1.0, 1)
+    w = wl.normal_bf16((N, K), 0.02, 2)
+    g = wl.normal_bf16((M, N), 1e-3, 3)
+    sx, sw = np.float32(0.004), np.float32(2e-4)
+    scales_fwd = torch.tensor([sx, sw], dtype=torch.float32, device="cuda")
+    ws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    for need in [(1, 1, 1), (1, 0, 0), (0, 1, 0), (0, 0, 1)]:
+        rg = None if dynamic else lib.Ring(16)
+        og = None if dynamic else orc.Ring(16)
+        dx = torch.empty(M * K, dtype=torch.int16, device="cuda") if need[0] else None
+        dw = torch.empty(N * K, dtype=torch.int16, device="cuda") if need[1] else None
+        db = torch.empty(N, dtype=torch.int16, device="cuda") if need[2] else None
+        lib.fp8_linear_bwd(to_dev_bf16(g), to_dev_bf16(x), to_dev_bf16(w), M, N, K, E5M2,
+                           dynamic, 0, scales_fwd, rg, ws, None, dx, dw, db)
+        torch.cuda.synchronize()
+        rb = orc.linear_bwd(g, x, w, M, N, K, E5M2, dynamic, sx, sw, og, bool(need[0]),
+                            bool(need[1]), bool(need[2]))
+        if need[0]:
+            w8b = orc.quantize(w, E5M2, rb.sw)
+            ad = orc.gemm_absdot(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+            check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, N, "dx")
+        if need[1]:
+            x8b = orc.quantize(x, E5M2, rb.sx)
+            ad = orc.gemm_absdot(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+            check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, M, "dw")
+        if need[2]:
+            absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+            check_gemm(from_dev_bf16(db), rb.db, absg, M, "db")
+        if not dynamic:
+            assert np.array_equal(rg.state.cpu().numpy(), og.state())
+
+
+def test_linear_invalid_arguments(lib):
+    M, N, K = 32, 32, 32
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(M * K, dtype=torch.int16, device="cuda")
+    sc = torch.zeros(2, dtype=torch.float32, device="cuda")
+    out = torch.empty(M * N, dtype=torch.int16, device="cuda")
+    with pytest.raises(ValueError, match="workspace"):
+        lib.fp8_linear_fwd(x, x, None, M, N, K, E4M3, True, 0, None, None, ws, sc, out)
+    ws = torch.zeros(lib.fp8_linear_fwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="ring"):
+        lib.fp8_linear_fwd(x, x, None, M, N, K, E4M3, False, 0, None, None, ws, sc, out)

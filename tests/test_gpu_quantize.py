@@ -1,0 +1,207 @@
+"""GPU parity of the quantize stage against the CPU oracle (bit-exact).
+
+Covers fp8_quantize (cast, measure-only, ring fold, scale snapshot),
+fp8_scale_ring_finalize and fp8_colsum on the configurations' tensors,
+ragged / misaligned / empty inputs, and an exhaustive sweep of the fp32 ->
+fp8 conversion through the kernel.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_util import dev_f32, from_dev_bf16, from_dev_u8, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_tensor_scaled_amd as f
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return f
+
+
+def _is_nan_code(c, fmt):
+    c = np.asarray(c)
+    if fmt == E4M3:
+        return (c & 0x7F) == 0x7F
+    return ((c & 0x7C) == 0x7C) & ((c & 0x03) != 0)
+
+
+def gpu_quantize(lib, x_bits, fmt, s, offset=0):
+    """Quantize on the GPU; ``offset`` shifts both buffers to test
+    misaligned bases."""
+    n = x_bits.size
+    xd = torch.zeros(n + offset, dtype=torch.int16, device="cuda")
+    if n:
+        xd[offset:] = to_dev_bf16(x_bits.ravel())
+    out = torch.full((n + offset,), 0xAA, dtype=torch.uint8, device="cuda")
+    sd = dev_f32(s)
+    used = dev_f32(-1.0)
+    lib.fp8_quantize(xd[offset:], fmt, scale=sd, out=out[offset:], scale_used=used)
+    torch.cuda.synchronize()
+    return from_dev_u8(out[offset:]), float(used.cpu()[0])
+
+
+CASES = [
+    ("linear256.x", lambda: wl.linear256()["x"]),
+    ("linear256.w", lambda: wl.linear256()["w"]),
+    ("smallm.w", lambda: wl.smallm()["w"]),
+    ("train.x1", lambda: wl.train()["x"][1]),
+    ("train.g0", lambda: wl.train()["g"][0]),
+]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+def test_quantize_config_tensors_bitexact(lib, orc, fmt, name, make):
+    x = make()
+    a = orc.amax(x)
+    for s in (orc.scale_from_peak(a, fmt), orc.scale_from_peak(a / 8, fmt),
+              np.float32(0.0137)):
+        got, used = gpu_quantize(lib, x, fmt, s)
+        ref = orc.quantize(x, fmt, s)
+        assert used == np.float32(s)
+        assert np.array_equal(got.reshape(ref.shape), ref), (name, fmt, s)
+
+
+@pytest.mark.parametrize("n,offset", [(1, 0), (15, 0), (16, 0), (17, 0), (1000003, 0),
+                                      (4096, 1), (4099, 3), (0, 0)])
+def test_quantize_ragged_and_misaligned(lib, orc, n, offset):
+    x = wl.normal_bf16((n,), 3.0, 1000 + n)
+    for fmt in (E4M3, E5M2):
+        s = np.float32(0.01)
+        got, _ = gpu_quantize(lib, x, fmt, s, offset)
+        assert np.array_equal(got, orc.quantize(x, fmt, s))
+
+
+def test_quantize_special_values(lib, orc):
+    """+-0, subnormal bf16, huge values (saturation), +-inf; NaN -> a NaN code."""
+    vals = np.array([0.0, -0.0, 1e-40, -1e-40, 3e38, -3e38, np.inf, -np.inf, 447.9, 449.0,
+                     -464.0, 57344.0, 61440.0, 1e-6, 2.0 ** -10, 2.0 ** -17], np.float32)
+    x = wl.f32_to_bf16_bits(vals)
+    x = np.concatenate([x, np.array([0x7FC0, 0xFFC0], np.uint16)])
+    for fmt in (E4M3, E5M2):
+        got, _ = gpu_quantize(lib, x, fmt, np.float32(1.0))
+        ref = orc.quantize(x, fmt, np.float32(1.0))
+        nan = np.zeros(x.size, bool)
+        nan[-2:] = True
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert _is_nan_code(got[nan], fmt).all()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_conversion_exhaustive_fp32(lib, orc, fmt):
+    """Every fp32 value a quantize can produce from a bf16 input times a
+    multiplier: all bf16 inputs at several multipliers, plus a dense sweep
+    of fp32 bit patterns through x * 1.0 (bf16 inputs are exact in fp32)."""
+    allbf = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for s in (np.float32(1.0), np.float32(1 / 3.0), np.float32(2.0 ** 20), np.float32(7e-5)):
+        got, _ = gpu_quantize(lib, allbf, fmt, s)
+        ref = orc.quantize(allbf, fmt, s)
+        nan = _is_nan_code(ref, fmt)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert _is_nan_code(got[nan], fmt).all()
+
+
+def test_ring_fold_measure_and_quantize(lib, orc):
+    """Delayed-scaling ring driven through fp8_quantize over four steps of
+    the training config's x: seed (measure-only fold), then quantize with
+    the published scale while the kernel folds; hist, scale and the scratch
+    slots must match the oracle bit for bit."""
+    d = wl.train()
+    ring = lib.Ring(16)
+    oring = orc.Ring(16)
+    fmt = E4M3
+    for t in range(4):
+        x = d["x"][t]
+        xd = to_dev_bf16(x.ravel())
+        if t == 0:
+            lib.fp8_quantize(xd, fmt, ring=ring)
+            oring.seed(x, fmt)
+        used = dev_f32(0.0)
+        out = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        lib.fp8_quantize(xd, fmt, scale=ring.scale, out=out, ring=ring, scale_used=used)
+        s_snap = np.float32(oring.scale)
+        ref = orc.quantize(x, fmt, s_snap)
+        oring.fold(orc.amax(x), fmt)
+        torch.cuda.synchronize()
+        assert float(used.cpu()[0]) == s_snap
+        assert np.array_equal(from_dev_u8(out), ref.ravel())
+        st = ring.state.cpu().numpy()
+        assert np.array_equal(st, oring.state()), (t, st, oring.state())
+        ring.idx = (ring.idx + 1) % 16
+        oring.advance()
+
+
+def test_ring_fold_many_workgroups_and_empty(lib, orc):
+    """A large tensor (thousands of workgroups) and an empty one both fold
+    exactly once; a dirty scratch slot written from the host is not part of
+    the contract, so the state is re-zeroed first."""
+    x = wl.square(4096)["a"]
+    ring = lib.Ring(4)
+    ring.idx = 3
+    lib.fp8_quantize(to_dev_bf16(x.ravel()), E5M2, ring=ring, margin=2)
+    torch.cuda.synchronize()
+    st = ring.state.cpu().numpy()
+    a = orc.amax(x)
+    assert st[3] == a
+    assert st[4] == orc.scale_from_peak(a, E5M2, 2)
+    assert st[6] == 0 and st[7] == 0
+    # empty input folds amax 0 into slot 0
+    ring.idx = 0
+    lib.fp8_quantize(torch.empty(0, dtype=torch.int16, device="cuda"), E5M2, ring=ring,
+                     margin=2)
+    torch.cuda.synchronize()
+    st = ring.state.cpu().numpy()
+    assert st[0] == 0 and st[4] == orc.scale_from_peak(a, E5M2, 2)
+
+
+def test_scale_ring_finalize(lib, orc):
+    ring = lib.Ring(16)
+    oring = orc.Ring(16, margin=1)
+    rng = np.random.default_rng(5)
+    for t in range(20):
+        a = np.float32(rng.uniform(0, 100))
+        lib.fp8_scale_ring_finalize(ring, E4M3, dev_f32(a), margin=1)
+        oring.fold(a, E4M3)
+        torch.cuda.synchronize()
+        assert np.array_equal(ring.state.cpu().numpy(), oring.state())
+        ring.idx = (ring.idx + 1) % 16
+        oring.advance()
+
+
+@pytest.mark.parametrize("M,N", [(2048, 4096), (1, 7), (33, 8), (300, 1000), (70000, 16)])
+def test_colsum(lib, orc, M, N):
+    from tests.gpu_util import check_gemm
+    g = wl.normal_bf16((M, N), 1e-3, 77 + M)
+    ws = torch.empty(lib.fp8_colsum_workspace(M, N), dtype=torch.uint8, device="cuda")
+    db = torch.empty(N, dtype=torch.int16, device="cuda")
+    lib.fp8_colsum(to_dev_bf16(g), M, N, db, ws)
+    torch.cuda.synchronize()
+    got = from_dev_bf16(db)
+    ref = orc.colsum(g, M, N)
+    absdot = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+    check_gemm(got, ref, absdot=absdot, K=M, what="colsum")
+    # deterministic
+    db2 = torch.empty_like(db)
+    lib.fp8_colsum(to_dev_bf16(g), M, N, db2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bf16(db2), got)
+
+
+def test_invalid_arguments_raise(lib):
+    x = torch.zeros(16, dtype=torch.int16, device="cuda")
+    with pytest.raises(ValueError):
+        lib.fp8_quantize(x, 2, scale=dev_f32(1.0), out=torch.empty(16, dtype=torch.uint8,
+                                                                   device="cuda"))
+    with pytest.raises(ValueError):
+        lib.fp8_quantize(x, 0)  # neither out nor ring
+    r = lib.Ring(4)
+    r.idx = 4
+    with pytest.raises(ValueError):
+        lib.fp8_quantize(x, 0, ring=r)

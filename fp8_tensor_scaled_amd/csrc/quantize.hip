@@ -11,13 +11,20 @@
 // step from the window's max and re-arms its scratch slots, so the delayed
 // update costs no extra launch.
 //
-// gfx950 design: one workgroup = 4 waves of 64; each lane streams 32 bytes
-// of bf16 per iteration (two 16-byte loads) and stores the 16 fp8 codes with
-// one 16-byte store; conversions use v_cvt_pk_{fp8,bf8}_f32 after a med3
-// clamp (satfinite).  The grid is sized to keep every CU busy with several
-// resident workgroups.  Cross-XCD correctness of the fold uses agent-scope
-// atomics: the amax slot is an atomic max on fp32 bits (non-negative
-// floats order like unsigned ints) and the done counter an acq_rel add.
+// gfx950 design:
+//  * HBM streaming: one workgroup = 4 waves of 64; the grid is at most two
+//    workgroups per CU and every lane keeps four 32-byte loads in flight per
+//    iteration (16 bf16 each, two 16-byte loads), storing 16 fp8 codes with
+//    one 16-byte store.  Conversions are v_cvt_pk_{fp8,bf8}_f32 after a med3
+//    clamp to +-max (satfinite).
+//  * The fold uses relaxed agent-scope atomics only.  Release/acquire at
+//    agent scope write back / invalidate the per-XCD L2s and cost tens of ns
+//    per workgroup when every workgroup issues them; instead each workgroup
+//    waits for its atomic max to return (the returned value feeds the ticket
+//    increment) before taking a ticket, so by the time the last ticket is
+//    drawn every max has been performed at the device coherence point, where
+//    the last workgroup's atomic read sees it.  The fp8 outputs need no
+//    ordering against the fold (kernel boundaries publish them).
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -26,7 +33,8 @@ namespace fp8lin {
 
 constexpr int kQuantThreads = 256;
 constexpr int kQuantWaves = kQuantThreads / kWave;
-constexpr int kElemsPerIter = 16;  // per lane
+constexpr int kVecElems = 16;  // bf16 elements per lane per unrolled slot
+constexpr int kUnroll = 4;     // slots in flight per lane
 
 struct QuantParams {
     const uint16_t* x;
@@ -45,49 +53,72 @@ struct QuantParams {
     int vec;  // 1: x and out are 16-byte aligned
 };
 
-// Last-workgroup fold: hist[idx] = amax; scale = max(peak/fmax/2^m, 1e-12).
+// Last-workgroup fold (wave 0): hist[idx] = amax;
+// scale = max(peak / fmax / 2^margin, 1e-12).
 __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read) {
-    const int lane = threadIdx.x;  // wave 0 only
+    const int lane = threadIdx.x;
     float amax = 0.0f;
-    if (lane == 0) {
+    if (lane == 0)
         amax = __uint_as_float(
-            __hip_atomic_load(p.amax_slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
-        p.hist[p.idx] = amax;
-    }
+            __hip_atomic_load(p.amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     amax = __shfl(amax, 0, kWave);
     float peak = 0.0f;
     for (int i = lane; i < p.len; i += kWave) peak = fmaxf(peak, i == p.idx ? amax : p.hist[i]);
     peak = wave_max(peak);
     if (lane == 0) {
+        p.hist[p.idx] = amax;
         const float t = __fdiv_rn(peak, p.fmax);
         const float s = __fdiv_rn(t, p.pow2_margin);
         *p.scale_out = fmaxf(s, 1e-12f);
         if (p.scale_used) *p.scale_used = s_read;
         __hip_atomic_store(p.amax_slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.done, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-// Workgroup max -> one atomic; the last workgroup folds the ring.
+// Workgroup max -> one atomic max, then a ticket; the last workgroup folds.
 __device__ __forceinline__ void publish_amax(const QuantParams& p, float v, float s_read) {
     __shared__ float slots[kQuantWaves];
     __shared__ int is_last;
     v = wave_max(v);
-    const int wave = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) slots[wave] = v;
+    if ((threadIdx.x % kWave) == 0) slots[threadIdx.x / kWave] = v;
     __syncthreads();
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < kQuantWaves; ++w) v = fmaxf(v, slots[w]);
-        __hip_atomic_fetch_max(p.amax_slot, __float_as_uint(v), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t nblocks = gridDim.x;
+        const uint32_t old = __hip_atomic_fetch_max(p.amax_slot, __float_as_uint(v),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // |x| maxima are never all-ones bits; the comparison makes the ticket
+        // wait for the max to have been performed.
+        const uint32_t inc = old == 0xffffffffu ? 2u : 1u;
         const uint32_t ticket =
-            __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (ticket == nblocks - 1u);
+            __hip_atomic_fetch_add(p.done, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = (ticket == gridDim.x - 1u);
     }
     __syncthreads();
     if (is_last && threadIdx.x < kWave) fold_ring(p, s_read);
+}
+
+template <int FMT, bool MEASURE_ONLY>
+__device__ __forceinline__ void convert16(const uint4& r0, const uint4& r1, float m, float& amax,
+                                          uint4* dst) {
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    float f[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        f[2 * j] = bf16_lo(w[j]);
+        f[2 * j + 1] = bf16_hi(w[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) amax = fmaxf(amax, fmaxf(fabsf(f[j]), fabsf(f[j + 1])));
+    if constexpr (!MEASURE_ONLY) {
+        uint4 o;
+        o.x = cvt4<FMT>(f[0] * m, f[1] * m, f[2] * m, f[3] * m);
+        o.y = cvt4<FMT>(f[4] * m, f[5] * m, f[6] * m, f[7] * m);
+        o.z = cvt4<FMT>(f[8] * m, f[9] * m, f[10] * m, f[11] * m);
+        o.w = cvt4<FMT>(f[12] * m, f[13] * m, f[14] * m, f[15] * m);
+        *dst = o;
+    }
 }
 
 template <int FMT, bool MEASURE_ONLY>
@@ -100,35 +131,28 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     float amax = 0.0f;
     const int64_t tid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    const int64_t nvec = p.vec ? p.numel / kElemsPerIter : 0;
+    const int64_t nvec = p.vec ? p.numel / kVecElems : 0;
     const uint4* xv = reinterpret_cast<const uint4*>(p.x);
     uint4* ov = reinterpret_cast<uint4*>(p.out);
-    for (int64_t i = tid; i < nvec; i += stride) {
-        const uint4 r0 = xv[2 * i];
-        const uint4 r1 = xv[2 * i + 1];
-        const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-        float f[16];
+    int64_t i = tid;
+    for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
+        uint4 r[kUnroll][2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            f[2 * j] = bf16_lo(w[j]);
-            f[2 * j + 1] = bf16_hi(w[j]);
+        for (int u = 0; u < kUnroll; ++u) {
+            r[u][0] = xv[2 * (i + u * stride)];
+            r[u][1] = xv[2 * (i + u * stride) + 1];
         }
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) amax = fmaxf(amax, fmaxf(fabsf(f[j]), fabsf(f[j + 1])));
-        if constexpr (!MEASURE_ONLY) {
-            uint4 o;
-            o.x = cvt4<FMT>(f[0] * m, f[1] * m, f[2] * m, f[3] * m);
-            o.y = cvt4<FMT>(f[4] * m, f[5] * m, f[6] * m, f[7] * m);
-            o.z = cvt4<FMT>(f[8] * m, f[9] * m, f[10] * m, f[11] * m);
-            o.w = cvt4<FMT>(f[12] * m, f[13] * m, f[14] * m, f[15] * m);
-            ov[i] = o;
-        }
+        for (int u = 0; u < kUnroll; ++u)
+            convert16<FMT, MEASURE_ONLY>(r[u][0], r[u][1], m, amax, ov + i + u * stride);
     }
+    for (; i < nvec; i += stride)
+        convert16<FMT, MEASURE_ONLY>(xv[2 * i], xv[2 * i + 1], m, amax, ov + i);
     // Scalar tail (everything when the bases are not 16-byte aligned).
-    for (int64_t i = nvec * kElemsPerIter + tid; i < p.numel; i += stride) {
-        const float f = bf16_to_f32(p.x[i]);
+    for (int64_t e = nvec * kVecElems + tid; e < p.numel; e += stride) {
+        const float f = bf16_to_f32(p.x[e]);
         amax = fmaxf(amax, fabsf(f));
-        if constexpr (!MEASURE_ONLY) p.out[i] = cvt1<FMT>(f * m);
+        if constexpr (!MEASURE_ONLY) p.out[e] = cvt1<FMT>(f * m);
     }
     if (p.hist) {
         publish_amax(p, amax, s_read);
@@ -138,9 +162,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
 }
 
 static int quant_grid(int64_t numel, int vec) {
-    const int64_t per_block = (int64_t)kQuantThreads * (vec ? kElemsPerIter : 1);
+    const int64_t per_block = (int64_t)kQuantThreads * (vec ? kVecElems : 1);
     int64_t blocks = (numel + per_block - 1) / per_block;
-    const int64_t cap = 256 * 8;  // 8 resident workgroups per CU on 256 CUs
+    const int64_t cap = 256 * 2;  // two workgroups per CU on 256 CUs
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     return (int)blocks;
@@ -209,22 +233,36 @@ hipError_t launch_ring_finalize(float* state, int32_t len, int32_t idx, int fmt,
 }
 
 // ---------------------------------------------------------------------------
-// Bias gradient: db[j] = bf16(sum_i g[i][j]).  Pass 1: each lane sums 8
-// adjacent columns over a chunk of rows into fp32 partials; pass 2 adds the
-// partials of each column in chunk order (deterministic) and rounds once.
+// Bias gradient: db[j] = bf16(sum_i g[i][j]), fp32 sums in a fixed order.
+//
+// Pass 1 (vector path, n % 8 == 0 and 16-byte aligned rows): a workgroup
+// covers 256 columns x one chunk of rows; its 256 lanes are 32 column
+// groups (8 columns = one 16-byte load) x 8 row phases, each lane summing
+// every 8th row of the chunk with up to 8 loads in flight; the 8 phases are
+// then added in LDS and the chunk's 256 column sums written as partials.
+// Pass 2: 64 columns per workgroup, 4 lanes per column each adding a
+// quarter of the chunk partials, combined in a fixed order, one rounding.
 // ---------------------------------------------------------------------------
 constexpr int kColThreads = 256;
+constexpr int kColPhases = 8;  // row phases per workgroup (vector path)
 
-// Rows per chunk: 32, grown so that the chunk count fits gridDim.y.
-static int64_t colsum_rows(int64_t m) {
-    int64_t r = 32;
-    while ((m + r - 1) / r > 65535) r *= 2;
-    return r;
+// Rows per chunk: chosen for ~512+ workgroups over the whole matrix.
+static int64_t colsum_rows(int64_t m, int64_t n) {
+    const int64_t colblocks = (n + 255) / 256;
+    int64_t chunks = (512 + colblocks - 1) / colblocks;
+    int64_t rows = (m + chunks - 1) / chunks;
+    rows = (rows + kColPhases - 1) / kColPhases * kColPhases;
+    if (rows < 64) rows = 64;
+    while ((m + rows - 1) / rows > 65535) rows *= 2;
+    return rows;
 }
-static int64_t colsum_chunks(int64_t m) { return (m + colsum_rows(m) - 1) / colsum_rows(m); }
+static int64_t colsum_chunks(int64_t m, int64_t n) {
+    const int64_t r = colsum_rows(m, n);
+    return (m + r - 1) / r;
+}
 
 size_t colsum_workspace(int64_t m, int64_t n) {
-    return (size_t)colsum_chunks(m) * (size_t)n * sizeof(float);
+    return (size_t)colsum_chunks(m, n) * (size_t)n * sizeof(float);
 }
 
 __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const uint16_t* g,
@@ -235,21 +273,49 @@ __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const uint1
     const int64_t r0 = chunk * rows;
     const int64_t r1 = r0 + rows < m ? r0 + rows : m;
     if (vec) {
-        const int64_t c0 = ((int64_t)blockIdx.x * kColThreads + threadIdx.x) * 8;
-        if (c0 >= n) return;
+        __shared__ float red[kColPhases][256 + 4];
+        const int cg = threadIdx.x % 32;     // column group (8 columns)
+        const int ph = threadIdx.x / 32;     // row phase
+        const int64_t c0 = (int64_t)blockIdx.x * 256 + cg * 8;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int64_t r = r0; r < r1; ++r) {
-            const uint4 v = *reinterpret_cast<const uint4*>(g + r * n + c0);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if (c0 < n) {
+            int64_t r = r0 + ph;
+            for (; r + 7 * kColPhases < r1; r += 8 * kColPhases) {
+                uint4 v[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] += bf16_lo(w[j]);
-                acc[2 * j + 1] += bf16_hi(w[j]);
+                for (int u = 0; u < 8; ++u)
+                    v[u] = *reinterpret_cast<const uint4*>(g + (r + u * kColPhases) * n + c0);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] += bf16_lo(w[j]);
+                        acc[2 * j + 1] += bf16_hi(w[j]);
+                    }
+                }
+            }
+            for (; r < r1; r += kColPhases) {
+                const uint4 v = *reinterpret_cast<const uint4*>(g + r * n + c0);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] += bf16_lo(w[j]);
+                    acc[2 * j + 1] += bf16_hi(w[j]);
+                }
             }
         }
-        float4* dst = reinterpret_cast<float4*>(part + chunk * n + c0);
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[ph][cg * 8 + j] = acc[j];
+        __syncthreads();
+        const int col = threadIdx.x;  // 0..255
+        const int64_t gc = (int64_t)blockIdx.x * 256 + col;
+        if (gc < n) {
+            float s = red[0][col];
+#pragma unroll
+            for (int q = 1; q < kColPhases; ++q) s += red[q][col];
+            part[chunk * n + gc] = s;
+        }
     } else {
         const int64_t c = (int64_t)blockIdx.x * kColThreads + threadIdx.x;
         if (c >= n) return;
@@ -262,26 +328,35 @@ __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const uint1
 __global__ __launch_bounds__(kColThreads) void colsum_final_kernel(const float* part,
                                                                    int64_t chunks, int64_t n,
                                                                    uint16_t* db) {
-    const int64_t c = (int64_t)blockIdx.x * kColThreads + threadIdx.x;
-    if (c >= n) return;
+    __shared__ float red[4][64];
+    const int col = threadIdx.x % 64;
+    const int q = threadIdx.x / 64;
+    const int64_t c = (int64_t)blockIdx.x * 64 + col;
     float acc = 0.0f;
-    for (int64_t q = 0; q < chunks; ++q) acc += part[q * n + c];
-    db[c] = f32_to_bf16(acc);
+    if (c < n) {
+        const int64_t per = (chunks + 3) / 4;
+        const int64_t b = q * per;
+        const int64_t e = b + per < chunks ? b + per : chunks;
+        for (int64_t k = b; k < e; ++k) acc += part[k * n + c];
+    }
+    red[q][col] = acc;
+    __syncthreads();
+    if (q == 0 && c < n) db[c] = f32_to_bf16(((red[0][col] + red[1][col]) + red[2][col]) + red[3][col]);
 }
 
 hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, void* ws,
                          hipStream_t stream) {
     float* part = static_cast<float*>(ws);
-    const int64_t chunks = colsum_chunks(m);
-    const int vec = (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(g) & 15) == 0) &&
-                    ((reinterpret_cast<uintptr_t>(part) & 15) == 0);
-    const int64_t cols_per_block = vec ? (int64_t)kColThreads * 8 : kColThreads;
+    const int64_t rows = colsum_rows(m, n);
+    const int64_t chunks = colsum_chunks(m, n);
+    const int vec = (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+    const int64_t cols_per_block = vec ? 256 : kColThreads;
     const dim3 grid1((unsigned)((n + cols_per_block - 1) / cols_per_block), (unsigned)chunks);
-    hipLaunchKernelGGL(colsum_partial_kernel, grid1, dim3(kColThreads), 0, stream, g, m, n,
-                       colsum_rows(m), vec, part);
+    hipLaunchKernelGGL(colsum_partial_kernel, grid1, dim3(kColThreads), 0, stream, g, m, n, rows,
+                       vec, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid2((unsigned)((n + kColThreads - 1) / kColThreads));
+    const dim3 grid2((unsigned)((n + 63) / 64));
     hipLaunchKernelGGL(colsum_final_kernel, grid2, dim3(kColThreads), 0, stream, part, chunks, n,
                        db);
     return hipGetLastError();

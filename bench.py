@@ -46,7 +46,71 @@ def parse():
     p.add_argument("--size", type=int, default=4096)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
+    p.add_argument("--kernel", default=None,
+                   help="run only one kernel (for profilers): " + ", ".join(KERNELS))
+    p.add_argument("--reps", type=int, default=5)
     return p.parse_args()
+
+
+KERNELS = ("gemm_nt_4096", "gemm_nn_4096", "gemm_tn_4096", "gemm_nt_64x8192x2048",
+           "gemm_nt_8192", "quantize_8192x8192", "copy_192MB")
+
+
+def single_kernel(f, torch, name, reps):
+    """Launch one kernel `reps` times (after 2 warm-up launches) on synthetic
+    operands, for rocprofv3 counter and trace runs."""
+    dev = "cuda"
+    s = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
+    if name.startswith("gemm"):
+        shapes = {"gemm_nt_4096": (4096, 4096, 4096, 0, 1), "gemm_nn_4096": (4096, 4096, 4096, 0, 0),
+                  "gemm_tn_4096": (4096, 4096, 4096, 1, 0),
+                  "gemm_nt_64x8192x2048": (64, 8192, 2048, 0, 1),
+                  "gemm_nt_8192": (8192, 8192, 8192, 0, 1)}
+        M, N, K, ta, tb = shapes[name]
+        a = torch.randint(0, 120, (M * K,), dtype=torch.uint8, device=dev)
+        b = torch.randint(0, 120, (N * K,), dtype=torch.uint8, device=dev)
+        out = torch.empty(M * N, dtype=torch.int16, device=dev)
+        lda = M if ta else K
+        ldb = K if tb else N
+        fmt = E4M3 if (ta, tb) == (0, 1) else E5M2
+
+        def launch():
+            f.fp8_mm(a, b, fmt, ta, tb, M, N, K, lda, ldb, 1, 0, 0, s, s, None, out)
+        nbytes = M * K + N * K + 2 * M * N
+        work = dict(flop=2.0 * M * N * K, bytes=nbytes)
+    elif name == "quantize_8192x8192":
+        n = 8192 * 8192
+        x = torch.randn(n, device=dev).to(torch.bfloat16).view(torch.int16)
+        q = torch.empty(n, dtype=torch.uint8, device=dev)
+        ring = f.Ring(16)
+        f.fp8_quantize(x, E4M3, ring=ring)
+
+        def launch():
+            f.fp8_quantize(x, E4M3, scale=ring.scale, out=q, ring=ring)
+        work = dict(bytes=3 * n)
+    elif name == "copy_192MB":
+        # calibration for the FETCH_SIZE / WRITE_SIZE counters: a plain copy
+        # of 192 MiB (torch's copy kernel) reads and writes exactly that much
+        n = 192 * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+
+        def launch():
+            dst.copy_(src)
+        work = dict(bytes=2 * n)
+    else:
+        raise SystemExit(f"unknown kernel {name}; one of {KERNELS}")
+    for _ in range(2):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"kernel": name, "reps": reps, "avg_us": round(ms * 1e3, 2), **work}))
 
 
 class Layer:
@@ -256,6 +320,9 @@ def main():
     import torch
     import fp8_tensor_scaled_amd as f
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.kernel:
+        single_kernel(f, torch, args.kernel, args.reps)
+        return
     size = args.size
     layer = Layer(f, torch, size)
     check_against_linear_entry_points(f, torch)

@@ -1,4 +1,4 @@
-// LDS-tiled fp8 GEMM on CDNA4 MFMA (v_mfma_f32_16x16x128_f8f6f4).
+// LDS-tiled fp8 GEMM on CDNA4 MFMA (v_mfma_f32_32x32x64_f8f6f4).
 //
 // Computes out[b][i][j] = bf16(sum_k A[i][k] B[k][j] * fp32(sa*sb) + bias[j])
 // for the four storage layouts of the operands (AstrAI compare view
@@ -8,21 +8,30 @@
 // NVIDIA mainloop (cp.async rings, ldmatrix, byte-permute transposes) is
 // not followed; this is a gfx950 design:
 //
-//  * A workgroup of 4 waves (2x2) owns a BM x BN output tile; each wave owns
-//    (BM/2) x (BN/2) and keeps its fp32 accumulators in registers.
-//  * Operand tiles of 128 k are staged through LDS, double-buffered, with one
-//    barrier per k-step: the next k-step's global loads are issued before
-//    the MFMAs of the current one and written to the other buffer after.
+//  * A workgroup of WM x WN waves owns a BM x BN output tile; each wave owns
+//    (BM/WM) x (BN/WN) as 32x32 MFMA tiles with fp32 accumulators in
+//    registers.
+//  * k advances 64 per step.  Operand tiles go global -> LDS with
+//    buffer_load_dwordx4 ... lds (no register staging): each instruction
+//    writes 1 KB of LDS in lane order, and each lane picks the 16 global
+//    bytes that belong at its LDS slot, which is how the XOR swizzle is
+//    applied.  Out-of-range chunks (matrix tails, steps past the end of k)
+//    use an offset beyond the buffer range and arrive as zeros.
+//  * STAGES LDS buffers form a ring: at the top of step t each wave waits
+//    for its own loads of step t (vmcnt), a raw s_barrier makes everyone's
+//    loads visible and frees the buffer read in step t-1, which then
+//    receives step t+STAGES-1.  The loop is unrolled by STAGES so that every
+//    LDS offset is a compile-time constant.
 //  * A k-contiguous operand ("K-major": A stored [M][K], B stored [N][K]) is
-//    kept as [rows][128 B] with its 16-byte chunks XOR-swizzled by row, and
-//    read as two ds_read_b128 per fragment.
-//  * An m/n-contiguous operand ("MN-major": A stored [K][M], B stored
-//    [K][N]) is kept as [128 k][R bytes] with 16-byte chunks XOR-swizzled by
-//    k, and read with ds_read_b64_tr_b8, which transposes 8x8-byte blocks
-//    across lanes so each lane receives 8 consecutive k of one row: the
-//    NN / TN layouts need no separate transpose pass.
-//  * The MFMA is issued with the B fragment as its first operand, so each
-//    lane ends with 4 consecutive output columns of one row (8-byte bf16
+//    kept as [rows][64 B] and read with two ds_read_b128 per fragment; an
+//    m/n-contiguous operand ("MN-major": A stored [K][M], B stored [K][N])
+//    is kept as [64 k][R bytes] and read with ds_read_b64_tr_b8, which
+//    transposes 8x8-byte blocks across lanes so each lane receives 8
+//    consecutive k of one row: NN / TN need no transpose pass.  The
+//    swizzles make both read patterns conflict-free on gfx950's 64-bank LDS
+//    (16 lanes per cycle for 16-byte reads).
+//  * The MFMA takes the B fragment as its first operand, so each lane ends
+//    with runs of 4 consecutive output columns of one row (8-byte bf16
 //    stores, 4-wide bias loads).
 //  * Workgroup ids are remapped so that each XCD (consecutive ids go to the 8
 //    XCDs in turn) owns a contiguous, grouped range of output tiles: tiles
@@ -33,8 +42,8 @@
 
 namespace fp8lin {
 
-constexpr int kTThreads = 256;
-constexpr int kBK = 128;
+constexpr int kBK = 64;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct TiledParams {
     const uint8_t* a;
@@ -44,97 +53,181 @@ struct TiledParams {
     const uint16_t* bias;
     uint16_t* out;
     int64_t m, n, k, lda, ldb, stride_a, stride_b;
-    int64_t tiles_m, tiles_n, tiles_per_batch;
-    int64_t group_m;
-    int vec_out;  // out rows 8-byte aligned and n % 4 == 0
+    int tiles_m, tiles_n, tiles_per_batch;
+    int group_m;
+    int vec_out;    // out rows 8-byte aligned and n % 4 == 0
+    int vec_out16;  // out rows 16-byte aligned and n % 8 == 0 (LDS-staged stores)
     int xcd_remap;
 };
 
-// Chunk swizzle of a K-major tile row r (8 chunks of 16 B per 128-byte row).
-__device__ __forceinline__ int swz_kmajor(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// Chunk swizzle of an MN-major tile row k (R / 16 chunks per row).
-template <int R>
-__device__ __forceinline__ int swz_mnmajor(int k) {
-    if constexpr (R >= 256) return (k & 7) | (((k >> 5) & 1) << 3);
-    else if constexpr (R == 128) return (k & 7) ^ ((k >> 5) & 1);
-    else return (k >> 1) & 3;
+// vmcnt-only wait (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] at [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <bool MN, int R>
-struct TileIO {
-    static_assert(R % 32 == 0 && R >= 64 && R <= 256, "tile rows");
-    static constexpr int kPasses = R / 32;                   // 16-byte loads per thread
-    static constexpr int kChunksPerRowMN = R / 16;           // MN-major
-    static constexpr int kRowsPerPassMN = kTThreads / kChunksPerRowMN;
+// lgkmcnt(0) only (LDS reads of this wave complete).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
 
-    // Global -> registers for the k-step starting at k0.  `rows` is the
-    // operand's extent along m (A) or n (B); out-of-range chunks are zero.
-    __device__ static void load(uint4 (&r)[kPasses], const uint8_t* base, int64_t ld,
-                                int64_t row0, int64_t rows, int64_t k0, int64_t kdim, int tid) {
-#pragma unroll
-        for (int q = 0; q < kPasses; ++q) {
-            bool ok;
-            const uint8_t* src;
-            if constexpr (!MN) {
-                const int row = q * 32 + tid / 8;
-                const int c = tid % 8;
-                const int64_t gr = row0 + row, gk = k0 + 16 * c;
-                ok = gr < rows && gk < kdim;
-                src = base + gr * ld + gk;
-            } else {
-                const int kr = q * kRowsPerPassMN + tid / kChunksPerRowMN;
-                const int cm = tid % kChunksPerRowMN;
-                const int64_t gk = k0 + kr, gm = row0 + 16 * cm;
-                ok = gk < kdim && gm < rows;
-                src = base + gk * ld + gm;
-            }
-            r[q] = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+// Chunk swizzle of a K-major tile row r (4 chunks of 16 B per 64-byte row):
+// the 16 rows a ds_read_b128 phase touches land on 16 distinct
+// (row mod 4, chunk) bank groups.
+__device__ __forceinline__ int swz_kmajor(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// Chunk swizzle of an MN-major tile row k (R / 16 chunks per row): even
+// values, so the two 16-lane groups of a transposed-read phase (adjacent
+// chunks, same rows) never share a bank group.
+template <int R>
+__device__ __forceinline__ int swz_mnmajor(int k) {
+    if constexpr (R >= 256) return (k & 7) << 1;
+    else if constexpr (R == 128) return ((k >> 1) & 3) << 1;
+    else return ((k >> 2) & 1) << 1;
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer range -> zeros
+
+// Buffer descriptor (raw, 4 dwords): base address, no stride, the largest
+// record count (offsets past it, such as kOOB, read as zero), and the
+// default data format.  The base is uniform; readfirstlane says so to the
+// compiler, so the descriptor lives in SGPRs.
+__device__ __forceinline__ v4i make_rsrc(const void* base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// One buffer_load_dwordx4 ... lds: lane l fetches 16 bytes at descriptor base
+// + voff and the hardware writes them to LDS at M0 + 16*l.  Written as
+// inline asm so that the compiler does not track these LDS writes: its own
+// tracking merges them at the k-loop back edge and then waits for every load
+// in flight before the next fragment read, which drains the prefetch ring.
+// The ring's waits are explicit here (wait_vmcnt), and nothing else in the
+// k loop uses the vector memory counter.  The instruction has no output
+// register; the s_nop covers the M0-write-to-LDS-DMA hazard.
+__device__ __forceinline__ void dma16(const v4i& rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds_addr));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+
+template <bool MN, int R, int NW>
+struct Operand {
+    static_assert(R == 64 || R == 128 || R == 256, "tile rows");
+    static constexpr int kInstr = R * kBK / 1024;  // 1 KB DMA instructions per stage
+    static_assert(kInstr % NW == 0, "instructions per wave");
+    static constexpr int kPerWave = kInstr / NW;
+
+    // Lane layout of DMA instruction j of this wave: the tile row (K-major)
+    // or k row (MN-major) and the 16-byte chunk it fetches.
+    __device__ static void slot(int j, int wave, int lane, int& row, int& chunk) {
+        const int i = wave + j * NW;
+        if constexpr (!MN) {
+            row = 16 * i + (lane >> 2);
+            chunk = (lane & 3) ^ swz_kmajor(row);
+        } else {
+            constexpr int kRowsPer = 1024 / R;
+            constexpr int kChunks = R / 16;
+            row = kRowsPer * i + lane / kChunks;
+            chunk = (lane % kChunks) ^ swz_mnmajor<R>(row);
         }
     }
 
-    __device__ static void store(uint8_t* lds, const uint4 (&r)[kPasses], int tid) {
+    // Per-lane byte offset of each DMA instruction at k = 0 (kOOB when the
+    // lane's row or column lies outside the matrix).  `rows_left` = extent
+    // of the operand along m (A) or n (B) from this tile's origin.
+    __device__ static void init(uint32_t (&base)[kPerWave], uint32_t ld, int64_t rows_left,
+                                int wave, int lane) {
 #pragma unroll
-        for (int q = 0; q < kPasses; ++q) {
-            int off;
-            if constexpr (!MN) {
-                const int row = q * 32 + tid / 8;
-                const int c = tid % 8;
-                off = row * kBK + ((c ^ swz_kmajor(row)) << 4);
-            } else {
-                const int kr = q * kRowsPerPassMN + tid / kChunksPerRowMN;
-                const int cm = tid % kChunksPerRowMN;
-                off = kr * R + ((cm ^ swz_mnmajor<R>(kr)) << 4);
-            }
-            *reinterpret_cast<uint4*>(lds + off) = r[q];
+        for (int j = 0; j < kPerWave; ++j) {
+            int row, c;
+            slot(j, wave, lane, row, c);
+            if constexpr (!MN)
+                base[j] = row < rows_left ? (uint32_t)row * ld + 16 * c : kOOB;
+            else
+                base[j] = 16 * c < rows_left ? (uint32_t)row * ld + 16 * c : kOOB;
         }
     }
 
-    // MFMA operand for the 16 tile rows starting at rf: lane l gets row
-    // rf + l%16 and k = 32*(l/16) .. +31 of this k-step.
-    __device__ static v8i frag(const uint8_t* lds, int rf, int lane) {
+    // Issue this wave's DMA loads of the k-step starting at k0 into `lds`.
+    // All offsets are 32-bit (the host only takes this path when every
+    // operand slice is addressable that way).
+    __device__ static void issue(const v4i& rs, uint8_t* lds,
+                                 const uint32_t (&base)[kPerWave], uint32_t ld, int k0,
+                                 int kdim, int wave, int lane) {
+        const uint32_t delta = MN ? (uint32_t)k0 * ld : (uint32_t)k0;
+        const bool full = k0 + kBK <= kdim;  // uniform: no k tail in this step
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            uint32_t off = base[j] + delta;
+            if (!full) {
+                int row, c;
+                slot(j, wave, lane, row, c);
+                const int gk = MN ? k0 + row : k0 + 16 * c;
+                if (gk >= kdim) off = kOOB;
+            }
+            dma16(rs, lds_addr(lds + 1024 * (wave + j * NW)), off);
+        }
+    }
+
+    // Fragment addressing.  The MFMA operand of the 32 tile rows starting at
+    // rf gives lane l row rf + l%32 and k = 32*(l/32) .. +31 of the stage.
+    // The lane-dependent part of each address is computed once (frag_off);
+    // what varies with the stage and the k group is a compile-time constant,
+    // so every read in the k loop is one VGPR plus an immediate offset.
+    //
+    // K-major: row = rf + l%32 and rf is a multiple of 32, so the swizzle
+    // depends on the lane only and rf adds rf*64.  The two 16-byte halves
+    // sit in chunks c and c^1 (c = (2*(l/32)) ^ swizzle).
+    // MN-major (ds_read_b64_tr_b8): within each 16-lane group, lane p names
+    // the 8 bytes at (k = kb + 8q + p/2, m = mb + 8*(p%2)) and lane p of the
+    // group receives m = mb + p for k = kb+8q .. +7 (q = 0..3).  The swizzle
+    // of row k depends on p only (kb and 8q are multiples of 8), so q adds
+    // 8q*R; the chunk (mb/16) ^ swizzle depends on rf and stays per fragment.
+    __device__ static uint32_t frag_off(int rf, int lane) {
+        if constexpr (!MN) {
+            const int row = lane & 31;  // rf*64 is added as a constant
+            const int c = (2 * (lane >> 5)) ^ swz_kmajor(row);
+            (void)rf;
+            return (uint32_t)(row * kBK + (c << 4));
+        } else {
+            const int g = lane >> 4, p = lane & 15;
+            const int mb = rf + 16 * (g & 1);
+            const int kr = 32 * (g >> 1) + (p >> 1);
+            return (uint32_t)(kr * R + (((mb >> 4) ^ swz_mnmajor<R>(kr)) << 4) + 8 * (p & 1));
+        }
+    }
+
+    // Reads a fragment: `lds` = stage start (K-major: plus rf*64), `off` =
+    // frag_off(rf, lane).
+    __device__ static v8i frag(const uint8_t* lds, uint32_t off) {
         v8i v;
         if constexpr (!MN) {
-            const int row = rf + (lane & 15);
-            const int c0 = 2 * (lane >> 4);
-            const int sw = swz_kmajor(row);
-            const uint4 lo = *reinterpret_cast<const uint4*>(lds + row * kBK + ((c0 ^ sw) << 4));
-            const uint4 hi =
-                *reinterpret_cast<const uint4*>(lds + row * kBK + (((c0 + 1) ^ sw) << 4));
-            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+            // chunk c^1 is 16 bytes after c when c is even, before it when odd
+            const uint8_t* base = lds;
+            const v4i lo = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+                (lds_void*)(base + off));
+            const uint32_t off_hi = off ^ 16u;
+            const v4i hi = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+                (lds_void*)(base + off_hi));
+            v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+            v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
         } else {
-            // ds_read_b64_tr_b8: within each 16-lane group, lane p names the
-            // 8 bytes at (k = kb + p/2, m = rf + 8*(p%2)); lane l receives the
-            // bytes of m = rf + l for k = kb .. kb+7.
-            const int g = lane >> 4, p = lane & 15;
-            const int cm = rf >> 4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int kr = 32 * g + 8 * q + (p >> 1);
-                const int off = kr * R + ((cm ^ swz_mnmajor<R>(kr)) << 4) + 8 * (p & 1);
                 const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(lds + off));
+                    (__attribute__((address_space(3))) v2i*)(lds + off + 8 * q * R));
                 v[2 * q] = t[0];
                 v[2 * q + 1] = t[1];
             }
@@ -143,112 +236,243 @@ struct TileIO {
     }
 };
 
-template <int FMT, bool AMN, bool BMN, int BM, int BN>
-__global__ __launch_bounds__(kTThreads, 1) void gemm_tiled_kernel(TiledParams p) {
-    constexpr int kStage = (BM + BN) * kBK;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-    using IOA = TileIO<AMN, BM>;
-    using IOB = TileIO<BMN, BN>;
-    constexpr int FM = BM / 32;  // 16-row fragments per wave along m
-    constexpr int FN = BN / 32;  // along n
+template <int FMT>
+__device__ __forceinline__ v16f mfma32x32x64(const v8i& x, const v8i& y, v16f acc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, FMT, FMT, 0, 0, 0, 0);
+}
+
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p) {
+    constexpr int NW = WM * WN;
+    constexpr int kStageA = BM * kBK, kStageB = BN * kBK;
+    constexpr int kStage = kStageA + kStageB;
+    constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    using OA = Operand<AMN, BM, NW>;
+    using OB = Operand<BMN, BN, NW>;
+    constexpr int kLoads = OA::kPerWave + OB::kPerWave;  // DMA loads per wave per step
+    static_assert(kLoads * (STAGES - 1) < 64, "vmcnt range");
+    // One LDS array per stage rather than one array cut into stages: the
+    // compiler tracks pending LDS DMA per array, so reads of one stage do not
+    // get an implicit wait for the DMA still filling another.
+    static_assert(STAGES == 2 || STAGES == 4, "stage count");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGES > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem3[STAGES > 2 ? kStage : 16];
+    // Stage indices are compile-time constants after unrolling, so this folds.
+    auto stage_buf = [&](int st) -> uint8_t* {
+        return st == 0 ? smem0 : st == 1 ? smem1 : st == 2 ? smem2 : smem3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wm = wave / WN, wn = wave % WN;
 
-    // Tile of this workgroup.
-    int64_t bid = blockIdx.x;
-    const int64_t G = gridDim.x;
+    // Tile of this workgroup (32-bit, uniform: tile counts fit easily).
+    int bid = blockIdx.x;
+    const int G = gridDim.x;
     if (p.xcd_remap) bid = (bid & 7) * (G >> 3) + (bid >> 3);
-    const int64_t bz = bid / p.tiles_per_batch;
-    const int64_t t = bid - bz * p.tiles_per_batch;
-    const int64_t per_group = p.group_m * p.tiles_n;
-    const int64_t first_m = (t / per_group) * p.group_m;
-    const int64_t gsz = p.tiles_m - first_m < p.group_m ? p.tiles_m - first_m : p.group_m;
-    const int64_t r = t - (t / per_group) * per_group;
-    const int64_t tm = first_m + r % gsz;
-    const int64_t tn = r / gsz;
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int bz = bid / p.tiles_per_batch;
+    const int t = bid - bz * p.tiles_per_batch;
+    const int per_group = p.group_m * p.tiles_n;
+    const int first_m = (t / per_group) * p.group_m;
+    const int gsz = p.tiles_m - first_m < p.group_m ? p.tiles_m - first_m : p.group_m;
+    const int r = t - (t / per_group) * per_group;
+    const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((first_m + r % gsz) * BM);
+    const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((r / gsz) * BN);
 
-    const uint8_t* A = p.a + bz * p.stride_a;
-    const uint8_t* B = p.b + bz * p.stride_b;
+    // Buffer descriptors based at this tile's first row / column.
+    const uint8_t* A = p.a + (int64_t)bz * p.stride_a + (AMN ? m0 : m0 * p.lda);
+    const uint8_t* B = p.b + (int64_t)bz * p.stride_b + (BMN ? n0 : n0 * p.ldb);
+    const v4i ra = make_rsrc(A);
+    const v4i rb = make_rsrc(B);
+    const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
+    const int kdim = (int)p.k;
+    uint32_t abase[OA::kPerWave], bbase[OB::kPerWave];
+    OA::init(abase, lda, p.m - m0, wave, lane);
+    OB::init(bbase, ldb, p.n - n0, wave, lane);
 
-    uint4 ra[IOA::kPasses], rb[IOB::kPasses];
-    IOA::load(ra, A, p.lda, m0, p.m, 0, p.k, tid);
-    IOB::load(rb, B, p.ldb, n0, p.n, 0, p.k, tid);
-    IOA::store(smem, ra, tid);
-    IOB::store(smem + BM * kBK, rb, tid);
-    __syncthreads();
+    auto issue = [&](int stage, int step) {
+        uint8_t* s = stage_buf(stage);
+        OA::issue(ra, s, abase, lda, step * kBK, kdim, wave, lane);
+        OB::issue(rb, s + kStageA, bbase, ldb, step * kBK, kdim, wave, lane);
+    };
 
-    v4f acc[FM][FN];
+    // Fragments are read one step ahead: while step t's MFMAs run, the
+    // fragments of step t+1 are already coming in from LDS, so the MFMA pipe
+    // does not idle behind the barrier + LDS latency of each step.
+    v8i af[2][FM], bf[2][FN];
+    // Per-lane fragment offsets within a stage (see Operand::frag_off).
+    uint32_t aoff[FM], boff[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) aoff[i] = OA::frag_off(AMN ? wm * TM + 32 * i : 0, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) boff[j] = OB::frag_off(BMN ? wn * TN + 32 * j : 0, lane);
+    // K-major fragments add the wave's first tile row as a byte offset.
+    const uint32_t arow = AMN ? 0u : (uint32_t)(wm * TM * kBK);
+    const uint32_t brow = BMN ? 0u : (uint32_t)(wn * TN * kBK);
+    auto read_frags = [&](int buf, int slot) {
+        const uint8_t* la = stage_buf(buf) + arow;
+        const uint8_t* lb = stage_buf(buf) + kStageA + brow;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[slot][i] = OA::frag(la + (AMN ? 0 : 32 * i * kBK), aoff[i]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[slot][j] = OB::frag(lb + (BMN ? 0 : 32 * j * kBK), boff[j]);
+    };
+    // The empty asm statements keep the compiler from moving LDS accesses
+    // across the raw barriers.
+    auto barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // Prologue: every buffer starts loading; step 0's fragments are read.
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue(s, s);
+    wait_vmcnt<kLoads * (STAGES - 1)>();
+    barrier();
+    read_frags(0, 0);
+
+    v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int64_t nk = (p.k + kBK - 1) / kBK;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        const bool more = kt + 1 < nk;
-        if (more) {
-            IOA::load(ra, A, p.lda, m0, p.m, (kt + 1) * kBK, p.k, tid);
-            IOB::load(rb, B, p.ldb, n0, p.n, (kt + 1) * kBK, p.k, tid);
-        }
-        const uint8_t* la = smem + cur * kStage;
-        const uint8_t* lb = la + BM * kBK;
-        v8i af[FM];
+    static_assert(STAGES % 2 == 0, "fragment slots alternate with the unrolled step");
+    const int nk = (kdim + kBK - 1) / kBK;
+    for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = IOA::frag(la, wm * (BM / 2) + 16 * i, lane);
+        for (int s = 0; s < STAGES; ++s) {
+            const int step = t0 + s;
+            if (step >= nk) break;
+            const int cur = s & 1;
+            // Own loads of step+1 landed and own reads of step's buffer done;
+            // after the barrier that holds for every wave, so step+1 can be
+            // read and step's buffer refilled with step+STAGES.
+            wait_vmcnt<kLoads * (STAGES - 2)>();
+            wait_lgkmcnt0();
+            barrier();
+            issue(s, step + STAGES);
+            read_frags((s + 1) % STAGES, cur ^ 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const v8i bf = IOB::frag(lb, wn * (BN / 2) + 16 * j, lane);
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i][j] = mfma16x16x128<FMT>(bf, af[i], acc[i][j]);
-        }
-        if (more) {
-            uint8_t* nxt = smem + (cur ^ 1) * kStage;
-            IOA::store(nxt, ra, tid);
-            IOB::store(nxt + BM * kBK, rb, tid);
-        }
-        __syncthreads();
-    }
-
-    // Epilogue: lane holds rows m0 + wm*BM/2 + 16i + lane%16, columns
-    // n0 + wn*BN/2 + 16j + 4*(lane/16) + 0..3.
-    const float s = (*p.sa) * (*p.sb);
-    uint16_t* out = p.out + bz * p.m * p.n;
+                for (int i = 0; i < FM; ++i)
+                    acc[i][j] = mfma32x32x64<FMT>(bf[cur][j], af[cur][i], acc[i][j]);
+            // Interleave the step's LDS reads between its MFMAs (1 MFMA, then
+            // a share of the reads), so the matrix pipe stays fed while they
+            // issue.
+            constexpr int kMF = FM * FN;
+            constexpr int kDS = FM * (AMN ? 4 : 2) + FN * (BMN ? 4 : 2);
+            constexpr int kDSPer = (kDS + kMF - 1) / kMF;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int64_t gn = n0 + wn * (BN / 2) + 16 * j + 4 * (lane >> 4);
-        float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.bias) {
-            if (p.vec_out && gn + 3 < p.n) {
-                const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gn);
-                bias[0] = bf16_lo(bb.x); bias[1] = bf16_hi(bb.x);
-                bias[2] = bf16_lo(bb.y); bias[3] = bf16_hi(bb.y);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (gn + q < p.n) bias[q] = bf16_to_f32(p.bias[gn + q]);
+            for (int m = 0; m < kMF; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, kDSPer, 0);  // DS read
             }
         }
+    }
+    wait_vmcnt<0>();  // drain the (out-of-range) prefetches before exit
+
+    // Epilogue: acc[i][j][e] is row m0 + wm*TM + 32i + lane%32, column
+    // n0 + wn*TN + 32j + 8*(e/4) + 4*(lane/32) + e%4.
+    const float s = (*p.sa) * (*p.sb);
+    uint16_t* out = p.out + bz * p.m * p.n;
+    if (p.vec_out16) {
+        // Through LDS: each wave rounds its tile to bf16 into its own LDS
+        // region (16-byte chunks XOR-swizzled by row), then writes whole
+        // 16-byte chunks, 8 lanes per row, so every store instruction fills
+        // complete 128-byte lines instead of scattering 8-byte pieces.
+        constexpr int kRowBytes = TN * 2;
+        constexpr int kChunks = kRowBytes / 16;
+        constexpr int kRowsPerPass = 64 / kChunks;
+        constexpr int kRegion = TM * kRowBytes;  // one wave's staging bytes
+        static_assert(kStage % kRegion == 0 && NW * kRegion <= STAGES * kStage,
+                      "epilogue staging fits the stage buffers");
+        barrier();  // every wave is done with the operand buffers
+        uint8_t* wl = stage_buf(wave / (kStage / kRegion)) + (wave % (kStage / kRegion)) * kRegion;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t gm = m0 + wm * (BM / 2) + 16 * i + (lane & 15);
-            if (gm >= p.m) continue;
-            uint16_t h[4];
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16(fmaf(acc[i][j][q], s, bias[q]));
-            uint16_t* dst = out + gm * p.n + gn;
-            if (p.vec_out && gn + 3 < p.n) {
-                *reinterpret_cast<uint2*>(dst) =
-                    make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                               (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-            } else {
+            for (int q = 0; q < 4; ++q) {
+                const int cl = 32 * j + 8 * q + 4 * (lane >> 5);  // column in the wave tile
+                const int64_t gn = n0 + wn * TN + cl;
+                float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (p.bias && gn < p.n) {
+                    const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gn);
+                    bias[0] = bf16_lo(bb.x); bias[1] = bf16_hi(bb.x);
+                    bias[2] = bf16_lo(bb.y); bias[3] = bf16_hi(bb.y);
+                }
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (gn + q < p.n) dst[q] = h[q];
+                for (int i = 0; i < FM; ++i) {
+                    const int r = 32 * i + (lane & 31);
+                    uint16_t h[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], s, bias[c]));
+                    const int chunk = (cl >> 3) ^ (r % kChunks);
+                    v2i pk;
+                    pk[0] = (int)((uint32_t)h[0] | ((uint32_t)h[1] << 16));
+                    pk[1] = (int)((uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                    *reinterpret_cast<__attribute__((address_space(3))) v2i*>(
+                        (lds_void*)(wl + r * kRowBytes + chunk * 16 + 8 * (lane >> 5))) = pk;
+                }
+            }
+        }
+        const int cc = lane % kChunks;  // this lane's 16-byte chunk of a row
+        const int64_t gn = n0 + wn * TN + 8 * cc;
+#pragma unroll
+        for (int ps = 0; ps < TM / kRowsPerPass; ++ps) {
+            const int r = ps * kRowsPerPass + lane / kChunks;
+            const v4i v = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+                (lds_void*)(wl + r * kRowBytes + ((cc ^ (r % kChunks)) << 4)));
+            const int64_t gm = m0 + wm * TM + r;
+            if (gm < p.m && gn < p.n) *reinterpret_cast<v4i*>(out + gm * p.n + gn) = v;
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t gn = n0 + wn * TN + 32 * j + 8 * q + 4 * (lane >> 5);
+            float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                if (p.vec_out && gn + 3 < p.n) {
+                    const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gn);
+                    bias[0] = bf16_lo(bb.x); bias[1] = bf16_hi(bb.x);
+                    bias[2] = bf16_lo(bb.y); bias[3] = bf16_hi(bb.y);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (gn + c < p.n) bias[c] = bf16_to_f32(p.bias[gn + c]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int64_t gm = m0 + wm * TM + 32 * i + (lane & 31);
+                if (gm >= p.m) continue;
+                uint16_t h[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], s, bias[c]));
+                uint16_t* dst = out + gm * p.n + gn;
+                if (p.vec_out && gn + 3 < p.n) {
+                    *reinterpret_cast<uint2*>(dst) =
+                        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (gn + c < p.n) dst[c] = h[c];
+                }
             }
         }
     }
@@ -267,10 +491,16 @@ bool gemm_tiled_supported(const GemmLaunch& g) {
     if ((!a_mn || !b_mn) && (g.k % 16)) return false;  // k-contiguous operand
     if (a_mn && (g.m % 16)) return false;
     if (b_mn && (g.n % 16)) return false;
+    // 32-bit buffer offsets within one batch slice
+    const double lim = 2147483647.0;
+    if ((double)(a_mn ? g.k : g.m) * (double)g.lda >= lim) return false;
+    if ((double)(b_mn ? g.k : g.n) * (double)g.ldb >= lim) return false;
+    // 32-bit tile ids (64 x 64 is the smallest tile)
+    if ((double)((g.m + 63) / 64) * (double)((g.n + 63) / 64) * (double)g.batch >= lim) return false;
     return true;
 }
 
-template <int FMT, bool AMN, bool BMN, int BM, int BN>
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int ST>
 static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     TiledParams p{};
     p.a = g.a;
@@ -286,16 +516,17 @@ static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     p.ldb = g.ldb;
     p.stride_a = g.batch > 1 ? g.stride_a : 0;
     p.stride_b = g.batch > 1 ? g.stride_b : 0;
-    p.tiles_m = (g.m + BM - 1) / BM;
-    p.tiles_n = (g.n + BN - 1) / BN;
+    p.tiles_m = (int)((g.m + BM - 1) / BM);
+    p.tiles_n = (int)((g.n + BN - 1) / BN);
     p.tiles_per_batch = p.tiles_m * p.tiles_n;
     p.group_m = 4;
-    p.vec_out = ((reinterpret_cast<uintptr_t>(g.out) & 7) == 0) && (g.n % 4 == 0) &&
-                (g.bias == nullptr || (reinterpret_cast<uintptr_t>(g.bias) & 7) == 0);
+    const bool bias8 = g.bias == nullptr || (reinterpret_cast<uintptr_t>(g.bias) & 7) == 0;
+    p.vec_out = ((reinterpret_cast<uintptr_t>(g.out) & 7) == 0) && (g.n % 4 == 0) && bias8;
+    p.vec_out16 = ((reinterpret_cast<uintptr_t>(g.out) & 15) == 0) && (g.n % 8 == 0) && bias8;
     const int64_t total = p.tiles_per_batch * g.batch;
     p.xcd_remap = (total % 8) == 0;
-    hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN>), dim3((unsigned)total),
-                       dim3(kTThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, ST>),
+                       dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -304,9 +535,9 @@ static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
     // Pick the largest tile that still gives every CU at least one tile.
     const int64_t t256 = ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
     const int64_t t128 = ((g.m + 127) / 128) * ((g.n + 127) / 128) * g.batch;
-    if (t256 >= 256) return launch_cfg<FMT, AMN, BMN, 256, 256>(g, stream);
-    if (t128 >= 256 || g.m > 64) return launch_cfg<FMT, AMN, BMN, 128, 128>(g, stream);
-    return launch_cfg<FMT, AMN, BMN, 64, 64>(g, stream);
+    if (t256 >= 256) return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 4>(g, stream);
+    if (t128 >= 256 || g.m > 64) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 2, 4>(g, stream);
+    return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 4>(g, stream);
 }
 
 template <int FMT>

@@ -11,38 +11,42 @@
 //  * A workgroup of WM x WN waves owns a BM x BN output tile; each wave owns
 //    (BM/WM) x (BN/WN) as 32x32 MFMA tiles with fp32 accumulators in
 //    registers.
-//  * k advances 64 per step.  Operand tiles go global -> LDS with
+//  * A stage holds 128 k of both operand tiles; the MFMAs take it in two
+//    substeps of 64 k.  Operand tiles go global -> LDS with
 //    buffer_load_dwordx4 ... lds (no register staging): each instruction
 //    writes 1 KB of LDS in lane order, and each lane picks the 16 global
 //    bytes that belong at its LDS slot, which is how the XOR swizzle is
-//    applied.  Out-of-range chunks (matrix tails, steps past the end of k)
-//    use an offset beyond the buffer range and arrive as zeros.
-//  * STAGES LDS buffers form a ring: at the top of step t each wave waits
-//    for its own loads of step t (vmcnt), a raw s_barrier makes everyone's
-//    loads visible and frees the buffer read in step t-1, which then
-//    receives step t+STAGES-1.  The loop is unrolled by STAGES so that every
-//    LDS offset is a compile-time constant.
+//    applied.  128 k per stage makes every row segment a load touches a
+//    whole 128-byte line: half-line segments measured at half the load
+//    throughput on this part.  Out-of-range chunks (matrix tails, stages past
+//    the end of k) use an offset beyond the buffer range and arrive as zeros.
+//  * STAGES LDS buffers form a ring.  In the second substep of stage t each
+//    wave waits for its own loads of stage t+1 (vmcnt) and for its LDS reads
+//    of stage t; a raw s_barrier then makes everyone's loads visible and
+//    frees buffer t, which receives stage t+STAGES.  The loop is unrolled by
+//    STAGES so that every LDS offset is a compile-time constant.
 //  * A k-contiguous operand ("K-major": A stored [M][K], B stored [N][K]) is
-//    kept as [rows][64 B] and read with two ds_read_b128 per fragment; an
+//    kept as [rows][128 B] and read with two ds_read_b128 per fragment; an
 //    m/n-contiguous operand ("MN-major": A stored [K][M], B stored [K][N])
-//    is kept as [64 k][R bytes] and read with ds_read_b64_tr_b8, which
+//    is kept as [128 k][R bytes] and read with ds_read_b64_tr_b8, which
 //    transposes 8x8-byte blocks across lanes so each lane receives 8
 //    consecutive k of one row: NN / TN need no transpose pass.  The
 //    swizzles make both read patterns conflict-free on gfx950's 64-bank LDS
 //    (16 lanes per cycle for 16-byte reads).
 //  * The MFMA takes the B fragment as its first operand, so each lane ends
-//    with runs of 4 consecutive output columns of one row (8-byte bf16
-//    stores, 4-wide bias loads).
+//    with runs of 4 consecutive output columns of one row.
 //  * Workgroup ids are remapped so that each XCD (consecutive ids go to the 8
 //    XCDs in turn) owns a contiguous, grouped range of output tiles: tiles
 //    that share A row panels and B column panels share an L2.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "gemm_tiled.hpp"
 
 namespace fp8lin {
 
-constexpr int kBK = 64;
+constexpr int kSub = 64;  // k per MFMA substep
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct TiledParams {
@@ -73,14 +77,22 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Chunk swizzle of a K-major tile row r (4 chunks of 16 B per 64-byte row):
-// the 16 rows a ds_read_b128 phase touches land on 16 distinct
-// (row mod 4, chunk) bank groups.
-__device__ __forceinline__ int swz_kmajor(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// Chunk swizzle of a K-major tile row r (BK/16 chunks of 16 B per row).  A
+// ds_read_b128 phase reads one chunk column of 16 consecutive rows.
+// 128-byte rows: rows 2i and 2i+1 differ in the bank half and (r/2) % 8
+// spreads the 8 row pairs over the 8 chunk positions.  64-byte rows: 4 rows
+// share a 256-byte bank line, (r/2) % 4 and r/8 spread the rest.  Either way
+// the 16 reads hit 16 distinct bank groups.  Only bits 1..3 of r are used.
+template <int BK>
+__device__ __forceinline__ int swz_kmajor(int r) {
+    if constexpr (BK == 128) return (r >> 1) & 7;
+    else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
 
 // Chunk swizzle of an MN-major tile row k (R / 16 chunks per row): even
 // values, so the two 16-lane groups of a transposed-read phase (adjacent
-// chunks, same rows) never share a bank group.
+// chunks, same rows) never share a bank group.  Depends on k % 8 only
+// through the bits used, so rows k and k + 8q share it.
 template <int R>
 __device__ __forceinline__ int swz_mnmajor(int k) {
     if constexpr (R >= 256) return (k & 7) << 1;
@@ -122,20 +134,23 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
 }
 
-template <bool MN, int R, int NW>
+template <bool MN, int R, int NW, int BK>
 struct Operand {
     static_assert(R == 64 || R == 128 || R == 256, "tile rows");
-    static constexpr int kInstr = R * kBK / 1024;  // 1 KB DMA instructions per stage
+    static_assert(BK == 64 || BK == 128, "stage depth");
+    static constexpr int kInstr = R * BK / 1024;  // 1 KB DMA instructions per stage
     static_assert(kInstr % NW == 0, "instructions per wave");
     static constexpr int kPerWave = kInstr / NW;
 
-    // Lane layout of DMA instruction j of this wave: the tile row (K-major)
-    // or k row (MN-major) and the 16-byte chunk it fetches.
+    // Lane layout of DMA instruction j of this wave: the tile row (K-major:
+    // 1024/BK rows x BK bytes per instruction) or k row (MN-major: 1024/R
+    // rows x R bytes) and the 16-byte chunk it fetches.
     __device__ static void slot(int j, int wave, int lane, int& row, int& chunk) {
         const int i = wave + j * NW;
         if constexpr (!MN) {
-            row = 16 * i + (lane >> 2);
-            chunk = (lane & 3) ^ swz_kmajor(row);
+            constexpr int kLanesPerRow = BK / 16;
+            row = (64 / kLanesPerRow) * i + lane / kLanesPerRow;
+            chunk = (lane % kLanesPerRow) ^ swz_kmajor<BK>(row);
         } else {
             constexpr int kRowsPer = 1024 / R;
             constexpr int kChunks = R / 16;
@@ -144,63 +159,69 @@ struct Operand {
         }
     }
 
-    // Per-lane byte offset of each DMA instruction at k = 0 (kOOB when the
-    // lane's row or column lies outside the matrix).  `rows_left` = extent
-    // of the operand along m (A) or n (B) from this tile's origin.
-    __device__ static void init(uint32_t (&base)[kPerWave], uint32_t ld, int64_t rows_left,
-                                int wave, int lane) {
-#pragma unroll
-        for (int j = 0; j < kPerWave; ++j) {
-            int row, c;
-            slot(j, wave, lane, row, c);
-            if constexpr (!MN)
-                base[j] = row < rows_left ? (uint32_t)row * ld + 16 * c : kOOB;
-            else
-                base[j] = 16 * c < rows_left ? (uint32_t)row * ld + 16 * c : kOOB;
-        }
+    // Instruction j of a wave covers the rows of instruction 0 shifted by
+    // j*NW instructions; the swizzle of those rows is the same (the shift is
+    // a multiple of 16 rows for K-major, of 8 k rows for MN-major), so the
+    // offset of instruction j is that of instruction 0 plus a uniform stride.
+    static constexpr int kRowStep = NW * (MN ? 1024 / R : 1024 / BK);  // rows per j
+    static_assert(NW % 2 == 0, "row shift keeps the swizzle");
+
+    // Per-lane byte offset of instruction 0 at k = 0.  MN-major: kOOB when
+    // the lane's 16 columns lie outside the matrix (the same for every j).
+    // `rows_left` = extent of the operand along m (A) or n (B) from this
+    // tile's origin.
+    __device__ static uint32_t init(uint32_t ld, int64_t rows_left, int wave, int lane) {
+        int row, c;
+        slot(0, wave, lane, row, c);
+        if constexpr (!MN) return (uint32_t)row * ld + 16 * c;
+        else return 16 * c < rows_left ? (uint32_t)row * ld + 16 * c : kOOB;
     }
 
-    // Issue this wave's DMA loads of the k-step starting at k0 into `lds`.
+    // Issue this wave's DMA loads of the stage starting at k0 into `lds`.
     // All offsets are 32-bit (the host only takes this path when every
-    // operand slice is addressable that way).
-    __device__ static void issue(const v4i& rs, uint8_t* lds,
-                                 const uint32_t (&base)[kPerWave], uint32_t ld, int k0,
-                                 int kdim, int wave, int lane) {
+    // operand slice is addressable that way; kOOB plus any in-range offset
+    // stays below 2^32 and beyond the range).  `full_rows`: every tile row
+    // exists (uniform), else K-major rows past the edge read zeros.
+    __device__ static void issue(const v4i& rs, uint8_t* lds, uint32_t base, uint32_t ld, int k0,
+                                 int kdim, bool full_rows, int64_t rows_left, int wave, int lane) {
         const uint32_t delta = MN ? (uint32_t)k0 * ld : (uint32_t)k0;
-        const bool full = k0 + kBK <= kdim;  // uniform: no k tail in this step
+        const uint32_t jstride = (uint32_t)kRowStep * ld;
+        const bool full = k0 + BK <= kdim;  // uniform: no k tail in this stage
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
-            uint32_t off = base[j] + delta;
-            if (!full) {
+            uint32_t off = base + delta + j * jstride;
+            if (!full || (!MN && !full_rows)) {
                 int row, c;
                 slot(j, wave, lane, row, c);
                 const int gk = MN ? k0 + row : k0 + 16 * c;
                 if (gk >= kdim) off = kOOB;
+                if (!MN && row >= rows_left) off = kOOB;
             }
             dma16(rs, lds_addr(lds + 1024 * (wave + j * NW)), off);
         }
     }
 
     // Fragment addressing.  The MFMA operand of the 32 tile rows starting at
-    // rf gives lane l row rf + l%32 and k = 32*(l/32) .. +31 of the stage.
-    // The lane-dependent part of each address is computed once (frag_off);
-    // what varies with the stage and the k group is a compile-time constant,
-    // so every read in the k loop is one VGPR plus an immediate offset.
+    // rf, substep h, gives lane l row rf + l%32 and k = 64h + 32*(l/32) ..
+    // +31 of the stage.  The lane-dependent part of each address is computed
+    // once (frag_off); the rest is a compile-time constant or a fixed XOR.
     //
-    // K-major: row = rf + l%32 and rf is a multiple of 32, so the swizzle
-    // depends on the lane only and rf adds rf*64.  The two 16-byte halves
-    // sit in chunks c and c^1 (c = (2*(l/32)) ^ swizzle).
+    // K-major: rf is a multiple of 32, so the swizzle depends on the lane
+    // only and rf adds rf*128.  The 16-byte pieces wanted are chunks
+    // 4h + 2*(l/32) + e (e = 0, 1); their bits are disjoint, so the swizzled
+    // chunk is (2*(l/32) ^ swizzle) ^ 4h ^ e, i.e. the substep and the half
+    // flip bits 6 and 4 of the lane's offset.
     // MN-major (ds_read_b64_tr_b8): within each 16-lane group, lane p names
     // the 8 bytes at (k = kb + 8q + p/2, m = mb + 8*(p%2)) and lane p of the
-    // group receives m = mb + p for k = kb+8q .. +7 (q = 0..3).  The swizzle
-    // of row k depends on p only (kb and 8q are multiples of 8), so q adds
-    // 8q*R; the chunk (mb/16) ^ swizzle depends on rf and stays per fragment.
+    // group receives m = mb + p for k = kb+8q .. +7 (q = 0..3), with kb =
+    // 64h + 32*(group/2).  The swizzle of row k depends on p only, so h and
+    // q add (64h + 8q)*R; the chunk (mb/16) ^ swizzle stays per fragment.
     __device__ static uint32_t frag_off(int rf, int lane) {
         if constexpr (!MN) {
-            const int row = lane & 31;  // rf*64 is added as a constant
-            const int c = (2 * (lane >> 5)) ^ swz_kmajor(row);
+            const int row = lane & 31;  // rf*128 is added as a constant
+            const int c = (2 * (lane >> 5)) ^ swz_kmajor<BK>(row);
             (void)rf;
-            return (uint32_t)(row * kBK + (c << 4));
+            return (uint32_t)(row * BK + (c << 4));
         } else {
             const int g = lane >> 4, p = lane & 15;
             const int mb = rf + 16 * (g & 1);
@@ -209,25 +230,23 @@ struct Operand {
         }
     }
 
-    // Reads a fragment: `lds` = stage start (K-major: plus rf*64), `off` =
-    // frag_off(rf, lane).
+    // Reads the substep-H fragment: `lds` = stage start (K-major: plus
+    // rf*BK), `off` = frag_off(rf, lane).
+    template <int H>
     __device__ static v8i frag(const uint8_t* lds, uint32_t off) {
         v8i v;
         if constexpr (!MN) {
-            // chunk c^1 is 16 bytes after c when c is even, before it when odd
-            const uint8_t* base = lds;
             const v4i lo = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
-                (lds_void*)(base + off));
-            const uint32_t off_hi = off ^ 16u;
+                (lds_void*)(lds + (off ^ (64u * H))));
             const v4i hi = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
-                (lds_void*)(base + off_hi));
+                (lds_void*)(lds + (off ^ (64u * H + 16u))));
             v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
             v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(lds + off + 8 * q * R));
+                    (__attribute__((address_space(3))) v2i*)(lds + off + (kSub * H + 8 * q) * R));
                 v[2 * q] = t[0];
                 v[2 * q + 1] = t[1];
             }
@@ -241,30 +260,21 @@ __device__ __forceinline__ v16f mfma32x32x64(const v8i& x, const v8i& y, v16f ac
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, FMT, FMT, 0, 0, 0, 0);
 }
 
-template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int STAGES>
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p) {
     constexpr int NW = WM * WN;
-    constexpr int kStageA = BM * kBK, kStageB = BN * kBK;
+    constexpr int kSubs = BK / kSub;  // MFMA substeps per stage
+    static_assert((STAGES * kSubs) % 2 == 0, "fragment slots alternate with the unrolled steps");
+    constexpr int kStageA = BM * BK, kStageB = BN * BK;
     constexpr int kStage = kStageA + kStageB;
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
     static_assert(FM >= 1 && FN >= 1, "wave tile");
-    using OA = Operand<AMN, BM, NW>;
-    using OB = Operand<BMN, BN, NW>;
-    constexpr int kLoads = OA::kPerWave + OB::kPerWave;  // DMA loads per wave per step
-    static_assert(kLoads * (STAGES - 1) < 64, "vmcnt range");
-    // One LDS array per stage rather than one array cut into stages: the
-    // compiler tracks pending LDS DMA per array, so reads of one stage do not
-    // get an implicit wait for the DMA still filling another.
-    static_assert(STAGES == 2 || STAGES == 4, "stage count");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t smem1[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGES > 2 ? kStage : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t smem3[STAGES > 2 ? kStage : 16];
-    // Stage indices are compile-time constants after unrolling, so this folds.
-    auto stage_buf = [&](int st) -> uint8_t* {
-        return st == 0 ? smem0 : st == 1 ? smem1 : st == 2 ? smem2 : smem3;
-    };
+    using OA = Operand<AMN, BM, NW, BK>;
+    using OB = Operand<BMN, BN, NW, BK>;
+    constexpr int kLoads = OA::kPerWave + OB::kPerWave;  // DMA loads per wave per stage
+    static_assert(STAGES >= 2 && kLoads * (STAGES - 1) < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -291,19 +301,21 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     const v4i rb = make_rsrc(B);
     const uint32_t lda = (uint32_t)p.lda, ldb = (uint32_t)p.ldb;
     const int kdim = (int)p.k;
-    uint32_t abase[OA::kPerWave], bbase[OB::kPerWave];
-    OA::init(abase, lda, p.m - m0, wave, lane);
-    OB::init(bbase, ldb, p.n - n0, wave, lane);
+    const int64_t arows = p.m - m0, brows = p.n - n0;
+    const bool afull = arows >= BM, bfull = brows >= BN;
+    const uint32_t abase = OA::init(lda, arows, wave, lane);
+    const uint32_t bbase = OB::init(ldb, brows, wave, lane);
 
-    auto issue = [&](int stage, int step) {
-        uint8_t* s = stage_buf(stage);
-        OA::issue(ra, s, abase, lda, step * kBK, kdim, wave, lane);
-        OB::issue(rb, s + kStageA, bbase, ldb, step * kBK, kdim, wave, lane);
+    auto issue = [&](int stage, int kstage) {
+        uint8_t* s = smem + stage * kStage;
+        OA::issue(ra, s, abase, lda, kstage * BK, kdim, afull, arows, wave, lane);
+        OB::issue(rb, s + kStageA, bbase, ldb, kstage * BK, kdim, bfull, brows, wave, lane);
     };
 
-    // Fragments are read one step ahead: while step t's MFMAs run, the
-    // fragments of step t+1 are already coming in from LDS, so the MFMA pipe
-    // does not idle behind the barrier + LDS latency of each step.
+    // Fragments are read one substep ahead: while substep u's MFMAs run, the
+    // fragments of u+1 are already coming in from LDS, so the MFMA pipe does
+    // not idle behind LDS latency.  Substeps alternate between two register
+    // slots.
     v8i af[2][FM], bf[2][FN];
     // Per-lane fragment offsets within a stage (see Operand::frag_off).
     uint32_t aoff[FM], boff[FN];
@@ -312,15 +324,18 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 #pragma unroll
     for (int j = 0; j < FN; ++j) boff[j] = OB::frag_off(BMN ? wn * TN + 32 * j : 0, lane);
     // K-major fragments add the wave's first tile row as a byte offset.
-    const uint32_t arow = AMN ? 0u : (uint32_t)(wm * TM * kBK);
-    const uint32_t brow = BMN ? 0u : (uint32_t)(wn * TN * kBK);
-    auto read_frags = [&](int buf, int slot) {
-        const uint8_t* la = stage_buf(buf) + arow;
-        const uint8_t* lb = stage_buf(buf) + kStageA + brow;
+    constexpr int kRowA = AMN ? 0 : BK, kRowB = BMN ? 0 : BK;
+    const uint32_t arow = (uint32_t)(wm * TM * kRowA);
+    const uint32_t brow = (uint32_t)(wn * TN * kRowB);
+    // read_frags(slot, substep, buffer)
+    auto read_frags = [&](auto slotc, auto hc, int buf) {
+        constexpr int SL = decltype(slotc)::value, H = decltype(hc)::value;
+        const uint8_t* la = smem + buf * kStage + arow;
+        const uint8_t* lb = smem + buf * kStage + kStageA + brow;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[slot][i] = OA::frag(la + (AMN ? 0 : 32 * i * kBK), aoff[i]);
+        for (int i = 0; i < FM; ++i) af[SL][i] = OA::template frag<H>(la + 32 * i * kRowA, aoff[i]);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[slot][j] = OB::frag(lb + (BMN ? 0 : 32 * j * kBK), boff[j]);
+        for (int j = 0; j < FN; ++j) bf[SL][j] = OB::template frag<H>(lb + 32 * j * kRowB, boff[j]);
     };
     // The empty asm statements keep the compiler from moving LDS accesses
     // across the raw barriers.
@@ -329,14 +344,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-
-    // Prologue: every buffer starts loading; step 0's fragments are read.
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue(s, s);
-    wait_vmcnt<kLoads * (STAGES - 1)>();
-    barrier();
-    read_frags(0, 0);
-
     v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -344,38 +351,67 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    // MFMAs of the fragments in slot SL, with the LDS reads issued since the
+    // last call spread between them (1 MFMA, then a share of the reads).
+    auto mfmas = [&](auto slotc) {
+        constexpr int SL = decltype(slotc)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                acc[i][j] = mfma32x32x64<FMT>(bf[SL][j], af[SL][i], acc[i][j]);
+        constexpr int kMF = FM * FN;
+        constexpr int kDS = FM * (AMN ? 4 : 2) + FN * (BMN ? 4 : 2);
+        constexpr int kDSPer = (kDS + kMF - 1) / kMF;
+#pragma unroll
+        for (int m = 0; m < kMF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, kDSPer, 0);  // DS read
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
-    static_assert(STAGES % 2 == 0, "fragment slots alternate with the unrolled step");
-    const int nk = (kdim + kBK - 1) / kBK;
+    // Prologue: every buffer starts loading; stage 0's first fragments are read.
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue(s, s);
+    wait_vmcnt<kLoads * (STAGES - 1)>();
+    barrier();
+    read_frags(I0{}, I0{}, 0);
+
+    // One stage = kSubs substeps.  Every substep but the last reads the next
+    // substep of the same buffer.  The last one first waits for its own
+    // loads of stage st+1 and its reads of this stage; after the barrier
+    // that holds for every wave, so st+1 can be read and this buffer
+    // refilled with st+STAGES.
+    const int nk = (kdim + BK - 1) / BK;
     for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) {
-            const int step = t0 + s;
-            if (step >= nk) break;
-            const int cur = s & 1;
-            // Own loads of step+1 landed and own reads of step's buffer done;
-            // after the barrier that holds for every wave, so step+1 can be
-            // read and step's buffer refilled with step+STAGES.
-            wait_vmcnt<kLoads * (STAGES - 2)>();
-            wait_lgkmcnt0();
-            barrier();
-            issue(s, step + STAGES);
-            read_frags((s + 1) % STAGES, cur ^ 1);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    acc[i][j] = mfma32x32x64<FMT>(bf[cur][j], af[cur][i], acc[i][j]);
-            // Interleave the step's LDS reads between its MFMAs (1 MFMA, then
-            // a share of the reads), so the matrix pipe stays fed while they
-            // issue.
-            constexpr int kMF = FM * FN;
-            constexpr int kDS = FM * (AMN ? 4 : 2) + FN * (BMN ? 4 : 2);
-            constexpr int kDSPer = (kDS + kMF - 1) / kMF;
-#pragma unroll
-            for (int m = 0; m < kMF; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, kDSPer, 0);  // DS read
+            const int st = t0 + s;
+            if (st >= nk) break;
+            if constexpr (kSubs == 2) {
+                // substep 0 uses slot 0, substep 1 slot 1
+                read_frags(I1{}, I1{}, s);
+                mfmas(I0{});
+                wait_vmcnt<kLoads * (STAGES - 2)>();
+                wait_lgkmcnt0();
+                barrier();
+                issue(s, st + STAGES);
+                read_frags(I0{}, I0{}, (s + 1) % STAGES);
+                mfmas(I1{});
+            } else {
+                wait_vmcnt<kLoads * (STAGES - 2)>();
+                wait_lgkmcnt0();
+                barrier();
+                issue(s, st + STAGES);
+                if (s & 1) {
+                    read_frags(I0{}, I0{}, (s + 1) % STAGES);
+                    mfmas(I1{});
+                } else {
+                    read_frags(I1{}, I0{}, (s + 1) % STAGES);
+                    mfmas(I0{});
+                }
             }
         }
     }
@@ -394,10 +430,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
         constexpr int kChunks = kRowBytes / 16;
         constexpr int kRowsPerPass = 64 / kChunks;
         constexpr int kRegion = TM * kRowBytes;  // one wave's staging bytes
-        static_assert(kStage % kRegion == 0 && NW * kRegion <= STAGES * kStage,
-                      "epilogue staging fits the stage buffers");
+        static_assert(NW * kRegion <= STAGES * kStage, "epilogue staging fits the stage buffers");
         barrier();  // every wave is done with the operand buffers
-        uint8_t* wl = stage_buf(wave / (kStage / kRegion)) + (wave % (kStage / kRegion)) * kRegion;
+        uint8_t* wl = smem + wave * kRegion;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -500,7 +535,7 @@ bool gemm_tiled_supported(const GemmLaunch& g) {
     return true;
 }
 
-template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int ST>
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int ST>
 static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     TiledParams p{};
     p.a = g.a;
@@ -525,7 +560,7 @@ static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     p.vec_out16 = ((reinterpret_cast<uintptr_t>(g.out) & 15) == 0) && (g.n % 8 == 0) && bias8;
     const int64_t total = p.tiles_per_batch * g.batch;
     p.xcd_remap = (total % 8) == 0;
-    hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, ST>),
+    hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST>),
                        dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
     return hipGetLastError();
 }
@@ -535,9 +570,17 @@ static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
     // Pick the largest tile that still gives every CU at least one tile.
     const int64_t t256 = ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
     const int64_t t128 = ((g.m + 127) / 128) * ((g.n + 127) / 128) * g.batch;
-    if (t256 >= 256) return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 4>(g, stream);
-    if (t128 >= 256 || g.m > 64) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 2, 4>(g, stream);
-    return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 4>(g, stream);
+    // Both operands k-contiguous: 128-byte stages (every row segment a whole
+    // line), double-buffered.  Otherwise 64-byte stages, four deep: the
+    // m/n-contiguous operand reads whole lines anyway and the deeper ring
+    // hides more latency.
+    constexpr bool kBoth = !AMN && !BMN;
+    if (t256 >= 256) {
+        if constexpr (kBoth) return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
+        else return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 64, 4>(g, stream);
+    }
+    if (t128 >= 256 || g.m > 64) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 2, 128, 4>(g, stream);
+    return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 128, 4>(g, stream);
 }
 
 template <int FMT>

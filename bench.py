@@ -153,7 +153,7 @@ class Layer:
         for r in (self.rx, self.rw, self.rg):
             r.initialized = True
 
-    def step(self, f, ev=None):
+    def step(self, f):
         M, N, K = self.M, self.N, self.K
         sx, sw = self.sfwd[0:1], self.sfwd[1:2]
         # forward (E4M3): quantize with the ring's step, fold amax, NT GEMM
@@ -161,32 +161,33 @@ class Layer:
                        scale_used=sx)
         f.fp8_quantize(self.w, E4M3, scale=self.rw.scale, out=self.w8, ring=self.rw,
                        scale_used=sw)
-        if ev:
-            ev[0][0].record()
-        f.fp8_mm(self.x8, self.w8, E4M3, 0, 1, M, N, K, K, K, 1, 0, 0, sx, sw, self.bias,
-                 self.out)
-        if ev:
-            ev[0][1].record()
+        self.gemm_nt_fwd(f)
         # backward (E5M2): g with its ring, x and w with the forward steps
         f.fp8_quantize(self.g, E5M2, scale=self.rg.scale, out=self.g8, ring=self.rg,
                        scale_used=self.sg)
         f.fp8_quantize(self.w, E5M2, scale=sw, out=self.w8b)
-        if ev:
-            ev[1][0].record()
-        f.fp8_mm(self.g8, self.w8b, E5M2, 0, 0, M, K, N, N, K, 1, 0, 0, self.sg, sw, None,
-                 self.dx)
-        if ev:
-            ev[1][1].record()
+        self.gemm_nn_dx(f)
         f.fp8_quantize(self.x, E5M2, scale=sx, out=self.x8b)
-        if ev:
-            ev[2][0].record()
-        f.fp8_mm(self.g8, self.x8b, E5M2, 1, 0, N, K, M, N, K, 1, 0, 0, self.sg, sx, None,
-                 self.dw)
-        if ev:
-            ev[2][1].record()
+        self.gemm_tn_dw(f)
         f.fp8_colsum(self.g, M, N, self.db, self.cs_ws)
         for r in (self.rx, self.rw, self.rg):
             r.idx = (r.idx + 1) % r.len
+
+    # The step's three GEMMs on its own operands (also timed on their own).
+    def gemm_nt_fwd(self, f):
+        M, N, K = self.M, self.N, self.K
+        f.fp8_mm(self.x8, self.w8, E4M3, 0, 1, M, N, K, K, K, 1, 0, 0, self.sfwd[0:1],
+                 self.sfwd[1:2], self.bias, self.out)
+
+    def gemm_nn_dx(self, f):
+        M, N, K = self.M, self.N, self.K
+        f.fp8_mm(self.g8, self.w8b, E5M2, 0, 0, M, K, N, N, K, 1, 0, 0, self.sg,
+                 self.sfwd[1:2], None, self.dx)
+
+    def gemm_tn_dw(self, f):
+        M, N, K = self.M, self.N, self.K
+        f.fp8_mm(self.g8, self.x8b, E5M2, 1, 0, N, K, M, N, K, 1, 0, 0, self.sg,
+                 self.sfwd[0:1], None, self.dw)
 
 
 def check_against_linear_entry_points(f, torch):
@@ -210,19 +211,72 @@ def check_against_linear_entry_points(f, torch):
             raise SystemExit("benchmark step differs from fp8_linear_fwd/bwd")
 
 
+# HBM traffic of the step's GEMMs from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (KiB per dispatch, one counter per run, `bench.py --kernel NAME`), scaled by
+# what the same counters read for a 192 MiB copy (FETCH_SIZE x 2.0, WRITE_SIZE
+# x 1.0).  Valid only for the kernel sources they were taken on: `src` is the
+# sha256 of gemm_tiled.hip + common.hpp then; any other source gives null.
+PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+PMC_TRAFFIC = {
+    "gemm_nn_dx": {"FETCH_SIZE": 49309.2, "WRITE_SIZE": 32768.0,
+                   "src": "45212e95110c0a845e320312e1622297461559bc2a65672a10ea8429024063de"},
+}
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for part in ("gemm_tiled.hip", "common.hpp"):
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "fp8_tensor_scaled_amd",
+                               "csrc", part), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def pmc_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the recorded counters, or None."""
+    rec = PMC_TRAFFIC.get(kernel)
+    if rec is None or rec["src"] != gemm_source_hash():
+        return None
+    return int(1024 * sum(rec[c] * PMC_SCALE[c] for c in PMC_SCALE))
+
+
 def time_kernel(torch, launch, n, rotate=1):
-    """Average duration (ms) of `launch(i)` over n launches, HIP events."""
+    """Average duration (ms) per launch of `launch(i)`, n launches back to
+    back between two HIP events on the launch stream (torch's current one)."""
     for i in range(3):
         launch(i % rotate)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for i in range(n):
-        evs[i][0].record()
         launch(i % rotate)
-        evs[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return e0.elapsed_time(e1) / n
+
+
+def time_graph(torch, launch, n):
+    """Average duration (ms) per launch of n launches `launch(i)` captured in
+    one HIP graph and replayed between two HIP events: kernels run back to
+    back with no host gaps (for kernels shorter than a launch call)."""
+    launch(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n)
+    return float(np.median(ts))
 
 
 def components(f, torch):
@@ -242,73 +296,112 @@ def components(f, torch):
     res["gemm_nt_4096"] = dict(us=round(ms * 1e3, 2),
                                tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
     del a8, b8, out
-    # 64 x 8192 x 2048 NT, weight rotated over 32 copies (537 MB)
+    # 8192^3 NT + bias
+    n = 8192
+    a8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+    b8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+    bias = torch.zeros(n, dtype=torch.int16, device=dev)
+    out = torch.empty(n * n, dtype=torch.int16, device=dev)
+    ms = time_kernel(torch, lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s,
+                                                bias, out), 10)
+    res["gemm_nt_8192"] = dict(us=round(ms * 1e3, 2),
+                               tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
+    del a8, b8, out
+    # batched NT: 8 x [1024,2048] x [2048,2048], the same with B broadcast
+    # (stride 0), and 64 x 512^3
+    for name, (batch, M, N, K, bcast) in (("bmm_8x1024x2048x2048", (8, 1024, 2048, 2048, False)),
+                                          ("bmm_bcast_8x1024x2048x2048", (8, 1024, 2048, 2048, True)),
+                                          ("bmm_64x512x512x512", (64, 512, 512, 512, False))):
+        a8 = torch.randint(0, 120, (batch * M * K,), dtype=torch.uint8, device=dev)
+        b8 = torch.randint(0, 120, ((1 if bcast else batch) * N * K,), dtype=torch.uint8,
+                           device=dev)
+        out = torch.empty(batch * M * N, dtype=torch.int16, device=dev)
+        sb_ = 0 if bcast else N * K
+        ms = time_kernel(torch, lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, M, N, K, K, K, batch,
+                                                    M * K, sb_, s, s, None, out), 20)
+        byts = a8.numel() + b8.numel() + 2 * out.numel()
+        res[name] = dict(us=round(ms * 1e3, 2),
+                         tflops=round(2 * batch * M * N * K / (ms * 1e-3) / 1e12, 1),
+                         gbs=round(byts / (ms * 1e-3) / 1e9, 1))
+        del a8, b8, out
+    # 64 x 8192 x 2048 NT, weight rotated over 64 copies (1.07 GB)
     M, N, K = 64, 8192, 2048
     d = wl.smallm()
-    rot = 32
+    rot = 64
     xs = torch.randint(0, 120, (M * K,), dtype=torch.uint8, device=dev)
     ws = [torch.randint(0, 120, (N * K,), dtype=torch.uint8, device=dev) for _ in range(rot)]
     outs = [torch.empty(M * N, dtype=torch.int16, device=dev) for _ in range(rot)]
-    ms = time_kernel(torch, lambda i: f.fp8_mm(xs, ws[i], E4M3, 0, 1, M, N, K, K, K, 1, 0, 0, s,
-                                                s, None, outs[i]), 64, rotate=rot)
+    ms = time_graph(torch, lambda i: f.fp8_mm(xs, ws[i % rot], E4M3, 0, 1, M, N, K, K, K, 1, 0,
+                                               0, s, s, None, outs[i % rot]), rot)
     byts = M * K + N * K + 2 * M * N
     res["gemm_nt_64x8192x2048"] = dict(us=round(ms * 1e3, 2),
                                        tflops=round(2 * M * N * K / (ms * 1e-3) / 1e12, 1),
                                        gbs=round(byts / (ms * 1e-3) / 1e9, 1),
                                        hbm_frac=round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
     del ws, outs, d
-    # delayed-scaling quantize of bf16 [8192, 8192] (fold on), 3 buffer sets
+    # delayed-scaling quantize of bf16 [8192, 8192] (fold on), 6 buffer sets (1.2 GB)
     n = 8192 * 8192
-    rot = 3
+    rot = 6
     xs = [torch.randn(n, device=dev).to(torch.bfloat16).view(torch.int16) for _ in range(rot)]
     qs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(rot)]
     rings = [f.Ring(16) for _ in range(rot)]
     for i in range(rot):
         f.fp8_quantize(xs[i], E4M3, ring=rings[i])
-    ms = time_kernel(torch, lambda i: f.fp8_quantize(xs[i], E4M3, scale=rings[i].scale,
-                                                      out=qs[i], ring=rings[i]), 30, rotate=rot)
+    ms = time_graph(torch, lambda i: f.fp8_quantize(xs[i % rot], E4M3,
+                                                     scale=rings[i % rot].scale,
+                                                     out=qs[i % rot], ring=rings[i % rot]),
+                    4 * rot)
     res["quantize_8192x8192"] = dict(us=round(ms * 1e3, 2),
                                      gbs=round(3 * n / (ms * 1e-3) / 1e9, 1),
                                      hbm_frac=round(3 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
     return res
 
 
-def cpu_baseline(size):
-    """The CPU oracle timed on a bounded sample of the step: every quantize
-    of the step on a 256-row slice and the three GEMMs on 32 output rows
-    each, scaled to the whole step."""
+def cpu_baseline(size, rows=1024):
+    """The CPU oracle timed on a bounded sample of one step (delayed scaling,
+    rings seeded beforehand): every quantize of the step (with its ring
+    fold) and the bias gradient over the whole tensors, and each of the
+    three GEMMs (NT forward, NN dX, TN dW) on its first `rows` output rows;
+    the GEMM time is scaled by size/rows to a whole step."""
     import workloads as wl
     from oracle import oracle as orc
     M = N = K = size
-    rows = 256
-    grow = 32
-    x = wl.normal_bf16((rows, K), 1.0, 601)
+    x = wl.normal_bf16((M, K), 1.0, 601)
     w = wl.normal_bf16((N, K), 0.02, 602)
-    g = wl.normal_bf16((rows, N), 1e-3, 604)
+    bias = wl.normal_bf16((N,), 0.1, 603)
+    g = wl.normal_bf16((M, N), 1e-3, 604)
+    rx, rw, rg = orc.Ring(16), orc.Ring(16), orc.Ring(16)
+    rw.seed(w, E4M3)
+    rx.seed(x, E4M3)
+    rg.seed(g, E5M2)
+    tq = tg = 0.0
     t0 = time.perf_counter()
-    x8 = orc.quantize(x, E4M3, 0.01)
-    w8s = orc.quantize(w[:rows], E4M3, 1e-4)
-    orc.quantize(g, E5M2, 1e-7)
-    orc.quantize(w[:rows], E5M2, 1e-4)
-    orc.quantize(x, E5M2, 0.01)
-    orc.colsum(g, rows, N)
+    sx, sw, sg = rx.scale, rw.scale, rg.scale
+    x8 = orc.quantize(x, E4M3, sx)
+    rx.fold(orc.amax(x), E4M3)
+    w8 = orc.quantize(w, E4M3, sw)
+    rw.fold(orc.amax(w), E4M3)
+    g8 = orc.quantize(g, E5M2, sg)
+    rg.fold(orc.amax(g), E5M2)
+    w8b = orc.quantize(w, E5M2, sw)
+    x8b = orc.quantize(x, E5M2, sx)
+    orc.colsum(g, M, N)
     tq = time.perf_counter() - t0
-    w8 = orc.quantize(w, E4M3, 1e-4)
+    g8t = np.ascontiguousarray(g8[:, :rows])  # TN: the first `rows` columns of g
     t0 = time.perf_counter()
-    orc.gemm(x8[:grow], w8, E4M3, False, True, grow, N, K, 0.01, 1e-4, None)
+    orc.gemm(x8[:rows], w8, E4M3, False, True, rows, N, K, sx, sw, bias)       # NT
+    orc.gemm(g8[:rows], w8b, E5M2, False, False, rows, K, N, sg, sw)           # NN
+    orc.gemm(g8t, x8b, E5M2, True, False, rows, K, M, sg, sx)                  # TN
     tg = time.perf_counter() - t0
-    del w8s
-    # scale: quantizes and colsum touch 5 tensors of M*K-ish elements + g for
-    # colsum; each GEMM of the step has M (= N) output rows
-    t_step = tq * (M / rows) + 3 * tg * (M / grow)
+    t_step = tq + tg * (size / rows)
     flops = 3 * 2.0 * M * N * K
     return dict(value=round(flops / t_step / 1e12, 6), unit="TFLOP/s",
                 cores=int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()),
                 kind="oracle",
-                sample=(f"oracle quantize x5 + colsum on {rows} of {M} rows and the NT GEMM "
-                        f"on {grow} of {M} output rows (K={K}, N={N}), scaled to the full "
-                        f"step (3 GEMMs); measured {tq + tg:.1f} s, projected step "
-                        f"{t_step:.1f} s"))
+                sample=(f"one step at M=N=K={size}: the 5 quantizes (with ring folds) and the "
+                        f"bias gradient in full ({tq:.1f} s), the NT, NN and TN GEMMs on their "
+                        f"first {rows} of {size} output rows ({tg:.1f} s, scaled x{size // rows}); "
+                        f"projected step {t_step:.1f} s"))
 
 
 def main():
@@ -339,19 +432,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    # Timed region 2: the same K steps with HIP events on the launch stream
-    # around each GEMM, for the per-launch kernel durations.
+    # The step's GEMMs, each launched 20 times back to back on its own
+    # operands between two HIP events on the launch stream: the per-launch
+    # durations the roofline entry uses.
     names = ["gemm_nt_fwd", "gemm_nn_dx", "gemm_tn_dw"]
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        layer.step(f, ev[i])
-    torch.cuda.synchronize()
     gemm_flops = 2.0 * size ** 3
     kern = {}
-    for j, nm in enumerate(names):
-        dur = float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+    for nm in names:
+        fn = getattr(layer, nm)
+        dur = time_kernel(torch, lambda i: fn(f), 20)
         kern[nm] = dict(us=round(dur * 1e3, 2), tflops=round(gemm_flops / (dur * 1e-3) / 1e12, 1))
     dom = max(names, key=lambda k: kern[k]["us"])
     achieved = kern[dom]["tflops"]
@@ -375,7 +464,8 @@ def main():
                    "M": size, "N": size, "K": size},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": pmc_traffic(dom)},
         "kernels": kern,
     }
     if not args.no_components:

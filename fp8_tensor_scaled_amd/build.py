@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8lin.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_tiled.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_tiled.hip", "gemm_skinny.hip"]
 ARCH = "gfx950"
 
 
@@ -53,7 +53,7 @@ def build(verbose: bool = False) -> str:
             print(msgs, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

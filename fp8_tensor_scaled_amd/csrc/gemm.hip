@@ -7,10 +7,12 @@
 // This file holds the dispatcher and the general kernel, which accepts any
 // layout, size, stride and alignment: every lane gathers its MFMA operand
 // bytes one by one (zero outside the matrix) and each wave owns a 16x16
-// output tile.  It is the correctness fallback for shapes the tiled kernels
-// do not take; the tiled kernels live in gemm_tiled.hip.
+// output tile.  It is the correctness fallback for shapes the fast kernels
+// do not take: gemm_skinny.hip (NT with m <= 64, bandwidth-shaped) and
+// gemm_tiled.hip (LDS-tiled MFMA, every layout).
 
 #include "common.hpp"
+#include "gemm_skinny.hpp"
 #include "gemm_tiled.hpp"
 #include "internal.hpp"
 
@@ -104,6 +106,7 @@ static hipError_t launch_generic(const GemmLaunch& g, hipStream_t stream) {
 }
 
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream) {
+    if (gemm_skinny_supported(g)) return launch_gemm_skinny(g, stream);
     if (gemm_tiled_supported(g)) return launch_gemm_tiled(g, stream);
     return launch_generic(g, stream);
 }

@@ -294,6 +294,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((first_m + r % gsz) * BM);
     const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((r / gsz) * BN);
 
+    // The epilogue's scale, fetched now so its latency hides under the loop.
+    const float sc = (*p.sa) * (*p.sb);
+
     // Buffer descriptors based at this tile's first row / column.
     const uint8_t* A = p.a + (int64_t)bz * p.stride_a + (AMN ? m0 : m0 * p.lda);
     const uint8_t* B = p.b + (int64_t)bz * p.stride_b + (BMN ? n0 : n0 * p.ldb);
@@ -419,7 +422,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 
     // Epilogue: acc[i][j][e] is row m0 + wm*TM + 32i + lane%32, column
     // n0 + wn*TN + 32j + 8*(e/4) + 4*(lane/32) + e%4.
-    const float s = (*p.sa) * (*p.sb);
     uint16_t* out = p.out + bz * p.m * p.n;
     if (p.vec_out16) {
         // Through LDS: each wave rounds its tile to bf16 into its own LDS
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
                     uint16_t h[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], s, bias[c]));
+                        h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], sc, bias[c]));
                     const int chunk = (cl >> 3) ^ (r % kChunks);
                     v2i pk;
                     pk[0] = (int)((uint32_t)h[0] | ((uint32_t)h[1] << 16));
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
                 uint16_t h[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], s, bias[c]));
+                    h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], sc, bias[c]));
                 uint16_t* dst = out + gm * p.n + gn;
                 if (p.vec_out && gn + 3 < p.n) {
                     *reinterpret_cast<uint2*>(dst) =

@@ -118,6 +118,39 @@ def test_mm_batched_and_broadcast_small(lib, orc, fmt):
         check_gemm(got, ref, absdot, K, f"batched {stra} {strb}", max_frac=1e-2)
 
 
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("M,N,K", [(64, 8200, 2064), (17, 96, 4112), (32, 256, 64),
+                                   (1, 40, 16), (48, 264, 1040), (64, 33, 8192)])
+def test_mm_short_a_edges(lib, orc, fmt, M, N, K):
+    """NT with m <= 64 (the short-A kernel): k ranges that split unevenly over
+    the waves (some get none), a partial last k step, ragged n, a single row."""
+    a8 = wl.random_codes((M, K), fmt, M + K)
+    b8 = wl.random_codes((N, K), fmt, N + K)
+    sa, sb = np.float32(2.0 ** -9), np.float32(3e-3)
+    bias = wl.normal_bf16((N,), 0.1, N + 1)
+    got = run_mm(lib, a8, b8, fmt, 0, 1, M, N, K, sa, sb, bias)
+    ref = orc.gemm(a8, b8, fmt, False, True, M, N, K, sa, sb, bias)
+    absdot = orc.gemm_absdot(a8, b8, fmt, False, True, M, N, K, sa, sb)
+    check_gemm(got, ref, absdot, K, f"short-A {M}x{N}x{K} f{fmt}", max_frac=1e-2)
+
+
+def test_mm_short_a_batched(lib, orc):
+    """Short A with per-batch A and broadcast B (stride 0), and the reverse."""
+    batch, M, N, K = 3, 40, 200, 528
+    a8 = wl.random_codes((batch, M, K), E4M3, 60)
+    b8 = wl.random_codes((batch, N, K), E4M3, 61)
+    b1 = wl.random_codes((N, K), E4M3, 62)
+    a1 = wl.random_codes((M, K), E4M3, 63)
+    for a, b, stra, strb in [(a8, b8, M * K, N * K), (a8, b1, M * K, 0), (a1, b8, 0, N * K)]:
+        got = run_mm(lib, a, b, E4M3, 0, 1, M, N, K, 1e-3, 1e-3, batch=batch, stride_a=stra,
+                     stride_b=strb)
+        ref = orc.gemm(a, b, E4M3, False, True, M, N, K, 1e-3, 1e-3, batch=batch,
+                       stride_a=stra, stride_b=strb)
+        absdot = orc.gemm_absdot(a, b, E4M3, False, True, M, N, K, 1e-3, 1e-3, batch=batch,
+                                 stride_a=stra, stride_b=strb)
+        check_gemm(got, ref, absdot, K, f"short-A batched {stra} {strb}", max_frac=1e-2)
+
+
 def test_mm_extreme_codes(lib, orc):
     """Random codes over the whole E4M3 / E5M2 range (max, subnormals, zeros)."""
     for fmt in (E4M3, E5M2):

@@ -407,7 +407,7 @@ def cpu_baseline(size, rows=1024):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -7,7 +7,7 @@ the HIP path and the CPU oracle can take their inputs from it.
 
 The shapes and distributions follow the workloads the AstrAI pages measure
 (author commit search page: the fp8 GEMM micro-benchmark shapes; compare
-view: the fp8 linear layer) as fixed by the task's five configurations:
+view: the fp8 linear layer), in five benchmark configurations:
 
   linear256   x [256,256] N(0,1), w [256,256] N(0,0.02), bias [256] N(0,0.1);
               dynamic scaling, E4M3 (seeds 101, 102, 103)

@@ -201,6 +201,35 @@ struct Operand {
         }
     }
 
+    // Two consecutive stages (k0 into `lds0`, k0 + BK into `lds1`), their
+    // instructions interleaved: for a k-contiguous operand with 64-byte
+    // stages, the two halves of every 128-byte line are requested by
+    // back-to-back instructions, which the load path serves at whole-line
+    // rate (alone, half-line requests run at about half of it).
+    __device__ static void issue2(const v4i& rs, uint8_t* lds0, uint8_t* lds1, uint32_t base,
+                                  uint32_t ld, int k0, int kdim, bool full_rows,
+                                  int64_t rows_left, int wave, int lane) {
+        const uint32_t jstride = (uint32_t)kRowStep * ld;
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kh = k0 + h * BK;
+                const uint32_t delta = MN ? (uint32_t)kh * ld : (uint32_t)kh;
+                const bool full = kh + BK <= kdim;
+                uint32_t off = base + delta + j * jstride;
+                if (!full || (!MN && !full_rows)) {
+                    int row, c;
+                    slot(j, wave, lane, row, c);
+                    const int gk = MN ? kh + row : kh + 16 * c;
+                    if (gk >= kdim) off = kOOB;
+                    if (!MN && row >= rows_left) off = kOOB;
+                }
+                dma16(rs, lds_addr((h ? lds1 : lds0) + 1024 * (wave + j * NW)), off);
+            }
+        }
+    }
+
     // Fragment addressing.  The MFMA operand of the 32 tile rows starting at
     // rf, substep h, gives lane l row rf + l%32 and k = 64h + 32*(l/32) ..
     // +31 of the stage.  The lane-dependent part of each address is computed
@@ -265,6 +294,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     constexpr int NW = WM * WN;
     constexpr int kSubs = BK / kSub;  // MFMA substeps per stage
     static_assert((STAGES * kSubs) % 2 == 0, "fragment slots alternate with the unrolled steps");
+    static_assert(kSubs == 2 || (STAGES >= 4 && STAGES % 2 == 0), "64-k stages refill in pairs");
     constexpr int kStageA = BM * BK, kStageB = BN * BK;
     constexpr int kStage = kStageA + kStageB;
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -313,6 +343,14 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
         uint8_t* s = smem + stage * kStage;
         OA::issue(ra, s, abase, lda, kstage * BK, kdim, afull, arows, wave, lane);
         OB::issue(rb, s + kStageA, bbase, ldb, kstage * BK, kdim, bfull, brows, wave, lane);
+    };
+    // stages kstage and kstage+1 into ring slots s0 and s1
+    auto issue_pair = [&](int s0, int s1, int kstage) {
+        uint8_t* a0 = smem + s0 * kStage;
+        uint8_t* a1 = smem + s1 * kStage;
+        OA::issue2(ra, a0, a1, abase, lda, kstage * BK, kdim, afull, arows, wave, lane);
+        OB::issue2(rb, a0 + kStageA, a1 + kStageA, bbase, ldb, kstage * BK, kdim, bfull, brows,
+                   wave, lane);
     };
 
     // Fragments are read one substep ahead: while substep u's MFMAs run, the
@@ -376,8 +414,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     using I1 = std::integral_constant<int, 1>;
 
     // Prologue: every buffer starts loading; stage 0's first fragments are read.
+    if constexpr (kSubs == 1) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue(s, s);
+        for (int s = 0; s < STAGES; s += 2) issue_pair(s, s + 1, s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) issue(s, s);
+    }
     wait_vmcnt<kLoads * (STAGES - 1)>();
     barrier();
     read_frags(I0{}, I0{}, 0);
@@ -404,10 +447,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
                 read_frags(I0{}, I0{}, (s + 1) % STAGES);
                 mfmas(I1{});
             } else {
-                wait_vmcnt<kLoads * (STAGES - 2)>();
+                // 64-k stages are refilled in pairs: at every odd step the
+                // slots of this step and the one before take steps
+                // st+STAGES-1 and st+STAGES.  Loads in flight after the
+                // awaited step st+1: one step of its pair plus the later
+                // pairs (odd st), or the later pairs only (even st).
+                if (s & 1) wait_vmcnt<kLoads * (STAGES - 3)>();
+                else wait_vmcnt<kLoads * (STAGES - 2)>();
                 wait_lgkmcnt0();
                 barrier();
-                issue(s, st + STAGES);
+                if (s & 1) issue_pair(s - 1, s, st + STAGES - 1);
                 if (s & 1) {
                     read_frags(I0{}, I0{}, (s + 1) % STAGES);
                     mfmas(I1{});

@@ -12,11 +12,19 @@
 // update costs no extra launch.
 //
 // gfx950 design:
-//  * HBM streaming: one workgroup = 4 waves of 64; the grid is at most two
-//    workgroups per CU and every lane keeps four 32-byte loads in flight per
-//    iteration (16 bf16 each, two 16-byte loads), storing 16 fp8 codes with
-//    one 16-byte store.  Conversions are v_cvt_pk_{fp8,bf8}_f32 after a med3
-//    clamp to +-max (satfinite).
+//  * HBM streaming: one workgroup of 16 waves per CU (at most 256
+//    workgroups), every lane keeping four 32-byte loads in flight per
+//    iteration (16 bf16 each, two 16-byte loads) and storing 16 fp8 codes
+//    with one 16-byte store.  Plain (cached) accesses: the codes feed the
+//    GEMM that follows and the bf16 input is read again by the backward's
+//    quantizes, and in the layer's step non-temporal hints measured slower
+//    (they only win on a stream of cold, never-reused buffers).
+//    Conversions are v_cvt_pk_{fp8,bf8}_f32 after a med3 clamp to +-max
+//    (satfinite).
+//  * One workgroup per CU also keeps the fold cheap: each workgroup adds two
+//    dependent atomics at the end, and their count and chain (max, ticket,
+//    final read) sit on the kernel's critical path.  The window is read at
+//    kernel start, so the last workgroup does not wait for it.
 //  * The fold uses relaxed agent-scope atomics only.  Release/acquire at
 //    agent scope write back / invalidate the per-XCD L2s and cost tens of ns
 //    per workgroup when every workgroup issues them; instead each workgroup
@@ -31,7 +39,7 @@
 
 namespace fp8lin {
 
-constexpr int kQuantThreads = 256;
+constexpr int kQuantThreads = 1024;
 constexpr int kQuantWaves = kQuantThreads / kWave;
 constexpr int kVecElems = 16;  // bf16 elements per lane per unrolled slot
 constexpr int kUnroll = 4;     // slots in flight per lane
@@ -54,17 +62,20 @@ struct QuantParams {
 };
 
 // Last-workgroup fold (wave 0): hist[idx] = amax;
-// scale = max(peak / fmax / 2^margin, 1e-12).
-__device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read) {
+// scale = max(peak / fmax / 2^margin, 1e-12).  `win` = this lane's share of
+// the window's other slots, loaded at kernel start (only the fold writes the
+// window, and the previous launch's fold finished before this kernel began).
+__device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, float win) {
     const int lane = threadIdx.x;
     float amax = 0.0f;
     if (lane == 0)
         amax = __uint_as_float(
             __hip_atomic_load(p.amax_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     amax = __shfl(amax, 0, kWave);
-    float peak = 0.0f;
-    for (int i = lane; i < p.len; i += kWave) peak = fmaxf(peak, i == p.idx ? amax : p.hist[i]);
-    peak = wave_max(peak);
+    float w = win;
+    for (int i = lane + kWave; i < p.len; i += kWave)  // windows longer than a wave
+        if (i != p.idx) w = fmaxf(w, p.hist[i]);
+    const float peak = fmaxf(wave_max(w), amax);
     if (lane == 0) {
         p.hist[p.idx] = amax;
         const float t = __fdiv_rn(peak, p.fmax);
@@ -77,7 +88,8 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read) {
 }
 
 // Workgroup max -> one atomic max, then a ticket; the last workgroup folds.
-__device__ __forceinline__ void publish_amax(const QuantParams& p, float v, float s_read) {
+__device__ __forceinline__ void publish_amax(const QuantParams& p, float v, float s_read,
+                                             float win) {
     __shared__ float slots[kQuantWaves];
     __shared__ int is_last;
     v = wave_max(v);
@@ -96,7 +108,7 @@ __device__ __forceinline__ void publish_amax(const QuantParams& p, float v, floa
         is_last = (ticket == gridDim.x - 1u);
     }
     __syncthreads();
-    if (is_last && threadIdx.x < kWave) fold_ring(p, s_read);
+    if (is_last && threadIdx.x < kWave) fold_ring(p, s_read, win);
 }
 
 template <int FMT, bool MEASURE_ONLY>
@@ -128,6 +140,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         s_read = *p.scale;
         m = __fdiv_rn(1.0f, s_read);
     }
+    // the window slot of this lane (wave 0), loaded now so that its latency
+    // hides under the streaming loop
+    const int wl = threadIdx.x;
+    const float win = (p.hist && wl < p.len && wl < kWave && wl != p.idx) ? p.hist[wl] : 0.0f;
     float amax = 0.0f;
     const int64_t tid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
@@ -155,7 +171,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         if constexpr (!MEASURE_ONLY) p.out[e] = cvt1<FMT>(f * m);
     }
     if (p.hist) {
-        publish_amax(p, amax, s_read);
+        publish_amax(p, amax, s_read, win);
     } else if constexpr (!MEASURE_ONLY) {
         if (p.scale_used && blockIdx.x == 0 && threadIdx.x == 0) *p.scale_used = s_read;
     }
@@ -164,7 +180,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
 static int quant_grid(int64_t numel, int vec) {
     const int64_t per_block = (int64_t)kQuantThreads * (vec ? kVecElems : 1);
     int64_t blocks = (numel + per_block - 1) / per_block;
-    const int64_t cap = 256 * 2;  // two workgroups per CU on 256 CUs
+    const int64_t cap = 256;  // one workgroup per CU
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     return (int)blocks;

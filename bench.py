@@ -3,21 +3,23 @@
 One step = one pass of the whole hot path over one batch of synthetic input:
 the fp8 linear layer forward + backward at M = N = K = 4096 with delayed
 scaling (history 16, margin 0) in the HYBRID format (E4M3 forward, E5M2
-gradients), through the library's entry points in the order fp8_linear_fwd
-and fp8_linear_bwd issue them:
-  quantize x, w (E4M3, fused amax, in-kernel ring fold)  -> NT GEMM + bias
-  quantize g (E5M2, fold), w, x (E5M2, forward steps)    -> NN GEMM (dX),
-  TN GEMM (dW), column sum (bias gradient).
-The step is driven through fp8_quantize / fp8_mm / fp8_colsum so that HIP
-events can bracket each GEMM launch inside the timed region; before timing,
-its outputs are checked to be bit-identical to fp8_linear_fwd / _bwd.
+gradients):
+  quantize x, w with their rings' steps (fused amax, in-kernel ring fold),
+    each pass writing the E4M3 codes and the backward's E5M2 codes
+    (fp8_quantize2)                                         -> NT GEMM + bias
+  quantize g (E5M2, fold)          -> NN GEMM (dX), TN GEMM (dW),
+  column sum of g (bias gradient).
+The results are those of fp8_linear_fwd / fp8_linear_bwd (which quantize x
+and w again in the backward); before timing, the step's outputs are checked
+to be bit-identical to theirs.
 
 value = GEMM flops of the step (3 x 2 x 4096^3) / measured step time, in
 TFLOP/s: the fp8 GEMM rate the layer delivers with its quantize overhead
-included.  Components of the metric are reported beside it: the 4096^3 NT
-GEMM alone, the 64 x 8192 x 2048 NT GEMM (TFLOP/s and HBM GB/s) and the
-delayed-scaling quantize of a bf16 [8192, 8192] tensor (GB/s), each with
-operands rotated over > 256 MB so that the MALL cannot serve them.
+included.  Components of the metric are reported beside it: 4096^3 and
+8192^3 NT GEMMs, the batched shapes, the 64 x 8192 x 2048 NT GEMM (TFLOP/s
+and HBM GB/s) and the delayed-scaling quantize of a bf16 [8192, 8192]
+tensor (GB/s); bandwidth-bound ones rotate over >= 1 GB of buffers so that
+the MALL cannot serve them.
 """
 
 from __future__ import annotations
@@ -156,18 +158,18 @@ class Layer:
     def step(self, f):
         M, N, K = self.M, self.N, self.K
         sx, sw = self.sfwd[0:1], self.sfwd[1:2]
-        # forward (E4M3): quantize with the ring's step, fold amax, NT GEMM
-        f.fp8_quantize(self.x, E4M3, scale=self.rx.scale, out=self.x8, ring=self.rx,
-                       scale_used=sx)
-        f.fp8_quantize(self.w, E4M3, scale=self.rw.scale, out=self.w8, ring=self.rw,
-                       scale_used=sw)
+        # forward: x and w quantized with their rings' steps (amax folded),
+        # each in one pass that also writes the backward's E5M2 codes with
+        # the same step; NT GEMM in E4M3
+        f.fp8_quantize2(self.x, E4M3, self.rx.scale, self.x8, E5M2, self.x8b, ring=self.rx,
+                        scale_used=sx)
+        f.fp8_quantize2(self.w, E4M3, self.rw.scale, self.w8, E5M2, self.w8b, ring=self.rw,
+                        scale_used=sw)
         self.gemm_nt_fwd(f)
-        # backward (E5M2): g with its ring, x and w with the forward steps
+        # backward (E5M2): g with its ring; dX (NN) and dW (TN)
         f.fp8_quantize(self.g, E5M2, scale=self.rg.scale, out=self.g8, ring=self.rg,
                        scale_used=self.sg)
-        f.fp8_quantize(self.w, E5M2, scale=sw, out=self.w8b)
         self.gemm_nn_dx(f)
-        f.fp8_quantize(self.x, E5M2, scale=sx, out=self.x8b)
         self.gemm_tn_dw(f)
         f.fp8_colsum(self.g, M, N, self.db, self.cs_ws)
         for r in (self.rx, self.rw, self.rg):

@@ -15,7 +15,7 @@ import os
 import torch
 
 __all__ = [
-    "E4M3", "E5M2", "FMT_MAX", "Ring", "library_path", "fp8_quantize",
+    "E4M3", "E5M2", "FMT_MAX", "Ring", "library_path", "fp8_quantize", "fp8_quantize2",
     "fp8_scale_ring_finalize", "fp8_mm", "fp8_colsum", "fp8_colsum_workspace",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
     "fp8_linear_bwd_workspace", "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset",
@@ -30,7 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 
 EXPORTED_SYMBOLS = (
-    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_scale_ring_finalize",
+    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize2",
+    "fp8_scale_ring_finalize",
     "fp8_mm", "fp8_colsum_workspace", "fp8_colsum", "fp8_linear_fwd_workspace",
     "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
     "fp8_linear_bwd_workspace", "fp8_linear_bwd", "fp8_last_error", "fp8_version",
@@ -59,6 +60,7 @@ def _load() -> ctypes.CDLL:
         "fp8_ring_state_floats": (I64, [I32]),
         "fp8_format_max": (F, [I32]),
         "fp8_quantize": (I32, [P, I64, I32, P, P, R, I32, P, P]),
+        "fp8_quantize2": (I32, [P, I64, I32, P, P, I32, P, R, I32, P, P]),
         "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
         "fp8_mm": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P,
                          P, P]),
@@ -81,7 +83,20 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
+class _Library:
+    """The loaded library, loaded on first use: importing the package (for
+    instance to run its build module) never needs a built library, and the
+    first call raises if it is missing."""
+
+    _handle = None
+
+    def __getattr__(self, name: str):
+        if _Library._handle is None:
+            _Library._handle = _load()
+        return getattr(_Library._handle, name)
+
+
+_lib = _Library()
 
 
 def _check(status: int, what: str) -> None:
@@ -160,6 +175,16 @@ def fp8_quantize(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
     st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
                            margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize")
+
+
+def fp8_quantize2(x: torch.Tensor, fmt: int, scale: torch.Tensor, out: torch.Tensor, fmt2: int,
+                  out2: torch.Tensor, ring: Ring | None = None, margin: int = 0,
+                  scale_used: torch.Tensor | None = None, stream=None) -> None:
+    """bf16 x -> fp8 codes of format ``fmt`` in ``out`` and of ``fmt2`` in
+    ``out2`` from one read of x (same step); see fp8lin.h."""
+    st = _lib.fp8_quantize2(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), fmt2, _ptr(out2),
+                            _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
+    _check(st, "fp8_quantize2")
 
 
 def fp8_scale_ring_finalize(ring: Ring, fmt: int, amax: torch.Tensor, margin: int = 0,

@@ -101,13 +101,16 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
 
 fp8_status_t do_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
                          uint8_t* out, float* ring_state, int32_t len, int32_t idx,
-                         int32_t margin, float* scale_used, hipStream_t stream) {
+                         int32_t margin, float* scale_used, hipStream_t stream,
+                         uint8_t* out2 = nullptr, int fmt2 = -1) {
     fp8lin::QuantLaunch q;
     q.x = x;
     q.numel = numel;
     q.fmt = fmt;
     q.scale = scale;
     q.out = out;
+    q.out2 = out2;
+    q.fmt2 = fmt2;
     q.ring_state = ring_state;
     q.ring_len = len;
     q.ring_idx = idx;
@@ -179,6 +182,31 @@ fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const
     if (st) return st;
     return do_quantize(x, numel, fmt, out ? scale : nullptr, out, ring ? ring->state : nullptr,
                        ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, stream);
+}
+
+fp8_status_t fp8_quantize2(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+                           uint8_t* out, fp8_fmt_t fmt2, uint8_t* out2, const fp8_ring_t* ring,
+                           int32_t margin, float* scale_used, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_quantize2: unsupported fp8 format %d", fmt);
+    if (!fmt_ok(fmt2))
+        return fail(FP8_EINVAL, "fp8_quantize2: unsupported second fp8 format %d", fmt2);
+    if (numel < 0) return fail(FP8_EINVAL, "fp8_quantize2: numel %lld < 0", (long long)numel);
+    if (numel > 0 && !x) return fail(FP8_EINVAL, "fp8_quantize2: x is NULL");
+    if (numel == 0 && !ring) return FP8_OK;  // nothing to convert, nothing to fold
+    if (!out || !out2) return fail(FP8_EINVAL, "fp8_quantize2: out and out2 are required");
+    if (!scale) return fail(FP8_EINVAL, "fp8_quantize2: scale is NULL");
+    if (ring) {
+        fp8_status_t st = check_ring(ring, "fp8_quantize2");
+        if (st) return st;
+    }
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_quantize2: margin %d outside [0, 64]", margin);
+    fp8_status_t st = check_device();
+    if (st) return st;
+    return do_quantize(x, numel, fmt, scale, out, ring ? ring->state : nullptr,
+                       ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, stream,
+                       out2, fmt2);
 }
 
 fp8_status_t fp8_scale_ring_finalize(const fp8_ring_t* ring, fp8_fmt_t fmt, const float* amax,

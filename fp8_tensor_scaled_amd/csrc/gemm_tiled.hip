@@ -201,6 +201,26 @@ struct Operand {
         }
     }
 
+    // Offset of this lane for DMA instruction j of the stage at k0 (kOOB past
+    // the matrix), and the LDS address instruction j writes.
+    __device__ static uint32_t off_of(uint32_t base, uint32_t ld, int k0, int kdim,
+                                      bool full_rows, int64_t rows_left, int j, int wave,
+                                      int lane) {
+        const uint32_t delta = MN ? (uint32_t)k0 * ld : (uint32_t)k0;
+        uint32_t off = base + delta + j * ((uint32_t)kRowStep * ld);
+        if (!(k0 + BK <= kdim) || (!MN && !full_rows)) {
+            int row, c;
+            slot(j, wave, lane, row, c);
+            const int gk = MN ? k0 + row : k0 + 16 * c;
+            if (gk >= kdim) off = kOOB;
+            if (!MN && row >= rows_left) off = kOOB;
+        }
+        return off;
+    }
+    __device__ static uint32_t lds_of(uint8_t* lds, int j, int wave) {
+        return lds_addr(lds + 1024 * (wave + j * NW));
+    }
+
     // Two consecutive stages (k0 into `lds0`, k0 + BK into `lds1`), their
     // instructions interleaved: for a k-contiguous operand with 64-byte
     // stages, the two halves of every 128-byte line are requested by
@@ -392,22 +412,68 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    // MFMAs of the fragments in slot SL, with the LDS reads issued since the
-    // last call spread between them (1 MFMA, then a share of the reads).
-    auto mfmas = [&](auto slotc) {
-        constexpr int SL = decltype(slotc)::value;
+    // The DMA instructions of one refill (a stage, or a pair of 64-k stages
+    // whose instructions alternate so both halves of each line go out back
+    // to back): offsets and LDS addresses are computed right after the
+    // barrier, the instructions themselves are spread between the MFMAs.
+    // Issued in one burst, 8 waves x 8 instructions fill the texture
+    // addresser's queue and the waves at its back stall before their first
+    // MFMA.
+    constexpr int kPairs = kSubs == 1 ? 2 : 1;
+    constexpr int kNA = OA::kPerWave * kPairs, kNB = OB::kPerWave * kPairs;
+    constexpr int kND = kNA + kNB;
+    uint32_t doff[kND], dlds[kND];
+    auto plan_refill = [&](int s0, int s1, int kstage) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int x = 0; x < kNA; ++x) {
+            const int j = x / kPairs, h = x % kPairs;
+            uint8_t* dst = smem + (h ? s1 : s0) * kStage;
+            doff[x] = OA::off_of(abase, lda, (kstage + h) * BK, kdim, afull, arows, j, wave, lane);
+            dlds[x] = OA::lds_of(dst, j, wave);
+        }
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                acc[i][j] = mfma32x32x64<FMT>(bf[SL][j], af[SL][i], acc[i][j]);
-        constexpr int kMF = FM * FN;
-        constexpr int kDS = FM * (AMN ? 4 : 2) + FN * (BMN ? 4 : 2);
-        constexpr int kDSPer = (kDS + kMF - 1) / kMF;
+        for (int x = 0; x < kNB; ++x) {
+            const int j = x / kPairs, h = x % kPairs;
+            uint8_t* dst = smem + (h ? s1 : s0) * kStage + kStageA;
+            doff[kNA + x] =
+                OB::off_of(bbase, ldb, (kstage + h) * BK, kdim, bfull, brows, j, wave, lane);
+            dlds[kNA + x] = OB::lds_of(dst, j, wave);
+        }
+    };
+
+    // One substep: the MFMAs of register slot SL; between them, in this
+    // order, the fragment reads of the next substep (slot NSL, substep NH of
+    // buffer nbuf) and, when `refill`, the planned DMA instructions.  The
+    // sched_barriers keep that interleave exactly as written.
+    constexpr int kMF = FM * FN;
+    constexpr int kFR = FM + FN;
+    constexpr int kFRPer = (kFR + kMF - 1) / kMF;
+    constexpr int kDPer = (kND + kMF - 1) / kMF;
+    auto substep = [&](auto slc, auto nslc, auto nhc, int nbuf, bool refill) {
+        constexpr int SL = decltype(slc)::value, NSL = decltype(nslc)::value;
+        constexpr int NH = decltype(nhc)::value;
+        const uint8_t* la = smem + nbuf * kStage + arow;
+        const uint8_t* lb = smem + nbuf * kStage + kStageA + brow;
 #pragma unroll
         for (int m = 0; m < kMF; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, kDSPer, 0);  // DS read
+            const int i = m % FM, j = m / FM;
+            acc[i][j] = mfma32x32x64<FMT>(bf[SL][j], af[SL][i], acc[i][j]);
+#pragma unroll
+            for (int q = 0; q < kFRPer; ++q) {
+                const int f = m * kFRPer + q;
+                if (f < FM) af[NSL][f] = OA::template frag<NH>(la + 32 * f * kRowA, aoff[f]);
+                else if (f < kFR)
+                    bf[NSL][f - FM] =
+                        OB::template frag<NH>(lb + 32 * (f - FM) * kRowB, boff[f - FM]);
+            }
+            if (refill) {
+#pragma unroll
+                for (int q = 0; q < kDPer; ++q) {
+                    const int x = m * kDPer + q;
+                    if (x < kND) dma16(x < kNA ? ra : rb, dlds[x], doff[x]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -438,14 +504,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
             if (st >= nk) break;
             if constexpr (kSubs == 2) {
                 // substep 0 uses slot 0, substep 1 slot 1
-                read_frags(I1{}, I1{}, s);
-                mfmas(I0{});
+                substep(I0{}, I1{}, I1{}, s, false);
                 wait_vmcnt<kLoads * (STAGES - 2)>();
                 wait_lgkmcnt0();
                 barrier();
-                issue(s, st + STAGES);
-                read_frags(I0{}, I0{}, (s + 1) % STAGES);
-                mfmas(I1{});
+                plan_refill(s, s, st + STAGES);
+                substep(I1{}, I0{}, I0{}, (s + 1) % STAGES, true);
             } else {
                 // 64-k stages are refilled in pairs: at every odd step the
                 // slots of this step and the one before take steps
@@ -456,13 +520,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
                 else wait_vmcnt<kLoads * (STAGES - 2)>();
                 wait_lgkmcnt0();
                 barrier();
-                if (s & 1) issue_pair(s - 1, s, st + STAGES - 1);
                 if (s & 1) {
-                    read_frags(I0{}, I0{}, (s + 1) % STAGES);
-                    mfmas(I1{});
+                    plan_refill(s - 1, s, st + STAGES - 1);
+                    substep(I1{}, I0{}, I0{}, (s + 1) % STAGES, true);
                 } else {
-                    read_frags(I1{}, I0{}, (s + 1) % STAGES);
-                    mfmas(I0{});
+                    substep(I0{}, I1{}, I0{}, (s + 1) % STAGES, false);
                 }
             }
         }

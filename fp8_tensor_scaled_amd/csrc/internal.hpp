@@ -14,6 +14,8 @@ struct QuantLaunch {
     int fmt = 0;
     const float* scale = nullptr;  // step s (device); m = 1/s
     uint8_t* out = nullptr;        // null: measure only
+    uint8_t* out2 = nullptr;       // optional second encoding (format fmt2)
+    int fmt2 = -1;
     float* ring_state = nullptr;   // null: no fold
     int32_t ring_len = 0;
     int32_t ring_idx = 0;

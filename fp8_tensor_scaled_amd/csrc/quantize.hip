@@ -49,6 +49,7 @@ struct QuantParams {
     int64_t numel;
     const float* scale;
     uint8_t* out;
+    uint8_t* out2;        // second format's codes (dual quantize), or null
     float* hist;          // ring window (null: no fold)
     float* scale_out;     // ring scale slot
     uint32_t* amax_slot;  // ring scratch: running amax bits
@@ -111,9 +112,11 @@ __device__ __forceinline__ void publish_amax(const QuantParams& p, float v, floa
     if (is_last && threadIdx.x < kWave) fold_ring(p, s_read, win);
 }
 
-template <int FMT, bool MEASURE_ONLY>
+// FMT2 >= 0: also encode the same scaled values in the second format into
+// dst2 (one read of x feeds both encodings).
+template <int FMT, int FMT2, bool MEASURE_ONLY>
 __device__ __forceinline__ void convert16(const uint4& r0, const uint4& r1, float m, float& amax,
-                                          uint4* dst) {
+                                          uint4* dst, uint4* dst2) {
     const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
     float f[16];
 #pragma unroll
@@ -124,16 +127,27 @@ __device__ __forceinline__ void convert16(const uint4& r0, const uint4& r1, floa
 #pragma unroll
     for (int j = 0; j < 16; j += 2) amax = fmaxf(amax, fmaxf(fabsf(f[j]), fabsf(f[j + 1])));
     if constexpr (!MEASURE_ONLY) {
+        float g[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) g[j] = f[j] * m;
         uint4 o;
-        o.x = cvt4<FMT>(f[0] * m, f[1] * m, f[2] * m, f[3] * m);
-        o.y = cvt4<FMT>(f[4] * m, f[5] * m, f[6] * m, f[7] * m);
-        o.z = cvt4<FMT>(f[8] * m, f[9] * m, f[10] * m, f[11] * m);
-        o.w = cvt4<FMT>(f[12] * m, f[13] * m, f[14] * m, f[15] * m);
+        o.x = cvt4<FMT>(g[0], g[1], g[2], g[3]);
+        o.y = cvt4<FMT>(g[4], g[5], g[6], g[7]);
+        o.z = cvt4<FMT>(g[8], g[9], g[10], g[11]);
+        o.w = cvt4<FMT>(g[12], g[13], g[14], g[15]);
         *dst = o;
+        if constexpr (FMT2 >= 0) {
+            uint4 o2;
+            o2.x = cvt4<FMT2>(g[0], g[1], g[2], g[3]);
+            o2.y = cvt4<FMT2>(g[4], g[5], g[6], g[7]);
+            o2.z = cvt4<FMT2>(g[8], g[9], g[10], g[11]);
+            o2.w = cvt4<FMT2>(g[12], g[13], g[14], g[15]);
+            *dst2 = o2;
+        }
     }
 }
 
-template <int FMT, bool MEASURE_ONLY>
+template <int FMT, int FMT2, bool MEASURE_ONLY>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) {
     float m = 0.0f, s_read = 0.0f;
     if constexpr (!MEASURE_ONLY) {
@@ -150,6 +164,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     const int64_t nvec = p.vec ? p.numel / kVecElems : 0;
     const uint4* xv = reinterpret_cast<const uint4*>(p.x);
     uint4* ov = reinterpret_cast<uint4*>(p.out);
+    uint4* ov2 = reinterpret_cast<uint4*>(p.out2);
     int64_t i = tid;
     for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
         uint4 r[kUnroll][2];
@@ -160,15 +175,19 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            convert16<FMT, MEASURE_ONLY>(r[u][0], r[u][1], m, amax, ov + i + u * stride);
+            convert16<FMT, FMT2, MEASURE_ONLY>(r[u][0], r[u][1], m, amax, ov + i + u * stride,
+                                               ov2 + i + u * stride);
     }
     for (; i < nvec; i += stride)
-        convert16<FMT, MEASURE_ONLY>(xv[2 * i], xv[2 * i + 1], m, amax, ov + i);
+        convert16<FMT, FMT2, MEASURE_ONLY>(xv[2 * i], xv[2 * i + 1], m, amax, ov + i, ov2 + i);
     // Scalar tail (everything when the bases are not 16-byte aligned).
     for (int64_t e = nvec * kVecElems + tid; e < p.numel; e += stride) {
         const float f = bf16_to_f32(p.x[e]);
         amax = fmaxf(amax, fabsf(f));
-        if constexpr (!MEASURE_ONLY) p.out[e] = cvt1<FMT>(f * m);
+        if constexpr (!MEASURE_ONLY) {
+            p.out[e] = cvt1<FMT>(f * m);
+            if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
+        }
     }
     if (p.hist) {
         publish_amax(p, amax, s_read, win);
@@ -192,6 +211,7 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     p.numel = q.numel;
     p.scale = q.scale;
     p.out = q.out;
+    p.out2 = q.out2;
     if (q.ring_state) {
         p.hist = q.ring_state;
         p.scale_out = q.ring_state + q.ring_len;
@@ -203,21 +223,29 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     p.fmax = q.fmt ? 57344.0f : 448.0f;
     p.pow2_margin = q.pow2_margin;
     p.scale_used = q.scale_used;
-    const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out);
+    const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
+                         reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;
     const dim3 grid(quant_grid(q.numel, p.vec)), block(kQuantThreads);
     const bool measure = q.out == nullptr;
-    if (q.fmt == 0) {
-        if (measure)
-            hipLaunchKernelGGL((quantize_kernel<0, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((quantize_kernel<0, false>), grid, block, 0, stream, p);
+    const int dual = q.out2 ? q.fmt2 : -1;
+#define FP8_Q(F, F2, M) hipLaunchKernelGGL((quantize_kernel<F, F2, M>), grid, block, 0, stream, p)
+    if (measure) {
+        if (q.fmt == 0) FP8_Q(0, -1, true);
+        else FP8_Q(1, -1, true);
+    } else if (dual < 0) {
+        if (q.fmt == 0) FP8_Q(0, -1, false);
+        else FP8_Q(1, -1, false);
     } else {
-        if (measure)
-            hipLaunchKernelGGL((quantize_kernel<1, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((quantize_kernel<1, false>), grid, block, 0, stream, p);
+        if (q.fmt == 0) {
+            if (dual == 0) FP8_Q(0, 0, false);
+            else FP8_Q(0, 1, false);
+        } else {
+            if (dual == 0) FP8_Q(1, 0, false);
+            else FP8_Q(1, 1, false);
+        }
     }
+#undef FP8_Q
     return hipGetLastError();
 }
 

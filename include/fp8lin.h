@@ -125,6 +125,28 @@ fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt,
                           int32_t margin, float* scale_used, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_quantize2 -- one pass over x, two encodings of the same scaled values.
+ * (compare view: astrai/extension/fp8.py _LinearFp8.backward, where under
+ *  the HYBRID recipe x and w are quantized again in E5M2 with the forward's
+ *  steps, and commit log 3e57cc8: an operand that arrives pre-quantized
+ *  skips its quantize)
+ *
+ *   out[i]  = encode_fmt ( fp32( x[i] * (1.0f / *scale) ) )
+ *   out2[i] = encode_fmt2( fp32( x[i] * (1.0f / *scale) ) )
+ *
+ * Both outputs are bit-identical to two fp8_quantize calls with the same
+ * scale (the second without a ring): the forward can emit the backward's
+ * E5M2 copies of x and w while it reads them for its E4M3 ones.
+ * x, numel, scale, ring, margin, scale_used: as fp8_quantize; the ring (if
+ * any) folds with fmt's largest value.  out, out2: fp8 [numel], both
+ * required (no measure-only form).  Empty calls behave as fp8_quantize's.
+ * ------------------------------------------------------------------- */
+fp8_status_t fp8_quantize2(const uint16_t* x, int64_t numel, fp8_fmt_t fmt,
+                           const float* scale, uint8_t* out, fp8_fmt_t fmt2, uint8_t* out2,
+                           const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_scale_ring_finalize -- fold an externally measured amax.
  * (compare view: publish_amax's last-block step, as a standalone launch)
  *

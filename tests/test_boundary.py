@@ -78,6 +78,25 @@ def test_quantize_validation(f, args, needle):
     assert st == 1 and needle in _err(f._lib)
 
 
+@pytest.mark.parametrize("args,needle", [
+    ((FAKE, 10, 0, FAKE, FAKE, 4, FAKE, None, 0, None, None), "second fp8 format"),
+    ((FAKE, 10, 9, FAKE, FAKE, 1, FAKE, None, 0, None, None), "format"),
+    ((FAKE, 10, 0, FAKE, FAKE, 1, None, None, 0, None, None), "out2"),
+    ((FAKE, 10, 0, FAKE, None, 1, FAKE, None, 0, None, None), "out2"),
+    ((FAKE, 10, 0, None, FAKE, 1, FAKE, None, 0, None, None), "scale"),
+    ((None, 10, 0, FAKE, FAKE, 1, FAKE, None, 0, None, None), "NULL"),
+    ((FAKE, -1, 0, FAKE, FAKE, 1, FAKE, None, 0, None, None), "numel"),
+    ((FAKE, 10, 0, FAKE, FAKE, 1, FAKE, None, 65, None, None), "margin"),
+])
+def test_quantize2_validation(f, args, needle):
+    st = f._lib.fp8_quantize2(*args)
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
+def test_quantize2_empty_without_ring_is_a_noop(f):
+    assert f._lib.fp8_quantize2(None, 0, 0, None, None, 1, None, None, 0, None, None) == 0
+
+
 def test_ring_validation(f):
     lib = f._lib
     r = f._RingC(0x1000, 16, 16, 0, 0)

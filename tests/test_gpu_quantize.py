@@ -205,3 +205,32 @@ def test_invalid_arguments_raise(lib):
     r.idx = 4
     with pytest.raises(ValueError):
         lib.fp8_quantize(x, 0, ring=r)
+
+
+@pytest.mark.parametrize("fmt,fmt2", [(E4M3, E5M2), (E5M2, E4M3), (E4M3, E4M3)])
+@pytest.mark.parametrize("numel,offset", [(4096 * 1024, 0), (100003, 0), (5000, 1)])
+def test_quantize2_matches_two_single_quantizes(lib, orc, fmt, fmt2, numel, offset):
+    """fp8_quantize2 writes, from one pass, the codes two fp8_quantize calls
+    with the same step give (the second without a ring), and folds the ring
+    like the first; checked against the oracle too.  `offset` misaligns the
+    tensors (scalar path)."""
+    x_all = wl.normal_bf16((numel + offset,), 3.0, 77 + numel % 13)
+    x = x_all[offset:]
+    s = np.float32(0.0123)
+    xd = to_dev_bf16(x_all)[offset:]
+    q1 = torch.empty(numel + offset, dtype=torch.uint8, device="cuda")[offset:]
+    q2 = torch.empty(numel + offset, dtype=torch.uint8, device="cuda")[offset:]
+    r1, r2 = lib.Ring(16), lib.Ring(16)
+    sd = dev_f32(s)
+    used = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lib.fp8_quantize2(xd, fmt, sd, q1, fmt2, q2, ring=r1, scale_used=used)
+    a1 = torch.empty(numel, dtype=torch.uint8, device="cuda")
+    a2 = torch.empty(numel, dtype=torch.uint8, device="cuda")
+    lib.fp8_quantize(xd, fmt, scale=sd, out=a1, ring=r2)
+    lib.fp8_quantize(xd, fmt2, scale=sd, out=a2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, a1) and torch.equal(q2, a2)
+    assert np.array_equal(from_dev_u8(q1), orc.quantize(x, fmt, s))
+    assert np.array_equal(from_dev_u8(q2), orc.quantize(x, fmt2, s))
+    assert torch.equal(r1.state, r2.state)
+    assert used.item() == s

@@ -7,8 +7,8 @@ gradients):
   quantize x, w with their rings' steps (fused amax, in-kernel ring fold),
     each pass writing the E4M3 codes and the backward's E5M2 codes
     (fp8_quantize2)                                         -> NT GEMM + bias
-  quantize g (E5M2, fold)          -> NN GEMM (dX), TN GEMM (dW),
-  column sum of g (bias gradient).
+  quantize g (E5M2, fold) with its column sum (bias gradient) from the
+    same pass (fp8_quantize_colsum)              -> NN GEMM (dX), TN GEMM (dW).
 The results are those of fp8_linear_fwd / fp8_linear_bwd (which quantize x
 and w again in the backward); before timing, the step's outputs are checked
 to be bit-identical to theirs.
@@ -166,12 +166,12 @@ class Layer:
         f.fp8_quantize2(self.w, E4M3, self.rw.scale, self.w8, E5M2, self.w8b, ring=self.rw,
                         scale_used=sw)
         self.gemm_nt_fwd(f)
-        # backward (E5M2): g with its ring; dX (NN) and dW (TN)
-        f.fp8_quantize(self.g, E5M2, scale=self.rg.scale, out=self.g8, ring=self.rg,
-                       scale_used=self.sg)
+        # backward (E5M2): g with its ring, its column sum (bias gradient)
+        # from the same pass; dX (NN) and dW (TN)
+        f.fp8_quantize_colsum(self.g, M, N, E5M2, self.rg.scale, self.g8, self.db, self.cs_ws,
+                              ring=self.rg, scale_used=self.sg)
         self.gemm_nn_dx(f)
         self.gemm_tn_dw(f)
-        f.fp8_colsum(self.g, M, N, self.db, self.cs_ws)
         for r in (self.rx, self.rw, self.rg):
             r.idx = (r.idx + 1) % r.len
 

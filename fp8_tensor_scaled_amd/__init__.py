@@ -17,6 +17,7 @@ import torch
 __all__ = [
     "E4M3", "E5M2", "FMT_MAX", "Ring", "library_path", "fp8_quantize", "fp8_quantize2",
     "fp8_scale_ring_finalize", "fp8_mm", "fp8_colsum", "fp8_colsum_workspace",
+    "fp8_quantize_colsum",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
     "fp8_linear_bwd_workspace", "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset",
     "EXPORTED_SYMBOLS",
@@ -32,7 +33,8 @@ _LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 EXPORTED_SYMBOLS = (
     "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize2",
     "fp8_scale_ring_finalize",
-    "fp8_mm", "fp8_colsum_workspace", "fp8_colsum", "fp8_linear_fwd_workspace",
+    "fp8_mm", "fp8_colsum_workspace", "fp8_colsum", "fp8_quantize_colsum",
+    "fp8_linear_fwd_workspace",
     "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
     "fp8_linear_bwd_workspace", "fp8_linear_bwd", "fp8_last_error", "fp8_version",
 )
@@ -66,6 +68,7 @@ def _load() -> ctypes.CDLL:
                          P, P]),
         "fp8_colsum_workspace": (S, [I64, I64]),
         "fp8_colsum": (I32, [P, I64, I64, P, P, S, P]),
+        "fp8_quantize_colsum": (I32, [P, I64, I64, I32, P, P, R, I32, P, P, P, S, P]),
         "fp8_linear_fwd_workspace": (S, [I64, I64, I64]),
         "fp8_linear_fwd_x8_offset": (S, [I64, I64, I64]),
         "fp8_linear_fwd_w8_offset": (S, [I64, I64, I64]),
@@ -212,6 +215,18 @@ def fp8_colsum(g: torch.Tensor, m: int, n: int, db: torch.Tensor, workspace: tor
     st = _lib.fp8_colsum(_ptr(g), m, n, _ptr(db), _ptr(workspace), workspace.numel(),
                          _stream(stream))
     _check(st, "fp8_colsum")
+
+
+def fp8_quantize_colsum(g: torch.Tensor, m: int, n: int, fmt: int, scale: torch.Tensor,
+                        out: torch.Tensor, db: torch.Tensor, workspace: torch.Tensor,
+                        ring: Ring | None = None, margin: int = 0,
+                        scale_used: torch.Tensor | None = None, stream=None) -> None:
+    """Quantize of g [m][n] and its column sum db from one read of g; the
+    results equal fp8_quantize + fp8_colsum; see fp8lin.h."""
+    st = _lib.fp8_quantize_colsum(_ptr(g), m, n, fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
+                                  margin, _ptr(scale_used), _ptr(db), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "fp8_quantize_colsum")
 
 
 def fp8_linear_fwd_workspace(M: int, N: int, K: int) -> int:

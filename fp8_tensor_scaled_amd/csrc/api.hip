@@ -121,6 +121,26 @@ fp8_status_t do_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const 
     return FP8_OK;
 }
 
+fp8_status_t do_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt_t fmt,
+                                const float* scale, uint8_t* out, float* ring_state,
+                                int32_t len, int32_t idx, int32_t margin, float* scale_used,
+                                uint16_t* db, void* ws, hipStream_t stream) {
+    fp8lin::QuantLaunch q;
+    q.x = g;
+    q.numel = m * n;
+    q.fmt = fmt;
+    q.scale = scale;
+    q.out = out;
+    q.ring_state = ring_state;
+    q.ring_len = len;
+    q.ring_idx = idx;
+    q.pow2_margin = pow2f(margin);
+    q.scale_used = scale_used;
+    hipError_t e = fp8lin::launch_quantize_colsum(q, m, n, db, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize + colsum launch");
+    return FP8_OK;
+}
+
 fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, int tb,
                      int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
                      const float* sa, const float* sb, const uint16_t* bias, uint16_t* out,
@@ -297,6 +317,32 @@ fp8_status_t fp8_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, v
     return FP8_OK;
 }
 
+fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt_t fmt,
+                                 const float* scale, uint8_t* out, const fp8_ring_t* ring,
+                                 int32_t margin, float* scale_used, uint16_t* db,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt))
+        return fail(FP8_EINVAL, "fp8_quantize_colsum: unsupported fp8 format %d", fmt);
+    if (m < 1 || n < 1) return fail(FP8_EINVAL, "fp8_quantize_colsum: m, n must be >= 1");
+    if (!g || !out || !db || !scale || !workspace)
+        return fail(FP8_EINVAL, "fp8_quantize_colsum: NULL pointer");
+    if (workspace_bytes < fp8lin::colsum_workspace(m, n))
+        return fail(FP8_EINVAL, "fp8_quantize_colsum: workspace %zu < %zu bytes",
+                    workspace_bytes, fp8lin::colsum_workspace(m, n));
+    if (ring) {
+        fp8_status_t st = check_ring(ring, "fp8_quantize_colsum");
+        if (st) return st;
+    }
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_quantize_colsum: margin %d outside [0, 64]", margin);
+    fp8_status_t st = check_device();
+    if (st) return st;
+    return do_quantize_colsum(g, m, n, fmt, scale, out, ring ? ring->state : nullptr,
+                              ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, db,
+                              workspace, stream);
+}
+
 size_t fp8_linear_fwd_workspace(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || K < 1) return 0;
     return fwd_layout(M, N, K).total;
@@ -432,9 +478,14 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         if ((st = do_quantize(g, M * N, fmt, nullptr, nullptr, rg, kScratchRingLen, 0, margin,
                               nullptr, stream)))
             return st;
-        if ((st = do_quantize(g, M * N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0, margin, sg,
-                              stream)))
+        if (db) {
+            if ((st = do_quantize_colsum(g, M, N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0,
+                                         margin, sg, db, ws + L.colsum, stream)))
+                return st;
+        } else if ((st = do_quantize(g, M * N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0,
+                                     margin, sg, stream))) {
             return st;
+        }
         if (dw) {
             if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0,
                                   margin, nullptr, stream)))
@@ -454,9 +505,16 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
                 return st;
             ring_g->initialized = 1;
         }
-        if ((st = do_quantize(g, M * N, fmt, ring_g->state + ring_g->len, g8, ring_g->state,
-                              ring_g->len, ring_g->idx, margin, sg, stream)))
+        if (db) {
+            if ((st = do_quantize_colsum(g, M, N, fmt, ring_g->state + ring_g->len, g8,
+                                         ring_g->state, ring_g->len, ring_g->idx, margin, sg, db,
+                                         ws + L.colsum, stream)))
+                return st;
+        } else if ((st = do_quantize(g, M * N, fmt, ring_g->state + ring_g->len, g8,
+                                     ring_g->state, ring_g->len, ring_g->idx, margin, sg,
+                                     stream))) {
             return st;
+        }
         sx = scales_fwd;
         sw = scales_fwd + 1;
     }
@@ -475,10 +533,6 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         // dW[N][K] = g8^T . x8: A = g8 stored [M][N] (k-major rows of m), B = x8 [M][K]  (TN)
         if ((st = do_gemm(g8, x8, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw, stream)))
             return st;
-    }
-    if (db) {
-        hipError_t e = fp8lin::launch_colsum(g, M, N, db, ws + L.colsum, stream);
-        if (e != hipSuccess) return hip_fail(e, "colsum launch");
     }
     if (!dynamic) ring_g->idx = (ring_g->idx + 1) % ring_g->len;
     return FP8_OK;

@@ -46,5 +46,10 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
 size_t colsum_workspace(int64_t m, int64_t n);
 hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, void* ws,
                          hipStream_t stream);
+// Quantize of g [m][n] (q.x = g, q.numel = m*n) fused with its column sum:
+// one read of g when the shape allows, else the two launches in sequence;
+// the column sums are the bits launch_colsum gives for the same g.
+hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, uint16_t* db,
+                                  void* ws, hipStream_t stream);
 
 }  // namespace fp8lin

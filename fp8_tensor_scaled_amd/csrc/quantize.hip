@@ -90,7 +90,7 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, fl
 
 // Workgroup max -> one atomic max, then a ticket; the last workgroup folds.
 __device__ __forceinline__ void publish_amax(const QuantParams& p, float v, float s_read,
-                                             float win) {
+                                             float win, uint32_t nblocks) {
     __shared__ float slots[kQuantWaves];
     __shared__ int is_last;
     v = wave_max(v);
@@ -106,7 +106,7 @@ __device__ __forceinline__ void publish_amax(const QuantParams& p, float v, floa
         const uint32_t inc = old == 0xffffffffu ? 2u : 1u;
         const uint32_t ticket =
             __hip_atomic_fetch_add(p.done, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (ticket == gridDim.x - 1u);
+        is_last = (ticket == nblocks - 1u);
     }
     __syncthreads();
     if (is_last && threadIdx.x < kWave) fold_ring(p, s_read, win);
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         }
     }
     if (p.hist) {
-        publish_amax(p, amax, s_read, win);
+        publish_amax(p, amax, s_read, win, gridDim.x);
     } else if constexpr (!MEASURE_ONLY) {
         if (p.scale_used && blockIdx.x == 0 && threadIdx.x == 0) *p.scale_used = s_read;
     }
@@ -277,26 +277,36 @@ hipError_t launch_ring_finalize(float* state, int32_t len, int32_t idx, int fmt,
 }
 
 // ---------------------------------------------------------------------------
-// Bias gradient: db[j] = bf16(sum_i g[i][j]), fp32 sums in a fixed order.
+// Bias gradient: db[j] = bf16(sum_i g[i][j]), fp32 sums in a fixed order,
+// optionally fused with the quantize of g (one read of g for both).
 //
-// Pass 1 (vector path, n % 8 == 0 and 16-byte aligned rows): a workgroup
-// covers 256 columns x one chunk of rows; its 256 lanes are 32 column
-// groups (8 columns = one 16-byte load) x 8 row phases, each lane summing
-// every 8th row of the chunk with up to 8 loads in flight; the 8 phases are
-// then added in LDS and the chunk's 256 column sums written as partials.
+// Pass 1 (vector path, n % 8 == 0, 16-byte aligned rows): a workgroup of
+// 1024 lanes covers 256 columns x one chunk of rows; its lanes are 32 column
+// groups (8 columns = one 16-byte load) x 32 row phases, each lane summing
+// every 32nd row of the chunk in row order with up to 8 loads in flight; the
+// 32 phases are then added in LDS in phase order and the chunk's 256 column
+// sums written as partials.  When fused, the same lanes also encode the 8
+// values of each row they read (8 codes, one 8-byte store), take the max of
+// |x| and fold it like the quantize kernel.  Chunks are sized for about one
+// workgroup per CU (the fold's atomics stay few).
 // Pass 2: 64 columns per workgroup, 4 lanes per column each adding a
 // quarter of the chunk partials, combined in a fixed order, one rounding.
+// The scalar path (other shapes) sums a column per lane over the same
+// chunks, so both paths of a given shape always give the same bits.
 // ---------------------------------------------------------------------------
-constexpr int kColThreads = 256;
-constexpr int kColPhases = 8;  // row phases per workgroup (vector path)
+constexpr int kColThreads = 256;    // pass 2 and the scalar pass 1
+constexpr int kQCThreads = 1024;    // vector pass 1
+constexpr int kQCPhases = kQCThreads / 32;  // row phases (32 column groups each)
+static_assert(kQCThreads == kQuantThreads, "the fold's per-wave slots");
 
-// Rows per chunk: chosen for ~512+ workgroups over the whole matrix.
+// Rows per chunk: about 256 workgroups over the matrix, a multiple of the
+// phase count, at most 65535 chunks.
 static int64_t colsum_rows(int64_t m, int64_t n) {
     const int64_t colblocks = (n + 255) / 256;
-    int64_t chunks = (512 + colblocks - 1) / colblocks;
+    int64_t chunks = 256 / colblocks;
+    if (chunks < 1) chunks = 1;
     int64_t rows = (m + chunks - 1) / chunks;
-    rows = (rows + kColPhases - 1) / kColPhases * kColPhases;
-    if (rows < 64) rows = 64;
+    rows = (rows + kQCPhases - 1) / kQCPhases * kQCPhases;
     while ((m + rows - 1) / rows > 65535) rows *= 2;
     return rows;
 }
@@ -309,64 +319,97 @@ size_t colsum_workspace(int64_t m, int64_t n) {
     return (size_t)colsum_chunks(m, n) * (size_t)n * sizeof(float);
 }
 
+struct QCParams {
+    QuantParams q;       // quantize + fold (x = g, out = g8); unused when !QUANT
+    const uint16_t* g;
+    int64_t m, n, rows;
+    float* part;         // [chunks][n] partial column sums
+};
+
+template <int FMT, bool QUANT>
+__global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p) {
+    float mul = 0.0f, s_read = 0.0f;
+    if constexpr (QUANT) {
+        s_read = *p.q.scale;
+        mul = __fdiv_rn(1.0f, s_read);
+    }
+    const int wl = threadIdx.x;
+    const float win = (QUANT && p.q.hist && wl < p.q.len && wl < kWave && wl != p.q.idx)
+                          ? p.q.hist[wl] : 0.0f;
+    const int cg = threadIdx.x % 32;   // column group
+    const int ph = threadIdx.x / 32;   // row phase
+    const int64_t chunk = blockIdx.y;
+    const int64_t r0 = chunk * p.rows;
+    const int64_t r1 = r0 + p.rows < p.m ? r0 + p.rows : p.m;
+    const int64_t c0 = (int64_t)blockIdx.x * 256 + cg * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float amax = 0.0f;
+    auto row = [&](const uint4& v, int64_t r) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = bf16_lo(w[j]);
+            f[2 * j + 1] = bf16_hi(w[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += f[j];
+        if constexpr (QUANT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+            uint2 o;
+            o.x = cvt4<FMT>(f[0] * mul, f[1] * mul, f[2] * mul, f[3] * mul);
+            o.y = cvt4<FMT>(f[4] * mul, f[5] * mul, f[6] * mul, f[7] * mul);
+            *reinterpret_cast<uint2*>(p.q.out + r * p.n + c0) = o;
+        }
+    };
+    if (c0 < p.n) {
+        int64_t r = r0 + ph;
+        for (; r + 7 * kQCPhases < r1; r += 8 * kQCPhases) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = *reinterpret_cast<const uint4*>(p.g + (r + u * kQCPhases) * p.n + c0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) row(v[u], r + u * kQCPhases);
+        }
+        for (; r < r1; r += kQCPhases) row(*reinterpret_cast<const uint4*>(p.g + r * p.n + c0), r);
+    }
+    __shared__ float red[kQCPhases][256 + 4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[ph][cg * 8 + j] = acc[j];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int col = threadIdx.x;
+        const int64_t gc = (int64_t)blockIdx.x * 256 + col;
+        if (gc < p.n) {
+            float sum = red[0][col];
+#pragma unroll
+            for (int q = 1; q < kQCPhases; ++q) sum += red[q][col];
+            p.part[chunk * p.n + gc] = sum;
+        }
+    }
+    if constexpr (QUANT) {
+        if (p.q.hist) {
+            publish_amax(p.q, amax, s_read, win, gridDim.x * gridDim.y);
+        } else if (p.q.scale_used && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+            *p.q.scale_used = s_read;
+        }
+    }
+}
+
+// Scalar pass 1: one column per lane over a chunk, rows in order.
 __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const uint16_t* g,
                                                                      int64_t m, int64_t n,
-                                                                     int64_t rows, int vec,
-                                                                     float* part) {
+                                                                     int64_t rows, float* part) {
     const int64_t chunk = blockIdx.y;
     const int64_t r0 = chunk * rows;
     const int64_t r1 = r0 + rows < m ? r0 + rows : m;
-    if (vec) {
-        __shared__ float red[kColPhases][256 + 4];
-        const int cg = threadIdx.x % 32;     // column group (8 columns)
-        const int ph = threadIdx.x / 32;     // row phase
-        const int64_t c0 = (int64_t)blockIdx.x * 256 + cg * 8;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (c0 < n) {
-            int64_t r = r0 + ph;
-            for (; r + 7 * kColPhases < r1; r += 8 * kColPhases) {
-                uint4 v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    v[u] = *reinterpret_cast<const uint4*>(g + (r + u * kColPhases) * n + c0);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[2 * j] += bf16_lo(w[j]);
-                        acc[2 * j + 1] += bf16_hi(w[j]);
-                    }
-                }
-            }
-            for (; r < r1; r += kColPhases) {
-                const uint4 v = *reinterpret_cast<const uint4*>(g + r * n + c0);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] += bf16_lo(w[j]);
-                    acc[2 * j + 1] += bf16_hi(w[j]);
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) red[ph][cg * 8 + j] = acc[j];
-        __syncthreads();
-        const int col = threadIdx.x;  // 0..255
-        const int64_t gc = (int64_t)blockIdx.x * 256 + col;
-        if (gc < n) {
-            float s = red[0][col];
-#pragma unroll
-            for (int q = 1; q < kColPhases; ++q) s += red[q][col];
-            part[chunk * n + gc] = s;
-        }
-    } else {
-        const int64_t c = (int64_t)blockIdx.x * kColThreads + threadIdx.x;
-        if (c >= n) return;
-        float acc = 0.0f;
-        for (int64_t r = r0; r < r1; ++r) acc += bf16_to_f32(g[r * n + c]);
-        part[chunk * n + c] = acc;
-    }
+    const int64_t c = (int64_t)blockIdx.x * kColThreads + threadIdx.x;
+    if (c >= n) return;
+    float acc = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) acc += bf16_to_f32(g[r * n + c]);
+    part[chunk * n + c] = acc;
 }
 
 __global__ __launch_bounds__(kColThreads) void colsum_final_kernel(const float* part,
@@ -388,22 +431,83 @@ __global__ __launch_bounds__(kColThreads) void colsum_final_kernel(const float* 
     if (q == 0 && c < n) db[c] = f32_to_bf16(((red[0][col] + red[1][col]) + red[2][col]) + red[3][col]);
 }
 
+static bool colsum_vec(const uint16_t* g, int64_t n) {
+    return (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
+}
+
+static hipError_t launch_colsum_final(float* part, int64_t m, int64_t n, uint16_t* db,
+                                      hipStream_t stream) {
+    const dim3 grid2((unsigned)((n + 63) / 64));
+    hipLaunchKernelGGL(colsum_final_kernel, grid2, dim3(kColThreads), 0, stream, part,
+                       colsum_chunks(m, n), n, db);
+    return hipGetLastError();
+}
+
 hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, void* ws,
                          hipStream_t stream) {
     float* part = static_cast<float*>(ws);
     const int64_t rows = colsum_rows(m, n);
     const int64_t chunks = colsum_chunks(m, n);
-    const int vec = (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
-    const int64_t cols_per_block = vec ? 256 : kColThreads;
-    const dim3 grid1((unsigned)((n + cols_per_block - 1) / cols_per_block), (unsigned)chunks);
-    hipLaunchKernelGGL(colsum_partial_kernel, grid1, dim3(kColThreads), 0, stream, g, m, n, rows,
-                       vec, part);
+    if (colsum_vec(g, n)) {
+        QCParams p{};
+        p.g = g;
+        p.m = m;
+        p.n = n;
+        p.rows = rows;
+        p.part = part;
+        const dim3 grid1((unsigned)((n + 255) / 256), (unsigned)chunks);
+        hipLaunchKernelGGL((quantize_colsum_kernel<0, false>), grid1, dim3(kQCThreads), 0, stream,
+                           p);
+    } else {
+        const dim3 grid1((unsigned)((n + kColThreads - 1) / kColThreads), (unsigned)chunks);
+        hipLaunchKernelGGL(colsum_partial_kernel, grid1, dim3(kColThreads), 0, stream, g, m, n,
+                           rows, part);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid2((unsigned)((n + 63) / 64));
-    hipLaunchKernelGGL(colsum_final_kernel, grid2, dim3(kColThreads), 0, stream, part, chunks, n,
-                       db);
-    return hipGetLastError();
+    return launch_colsum_final(part, m, n, db, stream);
+}
+
+hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, uint16_t* db,
+                                  void* ws, hipStream_t stream) {
+    const bool vec = colsum_vec(q.x, n) && q.out &&
+                     (reinterpret_cast<uintptr_t>(q.out) & 15) == 0 && !q.out2;
+    if (!vec) {
+        hipError_t e = launch_quantize(q, stream);
+        if (e != hipSuccess) return e;
+        return launch_colsum(q.x, m, n, db, ws, stream);
+    }
+    QCParams p{};
+    p.q.x = q.x;
+    p.q.numel = m * n;
+    p.q.scale = q.scale;
+    p.q.out = q.out;
+    if (q.ring_state) {
+        p.q.hist = q.ring_state;
+        p.q.scale_out = q.ring_state + q.ring_len;
+        p.q.amax_slot = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 2);
+        p.q.done = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 3);
+        p.q.len = q.ring_len;
+        p.q.idx = q.ring_idx;
+    }
+    p.q.fmax = q.fmt ? 57344.0f : 448.0f;
+    p.q.pow2_margin = q.pow2_margin;
+    p.q.scale_used = q.scale_used;
+    p.g = q.x;
+    p.m = m;
+    p.n = n;
+    p.rows = colsum_rows(m, n);
+    p.part = static_cast<float*>(ws);
+    const dim3 grid1((unsigned)((n + 255) / 256), (unsigned)colsum_chunks(m, n));
+    if (q.fmt == 0)
+        hipLaunchKernelGGL((quantize_colsum_kernel<0, true>), grid1, dim3(kQCThreads), 0, stream,
+                           p);
+    else
+        hipLaunchKernelGGL((quantize_colsum_kernel<1, true>), grid1, dim3(kQCThreads), 0, stream,
+                           p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_colsum_final(p.part, m, n, db, stream);
 }
 
 }  // namespace fp8lin

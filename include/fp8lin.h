@@ -203,6 +203,24 @@ fp8_status_t fp8_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_quantize_colsum -- quantize of the output gradient g [m][n] fused with
+ * the bias gradient: one read of g gives the codes, the amax / ring fold of
+ * fp8_quantize and db[j] = bf16( sum_i g[i][j] ).
+ * (compare view: astrai/extension/fp8.py _LinearFp8.backward quantizes g and
+ *  takes grad_bias as the column sum of g; compare view quantize.cuh for
+ *  the quantize)
+ *
+ * out, db, the ring and scale_used are exactly what fp8_quantize (numel =
+ * m*n) and fp8_colsum give for the same arguments, bit for bit.
+ * workspace: device scratch of fp8_colsum_workspace(m, n) bytes.
+ * Every pointer is required except ring and scale_used.
+ * ------------------------------------------------------------------- */
+fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt_t fmt,
+                                 const float* scale, uint8_t* out, const fp8_ring_t* ring,
+                                 int32_t margin, float* scale_used, uint16_t* db,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_linear_fwd -- out[M][N] = x[M][K] w[N][K]^T * (sx*sw) + bias
  * (compare view: astrai/extension/fp8.py fp8_linear_forward)
  *

@@ -97,6 +97,28 @@ def test_quantize2_empty_without_ring_is_a_noop(f):
     assert f._lib.fp8_quantize2(None, 0, 0, None, None, 1, None, None, 0, None, None) == 0
 
 
+def qc(lib, **kw):
+    a = dict(g=FAKE, m=64, n=64, fmt=0, scale=FAKE, out=FAKE, ring=None, margin=0, used=None,
+             db=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.fp8_quantize_colsum(*a.values())
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(fmt=3), "format"),
+    (dict(m=0), ">= 1"),
+    (dict(g=None), "NULL"),
+    (dict(db=None), "NULL"),
+    (dict(scale=None), "NULL"),
+    (dict(ws=None), "NULL"),
+    (dict(ws_bytes=4), "workspace"),
+    (dict(margin=-1), "margin"),
+])
+def test_quantize_colsum_validation(f, kw, needle):
+    st = qc(f._lib, **kw)
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
 def test_ring_validation(f):
     lib = f._lib
     r = f._RingC(0x1000, 16, 16, 0, 0)

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import dev_f32, from_dev_bf16, from_dev_u8, to_dev_bf16
+from tests.gpu_util import check_gemm, dev_f32, from_dev_bf16, from_dev_u8, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -234,3 +234,36 @@ def test_quantize2_matches_two_single_quantizes(lib, orc, fmt, fmt2, numel, offs
     assert np.array_equal(from_dev_u8(q2), orc.quantize(x, fmt2, s))
     assert torch.equal(r1.state, r2.state)
     assert used.item() == s
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("M,N,offset", [(2048, 4096, 0), (777, 264, 0), (300, 136, 1),
+                                         (50, 13, 0), (4096, 8, 0)])
+def test_quantize_colsum_matches_separate_calls(lib, orc, fmt, M, N, offset):
+    """fp8_quantize_colsum gives exactly fp8_quantize's codes, ring and
+    scale_used and fp8_colsum's db (fused path for 8-column multiples on
+    16-byte aligned rows, separate launches otherwise), and matches the
+    oracle (codes bit-exact, db within the GEMM tolerance)."""
+    g_all = wl.normal_bf16((M * N + offset,), 1e-3, M + N)
+    g = g_all[offset:].reshape(M, N)
+    gd = to_dev_bf16(g_all)[offset:]
+    s = np.float32(1e-3 / 57344.0 * 4.0) if fmt else np.float32(1e-3 / 448.0 * 4.0)
+    sd = dev_f32(s)
+    ws = torch.empty(lib.fp8_colsum_workspace(M, N), dtype=torch.uint8, device="cuda")
+    q1 = torch.empty(M * N, dtype=torch.uint8, device="cuda")
+    db1 = torch.empty(N, dtype=torch.int16, device="cuda")
+    u1 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    r1, r2 = lib.Ring(16), lib.Ring(16)
+    lib.fp8_quantize_colsum(gd, M, N, fmt, sd, q1, db1, ws, ring=r1, scale_used=u1)
+    q2 = torch.empty(M * N, dtype=torch.uint8, device="cuda")
+    db2 = torch.empty(N, dtype=torch.int16, device="cuda")
+    u2 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lib.fp8_quantize(gd, fmt, scale=sd, out=q2, ring=r2, scale_used=u2)
+    lib.fp8_colsum(gd, M, N, db2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(db1, db2)
+    assert torch.equal(r1.state, r2.state) and torch.equal(u1, u2)
+    assert np.array_equal(from_dev_u8(q1), orc.quantize(g.ravel(), fmt, s))
+    ref = orc.colsum(g.ravel(), M, N)
+    absdot = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+    check_gemm(from_dev_bf16(db1), ref, absdot=absdot, K=M, what=f"colsum {M}x{N}")

@@ -234,14 +234,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gemm_skinny_kernel(SkinnyParam
             s += *reinterpret_cast<const v4f*>(red + w * (kRowsA * kRedStride) +
                                                row * kRedStride + c4);
         const int64_t gn = n0 + c4;
-        uint16_t h[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) h[c] = f32_to_bf16(fmaf(s[c], sc, bias[c]));
+        const uint32_t w0 = f32x2_to_bf16x2(fmaf(s[0], sc, bias[0]), fmaf(s[1], sc, bias[1]));
+        const uint32_t w1 = f32x2_to_bf16x2(fmaf(s[2], sc, bias[2]), fmaf(s[3], sc, bias[3]));
         uint16_t* dst = out + (int64_t)row * p.n + gn;
         if (gn + 3 < p.n && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                                        (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
         } else {
+            const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                                   (uint16_t)(w1 >> 16)};
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (gn + c < p.n) dst[c] = h[c];

@@ -561,14 +561,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     const int r = 32 * i + (lane & 31);
-                    uint16_t h[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], sc, bias[c]));
                     const int chunk = (cl >> 3) ^ (r % kChunks);
                     v2i pk;
-                    pk[0] = (int)((uint32_t)h[0] | ((uint32_t)h[1] << 16));
-                    pk[1] = (int)((uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                    pk[0] = (int)f32x2_to_bf16x2(fmaf(acc[i][j][4 * q + 0], sc, bias[0]),
+                                                 fmaf(acc[i][j][4 * q + 1], sc, bias[1]));
+                    pk[1] = (int)f32x2_to_bf16x2(fmaf(acc[i][j][4 * q + 2], sc, bias[2]),
+                                                 fmaf(acc[i][j][4 * q + 3], sc, bias[3]));
                     *reinterpret_cast<__attribute__((address_space(3))) v2i*>(
                         (lds_void*)(wl + r * kRowBytes + chunk * 16 + 8 * (lane >> 5))) = pk;
                 }
@@ -607,16 +605,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
             for (int i = 0; i < FM; ++i) {
                 const int64_t gm = m0 + wm * TM + 32 * i + (lane & 31);
                 if (gm >= p.m) continue;
-                uint16_t h[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    h[c] = f32_to_bf16(fmaf(acc[i][j][4 * q + c], sc, bias[c]));
+                const uint32_t w0 = f32x2_to_bf16x2(fmaf(acc[i][j][4 * q + 0], sc, bias[0]),
+                                                    fmaf(acc[i][j][4 * q + 1], sc, bias[1]));
+                const uint32_t w1 = f32x2_to_bf16x2(fmaf(acc[i][j][4 * q + 2], sc, bias[2]),
+                                                    fmaf(acc[i][j][4 * q + 3], sc, bias[3]));
                 uint16_t* dst = out + gm * p.n + gn;
                 if (p.vec_out && gn + 3 < p.n) {
-                    *reinterpret_cast<uint2*>(dst) =
-                        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
-                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
                 } else {
+                    const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                                           (uint16_t)(w1 >> 16)};
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         if (gn + c < p.n) dst[c] = h[c];

@@ -221,35 +221,6 @@ struct Operand {
         return lds_addr(lds + 1024 * (wave + j * NW));
     }
 
-    // Two consecutive stages (k0 into `lds0`, k0 + BK into `lds1`), their
-    // instructions interleaved: for a k-contiguous operand with 64-byte
-    // stages, the two halves of every 128-byte line are requested by
-    // back-to-back instructions, which the load path serves at whole-line
-    // rate (alone, half-line requests run at about half of it).
-    __device__ static void issue2(const v4i& rs, uint8_t* lds0, uint8_t* lds1, uint32_t base,
-                                  uint32_t ld, int k0, int kdim, bool full_rows,
-                                  int64_t rows_left, int wave, int lane) {
-        const uint32_t jstride = (uint32_t)kRowStep * ld;
-#pragma unroll
-        for (int j = 0; j < kPerWave; ++j) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int kh = k0 + h * BK;
-                const uint32_t delta = MN ? (uint32_t)kh * ld : (uint32_t)kh;
-                const bool full = kh + BK <= kdim;
-                uint32_t off = base + delta + j * jstride;
-                if (!full || (!MN && !full_rows)) {
-                    int row, c;
-                    slot(j, wave, lane, row, c);
-                    const int gk = MN ? kh + row : kh + 16 * c;
-                    if (gk >= kdim) off = kOOB;
-                    if (!MN && row >= rows_left) off = kOOB;
-                }
-                dma16(rs, lds_addr((h ? lds1 : lds0) + 1024 * (wave + j * NW)), off);
-            }
-        }
-    }
-
     // Fragment addressing.  The MFMA operand of the 32 tile rows starting at
     // rf, substep h, gives lane l row rf + l%32 and k = 64h + 32*(l/32) ..
     // +31 of the stage.  The lane-dependent part of each address is computed
@@ -303,6 +274,41 @@ struct Operand {
         return v;
     }
 };
+
+// Order of the DMA instructions of one refill.  A refill is one stage
+// (P = 1: A's instructions, then B's) or a pair of 64-k stages X, Y (P = 2).
+// In a pair, a k-contiguous operand alternates its X and Y instructions, so
+// the two 64-byte halves of every line it reads go out back to back; an
+// m/n-contiguous operand (whole lines either way) issues all of its X
+// instructions and then all of its Y instructions, after the alternating
+// ones.  Loads complete in issue order, so what may still be in flight once
+// X has landed is exactly the refill's instructions after the last X one
+// (pair_tail_x).
+struct DmaSlot {
+    int op;  // 0: A, 1: B
+    int j;   // instruction of that operand's stage
+    int h;   // 0: X (or the single stage), 1: Y
+};
+
+template <int NA, int NB, bool IA, bool IB, int P>
+__device__ constexpr DmaSlot dma_slot(int x) {
+    if (P == 1) return x < NA ? DmaSlot{0, x, 0} : DmaSlot{1, x - NA, 0};
+    const int ia = IA ? 2 * NA : 0, ib = IB ? 2 * NB : 0;
+    if (x < ia) return DmaSlot{0, x / 2, x % 2};
+    x -= ia;
+    if (x < ib) return DmaSlot{1, x / 2, x % 2};
+    x -= ib;
+    const int ba = IA ? 0 : NA, bb = IB ? 0 : NB;  // blocked instructions per stage
+    const int h = x / (ba + bb);
+    x -= h * (ba + bb);
+    return x < ba ? DmaSlot{0, x, h} : DmaSlot{1, x - ba, h};
+}
+
+template <int NA, int NB, bool IA, bool IB>
+constexpr int pair_tail_x() {
+    const int blocked = (IA ? 0 : NA) + (IB ? 0 : NB);
+    return blocked > 0 ? blocked : 1;
+}
 
 template <int FMT>
 __device__ __forceinline__ v16f mfma32x32x64(const v8i& x, const v8i& y, v16f acc) {
@@ -364,14 +370,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
         OA::issue(ra, s, abase, lda, kstage * BK, kdim, afull, arows, wave, lane);
         OB::issue(rb, s + kStageA, bbase, ldb, kstage * BK, kdim, bfull, brows, wave, lane);
     };
-    // stages kstage and kstage+1 into ring slots s0 and s1
-    auto issue_pair = [&](int s0, int s1, int kstage) {
-        uint8_t* a0 = smem + s0 * kStage;
-        uint8_t* a1 = smem + s1 * kStage;
-        OA::issue2(ra, a0, a1, abase, lda, kstage * BK, kdim, afull, arows, wave, lane);
-        OB::issue2(rb, a0 + kStageA, a1 + kStageA, bbase, ldb, kstage * BK, kdim, bfull, brows,
-                   wave, lane);
-    };
 
     // Fragments are read one substep ahead: while substep u's MFMAs run, the
     // fragments of u+1 are already coming in from LDS, so the MFMA pipe does
@@ -413,33 +411,38 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     // The DMA instructions of one refill (a stage, or a pair of 64-k stages
-    // whose instructions alternate so both halves of each line go out back
-    // to back): offsets and LDS addresses are computed right after the
-    // barrier, the instructions themselves are spread between the MFMAs.
-    // Issued in one burst, 8 waves x 8 instructions fill the texture
-    // addresser's queue and the waves at its back stall before their first
-    // MFMA.
+    // in the order dma_slot gives): offsets and LDS addresses are computed
+    // right after the barrier, the instructions themselves are spread
+    // between the MFMAs.  Issued in one burst, 8 waves x 8 instructions fill
+    // the texture addresser's queue and the waves at its back stall before
+    // their first MFMA.
     constexpr int kPairs = kSubs == 1 ? 2 : 1;
-    constexpr int kNA = OA::kPerWave * kPairs, kNB = OB::kPerWave * kPairs;
-    constexpr int kND = kNA + kNB;
+    constexpr int kND = (OA::kPerWave + OB::kPerWave) * kPairs;
+    constexpr int kPA = OA::kPerWave, kPB = OB::kPerWave;
+    constexpr bool kIA = !AMN, kIB = !BMN;  // k-contiguous: alternate X / Y
     uint32_t doff[kND], dlds[kND];
     auto plan_refill = [&](int s0, int s1, int kstage) {
 #pragma unroll
-        for (int x = 0; x < kNA; ++x) {
-            const int j = x / kPairs, h = x % kPairs;
-            uint8_t* dst = smem + (h ? s1 : s0) * kStage;
-            doff[x] = OA::off_of(abase, lda, (kstage + h) * BK, kdim, afull, arows, j, wave, lane);
-            dlds[x] = OA::lds_of(dst, j, wave);
-        }
-#pragma unroll
-        for (int x = 0; x < kNB; ++x) {
-            const int j = x / kPairs, h = x % kPairs;
-            uint8_t* dst = smem + (h ? s1 : s0) * kStage + kStageA;
-            doff[kNA + x] =
-                OB::off_of(bbase, ldb, (kstage + h) * BK, kdim, bfull, brows, j, wave, lane);
-            dlds[kNA + x] = OB::lds_of(dst, j, wave);
+        for (int x = 0; x < kND; ++x) {
+            const DmaSlot d = dma_slot<kPA, kPB, kIA, kIB, kPairs>(x);
+            uint8_t* dst = smem + (d.h ? s1 : s0) * kStage;
+            if (d.op == 0) {
+                doff[x] = OA::off_of(abase, lda, (kstage + d.h) * BK, kdim, afull, arows, d.j,
+                                     wave, lane);
+                dlds[x] = OA::lds_of(dst, d.j, wave);
+            } else {
+                doff[x] = OB::off_of(bbase, ldb, (kstage + d.h) * BK, kdim, bfull, brows, d.j,
+                                     wave, lane);
+                dlds[x] = OB::lds_of(dst + kStageA, d.j, wave);
+            }
         }
     };
+    auto issue_planned = [&](int x) {
+        dma16(dma_slot<kPA, kPB, kIA, kIB, kPairs>(x).op == 0 ? ra : rb, dlds[x], doff[x]);
+    };
+    // Pairs: loads that may be in flight when the first stage of a pair has
+    // landed (the pair's instructions after its last X one).
+    constexpr int kTailX = pair_tail_x<kPA, kPB, kIA, kIB>();
 
     // One substep: the MFMAs of register slot SL; between them, in this
     // order, the fragment reads of the next substep (slot NSL, substep NH of
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 #pragma unroll
                 for (int q = 0; q < kDPer; ++q) {
                     const int x = m * kDPer + q;
-                    if (x < kND) dma16(x < kNA ? ra : rb, dlds[x], doff[x]);
+                    if (x < kND) issue_planned(x);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -479,15 +482,23 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
-    // Prologue: every buffer starts loading; stage 0's first fragments are read.
+    // Prologue: every buffer starts loading; stage 0's first fragments are
+    // read.  Pairs go out in the loop's refill order; stage 0 is the X of
+    // the first pair, so the rest of that pair's tail and the later pairs
+    // may still be in flight.
     if constexpr (kSubs == 1) {
 #pragma unroll
-        for (int s = 0; s < STAGES; s += 2) issue_pair(s, s + 1, s);
+        for (int s = 0; s < STAGES; s += 2) {
+            plan_refill(s, s + 1, s);
+#pragma unroll
+            for (int x = 0; x < kND; ++x) issue_planned(x);
+        }
+        wait_vmcnt<kTailX + kLoads * (STAGES - 2)>();
     } else {
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) issue(s, s);
+        wait_vmcnt<kLoads * (STAGES - 1)>();
     }
-    wait_vmcnt<kLoads * (STAGES - 1)>();
     barrier();
     read_frags(I0{}, I0{}, 0);
 
@@ -513,10 +524,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
             } else {
                 // 64-k stages are refilled in pairs: at every odd step the
                 // slots of this step and the one before take steps
-                // st+STAGES-1 and st+STAGES.  Loads in flight after the
-                // awaited step st+1: one step of its pair plus the later
-                // pairs (odd st), or the later pairs only (even st).
-                if (s & 1) wait_vmcnt<kLoads * (STAGES - 3)>();
+                // st+STAGES-1 and st+STAGES, so pairs are (even, odd) steps.
+                // Loads that may be in flight when the awaited step st+1 has
+                // landed: odd st (st+1 is a pair's X): the tail of its pair
+                // after the last X instruction plus the later pairs; even st
+                // (st+1 is a Y): the later pairs only.
+                if (s & 1) wait_vmcnt<kTailX + kLoads * (STAGES - 4)>();
                 else wait_vmcnt<kLoads * (STAGES - 2)>();
                 wait_lgkmcnt0();
                 barrier();

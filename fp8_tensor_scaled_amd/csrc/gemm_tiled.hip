@@ -291,7 +291,7 @@ struct DmaSlot {
 };
 
 template <int NA, int NB, bool IA, bool IB, int P>
-__device__ constexpr DmaSlot dma_slot(int x) {
+__host__ __device__ constexpr DmaSlot dma_slot(int x) {
     if (P == 1) return x < NA ? DmaSlot{0, x, 0} : DmaSlot{1, x - NA, 0};
     const int ia = IA ? 2 * NA : 0, ib = IB ? 2 * NB : 0;
     if (x < ia) return DmaSlot{0, x / 2, x % 2};
@@ -309,6 +309,32 @@ constexpr int pair_tail_x() {
     const int blocked = (IA ? 0 : NA) + (IB ? 0 : NB);
     return blocked > 0 ? blocked : 1;
 }
+
+// Compile-time check of a pair order: every (operand, instruction, stage)
+// issued exactly once, and exactly pair_tail_x instructions after the last
+// X one.
+template <int NA, int NB, bool IA, bool IB>
+constexpr bool pair_order_ok() {
+    static_assert(NA <= 8 && NB <= 8, "checker bounds");
+    int seen[2][8][2] = {};
+    int last_x = -1;
+    const int n = 2 * (NA + NB);
+    for (int x = 0; x < n; ++x) {
+        const DmaSlot d = dma_slot<NA, NB, IA, IB, 2>(x);
+        if (d.op < 0 || d.op > 1 || d.h < 0 || d.h > 1 || d.j < 0 || d.j >= (d.op ? NB : NA))
+            return false;
+        ++seen[d.op][d.j][d.h];
+        if (d.h == 0) last_x = x;
+    }
+    for (int op = 0; op < 2; ++op)
+        for (int j = 0; j < (op ? NB : NA); ++j)
+            if (seen[op][j][0] != 1 || seen[op][j][1] != 1) return false;
+    return n - 1 - last_x == pair_tail_x<NA, NB, IA, IB>();
+}
+static_assert(pair_order_ok<2, 2, true, true>() && pair_order_ok<2, 2, true, false>() &&
+                  pair_order_ok<2, 2, false, true>() && pair_order_ok<2, 2, false, false>() &&
+                  pair_order_ok<1, 3, true, false>() && pair_order_ok<3, 1, false, true>(),
+              "pair refill order");
 
 template <int FMT>
 __device__ __forceinline__ v16f mfma32x32x64(const v8i& x, const v8i& y, v16f acc) {

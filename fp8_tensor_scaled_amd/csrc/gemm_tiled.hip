@@ -298,7 +298,8 @@ __host__ __device__ constexpr DmaSlot dma_slot(int x) {
     x -= ia;
     if (x < ib) return DmaSlot{1, x / 2, x % 2};
     x -= ib;
-    const int ba = IA ? 0 : NA, bb = IB ? 0 : NB;  // blocked instructions per stage
+    constexpr int ba = IA ? 0 : NA, bb = IB ? 0 : NB;  // blocked instructions per stage
+    if constexpr (ba + bb == 0) return DmaSlot{-1, -1, -1};  // x out of range
     const int h = x / (ba + bb);
     x -= h * (ba + bb);
     return x < ba ? DmaSlot{0, x, h} : DmaSlot{1, x - ba, h};

@@ -21,10 +21,13 @@
 //    (they only win on a stream of cold, never-reused buffers).
 //    Conversions are v_cvt_pk_{fp8,bf8}_f32 after a med3 clamp to +-max
 //    (satfinite).
-//  * One workgroup per CU also keeps the fold cheap: each workgroup adds two
-//    dependent atomics at the end, and their count and chain (max, ticket,
-//    final read) sit on the kernel's critical path.  The window is read at
-//    kernel start, so the last workgroup does not wait for it.
+//  * The fold's cost is its atomics: same-address atomics serialize at the
+//    coherence point (about 11 ns each, measured), and a returning atomic waits
+//    for every store its wave issued before it.  So there is one workgroup
+//    per CU (few atomics), each workgroup owns a contiguous range and
+//    publishes its max in its last round after the loads and before the
+//    stores (the round trips overlap the store drain), and the window is
+//    read at kernel start so the last workgroup does not wait for it.
 //  * The fold uses relaxed agent-scope atomics only.  Release/acquire at
 //    agent scope write back / invalidate the per-XCD L2s and cost tens of ns
 //    per workgroup when every workgroup issues them; instead each workgroup
@@ -88,65 +91,92 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, fl
     }
 }
 
-// Workgroup max -> one atomic max, then a ticket; the last workgroup folds.
-__device__ __forceinline__ void publish_amax(const QuantParams& p, float v, float s_read,
-                                             float win, uint32_t nblocks) {
+// Workgroup max of v -> one atomic max by thread 0, whose previous value
+// (meaningful at thread 0 only) is returned.  Every thread of the workgroup
+// must call it once.
+__device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v) {
     __shared__ float slots[kQuantWaves];
-    __shared__ int is_last;
     v = wave_max(v);
     if ((threadIdx.x % kWave) == 0) slots[threadIdx.x / kWave] = v;
     __syncthreads();
+    uint32_t old = 0;
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < kQuantWaves; ++w) v = fmaxf(v, slots[w]);
-        const uint32_t old = __hip_atomic_fetch_max(p.amax_slot, __float_as_uint(v),
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // |x| maxima are never all-ones bits; the comparison makes the ticket
-        // wait for the max to have been performed.
+        old = __hip_atomic_fetch_max(p.amax_slot, __float_as_uint(v), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return old;
+}
+
+// Thread 0 takes a ticket once its atomic max has been performed (the
+// increment depends on the returned value); the workgroup that draws the
+// last ticket folds, on its wave 0.  Code between publish_amax and this call
+// (the workgroup's last stores) overlaps the atomics' round trips.
+__device__ __forceinline__ void finish_fold(const QuantParams& p, uint32_t old, float s_read,
+                                            float win, uint32_t nblocks) {
+    if (threadIdx.x >= kWave) return;
+    int last = 0;
+    if (threadIdx.x == 0) {
+        // |x| maxima are never all-ones bits; the comparison makes the
+        // ticket wait for the max to have been performed.
         const uint32_t inc = old == 0xffffffffu ? 2u : 1u;
         const uint32_t ticket =
             __hip_atomic_fetch_add(p.done, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (ticket == nblocks - 1u);
+        last = ticket == nblocks - 1u;
     }
-    __syncthreads();
-    if (is_last && threadIdx.x < kWave) fold_ring(p, s_read, win);
+    if (__shfl(last, 0, kWave)) fold_ring(p, s_read, win);
 }
 
-// FMT2 >= 0: also encode the same scaled values in the second format into
-// dst2 (one read of x feeds both encodings).
-template <int FMT, int FMT2, bool MEASURE_ONLY>
-__device__ __forceinline__ void convert16(const uint4& r0, const uint4& r1, float m, float& amax,
-                                          uint4* dst, uint4* dst2) {
+__device__ __forceinline__ void unpack16(const uint4& r0, const uint4& r1, float f[16]) {
     const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    float f[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         f[2 * j] = bf16_lo(w[j]);
         f[2 * j + 1] = bf16_hi(w[j]);
     }
+}
+
+__device__ __forceinline__ float absmax16(const uint4& r0, const uint4& r1, float amax) {
+    float f[16];
+    unpack16(r0, r1, f);
 #pragma unroll
     for (int j = 0; j < 16; j += 2) amax = fmaxf(amax, fmaxf(fabsf(f[j]), fabsf(f[j + 1])));
-    if constexpr (!MEASURE_ONLY) {
-        float g[16];
+    return amax;
+}
+
+// 16 codes of x * m into dst; FMT2 >= 0: the same scaled values in the
+// second format into dst2 (one read of x feeds both encodings).
+template <int FMT, int FMT2>
+__device__ __forceinline__ void encode16(const uint4& r0, const uint4& r1, float m, uint4* dst,
+                                         uint4* dst2) {
+    float f[16];
+    unpack16(r0, r1, f);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) g[j] = f[j] * m;
-        uint4 o;
-        o.x = cvt4<FMT>(g[0], g[1], g[2], g[3]);
-        o.y = cvt4<FMT>(g[4], g[5], g[6], g[7]);
-        o.z = cvt4<FMT>(g[8], g[9], g[10], g[11]);
-        o.w = cvt4<FMT>(g[12], g[13], g[14], g[15]);
-        *dst = o;
-        if constexpr (FMT2 >= 0) {
-            uint4 o2;
-            o2.x = cvt4<FMT2>(g[0], g[1], g[2], g[3]);
-            o2.y = cvt4<FMT2>(g[4], g[5], g[6], g[7]);
-            o2.z = cvt4<FMT2>(g[8], g[9], g[10], g[11]);
-            o2.w = cvt4<FMT2>(g[12], g[13], g[14], g[15]);
-            *dst2 = o2;
-        }
+    for (int j = 0; j < 16; ++j) f[j] *= m;
+    uint4 o;
+    o.x = cvt4<FMT>(f[0], f[1], f[2], f[3]);
+    o.y = cvt4<FMT>(f[4], f[5], f[6], f[7]);
+    o.z = cvt4<FMT>(f[8], f[9], f[10], f[11]);
+    o.w = cvt4<FMT>(f[12], f[13], f[14], f[15]);
+    *dst = o;
+    if constexpr (FMT2 >= 0) {
+        uint4 o2;
+        o2.x = cvt4<FMT2>(f[0], f[1], f[2], f[3]);
+        o2.y = cvt4<FMT2>(f[4], f[5], f[6], f[7]);
+        o2.z = cvt4<FMT2>(f[8], f[9], f[10], f[11]);
+        o2.w = cvt4<FMT2>(f[12], f[13], f[14], f[15]);
+        *dst2 = o2;
     }
 }
 
+// Vector path (x, out, out2 16-byte aligned): workgroup b owns a contiguous
+// run of 16-element chunks and walks it in rounds of kUnroll chunks per
+// lane; the numel % 16 leftover elements go to workgroup 0 first.  With a
+// ring, the workgroup's max is published in its last round after the loads
+// and before the stores, so the fold's atomics overlap the store drain
+// instead of following it.  Scalar path (unaligned bases): grid-stride
+// elements, then the publish.
 template <int FMT, int FMT2, bool MEASURE_ONLY>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) {
     float m = 0.0f, s_read = 0.0f;
@@ -156,43 +186,73 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     }
     // the window slot of this lane (wave 0), loaded now so that its latency
     // hides under the streaming loop
-    const int wl = threadIdx.x;
-    const float win = (p.hist && wl < p.len && wl < kWave && wl != p.idx) ? p.hist[wl] : 0.0f;
+    const int t = threadIdx.x;
+    const float win = (p.hist && t < p.len && t < kWave && t != p.idx) ? p.hist[t] : 0.0f;
     float amax = 0.0f;
-    const int64_t tid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    const int64_t nvec = p.vec ? p.numel / kVecElems : 0;
-    const uint4* xv = reinterpret_cast<const uint4*>(p.x);
-    uint4* ov = reinterpret_cast<uint4*>(p.out);
-    uint4* ov2 = reinterpret_cast<uint4*>(p.out2);
-    int64_t i = tid;
-    for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
-        uint4 r[kUnroll][2];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            r[u][0] = xv[2 * (i + u * stride)];
-            r[u][1] = xv[2 * (i + u * stride) + 1];
+    uint32_t old = 0;
+    if (p.vec) {
+        const int64_t nvec = p.numel / kVecElems;
+        const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
+        const int64_t lo = (int64_t)blockIdx.x * per;
+        const int64_t hi = lo + per < nvec ? lo + per : nvec;
+        if (blockIdx.x == 0) {
+            const int64_t e = nvec * kVecElems + t;
+            if (e < p.numel) {
+                const float f = bf16_to_f32(p.x[e]);
+                amax = fmaxf(amax, fabsf(f));
+                if constexpr (!MEASURE_ONLY) {
+                    p.out[e] = cvt1<FMT>(f * m);
+                    if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
+                }
+            }
         }
+        const uint4* xv = reinterpret_cast<const uint4*>(p.x);
+        uint4* ov = reinterpret_cast<uint4*>(p.out);
+        uint4* ov2 = reinterpret_cast<uint4*>(p.out2);
+        constexpr int kRound = kQuantThreads * kUnroll;
+        const int64_t nr = hi > lo ? (hi - lo + kRound - 1) / kRound : 0;  // uniform
+        for (int64_t rd = 0; rd < nr; ++rd) {
+            const int64_t c0 = lo + rd * kRound + t;
+            uint4 r[kUnroll][2];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            convert16<FMT, FMT2, MEASURE_ONLY>(r[u][0], r[u][1], m, amax, ov + i + u * stride,
-                                               ov2 + i + u * stride);
-    }
-    for (; i < nvec; i += stride)
-        convert16<FMT, FMT2, MEASURE_ONLY>(xv[2 * i], xv[2 * i + 1], m, amax, ov + i, ov2 + i);
-    // Scalar tail (everything when the bases are not 16-byte aligned).
-    for (int64_t e = nvec * kVecElems + tid; e < p.numel; e += stride) {
-        const float f = bf16_to_f32(p.x[e]);
-        amax = fmaxf(amax, fabsf(f));
-        if constexpr (!MEASURE_ONLY) {
-            p.out[e] = cvt1<FMT>(f * m);
-            if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t c = c0 + u * kQuantThreads;
+                if (c < hi) {
+                    r[u][0] = xv[2 * c];
+                    r[u][1] = xv[2 * c + 1];
+                } else {
+                    r[u][0] = make_uint4(0, 0, 0, 0);
+                    r[u][1] = make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) amax = absmax16(r[u][0], r[u][1], amax);
+            if (p.hist && rd == nr - 1) old = publish_amax(p, amax);
+            if constexpr (!MEASURE_ONLY) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t c = c0 + u * kQuantThreads;
+                    if (c < hi) encode16<FMT, FMT2>(r[u][0], r[u][1], m, ov + c, ov2 + c);
+                }
+            }
         }
+        if (p.hist && nr == 0) old = publish_amax(p, amax);
+    } else {
+        const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+        for (int64_t e = (int64_t)blockIdx.x * kQuantThreads + t; e < p.numel; e += stride) {
+            const float f = bf16_to_f32(p.x[e]);
+            amax = fmaxf(amax, fabsf(f));
+            if constexpr (!MEASURE_ONLY) {
+                p.out[e] = cvt1<FMT>(f * m);
+                if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
+            }
+        }
+        if (p.hist) old = publish_amax(p, amax);
     }
     if (p.hist) {
-        publish_amax(p, amax, s_read, win, gridDim.x);
+        finish_fold(p, old, s_read, win, gridDim.x);
     } else if constexpr (!MEASURE_ONLY) {
-        if (p.scale_used && blockIdx.x == 0 && threadIdx.x == 0) *p.scale_used = s_read;
+        if (p.scale_used && blockIdx.x == 0 && t == 0) *p.scale_used = s_read;
     }
 }
 
@@ -391,7 +451,8 @@ __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p)
     }
     if constexpr (QUANT) {
         if (p.q.hist) {
-            publish_amax(p.q, amax, s_read, win, gridDim.x * gridDim.y);
+            const uint32_t old = publish_amax(p.q, amax);
+            finish_fold(p.q, old, s_read, win, gridDim.x * gridDim.y);
         } else if (p.q.scale_used && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
             *p.q.scale_used = s_read;
         }

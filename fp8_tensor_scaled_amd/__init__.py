@@ -127,9 +127,11 @@ def _stream(stream=None):
 
 
 class Ring:
-    """Delayed-scaling state of one operand: the device buffer
-    [hist len | scale | legacy | amax | done] (zero-filled) and the host-side
-    slot index / initialized flag the linear calls maintain."""
+    """Delayed-scaling state of one operand: the zero-filled device buffer
+    [hist len | scale | legacy | amax | done | kernel scratch] (only the first
+    len + 4 words, `published()`, mean anything to callers; the scratch is
+    zero between calls) and the host-side slot index / initialized flag the
+    linear calls maintain."""
 
     def __init__(self, length: int = 16, device="cuda"):
         n = int(_lib.fp8_ring_state_floats(length))
@@ -141,6 +143,14 @@ class Ring:
     @property
     def len(self) -> int:
         return self.c.len
+
+    def published(self) -> torch.Tensor:
+        """View of [hist len | scale | legacy | amax | done]."""
+        return self.state[: self.c.len + 4]
+
+    def scratch(self) -> torch.Tensor:
+        """View of the kernel scratch after `done` (zero between calls)."""
+        return self.state[self.c.len + 4:]
 
     @property
     def idx(self) -> int:

@@ -31,6 +31,11 @@ def _flags() -> list[str]:
         "-Wno-unused-function",
         # keep hipcc from forming packed-fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # keep single-lane atomics as written: the atomic optimizer turns
+        # them into wave-wide reductions that read the returned value at
+        # once, so the quantize fold's round trips would block the stores
+        # issued after them
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", os.path.join(HERE, "..", "include"),
     ]
 

@@ -170,7 +170,7 @@ fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, 
 
 extern "C" {
 
-int64_t fp8_ring_state_floats(int32_t len) { return len < 1 ? 0 : (int64_t)len + 4; }
+int64_t fp8_ring_state_floats(int32_t len) { return len < 1 ? 0 : fp8lin::ring_state_words(len); }
 
 float fp8_format_max(fp8_fmt_t fmt) {
     return fmt == FP8_E4M3 ? 448.0f : fmt == FP8_E5M2 ? 57344.0f : 0.0f;

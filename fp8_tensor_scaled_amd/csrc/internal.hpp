@@ -7,6 +7,17 @@
 
 namespace fp8lin {
 
+// Ring state layout (fp32 words): [hist len | scale | legacy | amax | done],
+// then, from the next 128-byte boundary, kRingGroups lines of 32 words whose
+// first two words are a group's running max and counter (the quantize
+// fold's first level; left at zero by every fold).
+constexpr int kRingGroups = 16;
+constexpr int kRingGroupWords = 32;
+inline int64_t ring_groups_offset(int32_t len) { return ((int64_t)len + 4 + 31) / 32 * 32; }
+inline int64_t ring_state_words(int32_t len) {
+    return ring_groups_offset(len) + (int64_t)kRingGroups * kRingGroupWords;
+}
+
 // Everything a quantize launch needs (plain values, no ownership).
 struct QuantLaunch {
     const uint16_t* x = nullptr;

@@ -6,7 +6,7 @@
 // FP8Recipe.scale_from_history and _ScaleRing): each element is multiplied
 // by the reciprocal of the step and converted with round-to-nearest-even and
 // saturation; the running max of |x| is taken over the raw inputs; every
-// workgroup contributes its max with one atomic, and the workgroup that
+// workgroup contributes its max through atomics, and the workgroup that
 // finishes last records the amax in the history slot, publishes the next
 // step from the window's max and re-arms its scratch slots, so the delayed
 // update costs no extra launch.
@@ -14,7 +14,7 @@
 // gfx950 design:
 //  * HBM streaming: one workgroup of 16 waves per CU (at most 256
 //    workgroups), every lane keeping four 32-byte loads in flight per
-//    iteration (16 bf16 each, two 16-byte loads) and storing 16 fp8 codes
+//    round (16 bf16 each, two 16-byte loads) and storing 16 fp8 codes
 //    with one 16-byte store.  Plain (cached) accesses: the codes feed the
 //    GEMM that follows and the bf16 input is read again by the backward's
 //    quantizes, and in the layer's step non-temporal hints measured slower
@@ -22,20 +22,23 @@
 //    Conversions are v_cvt_pk_{fp8,bf8}_f32 after a med3 clamp to +-max
 //    (satfinite).
 //  * The fold's cost is its atomics: same-address atomics serialize at the
-//    coherence point (about 11 ns each, measured), and a returning atomic waits
-//    for every store its wave issued before it.  So there is one workgroup
-//    per CU (few atomics), each workgroup owns a contiguous range and
-//    publishes its max in its last round after the loads and before the
-//    stores (the round trips overlap the store drain), and the window is
-//    read at kernel start so the last workgroup does not wait for it.
+//    coherence point (about 11 ns each, measured), and a returning atomic
+//    waits for every store its wave issued before it.  So there is one
+//    workgroup per CU, the maxima meet in two levels (16 groups, then the
+//    ring's words), each workgroup owns a contiguous range and publishes in
+//    its last round after the loads and before the stores (the round trips
+//    overlap the store drain), and the window is read at kernel start so
+//    the last workgroup does not wait for it.  The single-lane atomics are
+//    kept as written (the build turns off the compiler's atomic optimizer,
+//    whose wave-wide form would wait for the result at once).
 //  * The fold uses relaxed agent-scope atomics only.  Release/acquire at
 //    agent scope write back / invalidate the per-XCD L2s and cost tens of ns
-//    per workgroup when every workgroup issues them; instead each workgroup
-//    waits for its atomic max to return (the returned value feeds the ticket
-//    increment) before taking a ticket, so by the time the last ticket is
-//    drawn every max has been performed at the device coherence point, where
-//    the last workgroup's atomic read sees it.  The fp8 outputs need no
-//    ordering against the fold (kernel boundaries publish them).
+//    per workgroup when every workgroup issues them; instead each level
+//    takes its counter only after its max has returned (the returned value
+//    feeds the increment), so by the time a counter completes every max it
+//    covers has been performed at the device coherence point, where the
+//    following atomic reads see it.  The fp8 outputs need no ordering
+//    against the fold (kernel boundaries publish them).
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -57,6 +60,7 @@ struct QuantParams {
     float* scale_out;     // ring scale slot
     uint32_t* amax_slot;  // ring scratch: running amax bits
     uint32_t* done;       // ring scratch: finished-workgroup counter
+    uint32_t* groups;     // ring scratch: kRingGroups x (max, counter) lines
     int32_t len;
     int32_t idx;
     float fmax;
@@ -91,40 +95,56 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, fl
     }
 }
 
-// Workgroup max of v -> one atomic max by thread 0, whose previous value
-// (meaningful at thread 0 only) is returned.  Every thread of the workgroup
-// must call it once.
-__device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v) {
+// Workgroup max of v, published by thread 0 in two levels: workgroup b is
+// in group b % G (G = min(workgroups, kRingGroups)); it takes the group's
+// atomic max and then, once that has been performed (the increment depends
+// on the returned value), the group's counter.  The group's last workgroup
+// reads the group max, re-arms the group's line, and does the same on the
+// ring's amax / done words.  Same-address atomics serialize (about 11 ns
+// each, measured), so 16 x 16 contenders cost far less than 256 on one
+// word.  Returns, at thread 0, nblocks - 1 if this workgroup drew the last
+// top-level ticket (it folds), else ~0u.  The whole chain runs before the
+// caller's last stores, which go out while it is in flight.  Every thread
+// of the workgroup must call it once.
+__device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, uint32_t nblocks,
+                                                 uint32_t b) {
     __shared__ float slots[kQuantWaves];
     v = wave_max(v);
     if ((threadIdx.x % kWave) == 0) slots[threadIdx.x / kWave] = v;
     __syncthreads();
-    uint32_t old = 0;
+    uint32_t ticket = ~0u;
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < kQuantWaves; ++w) v = fmaxf(v, slots[w]);
-        old = __hip_atomic_fetch_max(p.amax_slot, __float_as_uint(v), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t ng = nblocks < kRingGroups ? nblocks : kRingGroups;
+        const uint32_t g = b % ng;
+        const uint32_t members = (nblocks - g + ng - 1) / ng;
+        uint32_t* line = p.groups + kRingGroupWords * g;
+        // |x| maxima are never all-ones bits; the comparisons make each
+        // increment wait for the max before it to have been performed.
+        const uint32_t old = __hip_atomic_fetch_max(line, __float_as_uint(v), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t gt = __hip_atomic_fetch_add(line + 1, old == ~0u ? 2u : 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (gt == members - 1) {
+            const uint32_t gm = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(line + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t o2 = __hip_atomic_fetch_max(p.amax_slot, gm, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t t = __hip_atomic_fetch_add(p.done, o2 == ~0u ? 2u : 1u,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t == ng - 1) ticket = nblocks - 1;
+        }
     }
-    return old;
+    return ticket;
 }
 
-// Thread 0 takes a ticket once its atomic max has been performed (the
-// increment depends on the returned value); the workgroup that draws the
-// last ticket folds, on its wave 0.  Code between publish_amax and this call
-// (the workgroup's last stores) overlaps the atomics' round trips.
-__device__ __forceinline__ void finish_fold(const QuantParams& p, uint32_t old, float s_read,
+// The workgroup that drew the last ticket folds, on its wave 0.
+__device__ __forceinline__ void finish_fold(const QuantParams& p, uint32_t ticket, float s_read,
                                             float win, uint32_t nblocks) {
     if (threadIdx.x >= kWave) return;
-    int last = 0;
-    if (threadIdx.x == 0) {
-        // |x| maxima are never all-ones bits; the comparison makes the
-        // ticket wait for the max to have been performed.
-        const uint32_t inc = old == 0xffffffffu ? 2u : 1u;
-        const uint32_t ticket =
-            __hip_atomic_fetch_add(p.done, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = ticket == nblocks - 1u;
-    }
+    const int last = threadIdx.x == 0 && ticket == nblocks - 1u;
     if (__shfl(last, 0, kWave)) fold_ring(p, s_read, win);
 }
 
@@ -189,7 +209,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     const int t = threadIdx.x;
     const float win = (p.hist && t < p.len && t < kWave && t != p.idx) ? p.hist[t] : 0.0f;
     float amax = 0.0f;
-    uint32_t old = 0;
+    uint32_t ticket = ~0u;  // publish_amax's result (thread 0)
     if (p.vec) {
         const int64_t nvec = p.numel / kVecElems;
         const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
@@ -214,20 +234,20 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         for (int64_t rd = 0; rd < nr; ++rd) {
             const int64_t c0 = lo + rd * kRound + t;
             uint4 r[kUnroll][2];
+            // Loads are unconditional (a chunk past the range re-reads the
+            // range's first one and is ignored), so their waits stay counted
+            // one by one instead of collapsing into a wait for all of them.
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t c = c0 + u * kQuantThreads;
-                if (c < hi) {
-                    r[u][0] = xv[2 * c];
-                    r[u][1] = xv[2 * c + 1];
-                } else {
-                    r[u][0] = make_uint4(0, 0, 0, 0);
-                    r[u][1] = make_uint4(0, 0, 0, 0);
-                }
+                const int64_t cl = c < hi ? c : lo;
+                r[u][0] = xv[2 * cl];
+                r[u][1] = xv[2 * cl + 1];
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) amax = absmax16(r[u][0], r[u][1], amax);
-            if (p.hist && rd == nr - 1) old = publish_amax(p, amax);
+            for (int u = 0; u < kUnroll; ++u)
+                if (c0 + u * kQuantThreads < hi) amax = absmax16(r[u][0], r[u][1], amax);
+            if (p.hist && rd == nr - 1) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
             if constexpr (!MEASURE_ONLY) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
@@ -236,7 +256,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
                 }
             }
         }
-        if (p.hist && nr == 0) old = publish_amax(p, amax);
+        if (p.hist && nr == 0) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
     } else {
         const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
         for (int64_t e = (int64_t)blockIdx.x * kQuantThreads + t; e < p.numel; e += stride) {
@@ -247,10 +267,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
                 if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
             }
         }
-        if (p.hist) old = publish_amax(p, amax);
+        if (p.hist) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
     }
     if (p.hist) {
-        finish_fold(p, old, s_read, win, gridDim.x);
+        finish_fold(p, ticket, s_read, win, gridDim.x);
     } else if constexpr (!MEASURE_ONLY) {
         if (p.scale_used && blockIdx.x == 0 && t == 0) *p.scale_used = s_read;
     }
@@ -277,6 +297,7 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
         p.scale_out = q.ring_state + q.ring_len;
         p.amax_slot = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 2);
         p.done = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 3);
+        p.groups = reinterpret_cast<uint32_t*>(q.ring_state + ring_groups_offset(q.ring_len));
         p.len = q.ring_len;
         p.idx = q.ring_idx;
     }
@@ -343,11 +364,12 @@ hipError_t launch_ring_finalize(float* state, int32_t len, int32_t idx, int fmt,
 // Pass 1 (vector path, n % 8 == 0, 16-byte aligned rows): a workgroup of
 // 1024 lanes covers 256 columns x one chunk of rows; its lanes are 32 column
 // groups (8 columns = one 16-byte load) x 32 row phases, each lane summing
-// every 32nd row of the chunk in row order with up to 8 loads in flight; the
-// 32 phases are then added in LDS in phase order and the chunk's 256 column
+// every 32nd row of the chunk in row order with 8 loads in flight; the 32
+// phases are then added in LDS in phase order and the chunk's 256 column
 // sums written as partials.  When fused, the same lanes also encode the 8
 // values of each row they read (8 codes, one 8-byte store), take the max of
-// |x| and fold it like the quantize kernel.  Chunks are sized for about one
+// |x| and fold it like the quantize kernel (published in the last round
+// before that round's stores).  Chunks are sized for about one
 // workgroup per CU (the fold's atomics stay few).
 // Pass 2: 64 columns per workgroup, 4 lanes per column each adding a
 // quarter of the chunk partials, combined in a fixed order, one rounding.
@@ -404,36 +426,63 @@ __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p)
     const int64_t c0 = (int64_t)blockIdx.x * 256 + cg * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float amax = 0.0f;
-    auto row = [&](const uint4& v, int64_t r) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
+    uint32_t ticket = ~0u;  // publish_amax's result (thread 0)
+    // Rounds of 8 rows per lane (8 loads in flight); the round count is
+    // uniform over the workgroup, rows past the chunk read as zeros and
+    // store nothing.  Column sums and |x| take the rows in order; with a
+    // ring, the max is published in the last round before its stores.
+    constexpr int kRows = 8;
+    const int64_t nr = (r1 - r0 + kRows * kQCPhases - 1) / (kRows * kQCPhases);
+    const bool colok = c0 < p.n;
+    for (int64_t rd = 0; rd < nr; ++rd) {
+        const int64_t rb = r0 + rd * (kRows * kQCPhases) + ph;
+        uint4 v[kRows];
+        // Unconditional loads (rows past the chunk re-read its first row
+        // and are ignored; so are column groups past n, which read column 0)
+        // keep their waits counted one by one.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[2 * j] = bf16_lo(w[j]);
-            f[2 * j + 1] = bf16_hi(w[j]);
+        for (int u = 0; u < kRows; ++u) {
+            const int64_t r = rb + u * kQCPhases;
+            const int64_t rl = r < r1 ? r : r0;
+            v[u] = *reinterpret_cast<const uint4*>(p.g + rl * p.n + (colok ? c0 : 0));
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += f[j];
+        for (int u = 0; u < kRows; ++u) {
+            if (!(colok && rb + u * kQCPhases < r1)) continue;  // adds nothing (keeps -0)
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+                acc[2 * j] += lo;
+                acc[2 * j + 1] += hi;
+                if constexpr (QUANT) amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+            }
+        }
         if constexpr (QUANT) {
+            if (p.q.hist && rd == nr - 1) ticket = publish_amax(p.q, amax, gridDim.x * gridDim.y,
+                                                    blockIdx.y * gridDim.x + blockIdx.x);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-            uint2 o;
-            o.x = cvt4<FMT>(f[0] * mul, f[1] * mul, f[2] * mul, f[3] * mul);
-            o.y = cvt4<FMT>(f[4] * mul, f[5] * mul, f[6] * mul, f[7] * mul);
-            *reinterpret_cast<uint2*>(p.q.out + r * p.n + c0) = o;
+            for (int u = 0; u < kRows; ++u) {
+                const int64_t r = rb + u * kQCPhases;
+                if (colok && r < r1) {
+                    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    float f[8];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        f[2 * j] = bf16_lo(w[j]) * mul;
+                        f[2 * j + 1] = bf16_hi(w[j]) * mul;
+                    }
+                    uint2 o;
+                    o.x = cvt4<FMT>(f[0], f[1], f[2], f[3]);
+                    o.y = cvt4<FMT>(f[4], f[5], f[6], f[7]);
+                    *reinterpret_cast<uint2*>(p.q.out + r * p.n + c0) = o;
+                }
+            }
         }
-    };
-    if (c0 < p.n) {
-        int64_t r = r0 + ph;
-        for (; r + 7 * kQCPhases < r1; r += 8 * kQCPhases) {
-            uint4 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = *reinterpret_cast<const uint4*>(p.g + (r + u * kQCPhases) * p.n + c0);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) row(v[u], r + u * kQCPhases);
-        }
-        for (; r < r1; r += kQCPhases) row(*reinterpret_cast<const uint4*>(p.g + r * p.n + c0), r);
+    }
+    if constexpr (QUANT) {
+        if (p.q.hist && nr == 0) ticket = publish_amax(p.q, amax, gridDim.x * gridDim.y,
+                                                    blockIdx.y * gridDim.x + blockIdx.x);
     }
     __shared__ float red[kQCPhases][256 + 4];
 #pragma unroll
@@ -451,8 +500,7 @@ __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p)
     }
     if constexpr (QUANT) {
         if (p.q.hist) {
-            const uint32_t old = publish_amax(p.q, amax);
-            finish_fold(p.q, old, s_read, win, gridDim.x * gridDim.y);
+            finish_fold(p.q, ticket, s_read, win, gridDim.x * gridDim.y);
         } else if (p.q.scale_used && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
             *p.q.scale_used = s_read;
         }
@@ -548,6 +596,7 @@ hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, ui
         p.q.scale_out = q.ring_state + q.ring_len;
         p.q.amax_slot = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 2);
         p.q.done = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 3);
+        p.q.groups = reinterpret_cast<uint32_t*>(q.ring_state + ring_groups_offset(q.ring_len));
         p.q.len = q.ring_len;
         p.q.idx = q.ring_idx;
     }

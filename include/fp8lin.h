@@ -60,13 +60,17 @@ typedef enum {
 /* Delayed-scaling state of one operand (compare view: astrai/extension/
  * fp8.py, _ScaleRing; csrc/kernels/fp8/quantize.cuh, publish_amax).
  *
- * `state` is a device buffer of len + 4 fp32 words:
- *     [ hist[0..len) | scale | legacy | amax | done ]
+ * `state` is a device buffer of fp8_ring_state_floats(len) fp32 words:
+ *     [ hist[0..len) | scale | legacy | amax | done | pad | groups ]
  * hist  : amax history window;
  * scale : the published step for the next use;
  * legacy: unused (kept so the buffer layout matches the pages' ring);
  * amax, done: kernel scratch (running amax as fp32 bits, block counter as
- *        uint32 bits) that every fold leaves at zero again.
+ *        uint32 bits) that every fold leaves at zero again;
+ * pad, groups: more kernel scratch, also left at zero by every fold: from
+ *        the first 128-byte boundary after `done`, 16 lines of 32 words
+ *        (the first level of the quantize kernels' amax reduction).
+ * Only the first len + 4 words have a meaning for callers.
  * The caller zero-fills `state` once when the ring is created.
  * `len`, `idx`, `initialized` live on the host: `idx` is the slot the next
  * fold writes; `initialized` = 0 makes the linear calls seed the ring from
@@ -75,14 +79,15 @@ typedef enum {
  * fp8_linear_fwd / fp8_linear_bwd seed (set initialized = 1) and advance
  * idx = (idx + 1) % len after enqueueing their work. */
 typedef struct fp8_ring {
-    float* state;        /* device, len + 4 floats */
+    float* state;        /* device, fp8_ring_state_floats(len) floats */
     int32_t len;         /* history length, 1 <= len <= 4096 */
     int32_t idx;         /* 0 <= idx < len */
     int32_t initialized; /* host flag for the linear calls */
     int32_t reserved;
 } fp8_ring_t;
 
-/* Number of fp32 words of a ring state buffer with history length len. */
+/* Number of fp32 words of a ring state buffer with history length len
+ * (0 for len < 1): len + 4 rounded up to a multiple of 32, plus 512. */
 int64_t fp8_ring_state_floats(int32_t len);
 
 /* Largest finite value of a format (448 or 57344); 0 for a bad format. */

@@ -44,6 +44,13 @@ def dev_f32(v) -> torch.Tensor:
     return torch.tensor(np.atleast_1d(np.asarray(v, np.float32)), device="cuda")
 
 
+def ring_state_equal(ring, oring) -> bool:
+    """A device ring's published words [hist | scale | legacy | amax | done]
+    equal the oracle ring's state, and its kernel scratch is all zero."""
+    pub = ring.published().cpu().numpy()
+    return np.array_equal(pub, oring.state()) and not ring.scratch().cpu().numpy().any()
+
+
 def bf16_ulp(r: np.ndarray) -> np.ndarray:
     a = np.abs(r.astype(np.float64))
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))

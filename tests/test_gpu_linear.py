@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import check_gemm, from_dev_bf16, from_dev_u8, to_dev_bf16
+from tests.gpu_util import (check_gemm, from_dev_bf16, from_dev_u8, ring_state_equal,
+                            to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,7 +92,7 @@ def test_train_delayed_hybrid_four_steps(lib, orc):
         sbh = sb.cpu().numpy()
         assert (sbh[0], sbh[1], sbh[2]) == (rb.sg, rb.sx, rb.sw), t
         for gr, orr in ((rx, ox), (rw, ow), (rg, og)):
-            assert np.array_equal(gr.state.cpu().numpy(), orr.state()), t
+            assert ring_state_equal(gr, orr), t
             assert gr.idx == orr.idx and gr.initialized == orr.initialized
         assert np.array_equal(f.x8(), rf.x8.ravel())
         assert np.array_equal(f.w8(), rf.w8.ravel())
@@ -148,7 +149,7 @@ def test_backward_masks_and_dynamic_small(lib, orc, dynamic):
             absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
             check_gemm(from_dev_bf16(db), rb.db, absg, M, "db")
         if not dynamic:
-            assert np.array_equal(rg.state.cpu().numpy(), og.state())
+            assert ring_state_equal(rg, og)
 
 
 def test_linear_invalid_arguments(lib):

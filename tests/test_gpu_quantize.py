@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import check_gemm, dev_f32, from_dev_bf16, from_dev_u8, to_dev_bf16
+from tests.gpu_util import (check_gemm, dev_f32, from_dev_bf16, from_dev_u8, ring_state_equal,
+                            to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,8 +133,7 @@ def test_ring_fold_measure_and_quantize(lib, orc):
         torch.cuda.synchronize()
         assert float(used.cpu()[0]) == s_snap
         assert np.array_equal(from_dev_u8(out), ref.ravel())
-        st = ring.state.cpu().numpy()
-        assert np.array_equal(st, oring.state()), (t, st, oring.state())
+        assert ring_state_equal(ring, oring), (t, ring.state.cpu().numpy(), oring.state())
         ring.idx = (ring.idx + 1) % 16
         oring.advance()
 
@@ -151,7 +151,7 @@ def test_ring_fold_many_workgroups_and_empty(lib, orc):
     a = orc.amax(x)
     assert st[3] == a
     assert st[4] == orc.scale_from_peak(a, E5M2, 2)
-    assert st[6] == 0 and st[7] == 0
+    assert st[6] == 0 and st[7] == 0 and not ring.scratch().cpu().numpy().any()
     # empty input folds amax 0 into slot 0
     ring.idx = 0
     lib.fp8_quantize(torch.empty(0, dtype=torch.int16, device="cuda"), E5M2, ring=ring,
@@ -159,6 +159,29 @@ def test_ring_fold_many_workgroups_and_empty(lib, orc):
     torch.cuda.synchronize()
     st = ring.state.cpu().numpy()
     assert st[0] == 0 and st[4] == orc.scale_from_peak(a, E5M2, 2)
+    assert not ring.scratch().cpu().numpy().any()
+
+
+@pytest.mark.parametrize("blocks", [1, 5, 16, 17, 37, 256])
+def test_ring_fold_group_counts(lib, orc, blocks):
+    """The fold's two-level reduction over workgroup counts below, at and
+    above its 16 groups (uneven group sizes included), for the vector path
+    (a ragged tail) and the unaligned scalar path, three folds in a row:
+    hist and scale match the oracle, the scratch is zero after each."""
+    rng = np.random.default_rng(blocks)
+    numel = blocks * 1024 * 16 - 5  # the grid is ceil(numel / 16384) workgroups
+    ring = lib.Ring(8)
+    oring = orc.Ring(8)
+    for t in range(3):
+        x = wl.normal_bf16((numel,), float(rng.uniform(0.5, 4.0)), 1000 + 10 * blocks + t)
+        offset = t % 2  # odd start: unaligned, scalar path
+        xd = to_dev_bf16(np.concatenate([np.zeros(offset, np.uint16), x]))[offset:]
+        lib.fp8_quantize(xd, E4M3, ring=ring)
+        oring.fold(orc.amax(x), E4M3)
+        torch.cuda.synchronize()
+        assert ring_state_equal(ring, oring), (blocks, t)
+        ring.idx = (ring.idx + 1) % 8
+        oring.advance()
 
 
 def test_scale_ring_finalize(lib, orc):
@@ -170,7 +193,7 @@ def test_scale_ring_finalize(lib, orc):
         lib.fp8_scale_ring_finalize(ring, E4M3, dev_f32(a), margin=1)
         oring.fold(a, E4M3)
         torch.cuda.synchronize()
-        assert np.array_equal(ring.state.cpu().numpy(), oring.state())
+        assert ring_state_equal(ring, oring)
         ring.idx = (ring.idx + 1) % 16
         oring.advance()
 

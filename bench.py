@@ -216,13 +216,15 @@ def check_against_linear_entry_points(f, torch):
 # HBM traffic of the step's GEMMs from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch, one counter per run, `bench.py --kernel NAME`), scaled by
 # what the same counters read for a 192 MiB copy (FETCH_SIZE x 2.0, WRITE_SIZE
-# x 1.0).  Valid only for the kernel sources they were taken on: `src` is the
-# sha256 of gemm_tiled.hip + common.hpp then; any other source gives null.
+# x 1.0).  Valid only for the kernel sources they were taken on: PMC_SRC is
+# the sha256 of gemm_tiled.hip + common.hpp then; any other source gives null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 PMC_TRAFFIC = {
-    "gemm_nn_dx": {"FETCH_SIZE": 49309.2, "WRITE_SIZE": 32768.0,
-                   "src": "45212e95110c0a845e320312e1622297461559bc2a65672a10ea8429024063de"},
+    "gemm_nt_fwd": {"FETCH_SIZE": 49232.0, "WRITE_SIZE": 32768.0},
+    "gemm_nn_dx": {"FETCH_SIZE": 49235.5, "WRITE_SIZE": 32768.0},
+    "gemm_tn_dw": {"FETCH_SIZE": 49234.5, "WRITE_SIZE": 32768.0},
 }
+PMC_SRC = "9fbd02544cd04fa8df339ab851e4ac367d11394de7fe341555e7b779765c0f30"
 
 
 def gemm_source_hash():
@@ -238,7 +240,7 @@ def gemm_source_hash():
 def pmc_traffic(kernel):
     """HBM bytes per launch of `kernel` from the recorded counters, or None."""
     rec = PMC_TRAFFIC.get(kernel)
-    if rec is None or rec["src"] != gemm_source_hash():
+    if rec is None or PMC_SRC != gemm_source_hash():
         return None
     return int(1024 * sum(rec[c] * PMC_SCALE[c] for c in PMC_SCALE))
 

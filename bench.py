@@ -8,7 +8,8 @@ gradients):
     each pass writing the E4M3 codes and the backward's E5M2 codes
     (fp8_quantize2)                                         -> NT GEMM + bias
   quantize g (E5M2, fold) with its column sum (bias gradient) from the
-    same pass (fp8_quantize_colsum)              -> NN GEMM (dX), TN GEMM (dW).
+    same pass (fp8_quantize_colsum)   -> NN GEMM (dX) + TN GEMM (dW), one
+    launch (fp8_mm_pair).
 The results are those of fp8_linear_fwd / fp8_linear_bwd (which quantize x
 and w again in the backward); before timing, the step's outputs are checked
 to be bit-identical to theirs.
@@ -54,8 +55,8 @@ def parse():
     return p.parse_args()
 
 
-KERNELS = ("gemm_nt_4096", "gemm_nn_4096", "gemm_tn_4096", "gemm_nt_64x8192x2048",
-           "gemm_nt_8192", "quantize_8192x8192", "copy_192MB")
+KERNELS = ("gemm_nt_4096", "gemm_nn_4096", "gemm_tn_4096", "gemm_bwd_pair_4096",
+           "gemm_nt_64x8192x2048", "gemm_nt_8192", "quantize_8192x8192", "copy_192MB")
 
 
 def single_kernel(f, torch, name, reps):
@@ -80,6 +81,18 @@ def single_kernel(f, torch, name, reps):
             f.fp8_mm(a, b, fmt, ta, tb, M, N, K, lda, ldb, 1, 0, 0, s, s, None, out)
         nbytes = M * K + N * K + 2 * M * N
         work = dict(flop=2.0 * M * N * K, bytes=nbytes)
+    elif name == "gemm_bwd_pair_4096":
+        # the step's backward: dX (NN) and dW (TN) at M = N = K = 4096, one launch
+        n = 4096
+        g8, w8, x8 = (torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+                      for _ in range(3))
+        dx = torch.empty(n * n, dtype=torch.int16, device=dev)
+        dw = torch.empty(n * n, dtype=torch.int16, device=dev)
+
+        def launch():
+            f.fp8_mm_pair((g8, w8, E5M2, 0, 0, n, n, n, n, n, 1, 0, 0, s, s, None, dx),
+                          (g8, x8, E5M2, 1, 0, n, n, n, n, n, 1, 0, 0, s, s, None, dw))
+        work = dict(flop=2 * 2.0 * n ** 3, bytes=2 * (2 * n * n + 2 * n * n))
     elif name == "quantize_8192x8192":
         n = 8192 * 8192
         x = torch.randn(n, device=dev).to(torch.bfloat16).view(torch.int16)
@@ -170,8 +183,7 @@ class Layer:
         # from the same pass; dX (NN) and dW (TN)
         f.fp8_quantize_colsum(self.g, M, N, E5M2, self.rg.scale, self.g8, self.db, self.cs_ws,
                               ring=self.rg, scale_used=self.sg)
-        self.gemm_nn_dx(f)
-        self.gemm_tn_dw(f)
+        self.gemm_bwd_pair(f)
         for r in (self.rx, self.rw, self.rg):
             r.idx = (r.idx + 1) % r.len
 
@@ -181,15 +193,25 @@ class Layer:
         f.fp8_mm(self.x8, self.w8, E4M3, 0, 1, M, N, K, K, K, 1, 0, 0, self.sfwd[0:1],
                  self.sfwd[1:2], self.bias, self.out)
 
-    def gemm_nn_dx(self, f):
+    def nn_dx_args(self):
         M, N, K = self.M, self.N, self.K
-        f.fp8_mm(self.g8, self.w8b, E5M2, 0, 0, M, K, N, N, K, 1, 0, 0, self.sg,
-                 self.sfwd[1:2], None, self.dx)
+        return (self.g8, self.w8b, E5M2, 0, 0, M, K, N, N, K, 1, 0, 0, self.sg, self.sfwd[1:2],
+                None, self.dx)
+
+    def tn_dw_args(self):
+        M, N, K = self.M, self.N, self.K
+        return (self.g8, self.x8b, E5M2, 1, 0, N, K, M, N, K, 1, 0, 0, self.sg, self.sfwd[0:1],
+                None, self.dw)
+
+    def gemm_nn_dx(self, f):
+        f.fp8_mm(*self.nn_dx_args())
 
     def gemm_tn_dw(self, f):
-        M, N, K = self.M, self.N, self.K
-        f.fp8_mm(self.g8, self.x8b, E5M2, 1, 0, N, K, M, N, K, 1, 0, 0, self.sg,
-                 self.sfwd[0:1], None, self.dw)
+        f.fp8_mm(*self.tn_dw_args())
+
+    def gemm_bwd_pair(self, f):
+        """dX (NN) and dW (TN) from one call, as fp8_linear_bwd runs them."""
+        f.fp8_mm_pair(self.nn_dx_args(), self.tn_dw_args())
 
 
 def check_against_linear_entry_points(f, torch):
@@ -436,17 +458,20 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    # The step's GEMMs, each launched 20 times back to back on its own
-    # operands between two HIP events on the launch stream: the per-launch
-    # durations the roofline entry uses.
-    names = ["gemm_nt_fwd", "gemm_nn_dx", "gemm_tn_dw"]
+    # The step's GEMM launches (the forward NT, and the backward's dX and dW
+    # from one paired launch), plus dX and dW launched on their own for
+    # reference: each launched 20 times back to back on its operands
+    # between two HIP events on the launch stream.  The roofline entry takes
+    # the step's GEMM launch with the largest duration.
+    n_gemms = {"gemm_nt_fwd": 1, "gemm_bwd_pair": 2, "gemm_nn_dx": 1, "gemm_tn_dw": 1}
     gemm_flops = 2.0 * size ** 3
     kern = {}
-    for nm in names:
+    for nm, cnt in n_gemms.items():
         fn = getattr(layer, nm)
         dur = time_kernel(torch, lambda i: fn(f), 20)
-        kern[nm] = dict(us=round(dur * 1e3, 2), tflops=round(gemm_flops / (dur * 1e-3) / 1e12, 1))
-    dom = max(names, key=lambda k: kern[k]["us"])
+        kern[nm] = dict(us=round(dur * 1e3, 2),
+                        tflops=round(cnt * gemm_flops / (dur * 1e-3) / 1e12, 1))
+    dom = max(("gemm_nt_fwd", "gemm_bwd_pair"), key=lambda k: kern[k]["us"])
     achieved = kern[dom]["tflops"]
     value = 3 * gemm_flops / (ms_step * 1e-3) / 1e12
     line = {

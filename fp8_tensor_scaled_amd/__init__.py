@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "FMT_MAX", "Ring", "library_path", "fp8_quantize", "fp8_quantize2",
-    "fp8_scale_ring_finalize", "fp8_mm", "fp8_colsum", "fp8_colsum_workspace",
+    "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_pair", "fp8_colsum", "fp8_colsum_workspace",
     "fp8_quantize_colsum",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
     "fp8_linear_bwd_workspace", "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset",
@@ -33,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 EXPORTED_SYMBOLS = (
     "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize2",
     "fp8_scale_ring_finalize",
-    "fp8_mm", "fp8_colsum_workspace", "fp8_colsum", "fp8_quantize_colsum",
+    "fp8_mm", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum", "fp8_quantize_colsum",
     "fp8_linear_fwd_workspace",
     "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
     "fp8_linear_bwd_workspace", "fp8_linear_bwd", "fp8_last_error", "fp8_version",
@@ -43,6 +43,16 @@ EXPORTED_SYMBOLS = (
 class _RingC(ctypes.Structure):
     _fields_ = [("state", ctypes.c_void_p), ("len", ctypes.c_int32), ("idx", ctypes.c_int32),
                 ("initialized", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class _MmArgs(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("fmt", ctypes.c_int32),
+                ("trans_a", ctypes.c_int32), ("trans_b", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("m", ctypes.c_int64), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64),
+                ("batch", ctypes.c_int64), ("stride_a", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("scale_a", ctypes.c_void_p),
+                ("scale_b", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("out", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -66,6 +76,7 @@ def _load() -> ctypes.CDLL:
         "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
         "fp8_mm": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P,
                          P, P]),
+        "fp8_mm_pair": (I32, [ctypes.POINTER(_MmArgs), ctypes.POINTER(_MmArgs), P]),
         "fp8_colsum_workspace": (S, [I64, I64]),
         "fp8_colsum": (I32, [P, I64, I64, P, P, S, P]),
         "fp8_quantize_colsum": (I32, [P, I64, I64, I32, P, P, R, I32, P, P, P, S, P]),
@@ -214,6 +225,22 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt: int, trans_a: int, trans_b: in
                      stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias), _ptr(out),
                      _stream(stream))
     _check(st, "fp8_mm")
+
+
+def _mm_args(a, b, fmt, trans_a, trans_b, m, n, k, lda, ldb, batch, stride_a, stride_b,
+             scale_a, scale_b, bias, out) -> _MmArgs:
+    return _MmArgs(_ptr(a), _ptr(b), fmt, trans_a, trans_b, 0, m, n, k, lda, ldb, batch,
+                   stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias), _ptr(out))
+
+
+def fp8_mm_pair(p0: tuple, p1: tuple, stream=None) -> None:
+    """Two independent fp8_mm products from one call; p0, p1 are fp8_mm's
+    positional arguments (a, b, fmt, trans_a, trans_b, m, n, k, lda, ldb,
+    batch, stride_a, stride_b, scale_a, scale_b, bias, out).  One launch when
+    p0 is NN and p1 is TN and both are large; see fp8lin.h."""
+    a0, a1 = _mm_args(*p0), _mm_args(*p1)
+    st = _lib.fp8_mm_pair(ctypes.byref(a0), ctypes.byref(a1), _stream(stream))
+    _check(st, "fp8_mm_pair")
 
 
 def fp8_colsum_workspace(m: int, n: int) -> int:

@@ -141,10 +141,10 @@ fp8_status_t do_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt
     return FP8_OK;
 }
 
-fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, int tb,
-                     int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
-                     const float* sa, const float* sb, const uint16_t* bias, uint16_t* out,
-                     hipStream_t stream) {
+fp8lin::GemmLaunch gemm_of(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, int tb,
+                           int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
+                           const float* sa, const float* sb, const uint16_t* bias,
+                           uint16_t* out) {
     fp8lin::GemmLaunch g;
     g.a = a;
     g.b = b;
@@ -161,8 +161,60 @@ fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, 
     g.scale_b = sb;
     g.bias = bias;
     g.out = out;
+    return g;
+}
+
+fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, int tb,
+                     int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
+                     const float* sa, const float* sb, const uint16_t* bias, uint16_t* out,
+                     hipStream_t stream) {
+    hipError_t e = fp8lin::launch_gemm(
+        gemm_of(a, b, fmt, ta, tb, m, n, k, lda, ldb, sa, sb, bias, out), stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return FP8_OK;
+}
+
+fp8_status_t do_gemm_launch(const fp8lin::GemmLaunch& g, hipStream_t stream) {
     hipError_t e = fp8lin::launch_gemm(g, stream);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return FP8_OK;
+}
+
+fp8_status_t do_gemm_pair(const fp8lin::GemmLaunch& g0, const fp8lin::GemmLaunch& g1,
+                          hipStream_t stream) {
+    hipError_t e = fp8lin::launch_gemm_pair(g0, g1, stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm pair launch");
+    return FP8_OK;
+}
+
+// fp8_mm's argument checks; fills g on success.
+fp8_status_t check_mm(const char* who, const fp8_mm_args_t& x, fp8lin::GemmLaunch& g) {
+    if (!fmt_ok(x.fmt)) return fail(FP8_EINVAL, "%s: unsupported fp8 format %d", who, x.fmt);
+    if (!x.a || !x.b || !x.out || !x.scale_a || !x.scale_b)
+        return fail(FP8_EINVAL, "%s: NULL operand, output or scale", who);
+    if ((x.trans_a != 0 && x.trans_a != 1) || (x.trans_b != 0 && x.trans_b != 1))
+        return fail(FP8_EINVAL, "%s: trans flags must be 0 or 1", who);
+    if (x.m < 1 || x.n < 1 || x.k < 1)
+        return fail(FP8_EINVAL, "%s: m, n, k must be >= 1 (got %lld, %lld, %lld)", who,
+                    (long long)x.m, (long long)x.n, (long long)x.k);
+    if (x.batch < 1 || x.batch > 65535)
+        return fail(FP8_EINVAL, "%s: batch %lld outside [1, 65535]", who, (long long)x.batch);
+    const int64_t a_cols = x.trans_a ? x.m : x.k, b_cols = x.trans_b ? x.k : x.n;
+    if (x.lda < a_cols)
+        return fail(FP8_EINVAL, "%s: lda %lld < %lld", who, (long long)x.lda,
+                    (long long)a_cols);
+    if (x.ldb < b_cols)
+        return fail(FP8_EINVAL, "%s: ldb %lld < %lld", who, (long long)x.ldb,
+                    (long long)b_cols);
+    if (x.batch > 1 && (x.stride_a < 0 || x.stride_b < 0))
+        return fail(FP8_EINVAL, "%s: negative batch stride", who);
+    if ((double)x.m * (double)x.n * (double)x.batch >= 1099511627776.0)
+        return fail(FP8_EINVAL, "%s: output too large", who);
+    g = gemm_of(x.a, x.b, x.fmt, x.trans_a, x.trans_b, x.m, x.n, x.k, x.lda, x.ldb, x.scale_a,
+                x.scale_b, x.bias, x.out);
+    g.batch = x.batch;
+    g.stride_a = x.stride_a;
+    g.stride_b = x.stride_b;
     return FP8_OK;
 }
 
@@ -253,48 +305,46 @@ fp8_status_t fp8_mm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t t
                     const float* scale_b, const uint16_t* bias, uint16_t* out,
                     hipStream_t stream) {
     g_err[0] = 0;
-    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_mm: unsupported fp8 format %d", fmt);
-    if (!a || !b || !out || !scale_a || !scale_b)
-        return fail(FP8_EINVAL, "fp8_mm: NULL operand, output or scale");
-    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
-        return fail(FP8_EINVAL, "fp8_mm: trans flags must be 0 or 1");
-    if (m < 1 || n < 1 || k < 1)
-        return fail(FP8_EINVAL, "fp8_mm: m, n, k must be >= 1 (got %lld, %lld, %lld)",
-                    (long long)m, (long long)n, (long long)k);
-    if (batch < 1 || batch > 65535)
-        return fail(FP8_EINVAL, "fp8_mm: batch %lld outside [1, 65535]", (long long)batch);
-    const int64_t a_cols = trans_a ? m : k, b_cols = trans_b ? k : n;
-    if (lda < a_cols)
-        return fail(FP8_EINVAL, "fp8_mm: lda %lld < %lld", (long long)lda, (long long)a_cols);
-    if (ldb < b_cols)
-        return fail(FP8_EINVAL, "fp8_mm: ldb %lld < %lld", (long long)ldb, (long long)b_cols);
-    if (batch > 1 && (stride_a < 0 || stride_b < 0))
-        return fail(FP8_EINVAL, "fp8_mm: negative batch stride");
-    if ((double)m * (double)n * (double)batch >= 1099511627776.0)
-        return fail(FP8_EINVAL, "fp8_mm: output too large");
-    fp8_status_t st = check_device();
-    if (st) return st;
+    fp8_mm_args_t x{};
+    x.a = a;
+    x.b = b;
+    x.fmt = fmt;
+    x.trans_a = trans_a;
+    x.trans_b = trans_b;
+    x.m = m;
+    x.n = n;
+    x.k = k;
+    x.lda = lda;
+    x.ldb = ldb;
+    x.batch = batch;
+    x.stride_a = stride_a;
+    x.stride_b = stride_b;
+    x.scale_a = scale_a;
+    x.scale_b = scale_b;
+    x.bias = bias;
+    x.out = out;
     fp8lin::GemmLaunch g;
-    g.a = a;
-    g.b = b;
-    g.fmt = fmt;
-    g.trans_a = trans_a;
-    g.trans_b = trans_b;
-    g.m = m;
-    g.n = n;
-    g.k = k;
-    g.lda = lda;
-    g.ldb = ldb;
-    g.batch = batch;
-    g.stride_a = stride_a;
-    g.stride_b = stride_b;
-    g.scale_a = scale_a;
-    g.scale_b = scale_b;
-    g.bias = bias;
-    g.out = out;
+    fp8_status_t st = check_mm("fp8_mm", x, g);
+    if (st) return st;
+    if ((st = check_device())) return st;
     hipError_t e = fp8lin::launch_gemm(g, stream);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return FP8_OK;
+}
+
+fp8_status_t fp8_mm_pair(const fp8_mm_args_t* p0, const fp8_mm_args_t* p1, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!p0 || !p1) return fail(FP8_EINVAL, "fp8_mm_pair: NULL argument block");
+    fp8lin::GemmLaunch g0, g1;
+    fp8_status_t st = check_mm("fp8_mm_pair (problem 0)", *p0, g0);
+    if (st) return st;
+    if ((st = check_mm("fp8_mm_pair (problem 1)", *p1, g1))) return st;
+    const uintptr_t o0 = (uintptr_t)p0->out, o1 = (uintptr_t)p1->out;
+    const uintptr_t e0 = o0 + (uintptr_t)(p0->batch * p0->m * p0->n * 2);
+    const uintptr_t e1 = o1 + (uintptr_t)(p1->batch * p1->m * p1->n * 2);
+    if (o0 < e1 && o1 < e0) return fail(FP8_EINVAL, "fp8_mm_pair: the outputs overlap");
+    if ((st = check_device())) return st;
+    return do_gemm_pair(g0, g1, stream);
 }
 
 size_t fp8_colsum_workspace(int64_t m, int64_t n) {
@@ -518,21 +568,23 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         sx = scales_fwd;
         sw = scales_fwd + 1;
     }
-    if (dx) {
-        if ((st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
-                              scales_out ? scales_out + 2 : nullptr, stream)))
-            return st;
-        // dX[M][K] = g8[M][N] . w8[N][K]  (NN)
-        if ((st = do_gemm(g8, w8, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx, stream)))
-            return st;
-    }
-    if (dw) {
-        if ((st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
-                              scales_out ? scales_out + 1 : nullptr, stream)))
-            return st;
-        // dW[N][K] = g8^T . x8: A = g8 stored [M][N] (k-major rows of m), B = x8 [M][K]  (TN)
-        if ((st = do_gemm(g8, x8, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw, stream)))
-            return st;
+    if (dx && (st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
+                                scales_out ? scales_out + 2 : nullptr, stream)))
+        return st;
+    if (dw && (st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
+                                scales_out ? scales_out + 1 : nullptr, stream)))
+        return st;
+    // dX[M][K] = g8[M][N] . w8[N][K]  (NN)
+    // dW[N][K] = g8^T . x8: A = g8 stored [M][N] (k-major rows of m), B = x8 [M][K]  (TN)
+    // Both from one launch when both are wanted (independent products).
+    const fp8lin::GemmLaunch gdx = gemm_of(g8, w8, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx);
+    const fp8lin::GemmLaunch gdw = gemm_of(g8, x8, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw);
+    if (dx && dw) {
+        if ((st = do_gemm_pair(gdx, gdw, stream))) return st;
+    } else if (dx) {
+        if ((st = do_gemm_launch(gdx, stream))) return st;
+    } else if (dw) {
+        if ((st = do_gemm_launch(gdw, stream))) return st;
     }
     if (!dynamic) ring_g->idx = (ring_g->idx + 1) % ring_g->len;
     return FP8_OK;

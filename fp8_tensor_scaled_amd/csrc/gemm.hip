@@ -111,4 +111,13 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream) {
     return launch_generic(g, stream);
 }
 
+hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream) {
+    if (!gemm_skinny_supported(g0) && !gemm_skinny_supported(g1) &&
+        gemm_tiled_pair_supported(g0, g1))
+        return launch_gemm_tiled_pair(g0, g1, stream);
+    hipError_t e = launch_gemm(g0, stream);
+    if (e != hipSuccess) return e;
+    return launch_gemm(g1, stream);
+}
+
 }  // namespace fp8lin

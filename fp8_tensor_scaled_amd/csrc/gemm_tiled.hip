@@ -342,8 +342,17 @@ __device__ __forceinline__ v16f mfma32x32x64(const v8i& x, const v8i& y, v16f ac
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, FMT, FMT, 0, 0, 0, 0);
 }
 
+// LDS bytes of a configuration's ring (also its epilogue staging area).
+template <int BM, int BN, int BK, int STAGES>
+constexpr int tiled_lds_bytes() {
+    return STAGES * (BM + BN) * BK;
+}
+
+// One output tile: workgroup `bid` of a grid of G workgroups over problem p,
+// with `smem` the workgroup's LDS ring of tiled_lds_bytes<...>() bytes.
 template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p) {
+__device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const int G,
+                                          uint8_t* smem) {
     constexpr int NW = WM * WN;
     constexpr int kSubs = BK / kSub;  // MFMA substeps per stage
     static_assert((STAGES * kSubs) % 2 == 0, "fragment slots alternate with the unrolled steps");
@@ -357,7 +366,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     using OB = Operand<BMN, BN, NW, BK>;
     constexpr int kLoads = OA::kPerWave + OB::kPerWave;  // DMA loads per wave per stage
     static_assert(STAGES >= 2 && kLoads * (STAGES - 1) < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -365,8 +373,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     const int wm = wave / WN, wn = wave % WN;
 
     // Tile of this workgroup (32-bit, uniform: tile counts fit easily).
-    int bid = blockIdx.x;
-    const int G = gridDim.x;
     if (p.xcd_remap) bid = (bid & 7) * (G >> 3) + (bid >> 3);
     const int bz = bid / p.tiles_per_batch;
     const int t = bid - bz * p.tiles_per_batch;
@@ -664,6 +670,28 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
     }
 }
 
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<BM, BN, BK, STAGES>()];
+    gemm_tile<FMT, AMN, BMN, BM, BN, WM, WN, BK, STAGES>(p, blockIdx.x, gridDim.x, smem);
+}
+
+// Two independent problems in one launch (the linear backward's dX, NN, and
+// dW, TN, at 256x256 tiles): workgroups [0, n0) take problem 0's tiles and
+// the rest problem 1's.  One workgroup fits a CU, so problem 1's tiles start
+// on CUs as problem 0's finish: their prologue loads overlap problem 0's
+// output stores, and there is one launch boundary instead of two.
+template <int FMT>
+__global__ __launch_bounds__(512, 1) void gemm_tiled_pair_kernel(TiledParams p0, TiledParams p1,
+                                                                  int n0) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<256, 256, 64, 4>()];
+    const int b = blockIdx.x;
+    if (b < n0)
+        gemm_tile<FMT, false, true, 256, 256, 2, 4, 64, 4>(p0, b, n0, smem);
+    else
+        gemm_tile<FMT, true, true, 256, 256, 2, 4, 64, 4>(p1, b - n0, (int)gridDim.x - n0, smem);
+}
+
 // ---------------------------------------------------------------------------
 // Host side: support test, tile choice, launch.
 // ---------------------------------------------------------------------------
@@ -686,8 +714,8 @@ bool gemm_tiled_supported(const GemmLaunch& g) {
     return true;
 }
 
-template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int ST>
-static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
+template <int BM, int BN>
+static TiledParams tiled_params(const GemmLaunch& g) {
     TiledParams p{};
     p.a = g.a;
     p.b = g.b;
@@ -711,6 +739,13 @@ static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     p.vec_out16 = ((reinterpret_cast<uintptr_t>(g.out) & 15) == 0) && (g.n % 8 == 0) && bias8;
     const int64_t total = p.tiles_per_batch * g.batch;
     p.xcd_remap = (total % 8) == 0;
+    return p;
+}
+
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int ST>
+static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
+    const TiledParams p = tiled_params<BM, BN>(g);
+    const int64_t total = (int64_t)p.tiles_per_batch * g.batch;
     hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST>),
                        dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
     return hipGetLastError();
@@ -745,6 +780,35 @@ static hipError_t launch_fmt(const GemmLaunch& g, hipStream_t stream) {
 
 hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream) {
     return g.fmt == 0 ? launch_fmt<0>(g, stream) : launch_fmt<1>(g, stream);
+}
+
+static int64_t tiles256(const GemmLaunch& g) {
+    return ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
+}
+
+bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1) {
+    if (!gemm_tiled_supported(g0) || !gemm_tiled_supported(g1) || g0.fmt != g1.fmt) return false;
+    // problem 0 NN (A k-contiguous, B n-contiguous), problem 1 TN (both
+    // m/n-contiguous), each big enough for the 256x256 configuration
+    if (g0.trans_a != 0 || g0.trans_b != 0 || g1.trans_a != 1 || g1.trans_b != 0) return false;
+    const int64_t n0 = tiles256(g0), n1 = tiles256(g1);
+    return n0 >= 256 && n1 >= 256 && (double)n0 + (double)n1 < 2147483647.0;
+}
+
+hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
+                                  hipStream_t stream) {
+    TiledParams p0 = tiled_params<256, 256>(g0);
+    TiledParams p1 = tiled_params<256, 256>(g1);
+    const int n0 = (int)tiles256(g0), n1 = (int)tiles256(g1);
+    // problem 1's local ids line up with the XCDs only if n0 is a multiple of 8
+    p1.xcd_remap = p1.xcd_remap && (n0 % 8) == 0;
+    if (g0.fmt == 0)
+        hipLaunchKernelGGL(gemm_tiled_pair_kernel<0>, dim3((unsigned)(n0 + n1)), dim3(512), 0,
+                           stream, p0, p1, n0);
+    else
+        hipLaunchKernelGGL(gemm_tiled_pair_kernel<1>, dim3((unsigned)(n0 + n1)), dim3(512), 0,
+                           stream, p0, p1, n0);
+    return hipGetLastError();
 }
 
 }  // namespace fp8lin

@@ -12,4 +12,9 @@ namespace fp8lin {
 bool gemm_tiled_supported(const GemmLaunch& g);
 hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream);
 
+// Two independent problems in one launch: problem 0 NN and problem 1 TN,
+// same format, both large enough for 256x256 tiles.
+bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1);
+hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream);
+
 }  // namespace fp8lin

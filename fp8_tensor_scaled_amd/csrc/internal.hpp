@@ -52,6 +52,10 @@ struct GemmLaunch {
     uint16_t* out = nullptr;
 };
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
+// Two independent GEMMs: one launch when both take the tiled kernels' paired
+// form (the linear backward's NN dX and TN dW), else launch_gemm twice in
+// order.  Results are bit-identical to the two separate launches.
+hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream);
 
 // Column sum (bias gradient).
 size_t colsum_workspace(int64_t m, int64_t n);

@@ -198,6 +198,40 @@ fp8_status_t fp8_mm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t t
                     uint16_t* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_mm_pair -- two independent fp8_mm products from one call: the
+ * linear backward's dX = g . W (NN) and dW = g^T . X (TN), which use the
+ * same g and nothing of each other (compare view: astrai/extension/fp8.py
+ * _LinearFp8.backward).
+ *
+ * p0, p1: host pointers to the two problems' fp8_mm arguments (the struct
+ *     below; fields as in fp8_mm).  When p0 is NN (trans_a 0, trans_b 0)
+ *     and p1 is TN (trans_a 1, trans_b 0) in the same format and both are
+ *     large enough for the 256 x 256 tiles (at least 256 tiles each), one
+ *     kernel runs both, problem 0's tiles first; otherwise the two products
+ *     are enqueued one after the other.  Either way each output is
+ *     bit-identical to fp8_mm with the same arguments.
+ * The problems must be independent: neither output may overlap the other
+ * problem's operands (checked: the two outputs must not overlap).
+ * Validation is fp8_mm's for each problem; on FP8_EINVAL nothing is
+ * enqueued.
+ * ------------------------------------------------------------------- */
+typedef struct fp8_mm_args {
+    const uint8_t* a;
+    const uint8_t* b;
+    fp8_fmt_t fmt;
+    int32_t trans_a;
+    int32_t trans_b;
+    int32_t reserved;
+    int64_t m, n, k, lda, ldb, batch, stride_a, stride_b;
+    const float* scale_a;
+    const float* scale_b;
+    const uint16_t* bias; /* NULL: no bias */
+    uint16_t* out;
+} fp8_mm_args_t;
+
+fp8_status_t fp8_mm_pair(const fp8_mm_args_t* p0, const fp8_mm_args_t* p1, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_colsum -- bias gradient db[j] = bf16( sum_i g[i][j] ), g bf16 [m][n].
  * (compare view: astrai/extension/fp8.py _LinearFp8.backward, grad_b)
  * fp32 accumulation in a fixed order (deterministic).  workspace: device
@@ -274,7 +308,8 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  * dynamic != 0: sg, sx, sw are measured now from g, x, w in `fmt`;
  *     scales_fwd and ring_g are ignored.
  * dx, dw, db: each NULL to skip that gradient (x8b is only made for dw,
- *     w8b only for dx).
+ *     w8b only for dx).  With both dx and dw, the two products run as
+ *     fp8_mm_pair (one launch when the shapes allow).
  * workspace: fp8_linear_bwd_workspace(M, N, K) bytes, same zero-once
  *     contract as the forward's.
  * scales_out: nullable fp32 [3] receives [sg, sx, sw].

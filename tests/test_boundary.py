@@ -28,7 +28,7 @@ def f():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_scale_ring_finalize", "fp8_mm", "fp8_linear_fwd",
+    for n in ("fp8_quantize", "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_pair", "fp8_linear_fwd",
               "fp8_linear_bwd", "fp8_colsum", "fp8_last_error"):
         assert n in names
 
@@ -157,6 +157,50 @@ def mm(lib, **kw):
 def test_mm_validation(f, kw, needle):
     st = mm(f._lib, **kw)
     assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
+def mm_args(f, **kw):
+    a = dict(a=FAKE, b=FAKE, fmt=0, trans_a=0, trans_b=0, reserved=0, m=4096, n=4096, k=4096,
+             lda=4096, ldb=4096, batch=1, stride_a=0, stride_b=0, scale_a=FAKE, scale_b=FAKE,
+             bias=None, out=FAKE)
+    a.update(kw)
+    return f._MmArgs(**a)
+
+
+def test_mm_args_layout(f):
+    """The binding's struct matches fp8_mm_args_t: pointers, three int32
+    flags and a reserved word, eight int64, four pointers (128 bytes)."""
+    A = f._MmArgs
+    assert ctypes.sizeof(A) == 128
+    assert (A.fmt.offset, A.trans_a.offset, A.m.offset, A.stride_b.offset,
+            A.scale_a.offset, A.out.offset) == (16, 20, 32, 88, 96, 120)
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct fp8_mm_args {"):text.index("} fp8_mm_args_t;")]
+    fields = re.findall(r"\b(\w+)(?:,|;)", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [n for n, _ in A._fields_]
+
+
+@pytest.mark.parametrize("which,kw,needle", [
+    (0, dict(fmt=5), "(problem 0): unsupported fp8 format"),
+    (1, dict(trans_a=2), "(problem 1): trans"),
+    (0, dict(lda=100), "(problem 0): lda"),
+    (1, dict(m=0), "(problem 1): m, n, k"),
+    (1, dict(out=None), "(problem 1): NULL"),
+])
+def test_mm_pair_validation(f, which, kw, needle):
+    p = [mm_args(f, out=FAKE), mm_args(f, trans_a=1, out=P(FAKE.value + (1 << 30)))]
+    p[which] = mm_args(f, **{**dict(out=p[which].out, trans_a=p[which].trans_a), **kw})
+    st = f._lib.fp8_mm_pair(ctypes.byref(p[0]), ctypes.byref(p[1]), None)
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
+def test_mm_pair_rejects_overlapping_outputs_and_null(f):
+    p0 = mm_args(f)
+    p1 = mm_args(f, trans_a=1, out=P(FAKE.value + 4096 * 4096))  # inside p0's output
+    st = f._lib.fp8_mm_pair(ctypes.byref(p0), ctypes.byref(p1), None)
+    assert st == 1 and "overlap" in _err(f._lib)
+    st = f._lib.fp8_mm_pair(None, ctypes.byref(p1), None)
+    assert st == 1 and "NULL" in _err(f._lib)
 
 
 def test_valid_call_without_gpu_reports_hip_error(f):

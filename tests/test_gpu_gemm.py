@@ -249,3 +249,37 @@ def test_mfma_group_precision(lib, orc):
     assert y0 == 120 * 2.0 ** -4, y0
     absdot = orc.gemm_absdot(a8, b8, E4M3, False, True, M, N, K, 1.0, 1.0)
     assert abs(y0 - 126 * 2.0 ** -4) <= 2.0 ** -10 * absdot[0, 0]
+
+
+# ---------------------------------------------------------------------------
+# Two independent products from one call (the backward's dX and dW)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (4144, 4176, 272), (256, 512, 320)])
+def test_mm_pair_matches_two_calls(lib, orc, fmt, M, N, K):
+    """fp8_mm_pair of an NN and a TN product gives the bits of two fp8_mm
+    calls: through the paired kernel when both have at least 256 tiles of
+    256 x 256 (the first two shapes, the second with ragged tails), as two
+    launches otherwise; and it matches the oracle at sampled coordinates."""
+    # problem 0, NN: A [M][K], B [K][N]; problem 1, TN: A stored [K][M], B [K][N]
+    a0, sa0 = prequant(orc, wl.normal_bf16((M, K), 1.0, 700 + K), fmt)
+    b0, sb0 = prequant(orc, wl.normal_bf16((K, N), 0.02, 701 + K), fmt)
+    a1, sa1 = prequant(orc, wl.normal_bf16((K, M), 1.0, 702 + K), fmt)
+    b1, sb1 = prequant(orc, wl.normal_bf16((K, N), 1.0, 703 + K), fmt)
+    d = [to_dev_u8(v.ravel()) for v in (a0, b0, a1, b1)]
+    s = [dev_f32(v) for v in (sa0, sb0, sa1, sb1)]
+    outs = [torch.full((M * N,), 0x7FC1, dtype=torch.int16, device="cuda") for _ in range(4)]
+    p0 = (d[0], d[1], fmt, 0, 0, M, N, K, K, N, 1, 0, 0, s[0], s[1], None)
+    p1 = (d[2], d[3], fmt, 1, 0, M, N, K, M, N, 1, 0, 0, s[2], s[3], None)
+    lib.fp8_mm_pair(p0 + (outs[0],), p1 + (outs[1],))
+    lib.fp8_mm(*(p0 + (outs[2],)))
+    lib.fp8_mm(*(p1 + (outs[3],)))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
+    smp = sample_coords(1, M, N, 1500, K)
+    for o, (a, b, ta, sa, sb) in ((outs[0], (a0, b0, False, sa0, sb0)),
+                                  (outs[1], (a1, b1, True, sa1, sb1))):
+        ref, absdot = orc.gemm_sampled(a, b, fmt, ta, False, M, N, K, sa, sb, None, smp)
+        got = from_dev_bf16(o).reshape(1, M, N)
+        check_gemm(got[smp], ref, absdot, K, f"pair {'TN' if ta else 'NN'} {M}x{N}x{K}")

@@ -178,6 +178,43 @@ float orc_amax(const uint16_t* x, int64_t n)
 }
 
 /* ------------------------------------------------------------------------
+ * Other input types.  [CMP] csrc/kernels/fp8/quantize.cuh, quant_in_traits
+ * (bf16, fp16 and fp32 inputs, each widened to fp32 before the max and the
+ * multiply) and ops/fp8.py quantize ("bf16/fp16/fp32"); [LOG1] "templated
+ * on input type".  IEEE binary16 (the spec, not the pages): sign, 5-bit
+ * exponent with bias 15, 10-bit fraction; exponent 0 is subnormal with
+ * spacing 2^-24; exponent 31 is infinity (fraction 0) or NaN.  Every
+ * binary16 value is exact in fp32.
+ * in_type: 0 bf16 bits, 1 fp16 bits, 2 fp32.
+ * ---------------------------------------------------------------------- */
+float orc_f16_to_f32(uint16_t h)
+{
+    const int sign = h >> 15, e = (h >> 10) & 0x1F, frac = h & 0x3FF;
+    float v;
+    if (e == 0) v = ldexpf((float)frac, -24);
+    else if (e == 31) v = frac ? NAN : INFINITY;
+    else v = ldexpf((float)(1024 + frac), e - 25);
+    return sign ? -v : v;
+}
+
+static float in_value(const void* x, int64_t i, int in_type)
+{
+    if (in_type == 0) return orc_bf16_to_f32(((const uint16_t*)x)[i]);
+    if (in_type == 1) return orc_f16_to_f32(((const uint16_t*)x)[i]);
+    return ((const float*)x)[i];
+}
+
+float orc_amax_in(const void* x, int64_t n, int in_type)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        const float a = fabsf(in_value(x, i, in_type));
+        if (a > m) m = a; /* NaN skipped */
+    }
+    return m;
+}
+
+/* ------------------------------------------------------------------------
  * Scale from an amax peak.  [CMP] astrai/extension/fp8.py,
  * FP8Recipe.scale_from_history, and quantize.cuh publish_amax: the scale is
  * the quantization step (peak / FP8_MAX) / 2^margin, clamped below at
@@ -209,6 +246,14 @@ void orc_quantize(const uint16_t* x, int64_t n, int fmt, float s, uint8_t* out)
         const float prod = orc_bf16_to_f32(x[i]) * m;
         out[i] = orc_encode(prod, fmt);
     }
+}
+
+/* The same quantize for any input type (widened to fp32 first). */
+void orc_quantize_in(const void* x, int64_t n, int in_type, int fmt, float s, uint8_t* out)
+{
+    const float m = orc_multiplier(s);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_encode(in_value(x, i, in_type) * m, fmt);
 }
 
 /* ------------------------------------------------------------------------

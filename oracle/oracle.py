@@ -85,6 +85,11 @@ def _load():
     lib.orc_multiplier.argtypes = [F]
     lib.orc_multiplier.restype = F
     lib.orc_quantize.argtypes = [P, I64, I, F, P]
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_f32.restype = F
+    lib.orc_amax_in.argtypes = [P, I64, I]
+    lib.orc_amax_in.restype = F
+    lib.orc_quantize_in.argtypes = [P, I64, I, I, F, P]
     lib.orc_gemm.argtypes = [P, P, I, I, I, I64, I64, I64, I64, I64, I64, I64, I64,
                              F, F, P, P]
     lib.orc_gemm_sampled.argtypes = [P, P, I, I, I, I64, I64, I64, I64, I64, F, F, P,
@@ -148,6 +153,36 @@ def amax(x: np.ndarray) -> np.float32:
     """max |x_i| over the raw bf16 values ([CMP] quantize.cuh)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     return np.float32(_load().orc_amax(_ptr(x), x.size))
+
+
+IN_BF16, IN_F16, IN_F32 = 0, 1, 2
+
+
+def _in_array(x: np.ndarray, in_type: int) -> np.ndarray:
+    dt = np.float32 if in_type == IN_F32 else np.uint16
+    return np.ascontiguousarray(x, dtype=dt)
+
+
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bits -> fp32, from the format's definition."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    lib = _load()
+    return np.array([lib.orc_f16_to_f32(int(v)) for v in h.ravel()], np.float32).reshape(h.shape)
+
+
+def amax_in(x: np.ndarray, in_type: int) -> np.float32:
+    """max |x_i| over raw inputs of type in_type (0 bf16 bits, 1 fp16 bits,
+    2 fp32) ([CMP] quantize.cuh quant_in_traits)."""
+    x = _in_array(x, in_type)
+    return np.float32(_load().orc_amax_in(_ptr(x), x.size, in_type))
+
+
+def quantize_in(x: np.ndarray, in_type: int, fmt: int, s) -> np.ndarray:
+    """q_i = encode(fp32(fp32(x_i) * fp32(1/s))) for any input type."""
+    x = _in_array(x, in_type)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_quantize_in(_ptr(x), x.size, in_type, fmt, float(np.float32(s)), _ptr(out))
+    return out
 
 
 def scale_from_peak(peak, fmt: int, margin: int = 0) -> np.float32:

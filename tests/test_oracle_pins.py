@@ -219,6 +219,56 @@ def test_quantize_vs_torch_composition(orc, fmt):
         assert orc.multiplier(s) == m.item()
 
 
+def test_f16_decode_all_patterns_vs_torch(orc):
+    """fp16 decode written from the binary16 definition equals torch's CPU
+    float16 -> float32 conversion on all 65536 patterns (NaN stays NaN)."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.f16_to_f32(h)
+    ref = torch.from_numpy(h.view(np.int16)).view(torch.float16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.isnan(got[nan]).all()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_in_vs_torch_composition(orc, fmt):
+    """fp16 and fp32 inputs: encode(fp32(fp32(x) * fp32(1/s))) by torch's
+    widening, reciprocal, multiply, clamp and cast; amax by torch's max of
+    |x| (NaN-free data)."""
+    rng = np.random.default_rng(21 + fmt)
+    x32 = (rng.standard_normal(5000) * 3.0).astype(np.float32)
+    x32[:4] = [0.0, -0.0, 1e-30, -6.5e4]
+    x16 = x32.astype(np.float16)
+    for s in (np.float32(2.5 / FMAX[fmt]), np.float32(0.37), np.float32(1e-12)):
+        m = torch.reciprocal(torch.tensor([s], dtype=torch.float32))
+        for in_type, x, xt in ((2, x32, torch.from_numpy(x32)),
+                               (1, x16.view(np.uint16), torch.from_numpy(x16).float())):
+            ref = torch_encode((xt * m).numpy(), fmt)
+            assert np.array_equal(orc.quantize_in(x, in_type, fmt, s), ref), (in_type, s)
+            assert orc.amax_in(x, in_type) == np.float32(xt.abs().max().item())
+
+
+def test_quantize_in_reduces_to_the_bf16_path(orc):
+    """The same values given as bf16 bits, fp16 bits (values that fit both)
+    or fp32 quantize to the same codes and have the same amax; NaN is
+    skipped by every amax."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = orc.f16_to_f32(h)
+    fits = np.isfinite(f) & ((h & 0x7) == 0)        # 7 fraction bits or fewer
+    v = f[fits]
+    b = (v.view(np.uint32) >> 16).astype(np.uint16)   # exact bf16 bits of v
+    assert np.array_equal(wl.bf16_bits_to_f32(b), v)
+    for fmt, s in ((E4M3, np.float32(0.01)), (E5M2, np.float32(3.0))):
+        ref = orc.quantize(b, fmt, s)
+        assert np.array_equal(orc.quantize_in(b, 0, fmt, s), ref)
+        assert np.array_equal(orc.quantize_in(h[fits], 1, fmt, s), ref)
+        assert np.array_equal(orc.quantize_in(v, 2, fmt, s), ref)
+    assert orc.amax_in(h[fits], 1) == orc.amax(b) == orc.amax_in(v, 2)
+    nan32 = np.array([np.nan, 2.0, -3.0], np.float32)
+    assert orc.amax_in(nan32, 2) == 3.0
+    assert orc.amax_in(np.array([0x7E00, 0x4000, 0xC200], np.uint16), 1) == 3.0
+
+
 def test_quantize_multiplies_by_reciprocal(orc):
     """x * fp32(1/s) and x / s can round to different codes; the kernel on
     the pages multiplies by the reciprocal (reading of the scale

@@ -379,6 +379,30 @@ def components(f, torch):
     res["quantize_8192x8192"] = dict(us=round(ms * 1e3, 2),
                                      gbs=round(3 * n / (ms * 1e-3) / 1e9, 1),
                                      hbm_frac=round(3 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+    del xs
+    # the same with fp16 and fp32 inputs (fp8_quantize_ex): 3 and 5 bytes per
+    # element; 6 and 4 buffer sets (1.2 and 1.3 GB)
+    for name, dt, rot, bpe in (("quantize_f16_8192x8192", torch.float16, 6, 3),
+                               ("quantize_f32_8192x8192", torch.float32, 4, 5)):
+        xs = [torch.randn(n, device=dev).to(dt) for _ in range(rot)]
+        for i in range(rot):
+            f.fp8_quantize_ex(xs[i], E4M3, ring=rings[i])
+        ms = time_graph(torch, lambda i: f.fp8_quantize_ex(xs[i % rot], E4M3,
+                                                            scale=rings[i % rot].scale,
+                                                            out=qs[i % rot], ring=rings[i % rot]),
+                        4 * rot)
+        res[name] = dict(us=round(ms * 1e3, 2), gbs=round(bpe * n / (ms * 1e-3) / 1e9, 1),
+                         hbm_frac=round(bpe * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+        del xs
+    # reference for the quantize's practical ceiling: torch's copy of 1 GiB
+    # (read + write, 2 GiB moved)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = time_kernel(torch, lambda i: dst.copy_(src), 10)
+    res["hbm_copy_1GiB_reference"] = dict(us=round(ms * 1e3, 2),
+                                          gbs=round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
+                                          hbm_frac=round(2 * (1 << 30) / (ms * 1e-3) / 1e9
+                                                         / PEAK_HBM_GBS, 3))
     return res
 
 

@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = [
-    "E4M3", "E5M2", "FMT_MAX", "Ring", "library_path", "fp8_quantize", "fp8_quantize2",
+    "E4M3", "E5M2", "FMT_MAX", "IN_BF16", "IN_F16", "IN_F32", "Ring", "library_path",
+    "fp8_quantize", "fp8_quantize_ex", "fp8_quantize2",
     "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_pair", "fp8_colsum", "fp8_colsum_workspace",
     "fp8_quantize_colsum",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
@@ -31,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 
 EXPORTED_SYMBOLS = (
-    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize2",
+    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize_ex", "fp8_quantize2",
     "fp8_scale_ring_finalize",
     "fp8_mm", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum", "fp8_quantize_colsum",
     "fp8_linear_fwd_workspace",
@@ -72,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "fp8_ring_state_floats": (I64, [I32]),
         "fp8_format_max": (F, [I32]),
         "fp8_quantize": (I32, [P, I64, I32, P, P, R, I32, P, P]),
+        "fp8_quantize_ex": (I32, [P, I32, I64, I32, P, P, R, I32, P, P]),
         "fp8_quantize2": (I32, [P, I64, I32, P, P, I32, P, R, I32, P, P]),
         "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
         "fp8_mm": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P,
@@ -199,6 +201,26 @@ def fp8_quantize(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
     st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
                            margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize")
+
+
+IN_BF16, IN_F16, IN_F32 = 0, 1, 2
+_IN_OF_DTYPE = {torch.bfloat16: IN_BF16, torch.float16: IN_F16, torch.float32: IN_F32}
+
+
+def fp8_quantize_ex(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, ring: Ring | None = None, margin: int = 0,
+                    scale_used: torch.Tensor | None = None, in_type: int | None = None,
+                    stream=None) -> None:
+    """bf16, fp16 or fp32 x -> fp8 codes; ``in_type`` defaults to x's dtype
+    (bfloat16 / float16 / float32; give it for int16 bit views); see
+    fp8lin.h."""
+    if in_type is None:
+        if x.dtype not in _IN_OF_DTYPE:
+            raise ValueError(f"fp8_quantize_ex: no input type for dtype {x.dtype}")
+        in_type = _IN_OF_DTYPE[x.dtype]
+    st = _lib.fp8_quantize_ex(_ptr(x), in_type, x.numel(), fmt, _ptr(scale), _ptr(out),
+                              _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
+    _check(st, "fp8_quantize_ex")
 
 
 def fp8_quantize2(x: torch.Tensor, fmt: int, scale: torch.Tensor, out: torch.Tensor, fmt2: int,

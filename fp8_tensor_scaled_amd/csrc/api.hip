@@ -99,12 +99,14 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
     return l;
 }
 
-fp8_status_t do_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
                          uint8_t* out, float* ring_state, int32_t len, int32_t idx,
                          int32_t margin, float* scale_used, hipStream_t stream,
-                         uint8_t* out2 = nullptr, int fmt2 = -1) {
+                         uint8_t* out2 = nullptr, int fmt2 = -1,
+                         int in_type = fp8lin::kInBf16) {
     fp8lin::QuantLaunch q;
     q.x = x;
+    q.in_type = in_type;
     q.numel = numel;
     q.fmt = fmt;
     q.scale = scale;
@@ -232,28 +234,46 @@ const char* fp8_last_error(void) { return g_err; }
 
 const char* fp8_version(void) { return "fp8lin 0.1 (gfx950)"; }
 
-fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
-                          uint8_t* out, const fp8_ring_t* ring, int32_t margin,
-                          float* scale_used, hipStream_t stream) {
+static fp8_status_t quantize_entry(const char* who, const void* x, int in_type, int64_t numel,
+                                   fp8_fmt_t fmt, const float* scale, uint8_t* out,
+                                   const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                                   hipStream_t stream) {
     g_err[0] = 0;
-    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_quantize: unsupported fp8 format %d", fmt);
-    if (numel < 0) return fail(FP8_EINVAL, "fp8_quantize: numel %lld < 0", (long long)numel);
-    if (numel > 0 && !x) return fail(FP8_EINVAL, "fp8_quantize: x is NULL");
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "%s: unsupported fp8 format %d", who, fmt);
+    if (in_type != FP8_IN_BF16 && in_type != FP8_IN_F16 && in_type != FP8_IN_F32)
+        return fail(FP8_EINVAL, "%s: unsupported input type %d", who, in_type);
+    if (numel < 0) return fail(FP8_EINVAL, "%s: numel %lld < 0", who, (long long)numel);
+    if (numel > 0 && !x) return fail(FP8_EINVAL, "%s: x is NULL", who);
     if (numel == 0 && !ring) return FP8_OK;  // nothing to convert, nothing to fold
-    if (!out && !ring) return fail(FP8_EINVAL, "fp8_quantize: neither out nor ring given");
-    if (out && !scale) return fail(FP8_EINVAL, "fp8_quantize: scale is NULL");
+    if (!out && !ring) return fail(FP8_EINVAL, "%s: neither out nor ring given", who);
+    if (out && !scale) return fail(FP8_EINVAL, "%s: scale is NULL", who);
     if (ring) {
-        fp8_status_t st = check_ring(ring, "fp8_quantize");
+        fp8_status_t st = check_ring(ring, who);
         if (st) return st;
     }
     if (margin < 0 || margin > 64)
-        return fail(FP8_EINVAL, "fp8_quantize: margin %d outside [0, 64]", margin);
+        return fail(FP8_EINVAL, "%s: margin %d outside [0, 64]", who, margin);
     if (!out && scale_used)
-        return fail(FP8_EINVAL, "fp8_quantize: scale_used needs a quantizing call");
+        return fail(FP8_EINVAL, "%s: scale_used needs a quantizing call", who);
     fp8_status_t st = check_device();
     if (st) return st;
     return do_quantize(x, numel, fmt, out ? scale : nullptr, out, ring ? ring->state : nullptr,
-                       ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, stream);
+                       ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, stream,
+                       nullptr, -1, in_type);
+}
+
+fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+                          uint8_t* out, const fp8_ring_t* ring, int32_t margin,
+                          float* scale_used, hipStream_t stream) {
+    return quantize_entry("fp8_quantize", x, FP8_IN_BF16, numel, fmt, scale, out, ring, margin,
+                          scale_used, stream);
+}
+
+fp8_status_t fp8_quantize_ex(const void* x, fp8_in_t in_type, int64_t numel, fp8_fmt_t fmt,
+                             const float* scale, uint8_t* out, const fp8_ring_t* ring,
+                             int32_t margin, float* scale_used, hipStream_t stream) {
+    return quantize_entry("fp8_quantize_ex", x, in_type, numel, fmt, scale, out, ring, margin,
+                          scale_used, stream);
 }
 
 fp8_status_t fp8_quantize2(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,

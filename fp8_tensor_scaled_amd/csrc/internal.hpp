@@ -19,8 +19,12 @@ inline int64_t ring_state_words(int32_t len) {
 }
 
 // Everything a quantize launch needs (plain values, no ownership).
+// Quantize input element types (each widens exactly to fp32).
+enum InType : int { kInBf16 = 0, kInF16 = 1, kInF32 = 2 };
+
 struct QuantLaunch {
-    const uint16_t* x = nullptr;
+    const void* x = nullptr;  // numel elements of type in_type
+    int in_type = kInBf16;
     int64_t numel = 0;
     int fmt = 0;
     const float* scale = nullptr;  // step s (device); m = 1/s

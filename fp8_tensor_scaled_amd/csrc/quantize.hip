@@ -51,7 +51,7 @@ constexpr int kVecElems = 16;  // bf16 elements per lane per unrolled slot
 constexpr int kUnroll = 4;     // slots in flight per lane
 
 struct QuantParams {
-    const uint16_t* x;
+    const void* x;        // elements of the kernel's input type
     int64_t numel;
     const float* scale;
     uint8_t* out;
@@ -148,18 +148,71 @@ __device__ __forceinline__ void finish_fold(const QuantParams& p, uint32_t ticke
     if (__shfl(last, 0, kWave)) fold_ring(p, s_read, win);
 }
 
-__device__ __forceinline__ void unpack16(const uint4& r0, const uint4& r1, float f[16]) {
-    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        f[2 * j] = bf16_lo(w[j]);
-        f[2 * j + 1] = bf16_hi(w[j]);
+// Input element types.  A 16-element chunk is kLoads 16-byte loads; unpack
+// widens it to fp32 exactly ([CMP] quantize.cuh quant_in_traits: bf16,
+// fp16 and fp32 inputs), `one` reads a single element.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int IN>
+struct In;
+template <>
+struct In<kInBf16> {
+    static constexpr int kLoads = 2;
+    __device__ static float one(const void* x, int64_t e) {
+        return bf16_to_f32(static_cast<const uint16_t*>(x)[e]);
     }
-}
+    __device__ static void unpack(const uint4* r, float f[16]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f[8 * i + 2 * j] = bf16_lo(w[j]);
+                f[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+            }
+        }
+    }
+};
+template <>
+struct In<kInF16> {
+    static constexpr int kLoads = 2;
+    __device__ static float one(const void* x, int64_t e) {
+        return (float)static_cast<const _Float16*>(x)[e];
+    }
+    __device__ static void unpack(const uint4* r, float f[16]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x2_t v = __builtin_convertvector(__builtin_bit_cast(f16x2_t, w[j]),
+                                                          f32x2_t);
+                f[8 * i + 2 * j] = v[0];
+                f[8 * i + 2 * j + 1] = v[1];
+            }
+        }
+    }
+};
+template <>
+struct In<kInF32> {
+    static constexpr int kLoads = 4;
+    __device__ static float one(const void* x, int64_t e) {
+        return static_cast<const float*>(x)[e];
+    }
+    __device__ static void unpack(const uint4* r, float f[16]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[4 * i] = __uint_as_float(r[i].x);
+            f[4 * i + 1] = __uint_as_float(r[i].y);
+            f[4 * i + 2] = __uint_as_float(r[i].z);
+            f[4 * i + 3] = __uint_as_float(r[i].w);
+        }
+    }
+};
 
-__device__ __forceinline__ float absmax16(const uint4& r0, const uint4& r1, float amax) {
+template <int IN>
+__device__ __forceinline__ float absmax16(const uint4* r, float amax) {
     float f[16];
-    unpack16(r0, r1, f);
+    In<IN>::unpack(r, f);
 #pragma unroll
     for (int j = 0; j < 16; j += 2) amax = fmaxf(amax, fmaxf(fabsf(f[j]), fabsf(f[j + 1])));
     return amax;
@@ -167,11 +220,10 @@ __device__ __forceinline__ float absmax16(const uint4& r0, const uint4& r1, floa
 
 // 16 codes of x * m into dst; FMT2 >= 0: the same scaled values in the
 // second format into dst2 (one read of x feeds both encodings).
-template <int FMT, int FMT2>
-__device__ __forceinline__ void encode16(const uint4& r0, const uint4& r1, float m, uint4* dst,
-                                         uint4* dst2) {
+template <int IN, int FMT, int FMT2>
+__device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, uint4* dst2) {
     float f[16];
-    unpack16(r0, r1, f);
+    In<IN>::unpack(r, f);
 #pragma unroll
     for (int j = 0; j < 16; ++j) f[j] *= m;
     uint4 o;
@@ -197,8 +249,9 @@ __device__ __forceinline__ void encode16(const uint4& r0, const uint4& r1, float
 // and before the stores, so the fold's atomics overlap the store drain
 // instead of following it.  Scalar path (unaligned bases): grid-stride
 // elements, then the publish.
-template <int FMT, int FMT2, bool MEASURE_ONLY>
+template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) {
+    constexpr int kL = In<IN>::kLoads;
     float m = 0.0f, s_read = 0.0f;
     if constexpr (!MEASURE_ONLY) {
         s_read = *p.scale;
@@ -218,7 +271,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         if (blockIdx.x == 0) {
             const int64_t e = nvec * kVecElems + t;
             if (e < p.numel) {
-                const float f = bf16_to_f32(p.x[e]);
+                const float f = In<IN>::one(p.x, e);
                 amax = fmaxf(amax, fabsf(f));
                 if constexpr (!MEASURE_ONLY) {
                     p.out[e] = cvt1<FMT>(f * m);
@@ -233,7 +286,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
         const int64_t nr = hi > lo ? (hi - lo + kRound - 1) / kRound : 0;  // uniform
         for (int64_t rd = 0; rd < nr; ++rd) {
             const int64_t c0 = lo + rd * kRound + t;
-            uint4 r[kUnroll][2];
+            uint4 r[kUnroll][kL];
             // Loads are unconditional (a chunk past the range re-reads the
             // range's first one and is ignored), so their waits stay counted
             // one by one instead of collapsing into a wait for all of them.
@@ -241,18 +294,18 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t c = c0 + u * kQuantThreads;
                 const int64_t cl = c < hi ? c : lo;
-                r[u][0] = xv[2 * cl];
-                r[u][1] = xv[2 * cl + 1];
+#pragma unroll
+                for (int i = 0; i < kL; ++i) r[u][i] = xv[kL * cl + i];
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                if (c0 + u * kQuantThreads < hi) amax = absmax16(r[u][0], r[u][1], amax);
+                if (c0 + u * kQuantThreads < hi) amax = absmax16<IN>(r[u], amax);
             if (p.hist && rd == nr - 1) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
             if constexpr (!MEASURE_ONLY) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int64_t c = c0 + u * kQuantThreads;
-                    if (c < hi) encode16<FMT, FMT2>(r[u][0], r[u][1], m, ov + c, ov2 + c);
+                    if (c < hi) encode16<IN, FMT, FMT2>(r[u], m, ov + c, ov2 + c);
                 }
             }
         }
@@ -260,7 +313,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     } else {
         const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
         for (int64_t e = (int64_t)blockIdx.x * kQuantThreads + t; e < p.numel; e += stride) {
-            const float f = bf16_to_f32(p.x[e]);
+            const float f = In<IN>::one(p.x, e);
             amax = fmaxf(amax, fabsf(f));
             if constexpr (!MEASURE_ONLY) {
                 p.out[e] = cvt1<FMT>(f * m);
@@ -285,7 +338,34 @@ static int quant_grid(int64_t numel, int vec) {
     return (int)blocks;
 }
 
+template <int IN>
+static void launch_quantize_in(const QuantLaunch& q, const QuantParams& p, dim3 grid,
+                               hipStream_t stream) {
+    const dim3 block(kQuantThreads);
+    const bool measure = q.out == nullptr;
+    const int dual = q.out2 ? q.fmt2 : -1;
+#define FP8_Q(F, F2, M) \
+    hipLaunchKernelGGL((quantize_kernel<IN, F, F2, M>), grid, block, 0, stream, p)
+    if (measure) {
+        if (q.fmt == 0) FP8_Q(0, -1, true);
+        else FP8_Q(1, -1, true);
+    } else if (dual < 0) {
+        if (q.fmt == 0) FP8_Q(0, -1, false);
+        else FP8_Q(1, -1, false);
+    } else if constexpr (IN == kInBf16) {  // the dual-format pass takes bf16 only
+        if (q.fmt == 0) {
+            if (dual == 0) FP8_Q(0, 0, false);
+            else FP8_Q(0, 1, false);
+        } else {
+            if (dual == 0) FP8_Q(1, 0, false);
+            else FP8_Q(1, 1, false);
+        }
+    }
+#undef FP8_Q
+}
+
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
+    if (q.out2 && q.in_type != kInBf16) return hipErrorInvalidValue;
     QuantParams p{};
     p.x = q.x;
     p.numel = q.numel;
@@ -307,26 +387,10 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
                          reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;
-    const dim3 grid(quant_grid(q.numel, p.vec)), block(kQuantThreads);
-    const bool measure = q.out == nullptr;
-    const int dual = q.out2 ? q.fmt2 : -1;
-#define FP8_Q(F, F2, M) hipLaunchKernelGGL((quantize_kernel<F, F2, M>), grid, block, 0, stream, p)
-    if (measure) {
-        if (q.fmt == 0) FP8_Q(0, -1, true);
-        else FP8_Q(1, -1, true);
-    } else if (dual < 0) {
-        if (q.fmt == 0) FP8_Q(0, -1, false);
-        else FP8_Q(1, -1, false);
-    } else {
-        if (q.fmt == 0) {
-            if (dual == 0) FP8_Q(0, 0, false);
-            else FP8_Q(0, 1, false);
-        } else {
-            if (dual == 0) FP8_Q(1, 0, false);
-            else FP8_Q(1, 1, false);
-        }
-    }
-#undef FP8_Q
+    const dim3 grid(quant_grid(q.numel, p.vec));
+    if (q.in_type == kInF16) launch_quantize_in<kInF16>(q, p, grid, stream);
+    else if (q.in_type == kInF32) launch_quantize_in<kInF32>(q, p, grid, stream);
+    else launch_quantize_in<kInBf16>(q, p, grid, stream);
     return hipGetLastError();
 }
 
@@ -579,12 +643,13 @@ hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, 
 
 hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, uint16_t* db,
                                   void* ws, hipStream_t stream) {
-    const bool vec = colsum_vec(q.x, n) && q.out &&
+    const uint16_t* gx = static_cast<const uint16_t*>(q.x);
+    const bool vec = colsum_vec(gx, n) && q.out &&
                      (reinterpret_cast<uintptr_t>(q.out) & 15) == 0 && !q.out2;
     if (!vec) {
         hipError_t e = launch_quantize(q, stream);
         if (e != hipSuccess) return e;
-        return launch_colsum(q.x, m, n, db, ws, stream);
+        return launch_colsum(gx, m, n, db, ws, stream);
     }
     QCParams p{};
     p.q.x = q.x;
@@ -603,7 +668,7 @@ hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, ui
     p.q.fmax = q.fmt ? 57344.0f : 448.0f;
     p.q.pow2_margin = q.pow2_margin;
     p.q.scale_used = q.scale_used;
-    p.g = q.x;
+    p.g = gx;
     p.m = m;
     p.n = n;
     p.rows = colsum_rows(m, n);

@@ -130,6 +130,25 @@ fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt,
                           int32_t margin, float* scale_used, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_quantize_ex -- fp8_quantize for bf16, fp16 or fp32 inputs.
+ * (compare view: csrc/kernels/fp8/quantize.cuh quant_in_traits, the input
+ *  element types bf16 / fp16 / fp32 each widened to fp32 before the max and
+ *  the multiply; astrai/extension/ops/fp8.py quantize; commit log 3e57cc8,
+ *  quantize templated on the input type)
+ *
+ * x: numel elements of type in_type (device): FP8_IN_BF16 / FP8_IN_F16 as
+ *    uint16 bit patterns, FP8_IN_F32 as float.  Every other argument, the
+ *    result and the errors are those of fp8_quantize: amax = max |fp32(x)|
+ *    (NaN skipped), q = enc(fp32(fp32(x) * fp32(1/s))).  fp16 and bf16 are
+ *    exact in fp32, so the same values give the same codes in every type.
+ * ------------------------------------------------------------------- */
+typedef enum { FP8_IN_BF16 = 0, FP8_IN_F16 = 1, FP8_IN_F32 = 2 } fp8_in_t;
+
+fp8_status_t fp8_quantize_ex(const void* x, fp8_in_t in_type, int64_t numel, fp8_fmt_t fmt,
+                             const float* scale, uint8_t* out, const fp8_ring_t* ring,
+                             int32_t margin, float* scale_used, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_quantize2 -- one pass over x, two encodings of the same scaled values.
  * (compare view: astrai/extension/fp8.py _LinearFp8.backward, where under
  *  the HYBRID recipe x and w are quantized again in E5M2 with the forward's

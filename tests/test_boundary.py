@@ -96,6 +96,22 @@ def test_quantize2_validation(f, args, needle):
     assert st == 1 and needle in _err(f._lib), _err(f._lib)
 
 
+@pytest.mark.parametrize("in_type,kw,needle", [
+    (3, {}, "input type"),
+    (-1, {}, "input type"),
+    (1, dict(fmt=7), "format"),
+    (2, dict(x=None), "x is NULL"),
+    (1, dict(out=None), "neither out nor ring"),
+    (2, dict(scale=None), "scale is NULL"),
+])
+def test_quantize_ex_validation(f, in_type, kw, needle):
+    a = dict(x=FAKE, in_type=in_type, numel=10, fmt=0, scale=FAKE, out=FAKE, ring=None,
+             margin=0, used=None, stream=None)
+    a.update(kw)
+    st = f._lib.fp8_quantize_ex(*a.values())
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
 def test_quantize2_empty_without_ring_is_a_noop(f):
     assert f._lib.fp8_quantize2(None, 0, 0, None, None, 1, None, None, 0, None, None) == 0
 

@@ -290,3 +290,84 @@ def test_quantize_colsum_matches_separate_calls(lib, orc, fmt, M, N, offset):
     ref = orc.colsum(g.ravel(), M, N)
     absdot = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
     check_gemm(from_dev_bf16(db1), ref, absdot=absdot, K=M, what=f"colsum {M}x{N}")
+
+
+# ---------------------------------------------------------------------------
+# fp16 and fp32 inputs (fp8_quantize_ex)
+# ---------------------------------------------------------------------------
+
+def gpu_quantize_ex(lib, x, in_type, fmt, s, offset=0, ring=None):
+    """x: numpy uint16 bits (bf16 / fp16) or float32; ``offset`` elements of
+    padding in front misalign both buffers."""
+    n = x.size
+    if in_type == 2:
+        xd = torch.zeros(n + offset, dtype=torch.float32, device="cuda")
+        if n:
+            xd[offset:] = torch.from_numpy(np.ascontiguousarray(x, np.float32).ravel()).cuda()
+    else:
+        xd = torch.zeros(n + offset, dtype=torch.int16, device="cuda")
+        if n:
+            xd[offset:] = torch.from_numpy(
+                np.ascontiguousarray(x, np.uint16).ravel().view(np.int16)).cuda()
+    out = torch.full((n + offset,), 0xAA, dtype=torch.uint8, device="cuda")
+    used = dev_f32(-1.0)
+    lib.fp8_quantize_ex(xd[offset:], fmt, scale=dev_f32(s), out=out[offset:], ring=ring,
+                        scale_used=used, in_type=in_type)
+    torch.cuda.synchronize()
+    return from_dev_u8(out[offset:]), float(used.cpu()[0])
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_quantize_ex_all_f16_patterns(lib, orc, fmt):
+    """Every fp16 bit pattern at several multipliers, bit-exact against the
+    oracle (NaN inputs give a NaN code)."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    nan = np.isnan(orc.f16_to_f32(h))
+    for s in (np.float32(1.0), np.float32(1 / 3.0), np.float32(2.0 ** 10), np.float32(7e-5)):
+        got, used = gpu_quantize_ex(lib, h, 1, fmt, s)
+        ref = orc.quantize_in(h, 1, fmt, s)
+        assert used == s
+        assert np.array_equal(got[~nan], ref[~nan]), s
+        assert _is_nan_code(got[nan], fmt).all()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("n,offset", [(1, 0), (17, 0), (100003, 0), (4096, 1), (4099, 3)])
+def test_quantize_ex_f32_and_f16_ragged(lib, orc, fmt, n, offset):
+    """fp32 and fp16 inputs on ragged lengths and misaligned bases (scalar
+    path), including values beyond bf16 precision and the formats' ranges."""
+    rng = np.random.default_rng(n + offset)
+    x32 = (rng.standard_normal(n) * rng.choice([1e-3, 1.0, 300.0, 1e5], n)).astype(np.float32)
+    x16 = np.clip(x32, -6e4, 6e4).astype(np.float16).view(np.uint16)
+    s = np.float32(0.0173)
+    for in_type, x in ((2, x32), (1, x16)):
+        got, _ = gpu_quantize_ex(lib, x, in_type, fmt, s, offset)
+        assert np.array_equal(got, orc.quantize_in(x, in_type, fmt, s)), in_type
+
+
+def test_quantize_ex_ring_fold_and_same_values(lib, orc):
+    """The fold with fp16 / fp32 inputs records max |x| exactly, and the same
+    values given as bf16, fp16 and fp32 give the same codes and amax."""
+    v = wl.bf16_bits_to_f32(wl.normal_bf16((3000,), 2.0, 77))
+    v = v[np.abs(v) < 6e4]
+    v16 = v.astype(np.float16)
+    v = v16.astype(np.float32)[np.isfinite(v16)]
+    keep = (v.view(np.uint32) & 0xFFFF) == 0  # exact in bf16 as well
+    v = v[keep]
+    b = (v.view(np.uint32) >> 16).astype(np.uint16)
+    h = v.astype(np.float16).view(np.uint16)
+    for fmt in (E4M3, E5M2):
+        s = orc.scale_from_peak(orc.amax(b), fmt)
+        codes = [gpu_quantize_ex(lib, x, t, fmt, s)[0] for t, x in ((0, b), (1, h), (2, v))]
+        assert np.array_equal(codes[0], codes[1]) and np.array_equal(codes[0], codes[2])
+        assert np.array_equal(codes[0], orc.quantize(b, fmt, s))
+    x32 = (np.random.default_rng(5).standard_normal(50000) * 7.0).astype(np.float32)
+    for in_type, x in ((2, x32), (1, x32.astype(np.float16).view(np.uint16))):
+        ring, oring = lib.Ring(4), orc.Ring(4)
+        for t in range(3):
+            xt = x if in_type == 1 else x * np.float32(1 + t)
+            gpu_quantize_ex(lib, xt, in_type, E4M3, np.float32(1.0), ring=ring)
+            oring.fold(orc.amax_in(xt, in_type), E4M3)
+            assert ring_state_equal(ring, oring), (in_type, t)
+            ring.idx = (ring.idx + 1) % 4
+            oring.advance()

@@ -155,6 +155,16 @@ def amax(x: np.ndarray) -> np.float32:
     return np.float32(_load().orc_amax(_ptr(x), x.size))
 
 
+def quantize_t(x: np.ndarray, fmt: int, s) -> tuple[np.ndarray, np.ndarray]:
+    """Transposed / dual-orientation quantize of a bf16 [rows][cols] matrix
+    ([CMP] quantize.cuh fp8_quantize_tiled_kernel, layouts Transposed and
+    Dual; fp8.py _LinearFp8.backward feeds the NT GEMMs with them): the
+    codes of quantize() in row-major order and their transpose
+    ([cols][rows]).  amax is that of the untransposed values."""
+    q = quantize(x, fmt, s)
+    return q, np.ascontiguousarray(q.T)
+
+
 IN_BF16, IN_F16, IN_F32 = 0, 1, 2
 
 

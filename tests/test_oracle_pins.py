@@ -269,6 +269,21 @@ def test_quantize_in_reduces_to_the_bf16_path(orc):
     assert orc.amax_in(np.array([0x7E00, 0x4000, 0xC200], np.uint16), 1) == 3.0
 
 
+def test_quantize_t_elementwise(orc):
+    """Transposed codes: element (c, r) is the encode of x[r][c] * fp32(1/s)
+    by the (pinned) scalar encode, on a ragged matrix."""
+    x = wl.normal_bf16((37, 53), 2.0, 31)
+    s = np.float32(0.02)
+    q, qt = orc.quantize_t(x, E4M3, s)
+    m = orc.multiplier(s)
+    f = wl.bf16_bits_to_f32(x)
+    assert qt.shape == (53, 37) and q.shape == (37, 53)
+    for r in range(0, 37, 5):
+        for c in range(0, 53, 7):
+            code = orc.encode(float(np.float32(f[r, c] * m)), E4M3)
+            assert q[r, c] == code and qt[c, r] == code
+
+
 def test_quantize_multiplies_by_reciprocal(orc):
     """x * fp32(1/s) and x / s can round to different codes; the kernel on
     the pages multiplies by the reciprocal (reading of the scale

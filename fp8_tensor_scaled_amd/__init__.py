@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "FMT_MAX", "IN_BF16", "IN_F16", "IN_F32", "Ring", "library_path",
-    "fp8_quantize", "fp8_quantize_ex", "fp8_quantize2",
+    "fp8_quantize", "fp8_quantize_ex", "fp8_quantize_t", "fp8_quantize2",
     "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_pair", "fp8_colsum", "fp8_colsum_workspace",
     "fp8_quantize_colsum",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
@@ -32,7 +32,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 
 EXPORTED_SYMBOLS = (
-    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize_ex", "fp8_quantize2",
+    "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize_ex",
+    "fp8_quantize_t", "fp8_quantize2",
     "fp8_scale_ring_finalize",
     "fp8_mm", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum", "fp8_quantize_colsum",
     "fp8_linear_fwd_workspace",
@@ -74,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "fp8_format_max": (F, [I32]),
         "fp8_quantize": (I32, [P, I64, I32, P, P, R, I32, P, P]),
         "fp8_quantize_ex": (I32, [P, I32, I64, I32, P, P, R, I32, P, P]),
+        "fp8_quantize_t": (I32, [P, I64, I64, I32, P, P, P, R, I32, P, P]),
         "fp8_quantize2": (I32, [P, I64, I32, P, P, I32, P, R, I32, P, P]),
         "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
         "fp8_mm": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P,
@@ -201,6 +203,17 @@ def fp8_quantize(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
     st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
                            margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize")
+
+
+def fp8_quantize_t(x: torch.Tensor, rows: int, cols: int, fmt: int, scale: torch.Tensor,
+                   out_t: torch.Tensor, out: torch.Tensor | None = None,
+                   ring: Ring | None = None, margin: int = 0,
+                   scale_used: torch.Tensor | None = None, stream=None) -> None:
+    """bf16 x [rows][cols] -> codes transposed in out_t [cols][rows] (and
+    row-major in ``out`` when given) from one read of x; see fp8lin.h."""
+    st = _lib.fp8_quantize_t(_ptr(x), rows, cols, fmt, _ptr(scale), _ptr(out), _ptr(out_t),
+                             _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
+    _check(st, "fp8_quantize_t")
 
 
 IN_BF16, IN_F16, IN_F32 = 0, 1, 2

@@ -276,6 +276,50 @@ fp8_status_t fp8_quantize_ex(const void* x, fp8_in_t in_type, int64_t numel, fp8
                           scale_used, stream);
 }
 
+fp8_status_t fp8_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, fp8_fmt_t fmt,
+                            const float* scale, uint8_t* out, uint8_t* out_t,
+                            const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                            hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_quantize_t: unsupported fp8 format %d", fmt);
+    if (rows < 0 || cols < 0)
+        return fail(FP8_EINVAL, "fp8_quantize_t: rows, cols must be >= 0 (got %lld, %lld)",
+                    (long long)rows, (long long)cols);
+    if ((double)rows * (double)cols >= 9.0e15)
+        return fail(FP8_EINVAL, "fp8_quantize_t: too many elements");
+    const int64_t n = rows * cols;
+    if (n == 0 && !ring) return FP8_OK;
+    if (n > 0 && (!x || !out_t)) return fail(FP8_EINVAL, "fp8_quantize_t: x or out_t is NULL");
+    if (!scale) return fail(FP8_EINVAL, "fp8_quantize_t: scale is NULL");
+    if (ring) {
+        fp8_status_t st = check_ring(ring, "fp8_quantize_t");
+        if (st) return st;
+    }
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_quantize_t: margin %d outside [0, 64]", margin);
+    if (out && n > 0) {
+        const uintptr_t o0 = (uintptr_t)out, o1 = (uintptr_t)out_t;
+        if (o0 < o1 + (uintptr_t)n && o1 < o0 + (uintptr_t)n)
+            return fail(FP8_EINVAL, "fp8_quantize_t: out and out_t overlap");
+    }
+    fp8_status_t st = check_device();
+    if (st) return st;
+    fp8lin::QuantLaunch q;
+    q.x = x;
+    q.numel = n;
+    q.fmt = fmt;
+    q.scale = scale;
+    q.out = out;
+    q.ring_state = ring ? ring->state : nullptr;
+    q.ring_len = ring ? ring->len : 0;
+    q.ring_idx = ring ? ring->idx : 0;
+    q.pow2_margin = pow2f(margin);
+    q.scale_used = scale_used;
+    hipError_t e = fp8lin::launch_quantize_t(q, rows, cols, out_t, stream);
+    if (e != hipSuccess) return hip_fail(e, "transposed quantize launch");
+    return FP8_OK;
+}
+
 fp8_status_t fp8_quantize2(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
                            uint8_t* out, fp8_fmt_t fmt2, uint8_t* out2, const fp8_ring_t* ring,
                            int32_t margin, float* scale_used, hipStream_t stream) {

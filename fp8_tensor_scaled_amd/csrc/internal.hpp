@@ -39,6 +39,12 @@ struct QuantLaunch {
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
 
+// Transposed quantize of bf16 q.x [rows][cols] into out_t [cols][rows]; with
+// q.out also the row-major codes (one read of x).  Ring, scale, scale_used as
+// launch_quantize; q.in_type must be bf16.
+hipError_t launch_quantize_t(const QuantLaunch& q, int64_t rows, int64_t cols, uint8_t* out_t,
+                             hipStream_t stream);
+
 hipError_t launch_ring_finalize(float* state, int32_t len, int32_t idx, int fmt,
                                 float pow2_margin, const float* amax, hipStream_t stream);
 

@@ -685,4 +685,142 @@ hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, ui
     return launch_colsum_final(p.part, m, n, db, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Transposed / dual-orientation quantize ([CMP] quantize.cuh,
+// fp8_quantize_tiled_kernel with the Transposed and Dual layouts; fp8.py
+// _LinearFp8.backward feeds its NT GEMMs with them): bf16 x [rows][cols] ->
+// out_t [cols][rows], the codes of x transposed, and with `out` the
+// row-major codes too, from one read of x; amax and fold as the quantize.
+//
+// 128 x 128 tiles walked in grid-stride order by workgroups of 1024 lanes.
+// A tile is read in 2 passes of 64 rows x 16 lanes x 16 bytes (whole
+// 256-byte row segments); each lane converts its 8 values, stores the
+// row-major codes directly (8 bytes, DUAL) and scatters them into an LDS
+// tile [128 columns][128 rows] (pitch 144 bytes); after a barrier every
+// lane writes 16 bytes of one out_t row, 8 lanes a whole 128-byte line.
+// Other shapes (cols % 8, rows % 16, unaligned bases) take a per-element
+// path.
+// ---------------------------------------------------------------------------
+constexpr int kTT = 128;           // tile edge
+constexpr int kTPitch = kTT + 16;  // LDS bytes per tile column
+
+struct QTParams {
+    QuantParams q;   // x (bf16), out (row-major codes, nullable), scale, ring
+    uint8_t* out_t;  // [cols][rows]
+    int64_t rows, cols;
+    int vec;
+};
+
+template <int FMT, bool DUAL>
+__global__ __launch_bounds__(kQuantThreads) void quantize_t_kernel(QTParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kTT * kTPitch];
+    const float s_read = *p.q.scale;
+    const float m = __fdiv_rn(1.0f, s_read);
+    const int t = threadIdx.x;
+    const float win =
+        (p.q.hist && t < p.q.len && t < kWave && t != p.q.idx) ? p.q.hist[t] : 0.0f;
+    float amax = 0.0f;
+    const uint16_t* x = static_cast<const uint16_t*>(p.q.x);
+    if (p.vec) {
+        const int64_t tcols = (p.cols + kTT - 1) / kTT;
+        const int64_t ntiles = ((p.rows + kTT - 1) / kTT) * tcols;
+        const int lr = t / 16, lc = (t % 16) * 8;  // load: row within a pass, first column
+        const int sc = t / 8, sr = (t % 8) * 16;   // store: tile column, first row
+        for (int64_t id = blockIdx.x; id < ntiles; id += gridDim.x) {
+            const int64_t r0 = (id / tcols) * kTT, c0 = (id % tcols) * kTT;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                const int rr = pass * 64 + lr;
+                const int64_t r = r0 + rr, c = c0 + lc;
+                if (r < p.rows && c < p.cols) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(x + r * p.cols + c);
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    float f[8];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        f[2 * j] = bf16_lo(w[j]);
+                        f[2 * j + 1] = bf16_hi(w[j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+                    uint2 o;
+                    o.x = cvt4<FMT>(f[0] * m, f[1] * m, f[2] * m, f[3] * m);
+                    o.y = cvt4<FMT>(f[4] * m, f[5] * m, f[6] * m, f[7] * m);
+                    if constexpr (DUAL) *reinterpret_cast<uint2*>(p.q.out + r * p.cols + c) = o;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        tile[(lc + j) * kTPitch + rr] =
+                            (uint8_t)(((j < 4 ? o.x : o.y) >> (8 * (j % 4))) & 0xff);
+                }
+            }
+            __syncthreads();
+            const int64_t c = c0 + sc, r = r0 + sr;
+            if (c < p.cols && r < p.rows)
+                *reinterpret_cast<uint4*>(p.out_t + c * p.rows + r) =
+                    *reinterpret_cast<const uint4*>(tile + sc * kTPitch + sr);
+            __syncthreads();  // the next tile rewrites the LDS tile
+        }
+    } else {
+        const int64_t n = p.rows * p.cols;
+        const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+        for (int64_t e = (int64_t)blockIdx.x * kQuantThreads + t; e < n; e += stride) {
+            const int64_t r = e / p.cols, c = e - r * p.cols;
+            const float f = bf16_to_f32(x[e]);
+            amax = fmaxf(amax, fabsf(f));
+            const uint8_t code = cvt1<FMT>(f * m);
+            if constexpr (DUAL) p.q.out[e] = code;
+            p.out_t[c * p.rows + r] = code;
+        }
+    }
+    if (p.q.hist) {
+        const uint32_t ticket = publish_amax(p.q, amax, gridDim.x, blockIdx.x);
+        finish_fold(p.q, ticket, s_read, win, gridDim.x);
+    } else if (p.q.scale_used && blockIdx.x == 0 && t == 0) {
+        *p.q.scale_used = s_read;
+    }
+}
+
+hipError_t launch_quantize_t(const QuantLaunch& q, int64_t rows, int64_t cols, uint8_t* out_t,
+                             hipStream_t stream) {
+    QTParams p{};
+    p.q.x = q.x;
+    p.q.numel = rows * cols;
+    p.q.scale = q.scale;
+    p.q.out = q.out;
+    if (q.ring_state) {
+        p.q.hist = q.ring_state;
+        p.q.scale_out = q.ring_state + q.ring_len;
+        p.q.amax_slot = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 2);
+        p.q.done = reinterpret_cast<uint32_t*>(q.ring_state + q.ring_len + 3);
+        p.q.groups = reinterpret_cast<uint32_t*>(q.ring_state + ring_groups_offset(q.ring_len));
+        p.q.len = q.ring_len;
+        p.q.idx = q.ring_idx;
+    }
+    p.q.fmax = q.fmt ? 57344.0f : 448.0f;
+    p.q.pow2_margin = q.pow2_margin;
+    p.q.scale_used = q.scale_used;
+    p.out_t = out_t;
+    p.rows = rows;
+    p.cols = cols;
+    const uintptr_t ax = reinterpret_cast<uintptr_t>(q.x);
+    const uintptr_t ao = reinterpret_cast<uintptr_t>(q.out);
+    const uintptr_t at = reinterpret_cast<uintptr_t>(out_t);
+    p.vec = (cols % 8 == 0) && (rows % 16 == 0) && (ax % 16 == 0) && (ao % 8 == 0) &&
+            (at % 16 == 0);
+    int64_t blocks = p.vec ? ((rows + kTT - 1) / kTT) * ((cols + kTT - 1) / kTT)
+                           : (rows * cols + kQuantThreads - 1) / kQuantThreads;
+    if (blocks > 256) blocks = 256;  // one workgroup per CU
+    if (blocks < 1) blocks = 1;
+    const dim3 grid((unsigned)blocks), block(kQuantThreads);
+    const bool dual = q.out != nullptr;
+    if (q.fmt == 0) {
+        if (dual) hipLaunchKernelGGL((quantize_t_kernel<0, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((quantize_t_kernel<0, false>), grid, block, 0, stream, p);
+    } else {
+        if (dual) hipLaunchKernelGGL((quantize_t_kernel<1, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((quantize_t_kernel<1, false>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace fp8lin

@@ -149,6 +149,26 @@ fp8_status_t fp8_quantize_ex(const void* x, fp8_in_t in_type, int64_t numel, fp8
                              int32_t margin, float* scale_used, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_quantize_t -- transposed / dual-orientation quantize.
+ * (compare view: csrc/kernels/fp8/quantize.cuh fp8_quantize_tiled_kernel,
+ *  layouts Transposed and Dual; astrai/extension/fp8.py
+ *  _LinearFp8.backward, which feeds its two NT GEMMs with g8 / g8^T from
+ *  one dual pass and with x8^T, w8^T)
+ *
+ * x: bf16 [rows][cols] (device).  out_t: uint8 [cols][rows] receives the
+ * codes of x transposed: out_t[c][r] = enc(fp32(x[r][c]) * fp32(1/s)).
+ * out: nullable uint8 [rows][cols]; when given, the row-major codes too
+ * (one read of x gives both orientations).  scale (required), ring, margin
+ * and scale_used as fp8_quantize; the fold records max |x| like any
+ * quantize.  out and out_t must not overlap.  rows * cols == 0 without a
+ * ring does nothing.
+ * ------------------------------------------------------------------- */
+fp8_status_t fp8_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, fp8_fmt_t fmt,
+                            const float* scale, uint8_t* out, uint8_t* out_t,
+                            const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_quantize2 -- one pass over x, two encodings of the same scaled values.
  * (compare view: astrai/extension/fp8.py _LinearFp8.backward, where under
  *  the HYBRID recipe x and w are quantized again in E5M2 with the forward's

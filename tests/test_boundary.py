@@ -112,6 +112,23 @@ def test_quantize_ex_validation(f, in_type, kw, needle):
     assert st == 1 and needle in _err(f._lib), _err(f._lib)
 
 
+@pytest.mark.parametrize("kw,needle", [
+    (dict(fmt=3), "format"),
+    (dict(rows=-1), ">= 0"),
+    (dict(out_t=None), "NULL"),
+    (dict(x=None), "NULL"),
+    (dict(scale=None), "scale is NULL"),
+    (dict(out=FAKE), "overlap"),
+    (dict(margin=99), "margin"),
+])
+def test_quantize_t_validation(f, kw, needle):
+    a = dict(x=FAKE, rows=64, cols=64, fmt=0, scale=FAKE, out=None, out_t=FAKE, ring=None,
+             margin=0, used=None, stream=None)
+    a.update(kw)
+    st = f._lib.fp8_quantize_t(*a.values())
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
 def test_quantize2_empty_without_ring_is_a_noop(f):
     assert f._lib.fp8_quantize2(None, 0, 0, None, None, 1, None, None, 0, None, None) == 0
 

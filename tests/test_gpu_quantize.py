@@ -371,3 +371,87 @@ def test_quantize_ex_ring_fold_and_same_values(lib, orc):
             assert ring_state_equal(ring, oring), (in_type, t)
             ring.idx = (ring.idx + 1) % 4
             oring.advance()
+
+
+# ---------------------------------------------------------------------------
+# Transposed / dual-orientation quantize (fp8_quantize_t)
+# ---------------------------------------------------------------------------
+
+def gpu_quantize_t(lib, x, fmt, s, dual, offset=0, ring=None):
+    rows, cols = x.shape
+    n = x.size
+    xd = torch.zeros(n + offset, dtype=torch.int16, device="cuda")
+    xd[offset:] = to_dev_bf16(x.ravel())
+    out_t = torch.full((n + offset,), 0xAA, dtype=torch.uint8, device="cuda")
+    out = torch.full((n + offset,), 0xAA, dtype=torch.uint8, device="cuda") if dual else None
+    used = dev_f32(-1.0)
+    lib.fp8_quantize_t(xd[offset:], rows, cols, fmt, dev_f32(s), out_t[offset:],
+                       out=None if out is None else out[offset:], ring=ring, scale_used=used)
+    torch.cuda.synchronize()
+    q = from_dev_u8(out[offset:]).reshape(rows, cols) if dual else None
+    return q, from_dev_u8(out_t[offset:]).reshape(cols, rows), float(used.cpu()[0])
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("rows,cols,offset", [(4096, 4096, 0), (256, 384, 0), (272, 136, 0),
+                                              (16, 8, 0), (100, 36, 0), (33, 17, 0),
+                                              (128, 128, 1), (2048, 1024, 0)])
+def test_quantize_t_matches_oracle(lib, orc, fmt, rows, cols, offset):
+    """Transposed and dual-orientation codes, bit-exact, on full tiles,
+    partial tiles, the per-element path (rows % 16, cols % 8, misaligned
+    base) and the training config's x shape."""
+    x = wl.normal_bf16((rows, cols), 2.0, rows * 7 + cols)
+    s = orc.scale_from_peak(orc.amax(x), fmt)
+    q_ref, qt_ref = orc.quantize_t(x, fmt, s)
+    for dual in (False, True):
+        q, qt, used = gpu_quantize_t(lib, x, fmt, s, dual, offset)
+        assert used == s
+        assert np.array_equal(qt, qt_ref), dual
+        if dual:
+            assert np.array_equal(q, q_ref)
+
+
+def test_quantize_t_ring_fold(lib, orc):
+    """The dual pass folds max |x| into its ring like the quantize."""
+    ring, oring = lib.Ring(8), orc.Ring(8)
+    for t in range(3):
+        x = wl.normal_bf16((512, 768), 1.0 + t, 40 + t)
+        gpu_quantize_t(lib, x, E5M2, np.float32(0.5), True, ring=ring)
+        oring.fold(orc.amax(x), E5M2)
+        assert ring_state_equal(ring, oring), t
+        ring.idx = (ring.idx + 1) % 8
+        oring.advance()
+
+
+def test_backward_nt_only_route(lib, orc):
+    """The pages' NT-only backward (dual quantize of g, transposed copies of
+    x and w, two NT GEMMs) against the oracle's dX and dW."""
+    M, N, K = 2048, 1024, 512
+    g = wl.normal_bf16((M, N), 1e-3, 60)
+    x = wl.normal_bf16((M, K), 1.0, 61)
+    w = wl.normal_bf16((N, K), 0.02, 62)
+    fmt = E5M2
+    sg = orc.scale_from_peak(orc.amax(g), fmt)
+    sx = orc.scale_from_peak(orc.amax(x), fmt)
+    sw = orc.scale_from_peak(orc.amax(w), fmt)
+    g8, g8t = (torch.empty(M * N, dtype=torch.uint8, device="cuda") for _ in range(2))
+    x8t = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+    w8t = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+    dsg, dsx, dsw = dev_f32(sg), dev_f32(sx), dev_f32(sw)
+    lib.fp8_quantize_t(to_dev_bf16(g.ravel()), M, N, fmt, dsg, g8t, out=g8)
+    lib.fp8_quantize_t(to_dev_bf16(x.ravel()), M, K, fmt, dsx, x8t)
+    lib.fp8_quantize_t(to_dev_bf16(w.ravel()), N, K, fmt, dsw, w8t)
+    dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    # dX[M][K] = g8 [M][N] . w8^T stored [K][N] (NT);  dW[N][K] = g8^T [N][M] . x8^T [K][M] (NT)
+    lib.fp8_mm(g8, w8t, fmt, 0, 1, M, K, N, N, N, 1, 0, 0, dsg, dsw, None, dx)
+    lib.fp8_mm(g8t, x8t, fmt, 0, 1, N, K, M, M, M, 1, 0, 0, dsg, dsx, None, dw)
+    torch.cuda.synchronize()
+    g8r, x8r, w8r = orc.quantize(g, fmt, sg), orc.quantize(x, fmt, sx), orc.quantize(w, fmt, sw)
+    assert np.array_equal(from_dev_u8(g8), g8r.ravel())
+    ref_dx = orc.gemm(g8r, w8r, fmt, False, False, M, K, N, sg, sw)
+    ad_dx = orc.gemm_absdot(g8r, w8r, fmt, False, False, M, K, N, sg, sw)
+    check_gemm(from_dev_bf16(dx).reshape(M, K), ref_dx, ad_dx, N, "nt-route dX")
+    ref_dw = orc.gemm(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
+    ad_dw = orc.gemm_absdot(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
+    check_gemm(from_dev_bf16(dw).reshape(N, K), ref_dw, ad_dw, M, "nt-route dW")

@@ -394,6 +394,12 @@ def components(f, torch):
         res[name] = dict(us=round(ms * 1e3, 2), gbs=round(bpe * n / (ms * 1e-3) / 1e9, 1),
                          hbm_frac=round(bpe * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
         del xs
+    # the backward at M = N = K = 4096, two routes from bf16 g, x, w and the
+    # forward's steps: NN + TN on row-major codes (this library's route:
+    # quantize g with its column sums, w and x in E5M2, one paired launch)
+    # against the pages' NT-only route (dual-orientation quantize of g, the
+    # column sums, transposed quantizes of x and w, two NT GEMMs)
+    res.update(backward_routes(f, torch))
     # reference for the quantize's practical ceiling: torch's copy of 1 GiB
     # (read + write, 2 GiB moved)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -403,6 +409,44 @@ def components(f, torch):
                                           gbs=round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
                                           hbm_frac=round(2 * (1 << 30) / (ms * 1e-3) / 1e9
                                                          / PEAK_HBM_GBS, 3))
+    return res
+
+
+def backward_routes(f, torch, n=4096):
+    L = Layer(f, torch, n, seed0=700)
+    L.seed(f)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    g8t, x8t, w8t = (torch.empty(n * n, **u8) for _ in range(3))
+    sg, sx, sw = L.sg, L.sfwd[0:1], L.sfwd[1:2]
+    f.fp8_quantize(L.x, E4M3, scale=L.rx.scale, out=L.x8, scale_used=sx)
+    f.fp8_quantize(L.w, E4M3, scale=L.rw.scale, out=L.w8, scale_used=sw)
+    torch.cuda.synchronize()
+
+    def nn_tn():
+        f.fp8_quantize_colsum(L.g, n, n, E5M2, L.rg.scale, L.g8, L.db, L.cs_ws, ring=L.rg,
+                              scale_used=sg)
+        f.fp8_quantize(L.w, E5M2, scale=sw, out=L.w8b)
+        f.fp8_quantize(L.x, E5M2, scale=sx, out=L.x8b)
+        L.gemm_bwd_pair(f)
+
+    def nt_only():
+        f.fp8_quantize_t(L.g, n, n, E5M2, L.rg.scale, g8t, out=L.g8, ring=L.rg, scale_used=sg)
+        f.fp8_colsum(L.g, n, n, L.db, L.cs_ws)
+        f.fp8_quantize_t(L.x, n, n, E5M2, sx, x8t)
+        f.fp8_quantize_t(L.w, n, n, E5M2, sw, w8t)
+        f.fp8_mm(L.g8, w8t, E5M2, 0, 1, n, n, n, n, n, 1, 0, 0, sg, sw, None, L.dx)
+        f.fp8_mm(g8t, x8t, E5M2, 0, 1, n, n, n, n, n, 1, 0, 0, sg, sx, None, L.dw)
+
+    res = {}
+    for name, fn in (("bwd_route_nn_tn_4096", nn_tn), ("bwd_route_nt_only_4096", nt_only)):
+        ms = time_kernel(torch, lambda i: fn(), 10)
+        res[name] = dict(us=round(ms * 1e3, 2),
+                         tflops=round(2 * 2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1))
+    # the dual-orientation quantize alone (read 2 B, write 2 x 1 B per element)
+    ms = time_kernel(torch, lambda i: f.fp8_quantize_t(L.g, n, n, E5M2, L.rg.scale, g8t,
+                                                        out=L.g8), 20)
+    res["quantize_t_dual_4096x4096"] = dict(us=round(ms * 1e3, 2),
+                                            gbs=round(4 * n * n / (ms * 1e-3) / 1e9, 1))
     return res
 
 

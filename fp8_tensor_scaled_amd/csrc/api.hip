@@ -69,11 +69,17 @@ float pow2f(int32_t margin) { return ldexpf(1.0f, margin); }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace layouts.  Control block (256 B, zero-once, self-cleaning):
-// three length-1 scratch rings of 5 floats each, at float offsets 0, 8, 16.
-constexpr size_t kCtrl = 256;
+// Workspace layouts.  Control block (zero-once, self-cleaning): three
+// length-1 scratch rings, each a whole ring state (its group lines
+// included) starting on a 128-byte boundary, then slot 3 (three floats:
+// the backward's scales when the caller passes no scales_out).
 constexpr int kScratchRingLen = 1;
-float* scratch_ring(void* ws, int i) { return static_cast<float*>(ws) + 8 * i; }
+constexpr size_t kScratchRingBytes = sizeof(float) * fp8lin::ring_state_words(kScratchRingLen);
+static_assert(kScratchRingBytes % 128 == 0, "scratch rings must stay 128-byte aligned");
+constexpr size_t kCtrl = (3 * kScratchRingBytes + 3 * sizeof(float) + 255) / 256 * 256;
+float* scratch_ring(void* ws, int i) {
+    return reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + i * kScratchRingBytes);
+}
 
 struct FwdLayout {
     size_t x8, w8, total;
@@ -492,6 +498,8 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
     if (workspace_bytes < L.total)
         return fail(FP8_EINVAL, "fp8_linear_fwd: workspace %zu < %zu bytes", workspace_bytes,
                     L.total);
+    if ((uintptr_t)workspace & 255)
+        return fail(FP8_EINVAL, "fp8_linear_fwd: workspace not 256-byte aligned");
     fp8_status_t st = check_device();
     if (st) return st;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -574,6 +582,8 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     if (workspace_bytes < L.total)
         return fail(FP8_EINVAL, "fp8_linear_bwd: workspace %zu < %zu bytes", workspace_bytes,
                     L.total);
+    if ((uintptr_t)workspace & 255)
+        return fail(FP8_EINVAL, "fp8_linear_bwd: workspace not 256-byte aligned");
     fp8_status_t st = check_device();
     if (st) return st;
     uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -13,8 +13,8 @@ namespace fp8lin {
 // fold's first level; left at zero by every fold).
 constexpr int kRingGroups = 16;
 constexpr int kRingGroupWords = 32;
-inline int64_t ring_groups_offset(int32_t len) { return ((int64_t)len + 4 + 31) / 32 * 32; }
-inline int64_t ring_state_words(int32_t len) {
+constexpr int64_t ring_groups_offset(int32_t len) { return ((int64_t)len + 4 + 31) / 32 * 32; }
+constexpr int64_t ring_state_words(int32_t len) {
     return ring_groups_offset(len) + (int64_t)kRingGroups * kRingGroupWords;
 }
 

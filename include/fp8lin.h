@@ -310,9 +310,12 @@ fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fm
  *     each ring is snapshotted by the quantize that reads it, the quantize
  *     folds the current amax and publishes the next scale, the GEMM
  *     dequantizes with the snapshots, and both rings advance.
- * workspace: device scratch of fp8_linear_fwd_workspace(M, N, K) bytes; its
- *     first 256 bytes are control slots that must be zero before the first
- *     use and that every call leaves at zero (allocate zeroed, then reuse).
+ * workspace: device scratch of fp8_linear_fwd_workspace(M, N, K) bytes,
+ *     256-byte aligned; its first fp8_linear_fwd_x8_offset(M, N, K) bytes
+ *     (6656, whatever the shape) are control slots (scratch rings for the
+ *     dynamic amax) that must be zero before the first use and whose
+ *     reduction words every call leaves at zero (allocate zeroed, then
+ *     reuse).
  *     It receives x8 [M][K] and w8 [N][K] (fmt codes) at
  *     fp8_linear_fwd_x8_offset / _w8_offset.
  * scales_out: fp32 [2] (device) receives the steps used, [sx, sw]; the
@@ -349,9 +352,11 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  * dx, dw, db: each NULL to skip that gradient (x8b is only made for dw,
  *     w8b only for dx).  With both dx and dw, the two products run as
  *     fp8_mm_pair (one launch when the shapes allow).
- * workspace: fp8_linear_bwd_workspace(M, N, K) bytes, same zero-once
- *     contract as the forward's.
- * scales_out: nullable fp32 [3] receives [sg, sx, sw].
+ * workspace: fp8_linear_bwd_workspace(M, N, K) bytes, 256-byte aligned,
+ *     with the forward's 6656-byte control block and zero-once contract;
+ *     it receives g8 [M][N] at fp8_linear_fwd_x8_offset(M, N, K).
+ * scales_out: nullable fp32 [3] receives [sg, sx, sw]; sx is written only
+ *     when dw is made, sw only when dx is made.
  * ------------------------------------------------------------------- */
 size_t fp8_linear_bwd_workspace(int64_t M, int64_t N, int64_t K);
 fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t* w,

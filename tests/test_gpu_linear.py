@@ -47,17 +47,54 @@ def test_linear256_dynamic_forward(lib, orc):
     d = wl.linear256()
     M, N, K = d["M"], d["N"], d["K"]
     f = Fwd(lib, M, N, K)
-    for rep in range(2):  # the workspace's scratch slots re-arm themselves
-        lib.fp8_linear_fwd(to_dev_bf16(d["x"]), to_dev_bf16(d["w"]), to_dev_bf16(d["bias"]),
+    # The workspace's scratch rings re-arm themselves: the second call (other
+    # amaxes, so a scale left over from the first would fail) reuses it.
+    for rep, (fx, fw) in enumerate(((1.0, 1.0), (4.0, 0.25))):
+        x, w = wl.scaled_bf16(d["x"], fx), wl.scaled_bf16(d["w"], fw)
+        lib.fp8_linear_fwd(to_dev_bf16(x), to_dev_bf16(w), to_dev_bf16(d["bias"]),
                            M, N, K, E4M3, True, 0, None, None, f.ws, f.scales, f.out)
         torch.cuda.synchronize()
-        ref = orc.linear_fwd(d["x"], d["w"], d["bias"], M, N, K, E4M3, True)
+        ref = orc.linear_fwd(x, w, d["bias"], M, N, K, E4M3, True)
         sc = f.scales.cpu().numpy()
-        assert sc[0] == ref.sx and sc[1] == ref.sw
-        assert np.array_equal(f.x8(), ref.x8.ravel())
-        assert np.array_equal(f.w8(), ref.w8.ravel())
+        assert sc[0] == ref.sx and sc[1] == ref.sw, rep
+        assert np.array_equal(f.x8(), ref.x8.ravel()), rep
+        assert np.array_equal(f.w8(), ref.w8.ravel()), rep
         absdot = orc.gemm_absdot(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
-        check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, "linear256")
+        check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, f"linear256 {rep}")
+
+
+def test_dynamic_backward_reused_workspace(lib, orc):
+    # Tensors of 8 to 20 quantize workgroups, so every amax reduction uses
+    # several group lines of its scratch ring; the g8 codes the first call
+    # writes sit right after those rings.  Second call: other amaxes.
+    M, N, K = 256, 384, 640
+    x0 = wl.normal_bf16((M, K), 1.0, 31)
+    w0 = wl.normal_bf16((N, K), 0.02, 32)
+    g0 = wl.normal_bf16((M, N), 1e-3, 33)
+    ws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    dummy = torch.zeros(2, dtype=torch.float32, device="cuda")
+    so = torch.zeros(3, dtype=torch.float32, device="cuda")
+    dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    db = torch.empty(N, dtype=torch.int16, device="cuda")
+    g8_off = lib.fp8_linear_fwd_x8_offset(M, N, K)
+    for rep, (fg, fx, fw) in enumerate(((1.0, 1.0, 1.0), (8.0, 0.5, 4.0))):
+        g, x, w = wl.scaled_bf16(g0, fg), wl.scaled_bf16(x0, fx), wl.scaled_bf16(w0, fw)
+        lib.fp8_linear_bwd(to_dev_bf16(g), to_dev_bf16(x), to_dev_bf16(w), M, N, K, E5M2, True,
+                           0, dummy, None, ws, so, dx, dw, db)
+        torch.cuda.synchronize()
+        rb = orc.linear_bwd(g, x, w, M, N, K, E5M2, True, 0.0, 0.0, None)
+        s = so.cpu().numpy()
+        assert (s[0], s[1], s[2]) == (rb.sg, rb.sx, rb.sw), rep
+        assert np.array_equal(from_dev_u8(ws[g8_off: g8_off + M * N]), rb.g8.ravel()), rep
+        w8b = orc.quantize(w, E5M2, rb.sw)
+        ad = orc.gemm_absdot(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+        check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, N, f"dx {rep}")
+        x8b = orc.quantize(x, E5M2, rb.sx)
+        ad = orc.gemm_absdot(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+        check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, M, f"dw {rep}")
+        absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+        check_gemm(from_dev_bf16(db), rb.db, absg, M, f"db {rep}")
 
 
 def _samples(M, N, n, seed):
@@ -96,7 +133,8 @@ def test_train_delayed_hybrid_four_steps(lib, orc):
             assert gr.idx == orr.idx and gr.initialized == orr.initialized
         assert np.array_equal(f.x8(), rf.x8.ravel())
         assert np.array_equal(f.w8(), rf.w8.ravel())
-        g8 = from_dev_u8(bws[256: 256 + M * N])
+        g8_off = lib.fp8_linear_fwd_x8_offset(M, N, K)
+        g8 = from_dev_u8(bws[g8_off: g8_off + M * N])
         assert np.array_equal(g8, rb.g8.ravel())
         # GEMM outputs at sampled coordinates
         s = _samples(M, N, 2000, t)

@@ -400,6 +400,10 @@ def components(f, torch):
     # against the pages' NT-only route (dual-orientation quantize of g, the
     # column sums, transposed quantizes of x and w, two NT GEMMs)
     res.update(backward_routes(f, torch))
+    # the same layer step through the autograd layer (FP8Linear under
+    # fp8_autocast, delayed HYBRID): what the policy layer costs over the
+    # step's own launch sequence
+    res.update(autograd_layer(f, torch))
     # reference for the quantize's practical ceiling: torch's copy of 1 GiB
     # (read + write, 2 GiB moved)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -448,6 +452,39 @@ def backward_routes(f, torch, n=4096):
     res["quantize_t_dual_4096x4096"] = dict(us=round(ms * 1e3, 2),
                                             gbs=round(4 * n * n / (ms * 1e-3) / 1e9, 1))
     return res
+
+
+def autograd_layer(f, torch, n=4096):
+    """FP8Linear n -> n with bias, forward + backward of x [n][n] under
+    fp8_autocast (delayed scaling, HYBRID), gradients cleared each step."""
+    from fp8_tensor_scaled_amd import autocast as fa
+    dev = "cuda"
+    layer = fa.FP8Linear(n, n, device=dev, dtype=torch.bfloat16)
+    x = (torch.randn(n, n, device=dev)).to(torch.bfloat16).requires_grad_(True)
+    g = (torch.randn(n, n, device=dev) * 1e-3).to(torch.bfloat16)
+
+    def step():
+        x.grad = layer.weight.grad = layer.bias.grad = None
+        with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+            layer(x).backward(g)
+
+    ms = time_kernel(torch, lambda i: step(), 20)
+    # host time per step (Python, autograd, launches), the GPU kept busy
+    # by a long GEMM queued first so that no launch waits for a free slot
+    a8 = torch.randint(0, 120, (8192 * 8192,), dtype=torch.uint8, device=dev)
+    o = torch.empty(8192 * 8192, dtype=torch.int16, device=dev)
+    s = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        f.fp8_mm(a8, a8, E4M3, 0, 1, 8192, 8192, 8192, 8192, 8192, 1, 0, 0, s, s, None, o)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        step()
+    host_us = (time.perf_counter() - t0) / 5 * 1e6
+    torch.cuda.synchronize()
+    return {"autograd_fp8linear_step_4096": dict(
+        us=round(ms * 1e3, 2), tflops=round(3 * 2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1),
+        host_us=round(host_us, 1))}
 
 
 def cpu_baseline(size, rows=1024):

@@ -1,0 +1,398 @@
+"""Scaling policy and autograd layer over the C-ABI.
+
+The layer the pages put above their fp8 primitives (compare view
+3e57cc8...main, astrai/extension/fp8.py: FP8Format, FP8Recipe, _ScaleRing,
+FP8TensorMeta, FP8State, fp8_autocast, fp8_linear_forward, _LinearFp8):
+
+* ``FP8Format``: E4M3, E5M2, or HYBRID (E4M3 forward, E5M2 gradients).
+* ``FP8Recipe``: delayed scaling over an amax history of ``history_len``
+  steps (the default), or dynamic (current-amax) scaling; ``margin`` divides
+  the step by 2^margin.
+* ``fp8_autocast``: a context (a ContextVar, so threads and nested regions
+  each see their own) that turns the fp8 path on for ``fp8_linear`` /
+  ``FP8Linear`` with a recipe and a format.
+* Per-weight delayed-scaling state: one ring each for x, w and g, created on
+  a weight's first fp8 use and kept as long as the weight lives.
+* ``_LinearFp8``: forward and backward of ``y = x w^T + b`` for inputs of any
+  leading shape [..., K], flattened to 2-D for the kernels.
+
+Every number is computed in libfp8lin (``fp8_linear_fwd`` /
+``fp8_linear_bwd`` under dynamic scaling; under delayed scaling the
+quantize, GEMM and bias-gradient entry points they are made of, in an order
+that reads x and w once per step; ``fp8_quantize`` / ``fp8_mm`` for
+pre-quantized weights); this module only keeps the rings, picks formats,
+allocates outputs and reshapes.  Inputs, weights and biases are bf16.
+
+Pre-quantized weights: a ``torch.float8_e4m3fn`` / ``torch.float8_e5m2``
+weight is used as its codes with a step given by the caller (``w_scale``,
+fp32 [1] on the device); it is not re-quantized, has no ring and gets no
+gradient.  Its format must be the one the pass uses: the forward format,
+and for an input gradient the backward format too (E4M3 weights train
+under FP8Format.E4M3; under HYBRID only the forward is defined).
+"""
+
+from __future__ import annotations
+
+import contextvars
+import dataclasses
+import enum
+import weakref
+
+import torch
+
+from . import (E4M3, E5M2, Ring, fp8_colsum, fp8_colsum_workspace, fp8_linear_bwd,
+               fp8_linear_bwd_workspace, fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
+               fp8_mm_pair, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
+
+__all__ = ["FP8Format", "FP8Recipe", "FP8TensorMeta", "FP8State", "fp8_state", "fp8_autocast",
+           "current_config", "fp8_linear", "FP8Linear"]
+
+_FP8_DTYPES = {torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
+
+
+class FP8Format(str, enum.Enum):
+    E4M3 = "e4m3"
+    E5M2 = "e5m2"
+    HYBRID = "hybrid"
+
+    def fwd(self) -> int:
+        """Format of the forward operands (x, w)."""
+        return E5M2 if self is FP8Format.E5M2 else E4M3
+
+    def bwd(self) -> int:
+        """Format of the backward operands (g, and x, w re-quantized)."""
+        return E4M3 if self is FP8Format.E4M3 else E5M2
+
+
+@dataclasses.dataclass(frozen=True)
+class FP8Recipe:
+    """step = max(peak / FP8_MAX / 2^margin, 1e-12) with peak the max of the
+    amax history (delayed) or the current amax (dynamic)."""
+    history_len: int = 16
+    margin: int = 0
+    dynamic: bool = False
+
+    def __post_init__(self):
+        if not 1 <= self.history_len <= 4096:
+            raise ValueError(f"history_len {self.history_len} outside [1, 4096]")
+        if not 0 <= self.margin <= 64:
+            raise ValueError(f"margin {self.margin} outside [0, 64]")
+
+
+@dataclasses.dataclass(frozen=True)
+class _Config:
+    enabled: bool
+    recipe: FP8Recipe
+    fp8_format: FP8Format
+
+
+class FP8TensorMeta:
+    """Delayed-scaling rings of one weight's x, w and g operands."""
+    __slots__ = ("recipe", "x", "w", "g")
+
+    def __init__(self, device: torch.device, recipe: FP8Recipe):
+        self.recipe = recipe
+        self.x = Ring(recipe.history_len, device)
+        self.w = Ring(recipe.history_len, device)
+        self.g = Ring(recipe.history_len, device)
+
+
+class FP8State:
+    """Defaults that apply outside any fp8_autocast region, and the
+    per-weight metas (held weakly: a meta lives as long as its weight)."""
+
+    def __init__(self):
+        self.default_enabled = False
+        self.default_recipe = FP8Recipe()
+        self.default_format = FP8Format.HYBRID
+        # id(weight) -> (weak reference to the weight, meta); an entry leaves
+        # when its weight is collected (tensors compare elementwise, so they
+        # cannot be weak dictionary keys themselves)
+        self._metas: dict = {}
+
+    def get_weight_meta(self, w: torch.Tensor, recipe: FP8Recipe) -> FP8TensorMeta:
+        key = id(w)
+        entry = self._metas.get(key)
+        meta = entry[1] if entry is not None and entry[0]() is w else None
+        if meta is None or meta.recipe.history_len != recipe.history_len:
+            meta = FP8TensorMeta(w.device, recipe)
+            if entry is None or entry[0]() is not w:
+                weakref.finalize(w, self._drop, key)
+            self._metas[key] = (weakref.ref(w), meta)
+        return meta
+
+    def _drop(self, key: int) -> None:
+        entry = self._metas.get(key)
+        if entry is not None and entry[0]() is None:
+            del self._metas[key]
+
+    def reset(self) -> None:
+        """Defaults back to their initial values; every meta dropped."""
+        self.default_enabled = False
+        self.default_recipe = FP8Recipe()
+        self.default_format = FP8Format.HYBRID
+        self._metas.clear()
+
+
+_STATE = FP8State()
+_ACTIVE: contextvars.ContextVar = contextvars.ContextVar("fp8_active_config", default=None)
+
+
+def fp8_state() -> FP8State:
+    return _STATE
+
+
+def current_config() -> _Config:
+    cfg = _ACTIVE.get()
+    if cfg is not None:
+        return cfg
+    return _Config(_STATE.default_enabled, _STATE.default_recipe, _STATE.default_format)
+
+
+class fp8_autocast:
+    """``with fp8_autocast(enabled=True, recipe=FP8Recipe(), fp8_format=
+    FP8Format.HYBRID):`` -- fp8_linear / FP8Linear inside use the fp8 path
+    with that recipe and format; regions nest and restore on exit."""
+
+    def __init__(self, enabled: bool = True, recipe: FP8Recipe | None = None,
+                 fp8_format: FP8Format | str = FP8Format.HYBRID):
+        self._cfg = _Config(bool(enabled), recipe if recipe is not None else FP8Recipe(),
+                            FP8Format(fp8_format))
+        self._tokens: list = []
+
+    def __enter__(self):
+        self._tokens.append(_ACTIVE.set(self._cfg))
+        return self
+
+    def __exit__(self, *exc):
+        _ACTIVE.reset(self._tokens.pop())
+        return False
+
+
+# Linear workspaces: their control slots start at zero and every call
+# leaves them so, so one zero-filled buffer per (device, kind, shape) is
+# reused by calls that are ordered on a stream.
+_WS: dict = {}
+
+
+def _workspace(kind: str, device, M: int, N: int, K: int) -> torch.Tensor:
+    key = (str(device), kind, M, N, K)
+    ws = _WS.get(key)
+    if ws is None:
+        size = (fp8_linear_fwd_workspace if kind == "fwd" else fp8_linear_bwd_workspace)(M, N, K)
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def _bf16(t: torch.Tensor | None, what: str) -> torch.Tensor | None:
+    if t is None:
+        return None
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"fp8_linear: {what} must be bfloat16 (got {t.dtype})")
+    return t.contiguous()
+
+
+class _LinearFp8(torch.autograd.Function):
+    """y[..., N] = x[..., K] w[N][K]^T + b and its gradients in fp8 ([CMP]
+    fp8.py _LinearFp8).
+
+    Dynamic scaling: fp8_linear_fwd / fp8_linear_bwd (the backward measures
+    its own steps in the backward format, so it re-reads x and w).
+
+    Delayed scaling: the same operations as those two entry points, bit for
+    bit, in fewer passes.  The backward's x and w codes use the forward's
+    steps, so the forward writes them from its own read of x and w
+    (fp8_quantize2 when the formats differ; under one format they are the
+    forward codes) and keeps them -- one byte per element instead of bf16 x
+    and w.  The backward quantizes g with its ring, the bias gradient from
+    the same pass, then dX (NN) and dW (TN) in one paired launch."""
+
+    @staticmethod
+    def forward(ctx, x, w, bias, cfg):
+        N, K = w.shape
+        x2 = x.reshape(-1, K)
+        M = x2.shape[0]
+        dev = x.device
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        scales = torch.empty(2, dtype=torch.float32, device=dev)
+        recipe, fmt = cfg.recipe, cfg.fp8_format.fwd()
+        ctx.recipe, ctx.fmt_bwd = recipe, cfg.fp8_format.bwd()
+        ctx.has_bias, ctx.x_shape, ctx.mnk = bias is not None, x.shape, (M, N, K)
+        bias16 = None if bias is None else bias.view(torch.int16)
+        if recipe.dynamic:
+            ctx.meta = None
+            fp8_linear_fwd(x2.view(torch.int16), w.view(torch.int16), bias16, M, N, K, fmt, True,
+                           recipe.margin, None, None, _workspace("fwd", dev, M, N, K), scales,
+                           out.view(torch.int16))
+            ctx.save_for_backward(x2, w, scales)
+            return out.reshape(*x.shape[:-1], N)
+        meta = ctx.meta = _STATE.get_weight_meta(w, recipe)
+        m = recipe.margin
+        xi, wi = x2.view(torch.int16), w.view(torch.int16)
+        for ring, t in ((meta.x, xi), (meta.w, wi)):
+            if not ring.initialized:  # first use: the ring starts from this tensor's amax
+                fp8_quantize(t, fmt, ring=ring, margin=m)
+                ring.initialized = True
+
+        def codes(t, numel, ring, used, keep):
+            q = torch.empty(numel, dtype=torch.uint8, device=dev)
+            if keep and ctx.fmt_bwd != fmt:
+                qb = torch.empty(numel, dtype=torch.uint8, device=dev)
+                fp8_quantize2(t, fmt, ring.scale, q, ctx.fmt_bwd, qb, ring=ring, margin=m,
+                              scale_used=used)
+                return q, qb
+            fp8_quantize(t, fmt, scale=ring.scale, out=q, ring=ring, margin=m, scale_used=used)
+            return q, (q if keep else None)
+
+        need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        x8, x8b = codes(xi, M * K, meta.x, scales[0:1], need_w)  # dW = g^T x
+        w8, w8b = codes(wi, N * K, meta.w, scales[1:2], need_x)  # dX = g w
+        fp8_mm(x8, w8, fmt, 0, 1, M, N, K, K, K, 1, 0, 0, scales[0:1], scales[1:2], bias16,
+               out.view(torch.int16))
+        for ring in (meta.x, meta.w):
+            ring.idx = (ring.idx + 1) % ring.len
+        ctx.save_for_backward(x8b, w8b, scales)
+        return out.reshape(*x.shape[:-1], N)
+
+    @staticmethod
+    def backward(ctx, g):
+        M, N, K = ctx.mnk
+        g2 = _bf16(g.reshape(-1, N), "the output gradient")
+        need_x, need_w, need_b = ctx.needs_input_grad[:3]
+        dev = g.device
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if need_x else None
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if need_w else None
+        db = torch.empty(N, dtype=torch.bfloat16, device=dev) if need_b and ctx.has_bias else None
+        if dx is None and dw is None and db is None:
+            return None, None, None, None
+        i16 = (lambda t: None if t is None else t.view(torch.int16))
+        fmt, m = ctx.fmt_bwd, ctx.recipe.margin
+        if ctx.meta is None:
+            x2, w, scales = ctx.saved_tensors
+            fp8_linear_bwd(i16(g2), i16(x2), i16(w), M, N, K, fmt, True, m, scales, None,
+                           _workspace("bwd", dev, M, N, K), None, i16(dx), i16(dw), i16(db))
+        else:
+            x8b, w8b, scales = ctx.saved_tensors
+            rg, gi = ctx.meta.g, g2.view(torch.int16)
+            if not rg.initialized:
+                fp8_quantize(gi, fmt, ring=rg, margin=m)
+                rg.initialized = True
+            g8 = torch.empty(M * N, dtype=torch.uint8, device=dev)
+            sg = torch.empty(1, dtype=torch.float32, device=dev)
+            if db is not None:  # codes, fold and bias gradient from one read of g
+                cs_ws = torch.empty(fp8_colsum_workspace(M, N), dtype=torch.uint8, device=dev)
+                fp8_quantize_colsum(gi, M, N, fmt, rg.scale, g8, i16(db), cs_ws, ring=rg,
+                                    margin=m, scale_used=sg)
+            else:
+                fp8_quantize(gi, fmt, scale=rg.scale, out=g8, ring=rg, margin=m, scale_used=sg)
+            rg.idx = (rg.idx + 1) % rg.len
+            # dX[M][K] = g8[M][N] . w8b[N][K] (NN); dW[N][K] = g8^T . x8b[M][K] (TN)
+            pdx = (g8, w8b, fmt, 0, 0, M, K, N, N, K, 1, 0, 0, sg, scales[1:2], None, i16(dx))
+            pdw = (g8, x8b, fmt, 1, 0, N, K, M, N, K, 1, 0, 0, sg, scales[0:1], None, i16(dw))
+            if dx is not None and dw is not None:
+                fp8_mm_pair(pdx, pdw)
+            elif dx is not None:
+                fp8_mm(*pdx)
+            elif dw is not None:
+                fp8_mm(*pdw)
+        return (None if dx is None else dx.reshape(ctx.x_shape), dw, db, None)
+
+
+class _LinearFp8Weight(torch.autograd.Function):
+    """y = x w8^T * (sx * sw) + b with a pre-quantized weight (codes and a
+    caller-given step): x is quantized (ring or dynamic), the weight is
+    used as is ([CMP] fp8.py fp8_linear_forward, the fp8-weight branch)."""
+
+    @staticmethod
+    def forward(ctx, x, w8, w_scale, bias, cfg):
+        N, K = w8.shape
+        fmt = _FP8_DTYPES[w8.dtype]
+        if fmt != cfg.fp8_format.fwd():
+            raise ValueError("fp8_linear: the weight's fp8 format is not the forward format")
+        x2 = x.reshape(-1, K)
+        M = x2.shape[0]
+        dev = x.device
+        x8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sx = torch.empty(1, dtype=torch.float32, device=dev)
+        recipe = cfg.recipe
+        if recipe.dynamic:
+            scratch = Ring(1, dev)
+            fp8_quantize(x2.view(torch.int16), fmt, ring=scratch, margin=recipe.margin)
+            fp8_quantize(x2.view(torch.int16), fmt, scale=scratch.scale, out=x8,
+                         scale_used=sx)
+        else:
+            ring = _STATE.get_weight_meta(w8, recipe).x
+            if not ring.initialized:
+                fp8_quantize(x2.view(torch.int16), fmt, ring=ring, margin=recipe.margin)
+                ring.initialized = True
+            fp8_quantize(x2.view(torch.int16), fmt, scale=ring.scale, out=x8, ring=ring,
+                         margin=recipe.margin, scale_used=sx)
+            ring.idx = (ring.idx + 1) % ring.len
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fp8_mm(x8, w8.view(torch.uint8), fmt, 0, 1, M, N, K, K, K, 1, 0, 0, sx, w_scale,
+               None if bias is None else bias.view(torch.int16), out.view(torch.int16))
+        ctx.save_for_backward(w8, w_scale)
+        ctx.recipe, ctx.fmt_bwd, ctx.has_bias = recipe, cfg.fp8_format.bwd(), bias is not None
+        ctx.x_shape = x.shape
+        return out.reshape(*x.shape[:-1], N)
+
+    @staticmethod
+    def backward(ctx, g):
+        w8, w_scale = ctx.saved_tensors
+        N, K = w8.shape
+        g2 = _bf16(g.reshape(-1, N), "the output gradient")
+        M = g2.shape[0]
+        dev = g.device
+        dx = db = None
+        gi = g2.view(torch.int16)
+        if ctx.needs_input_grad[3] and ctx.has_bias:
+            db = torch.empty(N, dtype=torch.bfloat16, device=dev)
+            cs_ws = torch.empty(fp8_colsum_workspace(M, N), dtype=torch.uint8, device=dev)
+        if ctx.needs_input_grad[0]:
+            fmt = ctx.fmt_bwd
+            if fmt != _FP8_DTYPES[w8.dtype]:
+                raise NotImplementedError(
+                    "fp8_linear: an input gradient through a pre-quantized weight needs the "
+                    "weight in the backward format (use FP8Format.E4M3 for E4M3 weights)")
+            scratch = Ring(1, dev)
+            g8 = torch.empty((M, N), dtype=torch.uint8, device=dev)
+            sg = torch.empty(1, dtype=torch.float32, device=dev)
+            fp8_quantize(gi, fmt, ring=scratch, margin=ctx.recipe.margin)
+            if db is not None:  # the codes and the bias gradient from one read of g
+                fp8_quantize_colsum(gi, M, N, fmt, scratch.scale, g8, db.view(torch.int16),
+                                    cs_ws, scale_used=sg)
+            else:
+                fp8_quantize(gi, fmt, scale=scratch.scale, out=g8, scale_used=sg)
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+            # dX[M][K] = g8[M][N] . w8[N][K]  (NN)
+            fp8_mm(g8, w8.view(torch.uint8), fmt, 0, 0, M, K, N, N, K, 1, 0, 0, sg, w_scale,
+                   None, dx.view(torch.int16))
+            dx = dx.reshape(ctx.x_shape)
+        elif db is not None:
+            fp8_colsum(gi, M, N, db.view(torch.int16), cs_ws)
+        return dx, None, None, db, None
+
+
+def fp8_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+               w_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """``F.linear`` with the fp8 path when an fp8_autocast region (or the
+    default switch) enables it.  w: bf16 [N][K], or fp8 codes [N][K] with
+    their step ``w_scale`` (fp32 [1], device)."""
+    cfg = current_config()
+    if w.dtype in _FP8_DTYPES:
+        if w_scale is None:
+            raise ValueError("fp8_linear: a pre-quantized weight needs w_scale")
+        if not cfg.enabled:
+            raise ValueError("fp8_linear: a pre-quantized weight needs the fp8 path enabled")
+        return _LinearFp8Weight.apply(_bf16(x, "x"), w, w_scale, _bf16(bias, "bias"), cfg)
+    if not cfg.enabled:
+        return torch.nn.functional.linear(x, w, bias)
+    return _LinearFp8.apply(_bf16(x, "x"), _bf16(w, "w"), _bf16(bias, "bias"), cfg)
+
+
+class FP8Linear(torch.nn.Linear):
+    """nn.Linear whose forward takes the fp8 path inside fp8_autocast."""
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return fp8_linear(x, self.weight, self.bias)

@@ -1,0 +1,169 @@
+"""GPU parity of the fp8 policy / autograd layer: FP8Linear and fp8_linear
+under fp8_autocast give the bits of the C-ABI linear entry points driven by
+hand (delayed scaling in each format over four steps on [B, L, d] inputs,
+rings included),
+match the oracle (dynamic scaling; pre-quantized weights), and leave the
+plain path alone outside a region."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_util import check_gemm, from_dev_bf16, ring_state_equal, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_tensor_scaled_amd as f
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return f
+
+
+@pytest.fixture(scope="module")
+def fa(lib):
+    from fp8_tensor_scaled_amd import autocast
+    autocast.fp8_state().reset()
+    return autocast
+
+
+def bf16(bits, shape):
+    return to_dev_bf16(bits.ravel()).view(torch.bfloat16).reshape(shape)
+
+
+@pytest.mark.parametrize("fmt_name,frozen", [("HYBRID", False), ("E4M3", False),
+                                             ("E5M2", False), ("HYBRID", True)])
+def test_fp8linear_delayed_matches_entry_points(lib, fa, fmt_name, frozen):
+    """The delayed route (x and w read once per step, their backward codes
+    kept from the forward) against fp8_linear_fwd / _bwd: same bits, same
+    rings.  frozen: the weight takes no gradient (no x codes kept, no dW)."""
+    d = wl.train()
+    M, N, K = d["M"], d["N"], d["K"]
+    B = 2
+    fmt = fa.FP8Format[fmt_name]
+    layer = fa.FP8Linear(K, N).cuda().to(torch.bfloat16)
+    with torch.no_grad():
+        layer.weight.copy_(bf16(d["w"], (N, K)))
+        layer.bias.copy_(bf16(d["bias"], (N,)))
+    layer.weight.requires_grad_(not frozen)
+    fa.fp8_state().reset()
+    # the same steps by hand through the C-ABI
+    rx, rw, rg = lib.Ring(16), lib.Ring(16), lib.Ring(16)
+    fws = torch.zeros(lib.fp8_linear_fwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    bws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(2, dtype=torch.float32, device="cuda")
+    out = torch.empty(M * N, dtype=torch.int16, device="cuda")
+    dx, dw = (torch.empty(n, dtype=torch.int16, device="cuda") for n in (M * K, N * K))
+    db = torch.empty(N, dtype=torch.int16, device="cuda")
+    wd, bd = layer.weight.view(torch.int16), layer.bias.view(torch.int16)
+    with fa.fp8_autocast(recipe=fa.FP8Recipe(history_len=16), fp8_format=fmt):
+        for t in range(4):
+            x = bf16(d["x"][t], (B, M // B, K)).requires_grad_(True)
+            g = bf16(d["g"][t], (B, M // B, N))
+            layer.zero_grad()
+            y = layer(x)
+            y.backward(g)
+            xd, gd = x.detach().view(torch.int16), g.view(torch.int16)
+            lib.fp8_linear_fwd(xd, wd, bd, M, N, K, fmt.fwd(), False, 0, rx, rw, fws, sc, out)
+            lib.fp8_linear_bwd(gd, xd, wd, M, N, K, fmt.bwd(), False, 0, sc, rg, bws, None, dx,
+                               None if frozen else dw, db)
+            torch.cuda.synchronize()
+            assert y.shape == (B, M // B, N)
+            assert torch.equal(y.detach().reshape(-1).view(torch.int16), out), t
+            assert torch.equal(x.grad.reshape(-1).view(torch.int16), dx), t
+            if frozen:
+                assert layer.weight.grad is None
+            else:
+                assert torch.equal(layer.weight.grad.reshape(-1).view(torch.int16), dw), t
+            assert torch.equal(layer.bias.grad.view(torch.int16), db), t
+            meta = fa.fp8_state().get_weight_meta(layer.weight, fa.FP8Recipe(history_len=16))
+            for a, b in ((meta.x, rx), (meta.w, rw), (meta.g, rg)):
+                assert torch.equal(a.state, b.state) and a.idx == b.idx, t
+
+
+def test_fp8_linear_dynamic_vs_oracle(lib, fa, orc):
+    M, N, K = 256, 384, 512
+    xb = wl.normal_bf16((M, K), 1.0, 11)
+    wb = wl.normal_bf16((N, K), 0.02, 12)
+    gb = wl.normal_bf16((M, N), 1e-3, 13)
+    x = bf16(xb, (M, K)).requires_grad_(True)
+    w = bf16(wb, (N, K)).requires_grad_(True)
+    with fa.fp8_autocast(recipe=fa.FP8Recipe(dynamic=True), fp8_format=fa.FP8Format.HYBRID):
+        y = fa.fp8_linear(x, w)
+        y.backward(bf16(gb, (M, N)))
+    torch.cuda.synchronize()
+    rf = orc.linear_fwd(xb, wb, None, M, N, K, E4M3, True)
+    ad = orc.gemm_absdot(rf.x8, rf.w8, E4M3, False, True, M, N, K, rf.sx, rf.sw)
+    check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N), rf.out,
+               ad, K, "dynamic fwd")
+    rb = orc.linear_bwd(gb, xb, wb, M, N, K, E5M2, True)
+    w8b, x8b = orc.quantize(wb, E5M2, rb.sw), orc.quantize(xb, E5M2, rb.sx)
+    ad = orc.gemm_absdot(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+    check_gemm(from_dev_bf16(x.grad.reshape(-1).view(torch.int16)).reshape(M, K), rb.dx, ad, N,
+               "dynamic dX")
+    ad = orc.gemm_absdot(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+    check_gemm(from_dev_bf16(w.grad.reshape(-1).view(torch.int16)).reshape(N, K), rb.dw, ad, M,
+               "dynamic dW")
+
+
+def test_fp8_linear_prequantized_weight_vs_oracle(lib, fa, orc):
+    """E4M3 weight codes with their step, under FP8Format.E4M3: the forward
+    quantizes x only; dX uses the codes as they are."""
+    M, N, K = 128, 256, 320
+    xb = wl.normal_bf16((M, K), 1.0, 21)
+    wb = wl.normal_bf16((N, K), 0.02, 22)
+    gb = wl.normal_bf16((M, N), 1e-3, 23)
+    sw = orc.scale_from_peak(orc.amax(wb), E4M3)
+    w8 = orc.quantize(wb, E4M3, sw)
+    w8d = torch.from_numpy(w8).cuda().view(torch.float8_e4m3fn)
+    swd = torch.tensor([sw], dtype=torch.float32, device="cuda")
+    bb = wl.normal_bf16((N,), 0.1, 24)
+    x = bf16(xb, (M, K)).requires_grad_(True)
+    b = bf16(bb, (N,)).requires_grad_(True)
+    with fa.fp8_autocast(recipe=fa.FP8Recipe(dynamic=True), fp8_format=fa.FP8Format.E4M3):
+        y = fa.fp8_linear(x, w8d, b, w_scale=swd)
+        y.backward(bf16(gb, (M, N)))
+    torch.cuda.synchronize()
+    # bias gradient (fused with the g quantize here): the oracle's column sum
+    absg = np.abs(wl.bf16_bits_to_f32(gb).astype(np.float64)).sum(0)
+    check_gemm(from_dev_bf16(b.grad.view(torch.int16)), orc.colsum(gb, M, N), absg, M,
+               "prequant db fused")
+    sx = orc.scale_from_peak(orc.amax(xb), E4M3)
+    x8 = orc.quantize(xb, E4M3, sx)
+    ref = orc.gemm(x8, w8, E4M3, False, True, M, N, K, sx, sw, bb)
+    ad = orc.gemm_absdot(x8, w8, E4M3, False, True, M, N, K, sx, sw)
+    check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N), ref, ad,
+               K, "prequant fwd")
+    sg = orc.scale_from_peak(orc.amax(gb), E4M3)
+    g8 = orc.quantize(gb, E4M3, sg)
+    ref = orc.gemm(g8, w8, E4M3, False, False, M, K, N, sg, sw)
+    ad = orc.gemm_absdot(g8, w8, E4M3, False, False, M, K, N, sg, sw)
+    check_gemm(from_dev_bf16(x.grad.reshape(-1).view(torch.int16)).reshape(M, K), ref, ad, N,
+               "prequant dX")
+    # bias gradient alone (x without grad: no g quantize)
+    b.grad = None
+    with fa.fp8_autocast(recipe=fa.FP8Recipe(dynamic=True), fp8_format=fa.FP8Format.E4M3):
+        fa.fp8_linear(x.detach(), w8d, b, w_scale=swd).backward(bf16(gb, (M, N)))
+    torch.cuda.synchronize()
+    check_gemm(from_dev_bf16(b.grad.view(torch.int16)), orc.colsum(gb, M, N), absg, M,
+               "prequant db alone")
+    with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+        with pytest.raises(NotImplementedError):
+            x2 = bf16(xb, (M, K)).requires_grad_(True)
+            fa.fp8_linear(x2, w8d, w_scale=swd).backward(bf16(gb, (M, N)))
+
+
+def test_masks_and_plain_path(lib, fa):
+    M, N, K = 64, 96, 128
+    x = torch.randn(M, K, device="cuda").bfloat16().requires_grad_(True)
+    w = torch.randn(N, K, device="cuda").bfloat16() * 0.05
+    with fa.fp8_autocast(recipe=fa.FP8Recipe(dynamic=True)):
+        y = fa.fp8_linear(x, w)   # no bias, w without grad: only dX
+        y.sum().backward()
+    assert x.grad is not None and x.grad.shape == (M, K) and w.grad is None
+    ref = torch.nn.functional.linear(x.detach(), w)
+    assert torch.equal(fa.fp8_linear(x.detach(), w), ref)  # outside a region: plain linear

@@ -391,3 +391,76 @@ void orc_colsum(const uint16_t* g, int64_t M, int64_t N, uint16_t* db)
         db[j] = orc_bf16_from_f64(acc);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * GEMM with an fp8 bias and / or an fp8 output.  [CMP] ops/fp8.py, the
+ * removed fp8_gemm custom op (out_dtype 1: an fp8 E4M3 output that needs
+ * out_scale, the quantization step of the output); [LOG1] the FP8Params
+ * bias becomes untyped with a bias_scale beside it (no scale: a bf16 bias;
+ * a scale: fp8 codes, dequantized after the operand scaling and before any
+ * output quantization).
+ *
+ *   bv[j] = bias_fp8 ? fp32( dec_fmt(bias[j]) * bias_scale ) : bf16 bias[j]
+ *   y     = (sum_k A[b,i,k] * B[b,k,j]) * fp32(sa*sb) + bv[j]     (fp64)
+ *   out   = bf16(y)                                  out_type 0
+ *           enc_fo( fp32( fp32(y) * fp32(1/out_scale) ) )   out_type 1, 2
+ * with fo = E4M3 for out_type 1 and E5M2 for out_type 2; the codes are the
+ * cast's: nearest even, saturating at the format's largest value.  The fp8
+ * bias uses the operands' format.  Evaluated at listed coordinates (all of
+ * them for a full product); out holds uint16 bf16 bits or uint8 codes; yval
+ * (nullable) receives y, absdot (nullable) sum_k |A*B| * |s|.
+ * ---------------------------------------------------------------------- */
+uint8_t orc_out_code(double y, int out_fmt, float out_scale)
+{
+    const float r = orc_multiplier(out_scale); /* fp32(1 / out_scale) */
+    const float prod = (float)y * r;           /* two fp32 roundings */
+    return orc_encode(prod, out_fmt);
+}
+
+void orc_out_code_array(const double* y, int64_t n, int out_fmt, float out_scale,
+                        uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_out_code(y[i], out_fmt, out_scale);
+}
+
+void orc_gemm_ex(const uint8_t* A, const uint8_t* B, int fmt, int trans_a, int trans_b,
+                 int64_t K, int64_t lda, int64_t ldb, int64_t stride_a, int64_t stride_b,
+                 float sa, float sb, const void* bias, int bias_fp8, float bias_scale,
+                 int out_type, float out_scale, int64_t n_samples, const int64_t* sb_idx,
+                 const int64_t* si_idx, const int64_t* sj_idx, void* out, double* yval,
+                 double* absdot)
+{
+    dec_tables();
+    const float s = sa * sb;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_samples; ++t) {
+        const int64_t b = sb_idx[t], i = si_idx[t], j = sj_idx[t];
+        const double acc = gemm_one(A, B, fmt, trans_a, trans_b, K, lda, ldb, b, i, j,
+                                    stride_a, stride_b);
+        double y = acc * (double)s;
+        if (bias) {
+            float bv;
+            if (bias_fp8)
+                bv = g_dec[fmt][((const uint8_t*)bias)[j]] * bias_scale; /* fp32 product */
+            else
+                bv = orc_bf16_to_f32(((const uint16_t*)bias)[j]);
+            y += (double)bv;
+        }
+        if (out_type == 0)
+            ((uint16_t*)out)[t] = orc_bf16_from_f64(y);
+        else
+            ((uint8_t*)out)[t] = orc_out_code(y, out_type == 1 ? FMT_E4M3 : FMT_E5M2, out_scale);
+        if (yval) yval[t] = y;
+        if (absdot) {
+            const uint8_t* Ab = A + b * stride_a;
+            const uint8_t* Bb = B + b * stride_b;
+            double m = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t ca = trans_a ? Ab[k * lda + i] : Ab[i * lda + k];
+                const uint8_t cb = trans_b ? Bb[j * ldb + k] : Bb[k * ldb + j];
+                m += fabs((double)g_dec[fmt][ca] * (double)g_dec[fmt][cb]);
+            }
+            absdot[t] = m * fabs((double)s);
+        }
+    }
+}

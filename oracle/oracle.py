@@ -24,6 +24,11 @@ Readings of points the pages leave open (each listed in the design notes):
   * HYBRID: forward E4M3 (x, w), backward E5M2 (g, and x, w re-quantized in
     E5M2).  Delayed backward reuses the forward's sx, sw; dynamic backward
     re-measures them in the backward format, as the pages' backward does.
+  * fp8 GEMM output: out_scale is the output's step (the removed op calls it
+    the quantization step of the output); the codes follow the quantize's
+    convention, fp32(y) times the fp32 reciprocal of the step, then the
+    saturating cast.  An fp8 bias is in the operands' format; its value is
+    the fp32 product of the decoded code and bias_scale.
 """
 
 from __future__ import annotations
@@ -97,6 +102,11 @@ def _load():
     lib.orc_gemm_absdot.argtypes = [P, P, I, I, I, I64, I64, I64, I64, I64, I64, I64,
                                     I64, F, F, P]
     lib.orc_colsum.argtypes = [P, I64, I64, P]
+    lib.orc_out_code.argtypes = [ctypes.c_double, I, F]
+    lib.orc_out_code.restype = ctypes.c_uint8
+    lib.orc_out_code_array.argtypes = [P, I64, I, F, P]
+    lib.orc_gemm_ex.argtypes = [P, P, I, I, I, I64, I64, I64, I64, I64, F, F, P, I, F, I, F,
+                                I64, P, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -285,6 +295,65 @@ def gemm_absdot(a, b, fmt, trans_a, trans_b, M, N, K, sa, sb, batch=1,
                             lda, ldb, batch, stride_a, stride_b, float(np.float32(sa)),
                             float(np.float32(sb)), _ptr(out))
     return out if batch > 1 else out[0]
+
+
+# Output types of gemm_ex: bf16, or fp8 codes of E4M3 / E5M2.
+OUT_BF16, OUT_E4M3, OUT_E5M2 = 0, 1, 2
+
+
+def out_codes(y: np.ndarray, out_type: int, out_scale) -> np.ndarray:
+    """fp8 output codes of fp64 values y: enc(fp32(fp32(y) * fp32(1/out_scale)))
+    in E4M3 (out_type OUT_E4M3) or E5M2 (OUT_E5M2), nearest even, saturating."""
+    assert out_type in (OUT_E4M3, OUT_E5M2)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape, np.uint8)
+    _load().orc_out_code_array(_ptr(y), y.size, 0 if out_type == OUT_E4M3 else 1,
+                               float(np.float32(out_scale)), _ptr(out))
+    return out
+
+
+def gemm_ex(a, b, fmt, trans_a, trans_b, M, N, K, sa, sb, bias=None, bias_scale=None,
+            out_type=OUT_BF16, out_scale=None, samples=None, batch=1, stride_a=None,
+            stride_b=None, lda=None, ldb=None):
+    """GEMM with an fp8 bias (``bias`` uint8 codes of ``fmt`` and a float
+    ``bias_scale``) or a bf16 one (uint16 bits, no scale), and a bf16 or fp8
+    output ([CMP] the removed fp8_gemm op; [LOG1] bias_scale):
+
+        y   = sum_k A B * fp32(sa*sb) + bias value   (fp64)
+        out = bf16(y), or enc(fp32(fp32(y) * fp32(1/out_scale)))
+
+    At ``samples`` = (bi, i, j) coordinates, else at every output in
+    [batch][M][N] order.  Returns (out, y, absdot) as flat arrays."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    if lda is None:
+        lda = M if trans_a else K
+    if ldb is None:
+        ldb = K if trans_b else N
+    if stride_a is None:
+        stride_a = M * K
+    if stride_b is None:
+        stride_b = K * N
+    if samples is None:
+        bi, ii, jj = (np.ascontiguousarray(v.ravel(), dtype=np.int64)
+                      for v in np.indices((batch, M, N)))
+    else:
+        bi, ii, jj = (np.ascontiguousarray(v, dtype=np.int64) for v in samples)
+    n = bi.size
+    bias_fp8 = bias_scale is not None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint8 if bias_fp8 else np.uint16)
+    assert out_type == OUT_BF16 or out_scale is not None, "an fp8 output needs out_scale"
+    out = np.empty(n, np.uint16 if out_type == OUT_BF16 else np.uint8)
+    y = np.empty(n, np.float64)
+    absdot = np.empty(n, np.float64)
+    _load().orc_gemm_ex(_ptr(a), _ptr(b), fmt, int(trans_a), int(trans_b), K, lda, ldb,
+                        stride_a, stride_b, float(np.float32(sa)), float(np.float32(sb)),
+                        _ptr(bias), int(bias_fp8),
+                        float(np.float32(bias_scale if bias_fp8 else 0.0)), out_type,
+                        float(np.float32(out_scale if out_scale is not None else 1.0)), n,
+                        _ptr(bi), _ptr(ii), _ptr(jj), _ptr(out), _ptr(y), _ptr(absdot))
+    return out, y, absdot
 
 
 def colsum(g: np.ndarray, M: int, N: int) -> np.ndarray:

@@ -410,6 +410,128 @@ def test_gemm_sampled_matches_full(orc):
     assert np.allclose(ad, ref, rtol=1e-12, atol=0)
 
 
+# --------------------------------------------------------------------------
+# GEMM with an fp8 bias and / or an fp8 output ([CMP] the removed fp8_gemm
+# op's out_dtype / out_scale; [LOG1] bias_scale)
+# --------------------------------------------------------------------------
+
+def _torch_gemm_ex_ref(A, B, fmt, sa, sb, bias, bias_scale, out_type, out_scale):
+    """Independent composition: torch float8 decode, float64 matmul, the
+    bias value (torch-decoded code times its step in fp32, or bf16), then
+    for an fp8 output fp32(y) times the fp32 reciprocal of the step and
+    torch's clamped float8 cast.  Returns (codes or None, y)."""
+    a = torch.from_numpy(torch_decode(A, fmt))
+    b = torch.from_numpy(torch_decode(B, fmt))
+    s = float(np.float32(sa) * np.float32(sb))
+    y = (torch.matmul(a, b) * s).numpy()
+    if bias is not None:
+        if bias_scale is not None:
+            bv = torch_decode(bias, fmt).astype(np.float32) * np.float32(bias_scale)
+        else:
+            bv = wl.bf16_bits_to_f32(bias)
+        y = y + bv.astype(np.float64)
+    if out_type == 0:
+        return None, y
+    r = np.float32(1.0) / np.float32(out_scale)
+    fo = E4M3 if out_type == 1 else E5M2
+    return torch_encode(y.astype(np.float32) * r, fo), y
+
+
+@pytest.mark.parametrize("trans_a,trans_b", [(0, 1), (0, 0), (1, 0)])
+def test_gemm_ex_bf16_path_is_gemm(orc, trans_a, trans_b):
+    """bf16 bias and bf16 output: exactly the pinned orc.gemm."""
+    fmt = E4M3
+    M, N, K = 7, 9, 33
+    A = wl.random_codes((M, K), fmt, 81)
+    B = wl.random_codes((K, N), fmt, 82)
+    bias = wl.normal_bf16((N,), 0.5, 83)
+    ref = orc.gemm(_store(A, trans_a), _store(B, trans_b), fmt, bool(trans_a), bool(trans_b),
+                   M, N, K, 0.5, 0.125, bias)
+    out, _, _ = orc.gemm_ex(_store(A, trans_a), _store(B, trans_b), fmt, bool(trans_a),
+                            bool(trans_b), M, N, K, 0.5, 0.125, bias)
+    assert np.array_equal(out.reshape(M, N), ref)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("out_type", [1, 2])
+@pytest.mark.parametrize("bias_kind", ["none", "bf16", "fp8"])
+def test_gemm_ex_fp8_out_vs_torch(orc, fmt, out_type, bias_kind):
+    """Brute force on small shapes against the torch composition; operands
+    of moderate range so that every fp64 sum is exact; out_scale small
+    enough that some outputs saturate."""
+    seed = 900 + 10 * fmt + out_type
+    for M, N, K in ((1, 1, 1), (3, 5, 4), (6, 7, 8), (4, 16, 32)):
+        seed += 1
+        A = orc.quantize(wl.normal_bf16((M, K), 1.0, seed), fmt, 1.0)
+        B = orc.quantize(wl.normal_bf16((K, N), 1.0, seed + 1), fmt, 1.0)
+        bias = bias_scale = None
+        if bias_kind == "bf16":
+            bias = wl.normal_bf16((N,), 2.0, seed + 2)
+        elif bias_kind == "fp8":
+            bias = orc.quantize(wl.normal_bf16((N,), 2.0, seed + 2), fmt, 1.0)
+            bias_scale = np.float32(0.375)
+        sa, sb = np.float32(0.75), np.float32(1.5)
+        for out_scale in (np.float32(1.0 / 64), np.float32(0.01), np.float32(3.0)):
+            out, y, _ = orc.gemm_ex(A, B, fmt, False, False, M, N, K, sa, sb, bias, bias_scale,
+                                    out_type, out_scale)
+            ref, yref = _torch_gemm_ex_ref(A, B, fmt, sa, sb, bias, bias_scale, out_type,
+                                           out_scale)
+            assert np.array_equal(y, yref.ravel()), (M, N, K)
+            assert np.array_equal(out, ref.ravel()), (M, N, K, out_scale)
+            assert np.array_equal(orc.out_codes(y, out_type, out_scale), out)
+
+
+def test_gemm_ex_out_step_closed_form(orc):
+    """out_scale is the output's step: y = 3 with step 0.5 encodes 6.0
+    (E4M3 0 1001 100 = 0x4C), with step 2 encodes 1.5 (0x3C); a bf16 bias
+    of -1 and an fp8 bias code 0x38 (1.0) with step 0.5 both add after the
+    operand scaling and before the output's rounding; y = 1000 saturates at
+    448 (0x7E) and y = -1e6 at -448 (0xFE)."""
+    fmt = E4M3
+    A = np.array([[0x38]], np.uint8)   # 1.0
+    B = np.array([[0x40]], np.uint8)   # 2.0
+    # y = 1 * 2 * (1.5 * 1) = 3
+    out, y, _ = orc.gemm_ex(A, B, fmt, False, False, 1, 1, 1, 1.5, 1.0, out_type=1,
+                            out_scale=0.5)
+    assert y[0] == 3.0 and out[0] == 0x4C
+    out, _, _ = orc.gemm_ex(A, B, fmt, False, False, 1, 1, 1, 1.5, 1.0, out_type=1,
+                            out_scale=2.0)
+    assert out[0] == 0x3C
+    bneg = wl.f32_to_bf16_bits(np.array([-1.0], np.float32))
+    out, y, _ = orc.gemm_ex(A, B, fmt, False, False, 1, 1, 1, 1.5, 1.0, bneg, out_type=1,
+                            out_scale=0.5)
+    assert y[0] == 2.0 and out[0] == 0x48                      # 4.0
+    out, y, _ = orc.gemm_ex(A, B, fmt, False, False, 1, 1, 1, 1.5, 1.0,
+                            np.array([0x38], np.uint8), 0.5, out_type=1, out_scale=0.5)
+    assert y[0] == 3.5 and out[0] == 0x4E                      # 7.0
+    assert orc.out_codes(np.array([1000.0, -1e6]), 1, 1.0).tolist() == [0x7E, 0xFE]
+    assert orc.out_codes(np.array([1e9, -1e9]), 2, 1.0).tolist() == [0x7B, 0xFB]
+
+
+def test_planted_mistakes_fp8_out(orc):
+    """Slips in the extended epilogue change the oracle's codes."""
+    fmt = E4M3
+    M, N, K = 4, 6, 8
+    A = orc.quantize(wl.normal_bf16((M, K), 1.0, 91), fmt, 1.0)
+    B = orc.quantize(wl.normal_bf16((K, N), 1.0, 92), fmt, 1.0)
+    b8 = orc.quantize(wl.normal_bf16((N,), 4.0, 93), fmt, 1.0)
+    bs, sa, sb, so = np.float32(0.75), np.float32(0.5), np.float32(1.25), np.float32(0.0625)
+    out, _, _ = orc.gemm_ex(A, B, fmt, False, False, M, N, K, sa, sb, b8, bs, 1, so)
+    Ad, Bd = torch_decode(A, fmt), torch_decode(B, fmt)
+    bv = torch_decode(b8, fmt).astype(np.float32) * bs
+    s = float(sa * sb)
+    r = np.float32(1.0) / so
+    variants = {
+        "step multiplied, not divided": (Ad @ Bd * s + bv).astype(np.float32) * so,
+        "bias scale dropped": (Ad @ Bd * s + torch_decode(b8, fmt)).astype(np.float32) * r,
+        "bias added after the output scaling": (Ad @ Bd * s).astype(np.float32) * r + bv,
+        "operand scale dropped": (Ad @ Bd + bv).astype(np.float32) * r,
+    }
+    for name, v in variants.items():
+        assert not np.array_equal(torch_encode(np.asarray(v, np.float32), E4M3).ravel(),
+                                  out), name
+
+
 def test_colsum_vs_torch(orc):
     g = wl.normal_bf16((300, 37), 1e-3, 41)
     ours = orc.colsum(g, 300, 37)

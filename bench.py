@@ -320,7 +320,16 @@ def components(f, torch):
                                                 bias, out), 50)
     res["gemm_nt_4096"] = dict(us=round(ms * 1e3, 2),
                                tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
-    del a8, b8, out
+    # the same product with an fp8 bias and an E4M3 output (fp8_mm_ex)
+    b8_bias = torch.randint(0, 120, (n,), dtype=torch.uint8, device=dev)
+    out8 = torch.empty(n * n, dtype=torch.uint8, device=dev)
+    mm_ex = (lambda i: f.fp8_mm_ex(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s, b8_bias,
+                                   s, f.OUT_E4M3, s, out8))
+    time_kernel(torch, mm_ex, 20)  # first launches of this kernel: not timed
+    ms = time_kernel(torch, mm_ex, 100)
+    res["gemm_nt_4096_fp8_bias_e4m3_out"] = dict(
+        us=round(ms * 1e3, 2), tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
+    del a8, b8, out, out8
     # 8192^3 NT + bias
     n = 8192
     a8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)

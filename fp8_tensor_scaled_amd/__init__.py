@@ -17,8 +17,8 @@ import torch
 __all__ = [
     "E4M3", "E5M2", "FMT_MAX", "IN_BF16", "IN_F16", "IN_F32", "Ring", "library_path",
     "fp8_quantize", "fp8_quantize_ex", "fp8_quantize_t", "fp8_quantize2",
-    "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_pair", "fp8_colsum", "fp8_colsum_workspace",
-    "fp8_quantize_colsum",
+    "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_ex", "fp8_mm_pair", "fp8_colsum",
+    "fp8_colsum_workspace", "fp8_quantize_colsum", "OUT_BF16", "OUT_E4M3", "OUT_E5M2",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
     "fp8_linear_bwd_workspace", "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset",
     "EXPORTED_SYMBOLS",
@@ -35,8 +35,8 @@ EXPORTED_SYMBOLS = (
     "fp8_ring_state_floats", "fp8_format_max", "fp8_quantize", "fp8_quantize_ex",
     "fp8_quantize_t", "fp8_quantize2",
     "fp8_scale_ring_finalize",
-    "fp8_mm", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum", "fp8_quantize_colsum",
-    "fp8_linear_fwd_workspace",
+    "fp8_mm", "fp8_mm_ex", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum",
+    "fp8_quantize_colsum", "fp8_linear_fwd_workspace",
     "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
     "fp8_linear_bwd_workspace", "fp8_linear_bwd", "fp8_last_error", "fp8_version",
 )
@@ -80,6 +80,8 @@ def _load() -> ctypes.CDLL:
         "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
         "fp8_mm": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P,
                          P, P]),
+        "fp8_mm_ex": (I32, [P, P, I32, I32, I32, I64, I64, I64, I64, I64, I64, I64, I64, P, P,
+                            P, P, I32, P, P, P]),
         "fp8_mm_pair": (I32, [ctypes.POINTER(_MmArgs), ctypes.POINTER(_MmArgs), P]),
         "fp8_colsum_workspace": (S, [I64, I64]),
         "fp8_colsum": (I32, [P, I64, I64, P, P, S, P]),
@@ -260,6 +262,25 @@ def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt: int, trans_a: int, trans_b: in
                      stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias), _ptr(out),
                      _stream(stream))
     _check(st, "fp8_mm")
+
+
+# Output types of fp8_mm_ex (fp8_out_t).
+OUT_BF16, OUT_E4M3, OUT_E5M2 = 0, 1, 2
+
+
+def fp8_mm_ex(a: torch.Tensor, b: torch.Tensor, fmt: int, trans_a: int, trans_b: int, m: int,
+              n: int, k: int, lda: int, ldb: int, batch: int, stride_a: int, stride_b: int,
+              scale_a: torch.Tensor, scale_b: torch.Tensor, bias: torch.Tensor | None,
+              bias_scale: torch.Tensor | None, out_type: int, out_scale: torch.Tensor | None,
+              out: torch.Tensor, stream=None) -> None:
+    """fp8_mm with an fp8 bias (codes of ``fmt`` and their step ``bias_scale``)
+    and / or an fp8 output (``out_type`` OUT_E4M3 / OUT_E5M2, step
+    ``out_scale``); see fp8lin.h."""
+    st = _lib.fp8_mm_ex(_ptr(a), _ptr(b), fmt, trans_a, trans_b, m, n, k, lda, ldb, batch,
+                        stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias),
+                        _ptr(bias_scale), out_type, _ptr(out_scale), _ptr(out),
+                        _stream(stream))
+    _check(st, "fp8_mm_ex")
 
 
 def _mm_args(a, b, fmt, trans_a, trans_b, m, n, k, lda, ldb, batch, stride_a, stride_b,

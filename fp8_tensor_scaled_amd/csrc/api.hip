@@ -402,6 +402,50 @@ fp8_status_t fp8_mm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t t
     return FP8_OK;
 }
 
+fp8_status_t fp8_mm_ex(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t trans_a,
+                       int32_t trans_b, int64_t m, int64_t n, int64_t k, int64_t lda,
+                       int64_t ldb, int64_t batch, int64_t stride_a, int64_t stride_b,
+                       const float* scale_a, const float* scale_b, const void* bias,
+                       const float* bias_scale, fp8_out_t out_type, const float* out_scale,
+                       void* out, hipStream_t stream) {
+    g_err[0] = 0;
+    if (out_type != FP8_OUT_BF16 && out_type != FP8_OUT_E4M3 && out_type != FP8_OUT_E5M2)
+        return fail(FP8_EINVAL, "fp8_mm_ex: unsupported output type %d", (int)out_type);
+    if (out_type == FP8_OUT_BF16 && out_scale)
+        return fail(FP8_EINVAL, "fp8_mm_ex: out_scale given for a bf16 output");
+    if (out_type != FP8_OUT_BF16 && !out_scale)
+        return fail(FP8_EINVAL, "fp8_mm_ex: an fp8 output needs out_scale");
+    if (bias_scale && !bias) return fail(FP8_EINVAL, "fp8_mm_ex: bias_scale without a bias");
+    fp8_mm_args_t x{};
+    x.a = a;
+    x.b = b;
+    x.fmt = fmt;
+    x.trans_a = trans_a;
+    x.trans_b = trans_b;
+    x.m = m;
+    x.n = n;
+    x.k = k;
+    x.lda = lda;
+    x.ldb = ldb;
+    x.batch = batch;
+    x.stride_a = stride_a;
+    x.stride_b = stride_b;
+    x.scale_a = scale_a;
+    x.scale_b = scale_b;
+    x.bias = static_cast<const uint16_t*>(bias);
+    x.out = static_cast<uint16_t*>(out);
+    fp8lin::GemmLaunch g;
+    fp8_status_t st = check_mm("fp8_mm_ex", x, g);
+    if (st) return st;
+    g.bias_scale = bias_scale;
+    g.out_q = out_type == FP8_OUT_BF16 ? -1 : (out_type == FP8_OUT_E4M3 ? 0 : 1);
+    g.out_scale = out_scale;
+    if ((st = check_device())) return st;
+    hipError_t e = fp8lin::launch_gemm(g, stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return FP8_OK;
+}
+
 fp8_status_t fp8_mm_pair(const fp8_mm_args_t* p0, const fp8_mm_args_t* p1, hipStream_t stream) {
     g_err[0] = 0;
     if (!p0 || !p1) return fail(FP8_EINVAL, "fp8_mm_pair: NULL argument block");

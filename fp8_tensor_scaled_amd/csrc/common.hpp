@@ -75,6 +75,24 @@ __device__ __forceinline__ uint8_t cvt1(float a) {
     return (uint8_t)(w & 0xff);
 }
 
+// One fp8 code (byte SEL of w) -> fp32, exact: v_cvt_f32_{fp8,bf8}, which
+// decode the OCP encodings on gfx950.
+template <int FMT, int SEL>
+__device__ __forceinline__ float dec8(uint32_t w) {
+    if constexpr (FMT)
+        return __builtin_amdgcn_cvt_f32_bf8((int)w, SEL);
+    else
+        return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// cvt4 / cvt1 with the format chosen at run time (0 E4M3, 1 E5M2).
+__device__ __forceinline__ uint32_t cvt4_rt(int fmt, float a, float b, float c, float d) {
+    return fmt ? cvt4<1>(a, b, c, d) : cvt4<0>(a, b, c, d);
+}
+__device__ __forceinline__ uint8_t cvt1_rt(int fmt, float a) {
+    return fmt ? cvt1<1>(a) : cvt1<0>(a);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

@@ -2,7 +2,11 @@
 //
 // Method (AstrAI compare view 3e57cc8...main: astrai/extension/ops/fp8.py
 // mm_fp8; csrc/kernels/fp8/common.h operand layout tags and batch strides;
-// csrc/kernels/fp8/gemm/epilogue.cuh bias + single bf16 rounding).
+// csrc/kernels/fp8/gemm/epilogue.cuh bias + single bf16 rounding).  The
+// extended epilogue (the removed fp8_gemm op's fp8 output with its step;
+// the commit log's bias_scale for an fp8 bias) takes the bias as fp8 codes
+// times their step and/or writes fp8 codes of the value times the fp32
+// reciprocal of the output step, saturating.
 //
 // This file holds the dispatcher and the general kernel, which accepts any
 // layout, size, stride and alignment: every lane gathers its MFMA operand
@@ -23,8 +27,11 @@ struct GenericParams {
     const uint8_t* b;
     const float* sa;
     const float* sb;
-    const uint16_t* bias;
-    uint16_t* out;
+    const void* bias;
+    const float* bias_scale;  // non-null: bias holds fp8 codes of the operands' format
+    void* out;
+    int out_q;                // -1 bf16 output, else the fp8 output format
+    const float* out_scale;
     int64_t m, n, k, lda, ldb;
     int64_t stride_a, stride_b;
     int trans_a, trans_b;
@@ -67,12 +74,23 @@ __global__ __launch_bounds__(kGenThreads) void gemm_generic_kernel(GenericParams
     }
     const int64_t oc = col0 + lane % 16;
     if (oc < p.n) {
-        const float bias = p.bias ? bf16_to_f32(p.bias[oc]) : 0.0f;
+        float bias = 0.0f;
+        if (p.bias) {
+            bias = p.bias_scale
+                       ? dec8<FMT, 0>(static_cast<const uint8_t*>(p.bias)[oc]) * (*p.bias_scale)
+                       : bf16_to_f32(static_cast<const uint16_t*>(p.bias)[oc]);
+        }
+        const float rq = p.out_q >= 0 ? __fdiv_rn(1.0f, *p.out_scale) : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t orow = row0 + 4 * (lane / 16) + i;
-            if (orow < p.m)
-                p.out[(bz * p.m + orow) * p.n + oc] = f32_to_bf16(fmaf(acc[i], s, bias));
+            if (orow >= p.m) continue;
+            const int64_t o = (bz * p.m + orow) * p.n + oc;
+            const float v = fmaf(acc[i], s, bias);
+            if (p.out_q < 0)
+                static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+            else
+                static_cast<uint8_t*>(p.out)[o] = cvt1_rt(p.out_q, v * rq);
         }
     }
     }
@@ -85,7 +103,10 @@ static hipError_t launch_generic(const GemmLaunch& g, hipStream_t stream) {
     p.sa = g.scale_a;
     p.sb = g.scale_b;
     p.bias = g.bias;
+    p.bias_scale = g.bias_scale;
     p.out = g.out;
+    p.out_q = g.out_q;
+    p.out_scale = g.out_scale;
     p.m = g.m;
     p.n = g.n;
     p.k = g.k;

@@ -19,7 +19,9 @@
 //    of the chunk's 64-k steps (k is split across the waves), so every
 //    wave keeps a partial 32 x 32 tile.
 //  * The partial tiles are summed through LDS in a fixed order, then
-//    scaled, biased and rounded once to bf16.
+//    scaled, biased and rounded once to bf16 -- or, with the extended
+//    epilogue, biased by fp8 codes times their step and / or written as fp8
+//    codes of the value times the reciprocal of the output step.
 
 #include "common.hpp"
 #include "gemm_skinny.hpp"
@@ -40,8 +42,11 @@ struct SkinnyParams {
     const uint8_t* b;
     const float* sa;
     const float* sb;
-    const uint16_t* bias;
-    uint16_t* out;
+    const void* bias;         // bf16 [n], or fp8 codes [n] when bias_scale is set
+    const float* bias_scale;  // extended epilogue only
+    void* out;                // bf16, or fp8 codes of format out_q when out_q >= 0
+    int out_q;
+    const float* out_scale;
     int64_t m, n, k, lda, ldb, stride_a, stride_b;
     int tiles_n;
     int xcd_remap;
@@ -88,8 +93,8 @@ __device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, v16f acc) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc, FMT, FMT, 0, 0, 0, 0);
 }
 
-// MT = 32-row groups of A (1 when m <= 32, else 2).
-template <int FMT, int MT>
+// MT = 32-row groups of A (1 when m <= 32, else 2); EXT = extended epilogue.
+template <int FMT, int MT, bool EXT>
 __global__ __launch_bounds__(kWaves * 64, 1) void gemm_skinny_kernel(SkinnyParams p) {
     // A chunk is [32*MT A rows + 32 B rows][512 B]; the 16-byte pieces of row
     // r are stored at piece index c ^ (r % 16), so the 16 rows a
@@ -116,11 +121,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gemm_skinny_kernel(SkinnyParam
     const float sc = (*p.sa) * (*p.sb);
     const int c4 = 4 * (threadIdx.x % (kCols / 4));  // epilogue columns of this thread
     float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float rq = 0.0f;  // reciprocal of the fp8 output's step
     if (p.bias) {
+        if (EXT && p.bias_scale) {
+            const float bs = *p.bias_scale;
+            const uint8_t* bp = static_cast<const uint8_t*>(p.bias);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (n0 + c4 + c < p.n) bias[c] = bf16_to_f32(p.bias[n0 + c4 + c]);
+            for (int c = 0; c < 4; ++c)
+                if (n0 + c4 + c < p.n) bias[c] = dec8<FMT, 0>(bp[n0 + c4 + c]) * bs;
+        } else {
+            const uint16_t* bp = static_cast<const uint16_t*>(p.bias);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (n0 + c4 + c < p.n) bias[c] = bf16_to_f32(bp[n0 + c4 + c]);
+        }
     }
+    if (EXT && p.out_q >= 0) rq = __fdiv_rn(1.0f, *p.out_scale);
 
     const v4i ra = rsrc_of(p.a + (int64_t)bz * p.stride_a);
     const v4i rb = rsrc_of(p.b + (int64_t)bz * p.stride_b + n0 * p.ldb);
@@ -223,7 +239,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gemm_skinny_kernel(SkinnyParam
     __syncthreads();
 
     // Sum the partials in a fixed order, scale, add bias, round once.
-    uint16_t* out = p.out + (int64_t)bz * p.m * p.n;
+    uint16_t* out = static_cast<uint16_t*>(p.out) + (int64_t)bz * p.m * p.n;
+    uint8_t* out8 = static_cast<uint8_t*>(p.out) + (int64_t)bz * p.m * p.n;
     constexpr int kOut = kRowsA * kCols / 4;  // 4-column groups of the tile
     for (int t = threadIdx.x; t < kOut; t += kWaves * 64) {
         const int row = t / (kCols / 4);  // column group c4: t % 8 == threadIdx.x % 8
@@ -234,6 +251,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gemm_skinny_kernel(SkinnyParam
             s += *reinterpret_cast<const v4f*>(red + w * (kRowsA * kRedStride) +
                                                row * kRedStride + c4);
         const int64_t gn = n0 + c4;
+        if (EXT && p.out_q >= 0) {
+            const uint32_t w = cvt4_rt(p.out_q, fmaf(s[0], sc, bias[0]) * rq,
+                                       fmaf(s[1], sc, bias[1]) * rq, fmaf(s[2], sc, bias[2]) * rq,
+                                       fmaf(s[3], sc, bias[3]) * rq);
+            uint8_t* dst = out8 + (int64_t)row * p.n + gn;
+            if (gn + 3 < p.n && ((reinterpret_cast<uintptr_t>(dst) & 3) == 0)) {
+                *reinterpret_cast<uint32_t*>(dst) = w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (gn + c < p.n) dst[c] = (uint8_t)(w >> (8 * c));
+            }
+            continue;
+        }
         const uint32_t w0 = f32x2_to_bf16x2(fmaf(s[0], sc, bias[0]), fmaf(s[1], sc, bias[1]));
         const uint32_t w1 = f32x2_to_bf16x2(fmaf(s[2], sc, bias[2]), fmaf(s[3], sc, bias[3]));
         uint16_t* dst = out + (int64_t)row * p.n + gn;
@@ -271,7 +302,10 @@ hipError_t launch_gemm_skinny(const GemmLaunch& g, hipStream_t stream) {
     p.sa = g.scale_a;
     p.sb = g.scale_b;
     p.bias = g.bias;
+    p.bias_scale = g.bias_scale;
     p.out = g.out;
+    p.out_q = g.out_q;
+    p.out_scale = g.out_scale;
     p.m = g.m;
     p.n = g.n;
     p.k = g.k;
@@ -283,12 +317,16 @@ hipError_t launch_gemm_skinny(const GemmLaunch& g, hipStream_t stream) {
     p.xcd_remap = (p.tiles_n % 8) == 0;
     const dim3 grid((unsigned)p.tiles_n, (unsigned)g.batch);
     const dim3 block(kWaves * 64);
-    if (g.fmt == 0) {
-        if (g.m <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<0, 1>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_skinny_kernel<0, 2>), grid, block, 0, stream, p);
-    } else {
-        if (g.m <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<1, 1>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_skinny_kernel<1, 2>), grid, block, 0, stream, p);
+    const int sel = g.fmt * 4 + (g.m <= 32 ? 0 : 2) + (g.ext() ? 1 : 0);
+    switch (sel) {
+    case 0: hipLaunchKernelGGL((gemm_skinny_kernel<0, 1, false>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<0, 1, true>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<0, 2, false>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<0, 2, true>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((gemm_skinny_kernel<1, 1, false>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((gemm_skinny_kernel<1, 1, true>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((gemm_skinny_kernel<1, 2, false>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((gemm_skinny_kernel<1, 2, true>), grid, block, 0, stream, p); break;
     }
     return hipGetLastError();
 }

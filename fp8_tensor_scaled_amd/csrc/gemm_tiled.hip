@@ -1,6 +1,7 @@
 // LDS-tiled fp8 GEMM on CDNA4 MFMA (v_mfma_f32_32x32x64_f8f6f4).
 //
 // Computes out[b][i][j] = bf16(sum_k A[i][k] B[k][j] * fp32(sa*sb) + bias[j])
+// (or, with the extended epilogue, an fp8 bias and / or fp8 output codes)
 // for the four storage layouts of the operands (AstrAI compare view
 // 3e57cc8...main: csrc/kernels/fp8/common.h layout tags, the removed
 // linear_backward_fp8 binding's NN dX and TN dW products, and
@@ -54,13 +55,17 @@ struct TiledParams {
     const uint8_t* b;
     const float* sa;
     const float* sb;
-    const uint16_t* bias;
-    uint16_t* out;
+    const void* bias;         // bf16 [n], or fp8 codes [n] when bias_scale is set
+    const float* bias_scale;  // extended epilogue only
+    void* out;                // bf16, or fp8 codes when out_q >= 0
+    int out_q;                // extended epilogue only: -1 bf16, 0 E4M3, 1 E5M2
+    const float* out_scale;
     int64_t m, n, k, lda, ldb, stride_a, stride_b;
     int tiles_m, tiles_n, tiles_per_batch;
     int group_m;
-    int vec_out;    // out rows 8-byte aligned and n % 4 == 0
-    int vec_out16;  // out rows 16-byte aligned and n % 8 == 0 (LDS-staged stores)
+    int vec_out;    // 4-element output stores: out aligned for them and n % 4 == 0
+    int vec_out16;  // output rows in whole 16-byte chunks, 16-byte aligned (LDS-staged)
+    int vec_bias;   // 4-element bias loads: bias aligned for them (or no bias)
     int xcd_remap;
 };
 
@@ -350,7 +355,43 @@ constexpr int tiled_lds_bytes() {
 
 // One output tile: workgroup `bid` of a grid of G workgroups over problem p,
 // with `smem` the workgroup's LDS ring of tiled_lds_bytes<...>() bytes.
-template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES>
+// Four bias values of columns gn .. gn+3 (zero past n) for the extended
+// epilogue: bf16, or fp8 codes of FMT times their step bs.
+template <int FMT>
+__device__ __forceinline__ void ext_bias4(const TiledParams& p, float bs, int64_t gn,
+                                          float b[4]) {
+    b[0] = b[1] = b[2] = b[3] = 0.0f;
+    if (!p.bias || gn >= p.n) return;
+    const bool whole = p.vec_bias && gn + 3 < p.n;
+    if (p.bias_scale) {
+        const uint8_t* bp = static_cast<const uint8_t*>(p.bias) + gn;
+        if (whole) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(bp);
+            b[0] = dec8<FMT, 0>(w) * bs; b[1] = dec8<FMT, 1>(w) * bs;
+            b[2] = dec8<FMT, 2>(w) * bs; b[3] = dec8<FMT, 3>(w) * bs;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (gn + c < p.n) b[c] = dec8<FMT, 0>(bp[c]) * bs;
+        }
+    } else {
+        const uint16_t* bp = static_cast<const uint16_t*>(p.bias) + gn;
+        if (whole) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(bp);
+            b[0] = bf16_lo(bb.x); b[1] = bf16_hi(bb.x);
+            b[2] = bf16_lo(bb.y); b[3] = bf16_hi(bb.y);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (gn + c < p.n) b[c] = bf16_to_f32(bp[c]);
+        }
+    }
+}
+
+// EXT selects the extended epilogue (fp8 bias and / or fp8 output, chosen at
+// run time); without it the epilogue is the plain bf16 one.
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES,
+          bool EXT = false>
 __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const int G,
                                           uint8_t* smem) {
     constexpr int NW = WM * WN;
@@ -385,6 +426,11 @@ __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const i
 
     // The epilogue's scale, fetched now so its latency hides under the loop.
     const float sc = (*p.sa) * (*p.sb);
+    float ext_bs = 0.0f, ext_rq = 0.0f;  // bias step, output step's reciprocal
+    if constexpr (EXT) {
+        if (p.bias_scale) ext_bs = *p.bias_scale;
+        if (p.out_q >= 0) ext_rq = __fdiv_rn(1.0f, *p.out_scale);
+    }
 
     // Buffer descriptors based at this tile's first row / column.
     const uint8_t* A = p.a + (int64_t)bz * p.stride_a + (AMN ? m0 : m0 * p.lda);
@@ -579,7 +625,102 @@ __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const i
 
     // Epilogue: acc[i][j][e] is row m0 + wm*TM + 32i + lane%32, column
     // n0 + wn*TN + 32j + 8*(e/4) + 4*(lane/32) + e%4.
-    uint16_t* out = p.out + bz * p.m * p.n;
+    if constexpr (EXT) {
+        // Output element of OB bytes: 2 (bf16) or 1 (fp8 code of format
+        // out_q).  The same two store forms as the plain epilogue below.
+        auto store = [&](auto ob_tag) __attribute__((always_inline)) {
+            constexpr int OB = decltype(ob_tag)::value;
+            uint8_t* outb = static_cast<uint8_t*>(p.out) + (int64_t)bz * p.m * p.n * OB;
+            // four consecutive outputs -> their packed bytes (8 or 4)
+            auto pack = [&](float v0, float v1, float v2, float v3) __attribute__((always_inline)) {
+                if constexpr (OB == 2) {
+                    v2i pk;
+                    pk[0] = (int)f32x2_to_bf16x2(v0, v1);
+                    pk[1] = (int)f32x2_to_bf16x2(v2, v3);
+                    return pk;
+                } else {
+                    return cvt4_rt(p.out_q, v0 * ext_rq, v1 * ext_rq, v2 * ext_rq, v3 * ext_rq);
+                }
+            };
+            if (p.vec_out16) {
+                constexpr int kRowBytes = TN * OB;
+                constexpr int kChunks = kRowBytes / 16;
+                constexpr int kRowsPerPass = 64 / kChunks;
+                constexpr int kRegion = TM * kRowBytes;
+                static_assert(NW * kRegion <= STAGES * kStage, "epilogue staging fits");
+                barrier();  // every wave is done with the operand buffers
+                uint8_t* wl = smem + wave * kRegion;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int cl = 32 * j + 8 * q + 4 * (lane >> 5);
+                        float bias[4];
+                        ext_bias4<FMT>(p, ext_bs, n0 + wn * TN + cl, bias);
+#pragma unroll
+                        for (int i = 0; i < FM; ++i) {
+                            const int r = 32 * i + (lane & 31);
+                            const int byte = cl * OB;
+                            const int chunk = (byte >> 4) ^ (r % kChunks);
+                            const auto v = pack(fmaf(acc[i][j][4 * q + 0], sc, bias[0]),
+                                                fmaf(acc[i][j][4 * q + 1], sc, bias[1]),
+                                                fmaf(acc[i][j][4 * q + 2], sc, bias[2]),
+                                                fmaf(acc[i][j][4 * q + 3], sc, bias[3]));
+                            *reinterpret_cast<__attribute__((address_space(3)))
+                                              std::remove_const_t<decltype(v)>*>(
+                                (lds_void*)(wl + r * kRowBytes + chunk * 16 + (byte & 15))) = v;
+                        }
+                    }
+                }
+                const int cc = lane % kChunks;
+                const int64_t gn = n0 + wn * TN + (16 / OB) * cc;
+#pragma unroll
+                for (int ps = 0; ps < TM / kRowsPerPass; ++ps) {
+                    const int r = ps * kRowsPerPass + lane / kChunks;
+                    const v4i v = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+                        (lds_void*)(wl + r * kRowBytes + ((cc ^ (r % kChunks)) << 4)));
+                    const int64_t gm = m0 + wm * TM + r;
+                    if (gm < p.m && gn < p.n)
+                        *reinterpret_cast<v4i*>(outb + (gm * p.n + gn) * OB) = v;
+                }
+                return;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t gn = n0 + wn * TN + 32 * j + 8 * q + 4 * (lane >> 5);
+                    float bias[4];
+                    ext_bias4<FMT>(p, ext_bs, gn, bias);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const int64_t gm = m0 + wm * TM + 32 * i + (lane & 31);
+                        if (gm >= p.m || gn >= p.n) continue;
+                        const auto v = pack(fmaf(acc[i][j][4 * q + 0], sc, bias[0]),
+                                            fmaf(acc[i][j][4 * q + 1], sc, bias[1]),
+                                            fmaf(acc[i][j][4 * q + 2], sc, bias[2]),
+                                            fmaf(acc[i][j][4 * q + 3], sc, bias[3]));
+                        uint8_t* dst = outb + (gm * p.n + gn) * OB;
+                        if (p.vec_out && gn + 3 < p.n) {
+                            *reinterpret_cast<std::remove_const_t<decltype(v)>*>(dst) = v;
+                        } else {
+                            uint8_t bytes[4 * OB];
+                            __builtin_memcpy(bytes, &v, 4 * OB);
+                            for (int c = 0; c < 4 && gn + c < p.n; ++c)
+                                __builtin_memcpy(dst + c * OB, bytes + c * OB, OB);
+                        }
+                    }
+                }
+            }
+        };
+        if (p.out_q < 0)
+            store(std::integral_constant<int, 2>{});
+        else
+            store(std::integral_constant<int, 1>{});
+        return;
+    }
+    uint16_t* out = static_cast<uint16_t*>(p.out) + bz * p.m * p.n;
+    const uint16_t* bias_p = static_cast<const uint16_t*>(p.bias);
     if (p.vec_out16) {
         // Through LDS: each wave rounds its tile to bf16 into its own LDS
         // region (16-byte chunks XOR-swizzled by row), then writes whole
@@ -599,8 +740,8 @@ __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const i
                 const int cl = 32 * j + 8 * q + 4 * (lane >> 5);  // column in the wave tile
                 const int64_t gn = n0 + wn * TN + cl;
                 float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (p.bias && gn < p.n) {
-                    const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gn);
+                if (bias_p && gn < p.n) {
+                    const uint2 bb = *reinterpret_cast<const uint2*>(bias_p + gn);
                     bias[0] = bf16_lo(bb.x); bias[1] = bf16_hi(bb.x);
                     bias[2] = bf16_lo(bb.y); bias[3] = bf16_hi(bb.y);
                 }
@@ -636,15 +777,15 @@ __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const i
         for (int q = 0; q < 4; ++q) {
             const int64_t gn = n0 + wn * TN + 32 * j + 8 * q + 4 * (lane >> 5);
             float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.bias) {
+            if (bias_p) {
                 if (p.vec_out && gn + 3 < p.n) {
-                    const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + gn);
+                    const uint2 bb = *reinterpret_cast<const uint2*>(bias_p + gn);
                     bias[0] = bf16_lo(bb.x); bias[1] = bf16_hi(bb.x);
                     bias[2] = bf16_lo(bb.y); bias[3] = bf16_hi(bb.y);
                 } else {
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        if (gn + c < p.n) bias[c] = bf16_to_f32(p.bias[gn + c]);
+                        if (gn + c < p.n) bias[c] = bf16_to_f32(bias_p[gn + c]);
                 }
             }
 #pragma unroll
@@ -670,10 +811,11 @@ __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const i
     }
 }
 
-template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES,
+          bool EXT>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<BM, BN, BK, STAGES>()];
-    gemm_tile<FMT, AMN, BMN, BM, BN, WM, WN, BK, STAGES>(p, blockIdx.x, gridDim.x, smem);
+    gemm_tile<FMT, AMN, BMN, BM, BN, WM, WN, BK, STAGES, EXT>(p, blockIdx.x, gridDim.x, smem);
 }
 
 // Two independent problems in one launch (the linear backward's dX, NN, and
@@ -722,7 +864,10 @@ static TiledParams tiled_params(const GemmLaunch& g) {
     p.sa = g.scale_a;
     p.sb = g.scale_b;
     p.bias = g.bias;
+    p.bias_scale = g.bias_scale;
     p.out = g.out;
+    p.out_q = g.out_q;
+    p.out_scale = g.out_scale;
     p.m = g.m;
     p.n = g.n;
     p.k = g.k;
@@ -734,9 +879,18 @@ static TiledParams tiled_params(const GemmLaunch& g) {
     p.tiles_n = (int)((g.n + BN - 1) / BN);
     p.tiles_per_batch = p.tiles_m * p.tiles_n;
     p.group_m = 4;
-    const bool bias8 = g.bias == nullptr || (reinterpret_cast<uintptr_t>(g.bias) & 7) == 0;
-    p.vec_out = ((reinterpret_cast<uintptr_t>(g.out) & 7) == 0) && (g.n % 4 == 0) && bias8;
-    p.vec_out16 = ((reinterpret_cast<uintptr_t>(g.out) & 15) == 0) && (g.n % 8 == 0) && bias8;
+    const uintptr_t ob = reinterpret_cast<uintptr_t>(g.out), bb = reinterpret_cast<uintptr_t>(g.bias);
+    if (!g.ext()) {
+        const bool bias8 = g.bias == nullptr || (bb & 7) == 0;
+        p.vec_out = ((ob & 7) == 0) && (g.n % 4 == 0) && bias8;
+        p.vec_out16 = ((ob & 15) == 0) && (g.n % 8 == 0) && bias8;
+        p.vec_bias = bias8;
+    } else {
+        const int osz = g.out_q < 0 ? 2 : 1;  // output bytes per element
+        p.vec_out = ((ob & (4 * osz - 1)) == 0) && (g.n % 4 == 0);
+        p.vec_out16 = ((ob & 15) == 0) && ((g.n * osz) % 16 == 0);
+        p.vec_bias = g.bias == nullptr || (bb & (g.bias_scale ? 3 : 7)) == 0;
+    }
     const int64_t total = p.tiles_per_batch * g.batch;
     p.xcd_remap = (total % 8) == 0;
     return p;
@@ -746,8 +900,12 @@ template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, i
 static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     const TiledParams p = tiled_params<BM, BN>(g);
     const int64_t total = (int64_t)p.tiles_per_batch * g.batch;
-    hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST>),
-                       dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
+    if (g.ext())
+        hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, true>),
+                           dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, false>),
+                           dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -788,6 +946,7 @@ static int64_t tiles256(const GemmLaunch& g) {
 
 bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1) {
     if (!gemm_tiled_supported(g0) || !gemm_tiled_supported(g1) || g0.fmt != g1.fmt) return false;
+    if (g0.ext() || g1.ext()) return false;  // the paired kernel has the plain epilogue
     // problem 0 NN (A k-contiguous, B n-contiguous), problem 1 TN (both
     // m/n-contiguous), each big enough for the 256x256 configuration
     if (g0.trans_a != 0 || g0.trans_b != 0 || g1.trans_a != 1 || g1.trans_b != 0) return false;

@@ -58,8 +58,17 @@ struct GemmLaunch {
     int64_t batch = 1, stride_a = 0, stride_b = 0;
     const float* scale_a = nullptr;
     const float* scale_b = nullptr;
-    const uint16_t* bias = nullptr;
-    uint16_t* out = nullptr;
+    // bias: bf16 [n] when bias_scale is null, else fp8 codes [n] of fmt whose
+    // values are code * bias_scale[0]; NULL for none.
+    const void* bias = nullptr;
+    const float* bias_scale = nullptr;
+    // out: bf16 [batch][m][n] (out_q < 0) or fp8 codes of format out_q
+    // (0 E4M3, 1 E5M2) of the value times fp32(1 / out_scale[0]).
+    void* out = nullptr;
+    int out_q = -1;
+    const float* out_scale = nullptr;
+    // Needs the extended epilogue (fp8 bias or fp8 output).
+    bool ext() const { return bias_scale != nullptr || out_q >= 0; }
 };
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
 // Two independent GEMMs: one launch when both take the tiled kernels' paired

@@ -237,6 +237,41 @@ fp8_status_t fp8_mm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t t
                     uint16_t* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_mm_ex -- fp8_mm with an fp8 bias and / or an fp8 output.
+ * (compare view: astrai/extension/ops/fp8.py, the removed fp8_gemm op:
+ *  out_dtype selects an fp8 E4M3 output, which needs out_scale, the
+ *  output's quantization step; commit log 3e57cc8: FP8Params' bias becomes
+ *  untyped with a bias_scale beside it -- none for a bf16 bias, else fp8
+ *  storage dequantized after the operand scaling and before the output is
+ *  quantized)
+ *
+ *   v[b][i][j] = fp32( sum_k A_b[i][k] * B_b[k][j] * fp32(sa * sb) + bv[j] )
+ *   bv[j]      = bias_scale ? fp32( dec(bias8[j]) * bias_scale[0] )
+ *                           : bf16 bias[j]               (0 without a bias)
+ *   out        = bf16_rne(v)                              FP8_OUT_BF16
+ *                enc( fp32( v * fp32(1 / out_scale[0]) ) ) FP8_OUT_E4M3 / _E5M2
+ * enc rounds to nearest even and saturates at the format's largest value
+ * (the quantize's cast); an fp8 bias is in the operands' format `fmt`.
+ *
+ * a .. scale_b: as fp8_mm.
+ * bias: NULL, bf16 [n] (bias_scale NULL) or fp8 codes [n] (bias_scale:
+ *     fp32 [1] step of the codes, device).
+ * out_type: FP8_OUT_BF16 -> out is bf16 [batch][m][n] and out_scale must be
+ *     NULL; FP8_OUT_E4M3 / FP8_OUT_E5M2 -> out is fp8 codes [batch][m][n]
+ *     (one byte each) and out_scale (fp32 [1], device) is required.
+ * With bias_scale NULL and FP8_OUT_BF16 this is fp8_mm exactly (same
+ * kernels, same bits).  Accumulation order: as fp8_mm's.
+ * ------------------------------------------------------------------- */
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_E4M3 = 1, FP8_OUT_E5M2 = 2 } fp8_out_t;
+
+fp8_status_t fp8_mm_ex(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_t trans_a,
+                       int32_t trans_b, int64_t m, int64_t n, int64_t k, int64_t lda,
+                       int64_t ldb, int64_t batch, int64_t stride_a, int64_t stride_b,
+                       const float* scale_a, const float* scale_b, const void* bias,
+                       const float* bias_scale, fp8_out_t out_type, const float* out_scale,
+                       void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_mm_pair -- two independent fp8_mm products from one call: the
  * linear backward's dX = g . W (NN) and dW = g^T . X (TN), which use the
  * same g and nothing of each other (compare view: astrai/extension/fp8.py

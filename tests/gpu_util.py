@@ -93,3 +93,35 @@ def check_gemm(y_bits: np.ndarray, r_bits: np.ndarray, absdot: np.ndarray | None
                 max_rel_nonzero=float(rel[np.abs(r) > 1e-3].max()) if (np.abs(r) > 1e-3).any()
                 else 0.0,
                 allclose_pages=bool(np.allclose(y, r, rtol=1e-2, atol=1e-2)))
+
+
+def check_fp8_codes(orc, got: np.ndarray, y: np.ndarray, absdot: np.ndarray, K: int,
+                    out_type: int, out_scale, what: str = "", max_frac: float = 1e-2) -> dict:
+    """fp8 output codes against the oracle's exact value y of each output:
+    every code must be the cast of some value within the fp32 accumulation
+    bound of y (between the codes of y - e and y + e, e the bound of
+    check_gemm's fallback plus the epilogue's fp32 rounding), and all but a
+    few equal the code of y itself (only outputs within e of a rounding
+    boundary may differ)."""
+    got = np.asarray(got, np.uint8).ravel()
+    y = np.asarray(y, np.float64).ravel()
+    absdot = np.asarray(absdot, np.float64).ravel()
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    e = (2.0 ** -10 + gamma) * absdot + 4 * u * np.abs(y)
+    fo = 0 if out_type == 1 else 1
+    nominal = orc.out_codes(y, out_type, out_scale)
+    lo = orc.decode_array(orc.out_codes(y - e, out_type, out_scale), fo)
+    hi = orc.decode_array(orc.out_codes(y + e, out_type, out_scale), fo)
+    g = orc.decode_array(got, fo)
+    assert np.isfinite(g).all(), f"{what}: non-finite fp8 codes"
+    inside = (lo <= g) & (g <= hi)
+    assert inside.all(), (
+        f"{what}: {int((~inside).sum())} codes outside the accumulation bound; first at "
+        f"{int(np.argmax(~inside))}: got {got[~inside][0]:#04x} for y={y[~inside][0]}")
+    n_diff = int((got != nominal).sum())
+    assert n_diff <= max(3, max_frac * got.size), f"{what}: {n_diff} of {got.size} codes differ"
+    if n_diff:
+        print(f"[{what}] {n_diff} of {got.size} codes differ from the oracle's, each within "
+              "the accumulation bound")
+    return dict(n=int(got.size), differ=n_diff)

@@ -28,7 +28,8 @@ def f():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_pair", "fp8_linear_fwd",
+    for n in ("fp8_quantize", "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_ex", "fp8_mm_pair",
+              "fp8_linear_fwd",
               "fp8_linear_bwd", "fp8_colsum", "fp8_last_error"):
         assert n in names
 
@@ -190,6 +191,37 @@ def mm(lib, **kw):
 def test_mm_validation(f, kw, needle):
     st = mm(f._lib, **kw)
     assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
+def mm_ex(lib, **kw):
+    a = dict(a=FAKE, b=FAKE, fmt=0, ta=0, tb=1, m=64, n=64, k=64, lda=64, ldb=64, batch=1,
+             sta=0, stb=0, sa=FAKE, sb=FAKE, bias=None, bias_scale=None, out_type=1,
+             out_scale=FAKE, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.fp8_mm_ex(*a.values())
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(out_type=3), "output type"),
+    (dict(out_type=-1), "output type"),
+    (dict(out_type=0), "out_scale given for a bf16 output"),
+    (dict(out_type=2, out_scale=None), "needs out_scale"),
+    (dict(bias_scale=FAKE), "bias_scale without a bias"),
+    (dict(fmt=5), "fp8_mm_ex: unsupported fp8 format"),
+    (dict(out=None), "NULL"),
+    (dict(lda=32), "lda"),
+])
+def test_mm_ex_validation(f, kw, needle):
+    st = mm_ex(f._lib, **kw)
+    assert st == 1 and needle in _err(f._lib), _err(f._lib)
+
+
+def test_mm_ex_valid_call_without_gpu_reports_hip_error(f):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert mm_ex(f._lib, bias=FAKE, bias_scale=FAKE) in (2, 3)
+    assert mm_ex(f._lib, out_type=0, out_scale=None) in (2, 3)
 
 
 def mm_args(f, **kw):

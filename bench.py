@@ -44,8 +44,11 @@ E4M3, E5M2 = 0, 1
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # The GPU reaches its steady clocks only after some 30 ms of load (the
+    # first 50 steps run about 30 % slower than the steady state, the next
+    # 50 about 3 %); 200 warm-up steps (about 45 ms) cover that ramp.
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--size", type=int, default=4096)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
@@ -59,6 +62,19 @@ KERNELS = ("gemm_nt_4096", "gemm_nn_4096", "gemm_tn_4096", "gemm_bwd_pair_4096",
            "gemm_nt_64x8192x2048", "gemm_nt_8192", "quantize_8192x8192", "copy_192MB")
 
 
+def fp8_codes(f, torch, numel, seed, fmt=E4M3):
+    """fp8 codes of N(0, 1) values under their dynamic step: the workloads'
+    GEMM operands (pre-quantized from bf16 with a per-tensor step)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    x = torch.randn(numel, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    ring = f.Ring(1)
+    f.fp8_quantize(x, fmt, ring=ring)  # measure-only pass: the dynamic step
+    q = torch.empty(numel, dtype=torch.uint8, device="cuda")
+    f.fp8_quantize(x, fmt, scale=ring.scale, out=q)
+    return q
+
+
 def single_kernel(f, torch, name, reps):
     """Launch one kernel `reps` times (after 2 warm-up launches) on synthetic
     operands, for rocprofv3 counter and trace runs."""
@@ -67,8 +83,7 @@ def single_kernel(f, torch, name, reps):
     if name == "gemm_bwd_pair_4096":
         # the step's backward: dX (NN) and dW (TN) at M = N = K = 4096, one launch
         n = 4096
-        g8, w8, x8 = (torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
-                      for _ in range(3))
+        g8, w8, x8 = (fp8_codes(f, torch, n * n, 800 + i, E5M2) for i in range(3))
         dx = torch.empty(n * n, dtype=torch.int16, device=dev)
         dw = torch.empty(n * n, dtype=torch.int16, device=dev)
 
@@ -82,12 +97,12 @@ def single_kernel(f, torch, name, reps):
                   "gemm_nt_64x8192x2048": (64, 8192, 2048, 0, 1),
                   "gemm_nt_8192": (8192, 8192, 8192, 0, 1)}
         M, N, K, ta, tb = shapes[name]
-        a = torch.randint(0, 120, (M * K,), dtype=torch.uint8, device=dev)
-        b = torch.randint(0, 120, (N * K,), dtype=torch.uint8, device=dev)
+        fmt = E4M3 if (ta, tb) == (0, 1) else E5M2
+        a = fp8_codes(f, torch, M * K, 810, fmt)
+        b = fp8_codes(f, torch, N * K, 811, fmt)
         out = torch.empty(M * N, dtype=torch.int16, device=dev)
         lda = M if ta else K
         ldb = K if tb else N
-        fmt = E4M3 if (ta, tb) == (0, 1) else E5M2
 
         def launch():
             f.fp8_mm(a, b, fmt, ta, tb, M, N, K, lda, ldb, 1, 0, 0, s, s, None, out)
@@ -311,29 +326,36 @@ def components(f, torch):
     dev = "cuda"
     # 4096^3 NT GEMM + bias, pre-quantized E4M3
     n = 4096
-    a8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
-    b8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+    a8 = fp8_codes(f, torch, n * n, 820)
+    b8 = fp8_codes(f, torch, n * n, 821)
     s = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
     bias = torch.zeros(n, dtype=torch.int16, device=dev)
     out = torch.empty(n * n, dtype=torch.int16, device=dev)
-    ms = time_kernel(torch, lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s,
-                                                bias, out), 50)
-    res["gemm_nt_4096"] = dict(us=round(ms * 1e3, 2),
-                               tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
+    nt = (lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s, bias, out))
     # the same product with an fp8 bias and an E4M3 output (fp8_mm_ex)
-    b8_bias = torch.randint(0, 120, (n,), dtype=torch.uint8, device=dev)
+    b8_bias = fp8_codes(f, torch, n, 822)
     out8 = torch.empty(n * n, dtype=torch.uint8, device=dev)
     mm_ex = (lambda i: f.fp8_mm_ex(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s, b8_bias,
                                    s, f.OUT_E4M3, s, out8))
-    time_kernel(torch, mm_ex, 20)  # first launches of this kernel: not timed
-    ms = time_kernel(torch, mm_ex, 100)
-    res["gemm_nt_4096_fp8_bias_e4m3_out"] = dict(
-        us=round(ms * 1e3, 2), tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
+    # Short bursts (20 launches, ~1 ms), the two forms alternating over 10
+    # rounds, medians of the last 6: a stream of back-to-back GEMMs longer
+    # than a few ms draws enough power for the clocks to drop (launch
+    # durations climb by up to 25 % over some 5 ms, then fall back to within
+    # a few % of the burst figure), so the two forms are compared once that
+    # transient has passed, under the same clock state.  The step itself,
+    # whose quantize passes are HBM-bound, runs its GEMMs at the burst figure.
+    t_bf16, t_fp8 = [], []
+    for _ in range(10):
+        t_bf16.append(time_kernel(torch, nt, 20))
+        t_fp8.append(time_kernel(torch, mm_ex, 20))
+    for name, ts in (("gemm_nt_4096", t_bf16), ("gemm_nt_4096_fp8_bias_e4m3_out", t_fp8)):
+        ms = float(np.median(ts[4:]))
+        res[name] = dict(us=round(ms * 1e3, 2), tflops=round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1))
     del a8, b8, out, out8
     # 8192^3 NT + bias
     n = 8192
-    a8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
-    b8 = torch.randint(0, 120, (n * n,), dtype=torch.uint8, device=dev)
+    a8 = fp8_codes(f, torch, n * n, 830)
+    b8 = fp8_codes(f, torch, n * n, 831)
     bias = torch.zeros(n, dtype=torch.int16, device=dev)
     out = torch.empty(n * n, dtype=torch.int16, device=dev)
     ms = time_kernel(torch, lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, n, n, n, n, n, 1, 0, 0, s, s,
@@ -346,9 +368,8 @@ def components(f, torch):
     for name, (batch, M, N, K, bcast) in (("bmm_8x1024x2048x2048", (8, 1024, 2048, 2048, False)),
                                           ("bmm_bcast_8x1024x2048x2048", (8, 1024, 2048, 2048, True)),
                                           ("bmm_64x512x512x512", (64, 512, 512, 512, False))):
-        a8 = torch.randint(0, 120, (batch * M * K,), dtype=torch.uint8, device=dev)
-        b8 = torch.randint(0, 120, ((1 if bcast else batch) * N * K,), dtype=torch.uint8,
-                           device=dev)
+        a8 = fp8_codes(f, torch, batch * M * K, 840)
+        b8 = fp8_codes(f, torch, (1 if bcast else batch) * N * K, 841)
         out = torch.empty(batch * M * N, dtype=torch.int16, device=dev)
         sb_ = 0 if bcast else N * K
         ms = time_kernel(torch, lambda i: f.fp8_mm(a8, b8, E4M3, 0, 1, M, N, K, K, K, batch,
@@ -362,8 +383,8 @@ def components(f, torch):
     M, N, K = 64, 8192, 2048
     d = wl.smallm()
     rot = 64
-    xs = torch.randint(0, 120, (M * K,), dtype=torch.uint8, device=dev)
-    ws = [torch.randint(0, 120, (N * K,), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    xs = fp8_codes(f, torch, M * K, 850)
+    ws = [fp8_codes(f, torch, N * K, 851 + i) for i in range(rot)]
     outs = [torch.empty(M * N, dtype=torch.int16, device=dev) for _ in range(rot)]
     ms = time_graph(torch, lambda i: f.fp8_mm(xs, ws[i % rot], E4M3, 0, 1, M, N, K, K, K, 1, 0,
                                                0, s, s, None, outs[i % rot]), rot)

@@ -134,13 +134,24 @@ def _ptr(t: torch.Tensor | None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# torch's raw accessors of the current device and its current stream: the
+# public torch.cuda.current_stream() costs about 10 us a call in device
+# checks, several times per linear step.
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_RAW_DEVICE = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream=None):
-    """HIP stream handle: torch's current stream by default, an int handle
-    as given (0 = the null stream), or a torch.cuda.Stream."""
+    """HIP stream handle: torch's current stream (of the current device) by
+    default, an int handle as given (0 = the null stream), or a
+    torch.cuda.Stream."""
+    if stream is None:
+        if _RAW_STREAM is not None and _RAW_DEVICE is not None:
+            return ctypes.c_void_p(_RAW_STREAM(_RAW_DEVICE()))
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 class Ring:

@@ -167,3 +167,23 @@ def test_masks_and_plain_path(lib, fa):
     assert x.grad is not None and x.grad.shape == (M, K) and w.grad is None
     ref = torch.nn.functional.linear(x.detach(), w)
     assert torch.equal(fa.fp8_linear(x.detach(), w), ref)  # outside a region: plain linear
+
+
+def test_binding_launches_on_torch_current_stream(lib):
+    """The binding's default stream is torch's current one (also inside a
+    torch.cuda.stream context), and work enqueued there is ordered with
+    torch's own work on that stream."""
+    side = torch.cuda.Stream()
+    handle = (lambda: lib._stream().value or 0)  # c_void_p(0).value is None
+    assert handle() == torch.cuda.current_stream().cuda_stream
+    x = torch.randn(1 << 20, device="cuda").to(torch.bfloat16)
+    q = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    s = torch.ones(1, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(side):
+        assert handle() == side.cuda_stream
+        side.wait_stream(torch.cuda.default_stream())
+        lib.fp8_quantize(x.view(torch.int16), 0, scale=s, out=q)
+        ref = x.float().clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        same = torch.equal(q, ref)  # torch's compare runs on the same side stream
+    torch.cuda.synchronize()
+    assert same

@@ -73,8 +73,8 @@ def _load() -> ctypes.CDLL:
     sig = {
         "fp8_ring_state_floats": (I64, [I32]),
         "fp8_format_max": (F, [I32]),
-        "fp8_quantize": (I32, [P, I64, I32, P, P, R, I32, P, P]),
-        "fp8_quantize_ex": (I32, [P, I32, I64, I32, P, P, R, I32, P, P]),
+        "fp8_quantize": (I32, [P, I64, I32, P, P, P, R, I32, P, P]),
+        "fp8_quantize_ex": (I32, [P, I32, I64, I32, P, P, P, R, I32, P, P]),
         "fp8_quantize_t": (I32, [P, I64, I64, I32, P, P, P, R, I32, P, P]),
         "fp8_quantize2": (I32, [P, I64, I32, P, P, I32, P, R, I32, P, P]),
         "fp8_scale_ring_finalize": (I32, [R, I32, P, I32, P]),
@@ -211,10 +211,12 @@ def _ring_ref(r: Ring | None):
 
 def fp8_quantize(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
                  out: torch.Tensor | None = None, ring: Ring | None = None, margin: int = 0,
-                 scale_used: torch.Tensor | None = None, stream=None) -> None:
-    """bf16 x -> fp8 codes in ``out`` (uint8, same numel); see fp8lin.h."""
-    st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
-                           margin, _ptr(scale_used), _stream(stream))
+                 scale_used: torch.Tensor | None = None, stream=None,
+                 amax_out: torch.Tensor | None = None) -> None:
+    """bf16 x -> fp8 codes in ``out`` (uint8, same numel), and / or max |x|
+    in ``amax_out`` (float32 [1]); see fp8lin.h."""
+    st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ptr(amax_out),
+                           _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize")
 
 
@@ -236,7 +238,7 @@ _IN_OF_DTYPE = {torch.bfloat16: IN_BF16, torch.float16: IN_F16, torch.float32: I
 def fp8_quantize_ex(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
                     out: torch.Tensor | None = None, ring: Ring | None = None, margin: int = 0,
                     scale_used: torch.Tensor | None = None, in_type: int | None = None,
-                    stream=None) -> None:
+                    stream=None, amax_out: torch.Tensor | None = None) -> None:
     """bf16, fp16 or fp32 x -> fp8 codes; ``in_type`` defaults to x's dtype
     (bfloat16 / float16 / float32; give it for int16 bit views); see
     fp8lin.h."""
@@ -245,7 +247,8 @@ def fp8_quantize_ex(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None
             raise ValueError(f"fp8_quantize_ex: no input type for dtype {x.dtype}")
         in_type = _IN_OF_DTYPE[x.dtype]
     st = _lib.fp8_quantize_ex(_ptr(x), in_type, x.numel(), fmt, _ptr(scale), _ptr(out),
-                              _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
+                              _ptr(amax_out), _ring_ref(ring), margin, _ptr(scale_used),
+                              _stream(stream))
     _check(st, "fp8_quantize_ex")
 
 

@@ -109,7 +109,7 @@ fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const floa
                          uint8_t* out, float* ring_state, int32_t len, int32_t idx,
                          int32_t margin, float* scale_used, hipStream_t stream,
                          uint8_t* out2 = nullptr, int fmt2 = -1,
-                         int in_type = fp8lin::kInBf16) {
+                         int in_type = fp8lin::kInBf16, float* amax_out = nullptr) {
     fp8lin::QuantLaunch q;
     q.x = x;
     q.in_type = in_type;
@@ -124,6 +124,7 @@ fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const floa
     q.ring_idx = idx;
     q.pow2_margin = pow2f(margin);
     q.scale_used = scale_used;
+    q.amax_out = amax_out;
     hipError_t e = fp8lin::launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return FP8_OK;
@@ -242,16 +243,17 @@ const char* fp8_version(void) { return "fp8lin 0.1 (gfx950)"; }
 
 static fp8_status_t quantize_entry(const char* who, const void* x, int in_type, int64_t numel,
                                    fp8_fmt_t fmt, const float* scale, uint8_t* out,
-                                   const fp8_ring_t* ring, int32_t margin, float* scale_used,
-                                   hipStream_t stream) {
+                                   float* amax_out, const fp8_ring_t* ring, int32_t margin,
+                                   float* scale_used, hipStream_t stream) {
     g_err[0] = 0;
     if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "%s: unsupported fp8 format %d", who, fmt);
     if (in_type != FP8_IN_BF16 && in_type != FP8_IN_F16 && in_type != FP8_IN_F32)
         return fail(FP8_EINVAL, "%s: unsupported input type %d", who, in_type);
     if (numel < 0) return fail(FP8_EINVAL, "%s: numel %lld < 0", who, (long long)numel);
     if (numel > 0 && !x) return fail(FP8_EINVAL, "%s: x is NULL", who);
-    if (numel == 0 && !ring) return FP8_OK;  // nothing to convert, nothing to fold
-    if (!out && !ring) return fail(FP8_EINVAL, "%s: neither out nor ring given", who);
+    if (numel == 0 && !ring && !amax_out) return FP8_OK;  // nothing to convert or fold
+    if (!out && !ring && !amax_out)
+        return fail(FP8_EINVAL, "%s: neither out nor amax_out nor ring given", who);
     if (out && !scale) return fail(FP8_EINVAL, "%s: scale is NULL", who);
     if (ring) {
         fp8_status_t st = check_ring(ring, who);
@@ -265,21 +267,22 @@ static fp8_status_t quantize_entry(const char* who, const void* x, int in_type, 
     if (st) return st;
     return do_quantize(x, numel, fmt, out ? scale : nullptr, out, ring ? ring->state : nullptr,
                        ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, stream,
-                       nullptr, -1, in_type);
+                       nullptr, -1, in_type, amax_out);
 }
 
 fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
-                          uint8_t* out, const fp8_ring_t* ring, int32_t margin,
+                          uint8_t* out, float* amax_out, const fp8_ring_t* ring, int32_t margin,
                           float* scale_used, hipStream_t stream) {
-    return quantize_entry("fp8_quantize", x, FP8_IN_BF16, numel, fmt, scale, out, ring, margin,
-                          scale_used, stream);
+    return quantize_entry("fp8_quantize", x, FP8_IN_BF16, numel, fmt, scale, out, amax_out, ring,
+                          margin, scale_used, stream);
 }
 
 fp8_status_t fp8_quantize_ex(const void* x, fp8_in_t in_type, int64_t numel, fp8_fmt_t fmt,
-                             const float* scale, uint8_t* out, const fp8_ring_t* ring,
-                             int32_t margin, float* scale_used, hipStream_t stream) {
-    return quantize_entry("fp8_quantize_ex", x, in_type, numel, fmt, scale, out, ring, margin,
-                          scale_used, stream);
+                             const float* scale, uint8_t* out, float* amax_out,
+                             const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                             hipStream_t stream) {
+    return quantize_entry("fp8_quantize_ex", x, in_type, numel, fmt, scale, out, amax_out, ring,
+                          margin, scale_used, stream);
 }
 
 fp8_status_t fp8_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, fp8_fmt_t fmt,

@@ -36,6 +36,7 @@ struct QuantLaunch {
     int32_t ring_idx = 0;
     float pow2_margin = 1.0f;
     float* scale_used = nullptr;
+    float* amax_out = nullptr;     // optional: receives max |x| (fp32)
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
 

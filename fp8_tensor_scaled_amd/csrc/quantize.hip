@@ -66,6 +66,8 @@ struct QuantParams {
     float fmax;
     float pow2_margin;
     float* scale_used;
+    float* amax_out;  // optional max |x| output: written by the fold, or (no
+                      // ring) an atomic max over workgroups after an arming launch
     int vec;  // 1: x and out are 16-byte aligned
 };
 
@@ -86,6 +88,7 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, fl
     const float peak = fmaxf(wave_max(w), amax);
     if (lane == 0) {
         p.hist[p.idx] = amax;
+        if (p.amax_out) *p.amax_out = amax;
         const float t = __fdiv_rn(peak, p.fmax);
         const float s = __fdiv_rn(t, p.pow2_margin);
         *p.scale_out = fmaxf(s, 1e-12f);
@@ -139,6 +142,24 @@ __device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, 
     }
     return ticket;
 }
+
+// Without a ring: the workgroup max goes into *amax_out (armed to +0 by the
+// launch before) by one atomic max; non-negative floats order as their bits.
+// Every thread of the workgroup must call it once.
+__device__ __forceinline__ void publish_amax_out(const QuantParams& p, float v) {
+    __shared__ float slots[kQuantWaves];
+    v = wave_max(v);
+    if ((threadIdx.x % kWave) == 0) slots[threadIdx.x / kWave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < kQuantWaves; ++w) v = fmaxf(v, slots[w]);
+        __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(p.amax_out), __float_as_uint(v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__global__ void arm_amax_kernel(float* amax_out) { *amax_out = 0.0f; }
 
 // The workgroup that drew the last ticket folds, on its wave 0.
 __device__ __forceinline__ void finish_fold(const QuantParams& p, uint32_t ticket, float s_read,
@@ -324,8 +345,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     }
     if (p.hist) {
         finish_fold(p, ticket, s_read, win, gridDim.x);
-    } else if constexpr (!MEASURE_ONLY) {
-        if (p.scale_used && blockIdx.x == 0 && t == 0) *p.scale_used = s_read;
+    } else {
+        if constexpr (!MEASURE_ONLY) {
+            if (p.scale_used && blockIdx.x == 0 && t == 0) *p.scale_used = s_read;
+        }
+        if (p.amax_out) publish_amax_out(p, amax);
     }
 }
 
@@ -384,10 +408,13 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     p.fmax = q.fmt ? 57344.0f : 448.0f;
     p.pow2_margin = q.pow2_margin;
     p.scale_used = q.scale_used;
+    p.amax_out = q.amax_out;
     const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
                          reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;
     const dim3 grid(quant_grid(q.numel, p.vec));
+    if (q.amax_out && !q.ring_state)
+        hipLaunchKernelGGL(arm_amax_kernel, dim3(1), dim3(1), 0, stream, q.amax_out);
     if (q.in_type == kInF16) launch_quantize_in<kInF16>(q, p, grid, stream);
     else if (q.in_type == kInF32) launch_quantize_in<kInF32>(q, p, grid, stream);
     else launch_quantize_in<kInBf16>(q, p, grid, stream);

@@ -111,6 +111,12 @@ float fp8_format_max(fp8_fmt_t fmt);
  *             publishes; may alias ring->state + ring->len.  Required when
  *             out != NULL, ignored otherwise.
  * out       : fp8 [numel], or NULL for a measure-only pass (amax + fold).
+ * amax_out  : nullable fp32 [1]; receives amax = max_i |x[i]| over the raw
+ *             values (NaN skipped; +0 for numel == 0), the quantize's
+ *             second result in the pages.  The library initializes it (the
+ *             caller need not clear it): with a ring the folding workgroup
+ *             writes it; without one a one-thread launch arms it to +0 first
+ *             and each workgroup folds its max in with one atomic max.
  * ring      : host pointer, nullable.  When set, the launch's last
  *             workgroup folds amax = max_i |x[i]| over the raw bf16 values
  *             (NaN skipped; 0 for numel == 0) into hist[ring->idx] and
@@ -122,12 +128,14 @@ float fp8_format_max(fp8_fmt_t fmt);
  * margin    : 0 <= margin <= 64, used by the fold only.
  * scale_used: nullable fp32 [1]; receives *scale as this launch read it
  *             (the snapshot a later GEMM must dequantize with).
- * Either out or ring must be non-NULL, except that an empty call
- * (numel == 0) without a ring does nothing and returns FP8_OK.
+ * One of out, amax_out and ring must be non-NULL, except that an empty
+ * call (numel == 0) with neither ring nor amax_out does nothing and
+ * returns FP8_OK.
  * ------------------------------------------------------------------- */
 fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt,
-                          const float* scale, uint8_t* out, const fp8_ring_t* ring,
-                          int32_t margin, float* scale_used, hipStream_t stream);
+                          const float* scale, uint8_t* out, float* amax_out,
+                          const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                          hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * fp8_quantize_ex -- fp8_quantize for bf16, fp16 or fp32 inputs.
@@ -145,8 +153,9 @@ fp8_status_t fp8_quantize(const uint16_t* x, int64_t numel, fp8_fmt_t fmt,
 typedef enum { FP8_IN_BF16 = 0, FP8_IN_F16 = 1, FP8_IN_F32 = 2 } fp8_in_t;
 
 fp8_status_t fp8_quantize_ex(const void* x, fp8_in_t in_type, int64_t numel, fp8_fmt_t fmt,
-                             const float* scale, uint8_t* out, const fp8_ring_t* ring,
-                             int32_t margin, float* scale_used, hipStream_t stream);
+                             const float* scale, uint8_t* out, float* amax_out,
+                             const fp8_ring_t* ring, int32_t margin, float* scale_used,
+                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * fp8_quantize_t -- transposed / dual-orientation quantize.

@@ -455,3 +455,63 @@ def test_backward_nt_only_route(lib, orc):
     ref_dw = orc.gemm(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
     ad_dw = orc.gemm_absdot(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
     check_gemm(from_dev_bf16(dw).reshape(N, K), ref_dw, ad_dw, M, "nt-route dW")
+
+
+# ---------------------------------------------------------------------------
+# amax_out: the quantize's max |x| output
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("numel,offset", [(4096 * 4096, 0), (65536 * 3 + 5, 0), (1000, 1),
+                                          (16, 0), (1, 3), (0, 0)])
+def test_amax_out_without_ring(lib, orc, numel, offset):
+    """No ring: a quantizing call and a measure-only call both return the
+    oracle's amax bit for bit, over many workgroups (atomic max after the
+    arming launch), on the scalar path and for empty input (+0).  The
+    output starts with garbage: the library arms it."""
+    x = wl.normal_bf16((numel,), 3.0, numel % 1000 + offset)
+    if numel > 7:
+        x[numel // 3] = wl.f32_to_bf16_bits(np.array([-1234.0], np.float32))[0]
+    xd = torch.zeros(numel + offset, dtype=torch.int16, device="cuda")
+    if numel:
+        xd[offset:] = to_dev_bf16(x)
+    ref = np.float32(orc.amax(x)) if numel else np.float32(0.0)
+    for out in (True, False):
+        amax = dev_f32(-7.0)
+        q = torch.empty(numel + offset, dtype=torch.uint8, device="cuda") if out else None
+        s = dev_f32(0.5)
+        lib.fp8_quantize(xd[offset:], E4M3, scale=s if out else None,
+                         out=q[offset:] if out else None, amax_out=amax)
+        torch.cuda.synchronize()
+        got = amax.cpu().numpy()[0]
+        assert got == ref and not np.signbit(got), (numel, offset, out, got, ref)
+        if out and numel:
+            assert np.array_equal(from_dev_u8(q[offset:]), orc.quantize(x, E4M3, 0.5))
+
+
+def test_amax_out_with_ring_equals_fold(lib, orc):
+    """With a ring the folding workgroup writes amax_out: the value it puts
+    into hist[idx], over several calls that move idx."""
+    ring = lib.Ring(4)
+    oring = orc.Ring(4)
+    for t, factor in enumerate((1.0, 8.0, 0.25)):
+        x = wl.scaled_bf16(wl.normal_bf16((2048, 1024), 1.0, 70 + t), factor)
+        amax = dev_f32(-1.0)
+        lib.fp8_quantize(to_dev_bf16(x), E5M2, ring=ring, amax_out=amax)
+        torch.cuda.synchronize()
+        oring.fold(orc.amax(x), E5M2)
+        got = amax.cpu().numpy()[0]
+        assert got == np.float32(orc.amax(x)) == ring.state.cpu().numpy()[ring.idx]
+        assert ring_state_equal(ring, oring)
+        ring.idx = (ring.idx + 1) % ring.len
+        oring.advance()
+
+
+@pytest.mark.parametrize("dt,in_type", [(torch.float16, 1), (torch.float32, 2)])
+def test_amax_out_fp16_fp32_inputs(lib, orc, dt, in_type):
+    x = (torch.randn(1 << 20, generator=torch.Generator().manual_seed(5)) * 7).to(dt)
+    x[777] = -60000.0 if dt == torch.float16 else -1e9
+    amax = dev_f32(-1.0)
+    lib.fp8_quantize_ex(x.cuda(), E4M3, amax_out=amax)
+    torch.cuda.synchronize()
+    raw = x.numpy().view(np.uint16 if dt == torch.float16 else np.float32)
+    assert amax.cpu().numpy()[0] == np.float32(orc.amax_in(raw, in_type))

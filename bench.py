@@ -377,7 +377,8 @@ def components(f, torch):
         byts = a8.numel() + b8.numel() + 2 * out.numel()
         res[name] = dict(us=round(ms * 1e3, 2),
                          tflops=round(2 * batch * M * N * K / (ms * 1e-3) / 1e12, 1),
-                         gbs=round(byts / (ms * 1e-3) / 1e9, 1))
+                         gbs=round(byts / (ms * 1e-3) / 1e9, 1),
+                         hbm_frac=round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
         del a8, b8, out
     # 64 x 8192 x 2048 NT, weight rotated over 64 copies (1.07 GB)
     M, N, K = 64, 8192, 2048
@@ -409,6 +410,21 @@ def components(f, torch):
     res["quantize_8192x8192"] = dict(us=round(ms * 1e3, 2),
                                      gbs=round(3 * n / (ms * 1e-3) / 1e9, 1),
                                      hbm_frac=round(3 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+    # dynamic (current-amax) scaling of the same tensors: a measure-only pass
+    # into a length-1 ring, then the cast with its step -- 5 bytes moved per
+    # element, reported against the 3-byte compulsory floor (gbs) and as
+    # moved (moved_gbs)
+    dyn = [f.Ring(1) for _ in range(rot)]
+
+    def dyn_q(i):
+        k = i % rot
+        f.fp8_quantize(xs[k], E4M3, ring=dyn[k])
+        f.fp8_quantize(xs[k], E4M3, scale=dyn[k].scale, out=qs[k])
+    ms = time_graph(torch, dyn_q, 2 * rot)
+    res["quantize_dynamic_8192x8192"] = dict(
+        us=round(ms * 1e3, 2), gbs=round(3 * n / (ms * 1e-3) / 1e9, 1),
+        hbm_frac=round(3 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+        moved_gbs=round(5 * n / (ms * 1e-3) / 1e9, 1))
     del xs
     # the same with fp16 and fp32 inputs (fp8_quantize_ex): 3 and 5 bytes per
     # element; 6 and 4 buffer sets (1.2 and 1.3 GB)
@@ -424,6 +440,28 @@ def components(f, torch):
         res[name] = dict(us=round(ms * 1e3, 2), gbs=round(bpe * n / (ms * 1e-3) / 1e9, 1),
                          hbm_frac=round(bpe * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
         del xs
+    # the workloads' other quantize shapes (bf16, fold on), each rotated over
+    # at least 1 GB of buffers
+    for name, numel in (("quantize_4096x4096", 4096 * 4096), ("quantize_8192x2048", 8192 * 2048),
+                        ("quantize_2048x4096", 2048 * 4096)):
+        nrot = (1 << 30) // (3 * numel) + 1
+        xs = [torch.randn(numel, device=dev).to(torch.bfloat16).view(torch.int16)
+              for _ in range(nrot)]
+        q2 = [torch.empty(numel, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        r2 = [f.Ring(16) for _ in range(nrot)]
+        for i in range(nrot):
+            f.fp8_quantize(xs[i], E4M3, ring=r2[i])
+        ms = time_graph(torch, lambda i: f.fp8_quantize(xs[i % nrot], E4M3,
+                                                         scale=r2[i % nrot].scale,
+                                                         out=q2[i % nrot], ring=r2[i % nrot]),
+                        2 * nrot)
+        res[name] = dict(us=round(ms * 1e3, 2), gbs=round(3 * numel / (ms * 1e-3) / 1e9, 1),
+                         hbm_frac=round(3 * numel / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+        del xs, q2, r2
+    # the small dynamic linear forward (256^3, E4M3, bias): five launches
+    # (measure x and w, quantize x and w, NT GEMM), as a graph replay (GPU
+    # time) and launched one by one (with the host's launch costs)
+    res.update(linear_configs(f, torch))
     # the backward at M = N = K = 4096, two routes from bf16 g, x, w and the
     # forward's steps: NN + TN on row-major codes (this library's route:
     # quantize g with its column sums, w and x in E5M2, one paired launch)
@@ -443,6 +481,52 @@ def components(f, torch):
                                           gbs=round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
                                           hbm_frac=round(2 * (1 << 30) / (ms * 1e-3) / 1e9
                                                          / PEAK_HBM_GBS, 3))
+    return res
+
+
+def linear_configs(f, torch):
+    """The linear entry points on the workloads' small configurations: the
+    dynamic 256^3 forward, and the delayed HYBRID training step at
+    M, N, K = 2048, 4096, 1024 (fp8_linear_fwd + fp8_linear_bwd with rings,
+    dX, dW and the bias gradient)."""
+    import workloads as wl
+    dev = "cuda"
+
+    def up(h):
+        return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).to(dev)
+    res = {}
+    d = wl.linear256()
+    M = N = K = 256
+    x, w, b = up(d["x"]), up(d["w"]), up(d["bias"])
+    ws = torch.zeros(f.fp8_linear_fwd_workspace(M, N, K), dtype=torch.uint8, device=dev)
+    sc = torch.zeros(2, dtype=torch.float32, device=dev)
+    out = torch.empty(M * N, dtype=torch.int16, device=dev)
+    fwd = (lambda i: f.fp8_linear_fwd(x, w, b, M, N, K, E4M3, True, 0, None, None, ws, sc, out))
+    ms_g = time_graph(torch, fwd, 50)
+    ms_e = time_kernel(torch, fwd, 50)
+    res["linear_fwd_dynamic_256"] = dict(us_graph=round(ms_g * 1e3, 2),
+                                         us_eager=round(ms_e * 1e3, 2), launches=5)
+    d = wl.train()
+    M, N, K = d["M"], d["N"], d["K"]
+    x, w, b = up(d["x"][0]), up(d["w"]), up(d["bias"])
+    g = up(d["g"][0])
+    fws = torch.zeros(f.fp8_linear_fwd_workspace(M, N, K), dtype=torch.uint8, device=dev)
+    bws = torch.zeros(f.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device=dev)
+    sc = torch.zeros(2, dtype=torch.float32, device=dev)
+    out = torch.empty(M * N, dtype=torch.int16, device=dev)
+    dx = torch.empty(M * K, dtype=torch.int16, device=dev)
+    dw = torch.empty(N * K, dtype=torch.int16, device=dev)
+    db = torch.empty(N, dtype=torch.int16, device=dev)
+    rx, rw, rg = f.Ring(16), f.Ring(16), f.Ring(16)
+
+    def train_step(i):
+        f.fp8_linear_fwd(x, w, b, M, N, K, E4M3, False, 0, rx, rw, fws, sc, out)
+        f.fp8_linear_bwd(g, x, w, M, N, K, E5M2, False, 0, sc, rg, bws, None, dx, dw, db)
+    for _ in range(20):
+        train_step(0)
+    ms = time_kernel(torch, train_step, 50)
+    res["linear_train_step_2048x4096x1024"] = dict(
+        us=round(ms * 1e3, 2), tflops=round(3 * 2.0 * M * N * K / (ms * 1e-3) / 1e12, 1))
     return res
 
 

@@ -201,3 +201,54 @@ def test_linear_invalid_arguments(lib):
     ws = torch.zeros(lib.fp8_linear_fwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError, match="ring"):
         lib.fp8_linear_fwd(x, x, None, M, N, K, E4M3, False, 0, None, None, ws, sc, out)
+
+
+def test_benchmark_step_4096_vs_oracle(lib, orc):
+    """The benchmark's own step (bench.Layer at M = N = K = 4096, delayed
+    HYBRID, ring 16, bias), in the launch configuration the benchmark
+    times: seeded, then two steps.  Every code array, step and ring is
+    compared bit for bit with the oracle's quantize and fold; the NT output,
+    dX and dW at sampled coordinates, and the bias gradient in full, within
+    the GEMM tolerance."""
+    import bench
+    n = 4096
+    L = bench.Layer(lib, torch, n)
+    host = {k: from_dev_bf16(getattr(L, k)) for k in ("x", "w", "bias", "g")}
+    x, w, bias, g = host["x"], host["w"], host["bias"], host["g"]
+    ox, ow, og = orc.Ring(16), orc.Ring(16), orc.Ring(16)
+    L.seed(lib)
+    ow.seed(w, E4M3)
+    ox.seed(x, E4M3)
+    og.seed(g, E5M2)
+    amax_x, amax_w, amax_g = orc.amax(x), orc.amax(w), orc.amax(g)
+    absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+    for t in range(2):
+        L.step(lib)
+        torch.cuda.synchronize()
+        # the oracle's steps, in the kernels' order
+        sx, sw, sg = np.float32(ox.scale), np.float32(ow.scale), np.float32(og.scale)
+        x8, x8b = orc.quantize(x, E4M3, sx), orc.quantize(x, E5M2, sx)
+        ox.fold(amax_x, E4M3)
+        w8, w8b = orc.quantize(w, E4M3, sw), orc.quantize(w, E5M2, sw)
+        ow.fold(amax_w, E4M3)
+        g8 = orc.quantize(g, E5M2, sg)
+        og.fold(amax_g, E5M2)
+        for r in (ox, ow, og):
+            r.advance()
+        sc = L.sfwd.cpu().numpy()
+        assert (sc[0], sc[1], L.sg.cpu().numpy()[0]) == (sx, sw, sg), t
+        for got, ref, name in ((L.x8, x8, "x8"), (L.x8b, x8b, "x8b"), (L.w8, w8, "w8"),
+                               (L.w8b, w8b, "w8b"), (L.g8, g8, "g8")):
+            assert np.array_equal(from_dev_u8(got), ref.ravel()), (t, name)
+        for gr, orr in ((L.rx, ox), (L.rw, ow), (L.rg, og)):
+            assert ring_state_equal(gr, orr) and gr.idx == orr.idx, t
+        s = _samples(n, n, 2000, 40 + t)
+        ref, ad = orc.gemm_sampled(x8, w8, E4M3, False, True, n, n, n, sx, sw, bias, s)
+        check_gemm(from_dev_bf16(L.out).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step fwd {t}")
+        s = _samples(n, n, 2000, 50 + t)
+        ref, ad = orc.gemm_sampled(g8, w8b, E5M2, False, False, n, n, n, sg, sw, None, s)
+        check_gemm(from_dev_bf16(L.dx).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step dX {t}")
+        s = _samples(n, n, 2000, 60 + t)
+        ref, ad = orc.gemm_sampled(g8, x8b, E5M2, True, False, n, n, n, sg, sx, None, s)
+        check_gemm(from_dev_bf16(L.dw).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step dW {t}")
+        check_gemm(from_dev_bf16(L.db), orc.colsum(g, n, n), absg, n, f"step db {t}")

@@ -28,7 +28,12 @@ weight is used as its codes with a step given by the caller (``w_scale``,
 fp32 [1] on the device); it is not re-quantized, has no ring and gets no
 gradient.  Its format must be the one the pass uses: the forward format,
 and for an input gradient the backward format too (E4M3 weights train
-under FP8Format.E4M3; under HYBRID only the forward is defined).
+under FP8Format.E4M3; under HYBRID only the forward is defined).  Such a
+weight may come with an fp8 bias of the same format and its step
+(``b_scale``), dequantized in the GEMM's epilogue, also without gradient.
+
+The backward reads everything it needs from the forward's context, so it
+runs in fp8 wherever ``backward()`` is called, inside the region or not.
 """
 
 from __future__ import annotations
@@ -40,9 +45,9 @@ import weakref
 
 import torch
 
-from . import (E4M3, E5M2, Ring, fp8_colsum, fp8_colsum_workspace, fp8_linear_bwd,
+from . import (E4M3, E5M2, OUT_BF16, Ring, fp8_colsum, fp8_colsum_workspace, fp8_linear_bwd,
                fp8_linear_bwd_workspace, fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
-               fp8_mm_pair, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
+               fp8_mm_ex, fp8_mm_pair, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
 
 __all__ = ["FP8Format", "FP8Recipe", "FP8TensorMeta", "FP8State", "fp8_state", "fp8_autocast",
            "current_config", "fp8_linear", "FP8Linear"]
@@ -305,11 +310,14 @@ class _LinearFp8Weight(torch.autograd.Function):
     used as is ([CMP] fp8.py fp8_linear_forward, the fp8-weight branch)."""
 
     @staticmethod
-    def forward(ctx, x, w8, w_scale, bias, cfg):
+    def forward(ctx, x, w8, w_scale, bias, b_scale, cfg):
         N, K = w8.shape
         fmt = _FP8_DTYPES[w8.dtype]
         if fmt != cfg.fp8_format.fwd():
             raise ValueError("fp8_linear: the weight's fp8 format is not the forward format")
+        bias8 = bias is not None and bias.dtype in _FP8_DTYPES
+        if bias8 and _FP8_DTYPES[bias.dtype] != fmt:
+            raise ValueError("fp8_linear: an fp8 bias must be in the weight's format")
         x2 = x.reshape(-1, K)
         M = x2.shape[0]
         dev = x.device
@@ -330,10 +338,16 @@ class _LinearFp8Weight(torch.autograd.Function):
                          margin=recipe.margin, scale_used=sx)
             ring.idx = (ring.idx + 1) % ring.len
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        fp8_mm(x8, w8.view(torch.uint8), fmt, 0, 1, M, N, K, K, K, 1, 0, 0, sx, w_scale,
-               None if bias is None else bias.view(torch.int16), out.view(torch.int16))
+        if bias8:  # fp8 bias codes and their step, dequantized in the epilogue
+            fp8_mm_ex(x8, w8.view(torch.uint8), fmt, 0, 1, M, N, K, K, K, 1, 0, 0, sx, w_scale,
+                      bias.view(torch.uint8), b_scale, OUT_BF16, None, out.view(torch.int16))
+        else:
+            fp8_mm(x8, w8.view(torch.uint8), fmt, 0, 1, M, N, K, K, K, 1, 0, 0, sx, w_scale,
+                   None if bias is None else bias.view(torch.int16), out.view(torch.int16))
         ctx.save_for_backward(w8, w_scale)
-        ctx.recipe, ctx.fmt_bwd, ctx.has_bias = recipe, cfg.fp8_format.bwd(), bias is not None
+        # a pre-quantized bias, like the weight, takes no gradient
+        ctx.recipe, ctx.fmt_bwd = recipe, cfg.fp8_format.bwd()
+        ctx.has_bias = bias is not None and not bias8
         ctx.x_shape = x.shape
         return out.reshape(*x.shape[:-1], N)
 
@@ -371,21 +385,28 @@ class _LinearFp8Weight(torch.autograd.Function):
             dx = dx.reshape(ctx.x_shape)
         elif db is not None:
             fp8_colsum(gi, M, N, db.view(torch.int16), cs_ws)
-        return dx, None, None, db, None
+        return dx, None, None, db, None, None
 
 
 def fp8_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
-               w_scale: torch.Tensor | None = None) -> torch.Tensor:
+               w_scale: torch.Tensor | None = None,
+               b_scale: torch.Tensor | None = None) -> torch.Tensor:
     """``F.linear`` with the fp8 path when an fp8_autocast region (or the
     default switch) enables it.  w: bf16 [N][K], or fp8 codes [N][K] with
-    their step ``w_scale`` (fp32 [1], device)."""
+    their step ``w_scale`` (fp32 [1], device).  With fp8 weight codes the
+    bias may be fp8 codes [N] of the same format with their step
+    ``b_scale`` ([LOG1] bias_scale), dequantized in the GEMM's epilogue."""
     cfg = current_config()
+    bias8 = bias is not None and bias.dtype in _FP8_DTYPES
+    if bias8 and (w.dtype not in _FP8_DTYPES or b_scale is None):
+        raise ValueError("fp8_linear: an fp8 bias needs fp8 weight codes and b_scale")
     if w.dtype in _FP8_DTYPES:
         if w_scale is None:
             raise ValueError("fp8_linear: a pre-quantized weight needs w_scale")
         if not cfg.enabled:
             raise ValueError("fp8_linear: a pre-quantized weight needs the fp8 path enabled")
-        return _LinearFp8Weight.apply(_bf16(x, "x"), w, w_scale, _bf16(bias, "bias"), cfg)
+        return _LinearFp8Weight.apply(_bf16(x, "x"), w, w_scale,
+                                      bias if bias8 else _bf16(bias, "bias"), b_scale, cfg)
     if not cfg.enabled:
         return torch.nn.functional.linear(x, w, bias)
     return _LinearFp8.apply(_bf16(x, "x"), _bf16(w, "w"), _bf16(bias, "bias"), cfg)

@@ -187,3 +187,77 @@ def test_binding_launches_on_torch_current_stream(lib):
         same = torch.equal(q, ref)  # torch's compare runs on the same side stream
     torch.cuda.synchronize()
     assert same
+
+
+def test_prequantized_weight_and_fp8_bias_vs_oracle(lib, fa, orc):
+    """E4M3 weight codes and E4M3 bias codes with their steps (w8 / b8):
+    the forward against the oracle's GEMM with an fp8 bias; neither takes a
+    gradient; an fp8 bias without fp8 weights is refused."""
+    M, N, K = 192, 320, 256
+    xb = wl.normal_bf16((M, K), 1.0, 31)
+    w8, sw = orc.quantize(wl.normal_bf16((N, K), 0.02, 32), E4M3, np.float32(2e-4)), \
+        np.float32(2e-4)
+    b8, sbias = orc.quantize(wl.normal_bf16((N,), 0.5, 33), E4M3, np.float32(0.01)), \
+        np.float32(0.01)
+    w8d = torch.from_numpy(w8).cuda().view(torch.float8_e4m3fn)
+    b8d = torch.from_numpy(b8).cuda().view(torch.float8_e4m3fn)
+    swd = torch.tensor([sw], device="cuda")
+    sbd = torch.tensor([sbias], device="cuda")
+    x = bf16(xb, (M, K)).requires_grad_(True)
+    with fa.fp8_autocast(recipe=fa.FP8Recipe(dynamic=True), fp8_format=fa.FP8Format.E4M3):
+        y = fa.fp8_linear(x, w8d, b8d, w_scale=swd, b_scale=sbd)
+        y.sum().backward()
+    torch.cuda.synchronize()
+    sx = orc.scale_from_peak(orc.amax(xb), E4M3)
+    x8 = orc.quantize(xb, E4M3, sx)
+    ref, _, ad = orc.gemm_ex(x8, w8, E4M3, False, True, M, N, K, sx, sw, b8, sbias)
+    check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N),
+               ref.reshape(M, N), ad.reshape(M, N), K, "w8/b8 fwd")
+    assert x.grad is not None and x.grad.shape == (M, K)
+    with fa.fp8_autocast():
+        with pytest.raises(ValueError, match="fp8 bias"):
+            fa.fp8_linear(x, bf16(wl.normal_bf16((N, K), 0.02, 34), (N, K)), b8d, b_scale=sbd)
+
+
+def _cos_and_norm_ratio(got, ref):
+    got, ref = got.double().ravel(), ref.double().ravel()
+    cos = float((got @ ref) / (got.norm() * ref.norm()))
+    return cos, float(got.norm() / ref.norm())
+
+
+@pytest.mark.parametrize("dynamic", [True, False])
+def test_backward_outside_region_and_vs_bf16(lib, fa, dynamic):
+    """The fp8 backward runs wherever backward() is called: outside the
+    fp8_autocast region of the forward it gives the bits it gives inside
+    (dynamic scaling; under delayed scaling each run moves the rings, so only
+    the comparison below applies), and the gradients follow the bf16
+    reference (fp32 math) in direction and norm within E5M2 noise."""
+    M, N, K = 512, 768, 1024
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    x0 = torch.randn(M, K, device="cuda", generator=gen).bfloat16()
+    w0 = (torch.randn(N, K, device="cuda", generator=gen) * 0.02).bfloat16()
+    b0 = (torch.randn(N, device="cuda", generator=gen) * 0.1).bfloat16()
+    g = (torch.randn(M, N, device="cuda", generator=gen) * 1e-3).bfloat16()
+    recipe = fa.FP8Recipe(dynamic=dynamic)
+
+    def run(backward_inside):
+        fa.fp8_state().reset()
+        x, w, b = (t.clone().requires_grad_(True) for t in (x0, w0, b0))
+        with fa.fp8_autocast(recipe=recipe):
+            y = fa.fp8_linear(x, w, b)
+            if backward_inside:
+                y.backward(g)
+        if not backward_inside:
+            y.backward(g)  # outside the region
+        torch.cuda.synchronize()
+        return x.grad, w.grad, b.grad
+
+    outside = run(False)
+    inside = run(True)
+    if dynamic:
+        for a, c in zip(outside, inside):
+            assert torch.equal(a, c)
+    ref = (g.float() @ w0.float(), g.float().t() @ x0.float(), g.float().sum(0))
+    for name, got, r in zip(("dX", "dW", "db"), outside, ref):
+        cos, ratio = _cos_and_norm_ratio(got, r)
+        assert cos > 0.99 and abs(ratio - 1) < 0.03, (name, cos, ratio)

@@ -311,12 +311,20 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
             // Loads are unconditional (a chunk past the range re-reads the
             // range's first one and is ignored), so their waits stay counted
             // one by one instead of collapsing into a wait for all of them.
+            // The input is read once: non-temporal loads, which keep it from
+            // displacing cached lines the next kernel reads (the layer step
+            // measured 1 % faster; the codes' stores stay ordinary).
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t c = c0 + u * kQuantThreads;
                 const int64_t cl = c < hi ? c : lo;
 #pragma unroll
-                for (int i = 0; i < kL; ++i) r[u][i] = xv[kL * cl + i];
+                for (int i = 0; i < kL; ++i) {
+                    const v4i t = __builtin_nontemporal_load(
+                        reinterpret_cast<const v4i*>(xv + kL * cl + i));
+                    r[u][i] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2],
+                                         (uint32_t)t[3]);
+                }
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)

@@ -109,7 +109,8 @@ fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const floa
                          uint8_t* out, float* ring_state, int32_t len, int32_t idx,
                          int32_t margin, float* scale_used, hipStream_t stream,
                          uint8_t* out2 = nullptr, int fmt2 = -1,
-                         int in_type = fp8lin::kInBf16, float* amax_out = nullptr) {
+                         int in_type = fp8lin::kInBf16, float* amax_out = nullptr,
+                         bool cached_input = false) {
     fp8lin::QuantLaunch q;
     q.x = x;
     q.in_type = in_type;
@@ -125,6 +126,7 @@ fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const floa
     q.pow2_margin = pow2f(margin);
     q.scale_used = scale_used;
     q.amax_out = amax_out;
+    q.cached_input = cached_input;
     hipError_t e = fp8lin::launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return FP8_OK;
@@ -559,17 +561,18 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
         // quantize with the scale it published.
         float* rx = scratch_ring(workspace, 0);
         float* rw = scratch_ring(workspace, 1);
+        // x and w are read twice in a row: ordinary (cached) loads.
         if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0, margin,
-                              nullptr, stream)))
+                              nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
             return st;
         if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0, margin,
-                              nullptr, stream)))
+                              nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
             return st;
         if ((st = do_quantize(x, M * K, fmt, rx + kScratchRingLen, x8, nullptr, 0, 0, margin, sx,
-                              stream)))
+                              stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
             return st;
         if ((st = do_quantize(w, N * K, fmt, rw + kScratchRingLen, w8, nullptr, 0, 0, margin, sw,
-                              stream)))
+                              stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
             return st;
     } else {
         if (!ring_w->initialized) {
@@ -646,25 +649,26 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         float* rg = scratch_ring(workspace, 0);
         float* rx = scratch_ring(workspace, 1);
         float* rw = scratch_ring(workspace, 2);
+        // each tensor is read again right after its measure: cached loads
         if ((st = do_quantize(g, M * N, fmt, nullptr, nullptr, rg, kScratchRingLen, 0, margin,
-                              nullptr, stream)))
+                              nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
             return st;
         if (db) {
             if ((st = do_quantize_colsum(g, M, N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0,
                                          margin, sg, db, ws + L.colsum, stream)))
                 return st;
         } else if ((st = do_quantize(g, M * N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0,
-                                     margin, sg, stream))) {
+                                     margin, sg, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true))) {
             return st;
         }
         if (dw) {
             if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0,
-                                  margin, nullptr, stream)))
+                                  margin, nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
                 return st;
         }
         if (dx) {
             if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0,
-                                  margin, nullptr, stream)))
+                                  margin, nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
                 return st;
         }
         sx = rx + kScratchRingLen;
@@ -689,11 +693,16 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         sx = scales_fwd;
         sw = scales_fwd + 1;
     }
+    // dynamic: w and x were just measured (cached); delayed: last read in the
+    // forward (cold, non-temporal loads)
+    const bool cached = dynamic != 0;
     if (dx && (st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
-                                scales_out ? scales_out + 2 : nullptr, stream)))
+                                scales_out ? scales_out + 2 : nullptr, stream, nullptr, -1,
+                                fp8lin::kInBf16, nullptr, cached)))
         return st;
     if (dw && (st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
-                                scales_out ? scales_out + 1 : nullptr, stream)))
+                                scales_out ? scales_out + 1 : nullptr, stream, nullptr, -1,
+                                fp8lin::kInBf16, nullptr, cached)))
         return st;
     // dX[M][K] = g8[M][N] . w8[N][K]  (NN)
     // dW[N][K] = g8^T . x8: A = g8 stored [M][N] (k-major rows of m), B = x8 [M][K]  (TN)

@@ -37,6 +37,10 @@ struct QuantLaunch {
     float pow2_margin = 1.0f;
     float* scale_used = nullptr;
     float* amax_out = nullptr;     // optional: receives max |x| (fp32)
+    // The input was just read and sits in the caches (a measure pass then
+    // the cast): ordinary loads.  Otherwise 2-byte inputs are loaded
+    // non-temporally, which skips the MALL for data read once.
+    bool cached_input = false;
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
 

@@ -69,6 +69,7 @@ struct QuantParams {
     float* amax_out;  // optional max |x| output: written by the fold, or (no
                       // ring) an atomic max over workgroups after an arming launch
     int vec;  // 1: x and out are 16-byte aligned
+    int nt;   // 1: non-temporal input loads (vector path, 2-byte inputs)
 };
 
 // Last-workgroup fold (wave 0): hist[idx] = amax;
@@ -311,19 +312,25 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
             // Loads are unconditional (a chunk past the range re-reads the
             // range's first one and is ignored), so their waits stay counted
             // one by one instead of collapsing into a wait for all of them.
-            // The input is read once: non-temporal loads, which keep it from
-            // displacing cached lines the next kernel reads (the layer step
-            // measured 1 % faster; the codes' stores stay ordinary).
+            // An input read once is loaded non-temporally (p.nt): it then
+            // skips the MALL, neither displacing lines the next kernel reads
+            // nor, when cold, losing anything (the layer step measured 1 %
+            // faster).  An input that a measure pass just read is cached, and
+            // fp32 inputs measured slower with the hint: ordinary loads.
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t c = c0 + u * kQuantThreads;
                 const int64_t cl = c < hi ? c : lo;
 #pragma unroll
                 for (int i = 0; i < kL; ++i) {
-                    const v4i t = __builtin_nontemporal_load(
-                        reinterpret_cast<const v4i*>(xv + kL * cl + i));
-                    r[u][i] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2],
-                                         (uint32_t)t[3]);
+                    if (IN != kInF32 && p.nt) {
+                        const v4i t = __builtin_nontemporal_load(
+                            reinterpret_cast<const v4i*>(xv + kL * cl + i));
+                        r[u][i] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2],
+                                             (uint32_t)t[3]);
+                    } else {
+                        r[u][i] = xv[kL * cl + i];
+                    }
                 }
             }
 #pragma unroll
@@ -417,6 +424,7 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     p.pow2_margin = q.pow2_margin;
     p.scale_used = q.scale_used;
     p.amax_out = q.amax_out;
+    p.nt = q.cached_input ? 0 : 1;
     const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
                          reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;

@@ -458,9 +458,9 @@ def components(f, torch):
         res[name] = dict(us=round(ms * 1e3, 2), gbs=round(3 * numel / (ms * 1e-3) / 1e9, 1),
                          hbm_frac=round(3 * numel / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
         del xs, q2, r2
-    # the small dynamic linear forward (256^3, E4M3, bias): five launches
-    # (measure x and w, quantize x and w, NT GEMM), as a graph replay (GPU
-    # time) and launched one by one (with the host's launch costs)
+    # the small dynamic linear forward (256^3, E4M3, bias): two launches (x
+    # and w measured and cast by one workgroup each, NT GEMM), as a graph
+    # replay (GPU time) and launched one by one (with the host's launch costs)
     res.update(linear_configs(f, torch))
     # the backward at M = N = K = 4096, two routes from bf16 g, x, w and the
     # forward's steps: NN + TN on row-major codes (this library's route:
@@ -505,7 +505,7 @@ def linear_configs(f, torch):
     ms_g = time_graph(torch, fwd, 50)
     ms_e = time_kernel(torch, fwd, 50)
     res["linear_fwd_dynamic_256"] = dict(us_graph=round(ms_g * 1e3, 2),
-                                         us_eager=round(ms_e * 1e3, 2), launches=5)
+                                         us_eager=round(ms_e * 1e3, 2), launches=2)
     d = wl.train()
     M, N, K = d["M"], d["N"], d["K"]
     x, w, b = up(d["x"][0]), up(d["w"]), up(d["bias"])

@@ -561,19 +561,30 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
         // quantize with the scale it published.
         float* rx = scratch_ring(workspace, 0);
         float* rw = scratch_ring(workspace, 1);
-        // x and w are read twice in a row: ordinary (cached) loads.
-        if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0, margin,
-                              nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
-            return st;
-        if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0, margin,
-                              nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
-            return st;
-        if ((st = do_quantize(x, M * K, fmt, rx + kScratchRingLen, x8, nullptr, 0, 0, margin, sx,
-                              stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
-            return st;
-        if ((st = do_quantize(w, N * K, fmt, rw + kScratchRingLen, w8, nullptr, 0, 0, margin, sw,
-                              stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
-            return st;
+        if (M * K <= fp8lin::kSmallDynamicNumel && N * K <= fp8lin::kSmallDynamicNumel) {
+            // small tensors: measure, step and cast of x and w in one launch
+            fp8lin::SmallDynamicJob jobs[2];
+            jobs[0].x = x, jobs[0].numel = M * K, jobs[0].out = x8, jobs[0].scale_out = sx;
+            jobs[1].x = w, jobs[1].numel = N * K, jobs[1].out = w8, jobs[1].scale_out = sw;
+            hipError_t e = fp8lin::launch_quantize_small_dynamic(jobs, 2, fmt, pow2f(margin),
+                                                                 stream);
+            if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        } else {
+            // x and w are read twice in a row: ordinary (cached) loads.
+            const int in = fp8lin::kInBf16;
+            if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0, margin,
+                                  nullptr, stream, nullptr, -1, in, nullptr, true)))
+                return st;
+            if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0, margin,
+                                  nullptr, stream, nullptr, -1, in, nullptr, true)))
+                return st;
+            if ((st = do_quantize(x, M * K, fmt, rx + kScratchRingLen, x8, nullptr, 0, 0, margin,
+                                  sx, stream, nullptr, -1, in, nullptr, true)))
+                return st;
+            if ((st = do_quantize(w, N * K, fmt, rw + kScratchRingLen, w8, nullptr, 0, 0, margin,
+                                  sw, stream, nullptr, -1, in, nullptr, true)))
+                return st;
+        }
     } else {
         if (!ring_w->initialized) {
             if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, ring_w->state, ring_w->len,
@@ -645,6 +656,7 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     float* sg = sc;
     const float* sx;
     const float* sw;
+    bool xw_cast = false;  // x8 / w8 already made (small dynamic path)
     if (dynamic) {
         float* rg = scratch_ring(workspace, 0);
         float* rx = scratch_ring(workspace, 1);
@@ -661,18 +673,42 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
                                      margin, sg, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true))) {
             return st;
         }
-        if (dw) {
-            if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0,
-                                  margin, nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
-                return st;
+        const bool small = (!dw || M * K <= fp8lin::kSmallDynamicNumel) &&
+                           (!dx || N * K <= fp8lin::kSmallDynamicNumel);
+        if (small && (dx || dw)) {
+            // small x and w: measure, step and cast in one launch
+            float* sxo = scales_out ? scales_out + 1 : rx + kScratchRingLen;
+            float* swo = scales_out ? scales_out + 2 : rw + kScratchRingLen;
+            fp8lin::SmallDynamicJob jobs[2];
+            int nj = 0;
+            if (dx) {
+                jobs[nj].x = w, jobs[nj].numel = N * K, jobs[nj].out = w8, jobs[nj].scale_out = swo;
+                ++nj;
+            }
+            if (dw) {
+                jobs[nj].x = x, jobs[nj].numel = M * K, jobs[nj].out = x8, jobs[nj].scale_out = sxo;
+                ++nj;
+            }
+            hipError_t e = fp8lin::launch_quantize_small_dynamic(jobs, nj, fmt, pow2f(margin),
+                                                                 stream);
+            if (e != hipSuccess) return hip_fail(e, "quantize launch");
+            xw_cast = true;
+            sx = sxo;
+            sw = swo;
+        } else {
+            if (dw) {
+                if ((st = do_quantize(x, M * K, fmt, nullptr, nullptr, rx, kScratchRingLen, 0,
+                                      margin, nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
+                    return st;
+            }
+            if (dx) {
+                if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0,
+                                      margin, nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
+                    return st;
+            }
+            sx = rx + kScratchRingLen;
+            sw = rw + kScratchRingLen;
         }
-        if (dx) {
-            if ((st = do_quantize(w, N * K, fmt, nullptr, nullptr, rw, kScratchRingLen, 0,
-                                  margin, nullptr, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true)))
-                return st;
-        }
-        sx = rx + kScratchRingLen;
-        sw = rw + kScratchRingLen;
     } else {
         if (!ring_g->initialized) {
             if ((st = do_quantize(g, M * N, fmt, nullptr, nullptr, ring_g->state, ring_g->len,
@@ -696,11 +732,11 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     // dynamic: w and x were just measured (cached); delayed: last read in the
     // forward (cold, non-temporal loads)
     const bool cached = dynamic != 0;
-    if (dx && (st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
+    if (dx && !xw_cast && (st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
                                 scales_out ? scales_out + 2 : nullptr, stream, nullptr, -1,
                                 fp8lin::kInBf16, nullptr, cached)))
         return st;
-    if (dw && (st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
+    if (dw && !xw_cast && (st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
                                 scales_out ? scales_out + 1 : nullptr, stream, nullptr, -1,
                                 fp8lin::kInBf16, nullptr, cached)))
         return st;

@@ -44,6 +44,20 @@ struct QuantLaunch {
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
 
+// Dynamic (current-amax) quantize of up to two small bf16 tensors in one
+// launch, one workgroup each: measure max |x|, derive the step, cast.  The
+// codes and steps equal those of a measure-only pass into a length-1 ring
+// followed by the cast with its step.  For numel <= kSmallDynamicNumel.
+constexpr int64_t kSmallDynamicNumel = int64_t(1) << 17;
+struct SmallDynamicJob {
+    const uint16_t* x = nullptr;
+    int64_t numel = 0;
+    uint8_t* out = nullptr;
+    float* scale_out = nullptr;  // receives the step
+};
+hipError_t launch_quantize_small_dynamic(const SmallDynamicJob* jobs, int njobs, int fmt,
+                                         float pow2_margin, hipStream_t stream);
+
 // Transposed quantize of bf16 q.x [rows][cols] into out_t [cols][rows]; with
 // q.out also the row-major codes (one read of x).  Ring, scale, scale_used as
 // launch_quantize; q.in_type must be bf16.

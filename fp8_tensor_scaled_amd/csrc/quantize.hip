@@ -438,6 +438,74 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// Dynamic (current-amax) quantize of small tensors in one launch: workgroup b
+// takes job b, measures max |x| over its whole tensor, derives the step as a
+// measure pass folding into a length-1 window does (max(amax / fmax /
+// 2^margin, 1e-12), two IEEE divisions), writes it out and casts the tensor
+// with the fp32 reciprocal of that step.  The second read comes from L2.
+// For small tensors the three launch-bound passes (measure, fold, cast)
+// become one launch for x and w together.
+// ---------------------------------------------------------------------------
+struct SmallDynParams {
+    SmallDynamicJob job[2];
+    float fmax;
+    float pow2_margin;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kQuantThreads) void quantize_small_dynamic_kernel(SmallDynParams p) {
+    const SmallDynamicJob j = p.job[blockIdx.x];
+    const int t = threadIdx.x;
+    const bool vec =
+        ((reinterpret_cast<uintptr_t>(j.x) | reinterpret_cast<uintptr_t>(j.out)) & 15) == 0;
+    const int64_t nvec = vec ? j.numel / kVecElems : 0;
+    const uint4* xv = reinterpret_cast<const uint4*>(j.x);
+    float amax = 0.0f;
+    for (int64_t c = t; c < nvec; c += kQuantThreads) {
+        const uint4 r[2] = {xv[2 * c], xv[2 * c + 1]};
+        amax = absmax16<kInBf16>(r, amax);
+    }
+    for (int64_t e = nvec * kVecElems + t; e < j.numel; e += kQuantThreads)
+        amax = fmaxf(amax, fabsf(bf16_to_f32(j.x[e])));
+    __shared__ float slots[kQuantWaves];
+    amax = wave_max(amax);
+    if (t % kWave == 0) slots[t / kWave] = amax;
+    __syncthreads();
+    float peak = slots[0];
+#pragma unroll
+    for (int w = 1; w < kQuantWaves; ++w) peak = fmaxf(peak, slots[w]);
+    const float s = fmaxf(__fdiv_rn(__fdiv_rn(peak, p.fmax), p.pow2_margin), 1e-12f);
+    const float m = __fdiv_rn(1.0f, s);
+    if (t == 0 && j.scale_out) *j.scale_out = s;
+    uint4* ov = reinterpret_cast<uint4*>(j.out);
+    for (int64_t c = t; c < nvec; c += kQuantThreads) {
+        const uint4 r[2] = {xv[2 * c], xv[2 * c + 1]};
+        encode16<kInBf16, FMT, -1>(r, m, ov + c, nullptr);
+    }
+    for (int64_t e = nvec * kVecElems + t; e < j.numel; e += kQuantThreads)
+        j.out[e] = cvt1<FMT>(bf16_to_f32(j.x[e]) * m);
+}
+
+hipError_t launch_quantize_small_dynamic(const SmallDynamicJob* jobs, int njobs, int fmt,
+                                         float pow2_margin, hipStream_t stream) {
+    if (njobs < 1 || njobs > 2) return hipErrorInvalidValue;
+    SmallDynParams p{};
+    for (int i = 0; i < njobs; ++i) {
+        if (jobs[i].numel > kSmallDynamicNumel) return hipErrorInvalidValue;
+        p.job[i] = jobs[i];
+    }
+    p.fmax = fmt ? 57344.0f : 448.0f;
+    p.pow2_margin = pow2_margin;
+    if (fmt == 0)
+        hipLaunchKernelGGL(quantize_small_dynamic_kernel<0>, dim3(njobs), dim3(kQuantThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL(quantize_small_dynamic_kernel<1>, dim3(njobs), dim3(kQuantThreads), 0,
+                           stream, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Standalone fold of an externally measured amax (one wave).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kWave) void ring_finalize_kernel(float* state, int32_t len,

@@ -252,3 +252,25 @@ def test_benchmark_step_4096_vs_oracle(lib, orc):
         ref, ad = orc.gemm_sampled(g8, x8b, E5M2, True, False, n, n, n, sg, sx, None, s)
         check_gemm(from_dev_bf16(L.dw).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step dW {t}")
         check_gemm(from_dev_bf16(L.db), orc.colsum(g, n, n), absg, n, f"step db {t}")
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 640, 384), (96, 1024, 256), (33, 17, 19)])
+def test_dynamic_forward_launch_paths(lib, orc, M, N, K):
+    """Dynamic forward with x and w both above the one-launch size (measure
+    and cast passes), one above and one below it, and both small with
+    ragged sizes (the one-launch kernel's scalar tail): same codes, steps
+    and outputs as the oracle."""
+    x = wl.normal_bf16((M, K), 1.0, M + K)
+    w = wl.normal_bf16((N, K), 0.02, N + K)
+    bias = wl.normal_bf16((N,), 0.1, N)
+    f = Fwd(lib, M, N, K)
+    lib.fp8_linear_fwd(to_dev_bf16(x), to_dev_bf16(w), to_dev_bf16(bias), M, N, K, E4M3, True, 0,
+                       None, None, f.ws, f.scales, f.out)
+    torch.cuda.synchronize()
+    ref = orc.linear_fwd(x, w, bias, M, N, K, E4M3, True)
+    sc = f.scales.cpu().numpy()
+    assert sc[0] == ref.sx and sc[1] == ref.sw
+    assert np.array_equal(f.x8(), ref.x8.ravel())
+    assert np.array_equal(f.w8(), ref.w8.ravel())
+    absdot = orc.gemm_absdot(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
+    check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, f"dyn fwd {M}x{N}x{K}")

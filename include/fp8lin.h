@@ -347,7 +347,9 @@ fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fm
  * (compare view: astrai/extension/fp8.py fp8_linear_forward)
  *
  * dynamic != 0: sx, sw are derived from the current amax of x and w
- *     (measure-only pass into length-1 scratch rings, then quantize).
+ *     (measure-only pass into length-1 scratch rings, then quantize; when
+ *     x and w have at most 2^17 elements each, one launch measures and
+ *     casts both, with the same codes and steps).
  *     ring_x / ring_w are ignored (may be NULL).
  * dynamic == 0 (delayed): ring_x and ring_w (host pointers, required) are
  *     seeded from the current tensors when not initialized; the scale in

@@ -89,10 +89,11 @@ def _load() -> ctypes.CDLL:
         "fp8_linear_fwd_workspace": (S, [I64, I64, I64]),
         "fp8_linear_fwd_x8_offset": (S, [I64, I64, I64]),
         "fp8_linear_fwd_w8_offset": (S, [I64, I64, I64]),
-        "fp8_linear_fwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, R, R, P, S, P, P, P]),
+        "fp8_linear_fwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, R, R, P, S, P, P, I32, P,
+                                 P, P]),
         "fp8_linear_bwd_workspace": (S, [I64, I64, I64]),
         "fp8_linear_bwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, P, R, P, S, P, P, P, P,
-                                 P]),
+                                 P, P, P]),
         "fp8_last_error": (ctypes.c_char_p, []),
         "fp8_version": (ctypes.c_char_p, []),
     }
@@ -354,17 +355,26 @@ def fp8_linear_bwd_workspace(M: int, N: int, K: int) -> int:
 
 def fp8_linear_fwd(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x: Ring | None,
                    ring_w: Ring | None, workspace: torch.Tensor, scales_out: torch.Tensor,
-                   out: torch.Tensor, stream=None) -> None:
+                   out: torch.Tensor, stream=None, fmt_bwd: int = E5M2,
+                   x8_bwd: torch.Tensor | None = None, w8_bwd: torch.Tensor | None = None) -> None:
+    """Forward of the linear layer; with x8_bwd / w8_bwd (delayed scaling)
+    the same pass also writes x's and w's codes in fmt_bwd for the backward;
+    see fp8lin.h."""
     st = _lib.fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, fmt, int(dynamic), margin,
                              _ring_ref(ring_x), _ring_ref(ring_w), _ptr(workspace),
-                             workspace.numel(), _ptr(scales_out), _ptr(out), _stream(stream))
+                             workspace.numel(), _ptr(scales_out), _ptr(out), fmt_bwd,
+                             _ptr(x8_bwd), _ptr(w8_bwd), _stream(stream))
     _check(st, "fp8_linear_fwd")
 
 
 def fp8_linear_bwd(g, x, w, M, N, K, fmt, dynamic, margin, scales_fwd, ring_g: Ring | None,
-                   workspace: torch.Tensor, scales_out, dx, dw, db, stream=None) -> None:
+                   workspace: torch.Tensor, scales_out, dx, dw, db, stream=None,
+                   x8_bwd: torch.Tensor | None = None, w8_bwd: torch.Tensor | None = None) -> None:
+    """Gradients of the linear layer; x8_bwd / w8_bwd (delayed scaling) are
+    the forward's backward-format codes, used instead of quantizing x / w;
+    see fp8lin.h."""
     st = _lib.fp8_linear_bwd(_ptr(g), _ptr(x), _ptr(w), M, N, K, fmt, int(dynamic), margin,
                              _ptr(scales_fwd), _ring_ref(ring_g), _ptr(workspace),
                              workspace.numel(), _ptr(scales_out), _ptr(dx), _ptr(dw), _ptr(db),
-                             _stream(stream))
+                             _ptr(x8_bwd), _ptr(w8_bwd), _stream(stream))
     _check(st, "fp8_linear_bwd")

@@ -527,11 +527,20 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
                             int64_t M, int64_t N, int64_t K, fp8_fmt_t fmt, int32_t dynamic,
                             int32_t margin, fp8_ring_t* ring_x, fp8_ring_t* ring_w,
                             void* workspace, size_t workspace_bytes, float* scales_out,
-                            uint16_t* out, hipStream_t stream) {
+                            uint16_t* out, fp8_fmt_t fmt_bwd, uint8_t* x8_bwd, uint8_t* w8_bwd,
+                            hipStream_t stream) {
     g_err[0] = 0;
     if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_linear_fwd: unsupported fp8 format %d", fmt);
     if (!x || !w || !out || !workspace || !scales_out)
         return fail(FP8_EINVAL, "fp8_linear_fwd: NULL pointer argument");
+    if (x8_bwd || w8_bwd) {
+        if (dynamic)
+            return fail(FP8_EINVAL,
+                        "fp8_linear_fwd: backward codes need delayed scaling (the dynamic "
+                        "backward measures its own steps)");
+        if (!fmt_ok(fmt_bwd))
+            return fail(FP8_EINVAL, "fp8_linear_fwd: unsupported backward format %d", fmt_bwd);
+    }
     if (M < 1 || N < 1 || K < 1) return fail(FP8_EINVAL, "fp8_linear_fwd: M, N, K must be >= 1");
     if (margin < 0 || margin > 64)
         return fail(FP8_EINVAL, "fp8_linear_fwd: margin %d outside [0, 64]", margin);
@@ -600,11 +609,15 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
         }
         // Each quantize reads the ring's published step (its snapshot goes
         // to scales_out) before its own last workgroup folds the new amax.
+        // With x8_bwd / w8_bwd the same pass also writes the backward's
+        // codes: the same scaled values in fmt_bwd.
         if ((st = do_quantize(x, M * K, fmt, ring_x->state + ring_x->len, x8, ring_x->state,
-                              ring_x->len, ring_x->idx, margin, sx, stream)))
+                              ring_x->len, ring_x->idx, margin, sx, stream, x8_bwd,
+                              x8_bwd ? (int)fmt_bwd : -1)))
             return st;
         if ((st = do_quantize(w, N * K, fmt, ring_w->state + ring_w->len, w8, ring_w->state,
-                              ring_w->len, ring_w->idx, margin, sw, stream)))
+                              ring_w->len, ring_w->idx, margin, sw, stream, w8_bwd,
+                              w8_bwd ? (int)fmt_bwd : -1)))
             return st;
     }
     if ((st = do_gemm(x8, w8, fmt, 0, 1, M, N, K, K, K, sx, sw, bias, out, stream))) return st;
@@ -624,12 +637,17 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
                             int64_t N, int64_t K, fp8_fmt_t fmt, int32_t dynamic,
                             int32_t margin, const float* scales_fwd, fp8_ring_t* ring_g,
                             void* workspace, size_t workspace_bytes, float* scales_out,
-                            uint16_t* dx, uint16_t* dw, uint16_t* db, hipStream_t stream) {
+                            uint16_t* dx, uint16_t* dw, uint16_t* db, const uint8_t* x8_bwd,
+                            const uint8_t* w8_bwd, hipStream_t stream) {
     g_err[0] = 0;
     if (!fmt_ok(fmt)) return fail(FP8_EINVAL, "fp8_linear_bwd: unsupported fp8 format %d", fmt);
     if (!g || !workspace) return fail(FP8_EINVAL, "fp8_linear_bwd: NULL g or workspace");
-    if (dx && !w) return fail(FP8_EINVAL, "fp8_linear_bwd: dx needs w");
-    if (dw && !x) return fail(FP8_EINVAL, "fp8_linear_bwd: dw needs x");
+    if (dx && !w && !w8_bwd) return fail(FP8_EINVAL, "fp8_linear_bwd: dx needs w or w8_bwd");
+    if (dw && !x && !x8_bwd) return fail(FP8_EINVAL, "fp8_linear_bwd: dw needs x or x8_bwd");
+    if (dynamic && (x8_bwd || w8_bwd))
+        return fail(FP8_EINVAL,
+                    "fp8_linear_bwd: pre-quantized x / w need delayed scaling (the dynamic "
+                    "backward measures its own steps)");
     if (M < 1 || N < 1 || K < 1) return fail(FP8_EINVAL, "fp8_linear_bwd: M, N, K must be >= 1");
     if (margin < 0 || margin > 64)
         return fail(FP8_EINVAL, "fp8_linear_bwd: margin %d outside [0, 64]", margin);
@@ -732,19 +750,24 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     // dynamic: w and x were just measured (cached); delayed: last read in the
     // forward (cold, non-temporal loads)
     const bool cached = dynamic != 0;
-    if (dx && !xw_cast && (st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
-                                scales_out ? scales_out + 2 : nullptr, stream, nullptr, -1,
-                                fp8lin::kInBf16, nullptr, cached)))
+    const int in = fp8lin::kInBf16;
+    if (dx && !xw_cast && !w8_bwd &&
+        (st = do_quantize(w, N * K, fmt, sw, w8, nullptr, 0, 0, margin,
+                          scales_out ? scales_out + 2 : nullptr, stream, nullptr, -1, in,
+                          nullptr, cached)))
         return st;
-    if (dw && !xw_cast && (st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
-                                scales_out ? scales_out + 1 : nullptr, stream, nullptr, -1,
-                                fp8lin::kInBf16, nullptr, cached)))
+    if (dw && !xw_cast && !x8_bwd &&
+        (st = do_quantize(x, M * K, fmt, sx, x8, nullptr, 0, 0, margin,
+                          scales_out ? scales_out + 1 : nullptr, stream, nullptr, -1, in,
+                          nullptr, cached)))
         return st;
     // dX[M][K] = g8[M][N] . w8[N][K]  (NN)
     // dW[N][K] = g8^T . x8: A = g8 stored [M][N] (k-major rows of m), B = x8 [M][K]  (TN)
     // Both from one launch when both are wanted (independent products).
-    const fp8lin::GemmLaunch gdx = gemm_of(g8, w8, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx);
-    const fp8lin::GemmLaunch gdw = gemm_of(g8, x8, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw);
+    const uint8_t* w8u = w8_bwd ? w8_bwd : w8;  // caller's pre-quantized codes, if any
+    const uint8_t* x8u = x8_bwd ? x8_bwd : x8;
+    const fp8lin::GemmLaunch gdx = gemm_of(g8, w8u, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx);
+    const fp8lin::GemmLaunch gdw = gemm_of(g8, x8u, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw);
     if (dx && dw) {
         if ((st = do_gemm_pair(gdx, gdw, stream))) return st;
     } else if (dx) {

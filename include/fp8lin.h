@@ -367,6 +367,14 @@ fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fm
  * scales_out: fp32 [2] (device) receives the steps used, [sx, sw]; the
  *     delayed backward reuses them.
  * bias: bf16 [N] or NULL.  out: bf16 [M][N].  M, N, K >= 1.
+ * x8_bwd, w8_bwd: nullable outputs, fp8 [M][K] and [N][K] in fmt_bwd:
+ *     x and w quantized with the forward's steps sx, sw in the backward
+ *     format, written by the same pass that makes the forward's codes --
+ *     exactly the operands fp8_linear_bwd makes from bf16 x and w under
+ *     delayed scaling (commit log 3e57cc8: a pre-quantized operand skips
+ *     its quantize kernel).  Delayed scaling only (FP8_EINVAL with
+ *     dynamic != 0: the dynamic backward measures its own steps).
+ *     fmt_bwd is read only when one of them is given.
  * ------------------------------------------------------------------- */
 size_t fp8_linear_fwd_workspace(int64_t M, int64_t N, int64_t K);
 size_t fp8_linear_fwd_x8_offset(int64_t M, int64_t N, int64_t K);
@@ -375,7 +383,8 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
                             int64_t M, int64_t N, int64_t K, fp8_fmt_t fmt,
                             int32_t dynamic, int32_t margin, fp8_ring_t* ring_x,
                             fp8_ring_t* ring_w, void* workspace, size_t workspace_bytes,
-                            float* scales_out, uint16_t* out, hipStream_t stream);
+                            float* scales_out, uint16_t* out, fp8_fmt_t fmt_bwd,
+                            uint8_t* x8_bwd, uint8_t* w8_bwd, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * fp8_linear_bwd -- gradients of the linear layer in the backward format.
@@ -402,7 +411,11 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  *     with the forward's 6656-byte control block and zero-once contract;
  *     it receives g8 [M][N] at fp8_linear_fwd_x8_offset(M, N, K).
  * scales_out: nullable fp32 [3] receives [sg, sx, sw]; sx is written only
- *     when dw is made, sw only when dx is made.
+ *     when dw is made from x here, sw only when dx is made from w here.
+ * x8_bwd, w8_bwd: nullable, the backward-format codes of x and w with the
+ *     forward's steps (fp8_linear_fwd's outputs of the same names); when
+ *     given, that quantize is skipped and x (or w) may be NULL.  Delayed
+ *     scaling only (FP8_EINVAL with dynamic != 0).
  * ------------------------------------------------------------------- */
 size_t fp8_linear_bwd_workspace(int64_t M, int64_t N, int64_t K);
 fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t* w,
@@ -410,7 +423,7 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
                             int32_t dynamic, int32_t margin, const float* scales_fwd,
                             fp8_ring_t* ring_g, void* workspace, size_t workspace_bytes,
                             float* scales_out, uint16_t* dx, uint16_t* dw, uint16_t* db,
-                            hipStream_t stream);
+                            const uint8_t* x8_bwd, const uint8_t* w8_bwd, hipStream_t stream);
 
 /* Message of the last non-OK status returned on the calling thread
  * (thread-local; "" if none). */

@@ -294,16 +294,27 @@ def test_valid_call_without_gpu_reports_hip_error(f):
 def test_linear_validation(f):
     lib = f._lib
     st = lib.fp8_linear_fwd(FAKE, FAKE, None, 32, 32, 32, 0, 0, 0, None, None, FAKE, 1 << 20,
-                            FAKE, FAKE, None)
+                            FAKE, FAKE, 1, None, None, None)
     assert st == 1 and "ring" in _err(lib)
     st = lib.fp8_linear_fwd(FAKE, FAKE, None, 32, 32, 32, 0, 1, 0, None, None, FAKE, 16, FAKE,
-                            FAKE, None)
+                            FAKE, 1, None, None, None)
     assert st == 1 and "workspace" in _err(lib)
+    st = lib.fp8_linear_fwd(FAKE, FAKE, None, 32, 32, 32, 0, 1, 0, None, None, FAKE, 1 << 20,
+                            FAKE, FAKE, 1, FAKE, None, None)
+    assert st == 1 and "delayed scaling" in _err(lib)
+    r = f._RingC(0x1000, 16, 0, 0, 0)
+    r2 = f._RingC(0x2000, 16, 0, 0, 0)
+    st = lib.fp8_linear_fwd(FAKE, FAKE, None, 32, 32, 32, 0, 0, 0, ctypes.byref(r),
+                            ctypes.byref(r2), FAKE, 1 << 20, FAKE, FAKE, 7, None, FAKE, None)
+    assert st == 1 and "backward format" in _err(lib)
     st = lib.fp8_linear_bwd(FAKE, FAKE, FAKE, 32, 32, 32, 1, 0, 0, None, None, FAKE, 1 << 20,
-                            None, FAKE, FAKE, FAKE, None)
+                            None, FAKE, FAKE, FAKE, None, None, None)
     assert st == 1 and "scales_fwd" in _err(lib)
     st = lib.fp8_linear_bwd(FAKE, None, FAKE, 32, 32, 32, 1, 1, 0, None, None, FAKE, 1 << 20,
-                            None, FAKE, FAKE, FAKE, None)
-    assert st == 1 and "dw needs x" in _err(lib)
+                            None, FAKE, FAKE, FAKE, None, None, None)
+    assert st == 1 and "dw needs x or x8_bwd" in _err(lib)
+    st = lib.fp8_linear_bwd(FAKE, None, FAKE, 32, 32, 32, 1, 1, 0, None, None, FAKE, 1 << 20,
+                            None, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == 1 and "delayed scaling" in _err(lib)
     st = lib.fp8_colsum(FAKE, 10, 10, FAKE, FAKE, 4, None)
     assert st == 1 and "workspace" in _err(lib)

@@ -274,3 +274,49 @@ def test_dynamic_forward_launch_paths(lib, orc, M, N, K):
     assert np.array_equal(f.w8(), ref.w8.ravel())
     absdot = orc.gemm_absdot(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
     check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, f"dyn fwd {M}x{N}x{K}")
+
+
+def test_backward_codes_from_the_forward(lib, orc):
+    """Delayed HYBRID over three steps, twice: with bf16 x and w passed to
+    the backward, and with the forward writing x's and w's E5M2 codes
+    (x8_bwd, w8_bwd) that the backward takes instead (x and w NULL there).
+    Outputs, gradients, steps and rings are bit-identical; the codes equal
+    the oracle's quantize of x and w with the forward's steps."""
+    d = wl.train(M=512, N=768, K=384, steps=3)
+    M, N, K = d["M"], d["N"], d["K"]
+    wd, bd = to_dev_bf16(d["w"]), to_dev_bf16(d["bias"])
+    runs = []
+    for use_codes in (False, True):
+        f = Fwd(lib, M, N, K)
+        bws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8,
+                          device="cuda")
+        rx, rw, rg = lib.Ring(16), lib.Ring(16), lib.Ring(16)
+        x8b = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+        w8b = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+        rec = []
+        for t in range(3):
+            xd, gd = to_dev_bf16(d["x"][t]), to_dev_bf16(d["g"][t])
+            dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
+            dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
+            db = torch.empty(N, dtype=torch.int16, device="cuda")
+            if use_codes:
+                lib.fp8_linear_fwd(xd, wd, bd, M, N, K, E4M3, False, 0, rx, rw, f.ws, f.scales,
+                                   f.out, fmt_bwd=E5M2, x8_bwd=x8b, w8_bwd=w8b)
+                lib.fp8_linear_bwd(gd, None, None, M, N, K, E5M2, False, 0, f.scales, rg, bws,
+                                   None, dx, dw, db, x8_bwd=x8b, w8_bwd=w8b)
+                torch.cuda.synchronize()
+                sx, sw = (np.float32(v) for v in f.scales.cpu().numpy())
+                assert np.array_equal(from_dev_u8(x8b), orc.quantize(d["x"][t], E5M2, sx).ravel())
+                assert np.array_equal(from_dev_u8(w8b), orc.quantize(d["w"], E5M2, sw).ravel())
+            else:
+                lib.fp8_linear_fwd(xd, wd, bd, M, N, K, E4M3, False, 0, rx, rw, f.ws, f.scales,
+                                   f.out)
+                lib.fp8_linear_bwd(gd, xd, wd, M, N, K, E5M2, False, 0, f.scales, rg, bws, None,
+                                   dx, dw, db)
+                torch.cuda.synchronize()
+            rec.append([t.clone() for t in (f.out, dx, dw, db, f.scales, rx.state, rw.state,
+                                             rg.state)])
+        runs.append(rec)
+    for t in range(3):
+        for a, b in zip(runs[0][t], runs[1][t]):
+            assert torch.equal(a, b), t

@@ -161,9 +161,15 @@ class Layer:
         self.g = up(wl.normal_bf16((M, N), 1e-3, seed0 + 4))
         u8 = dict(dtype=torch.uint8, device=dev)
         i16 = dict(dtype=torch.int16, device=dev)
-        self.x8 = torch.empty(M * K, **u8)
-        self.w8 = torch.empty(N * K, **u8)
-        self.g8 = torch.empty(M * N, **u8)
+        # the linear calls' workspaces (zeroed once); the forward's codes of x
+        # and w, and the backward's codes of g, live in them
+        self.fws = torch.zeros(f.fp8_linear_fwd_workspace(M, N, K), **u8)
+        self.bws = torch.zeros(f.fp8_linear_bwd_workspace(M, N, K), **u8)
+        xo, wo = f.fp8_linear_fwd_x8_offset(M, N, K), f.fp8_linear_fwd_w8_offset(M, N, K)
+        self.x8 = self.fws[xo: xo + M * K]
+        self.w8 = self.fws[wo: wo + N * K]
+        self.g8 = self.bws[xo: xo + M * N]
+        # the backward's E5M2 codes of x and w, written by the forward's pass
         self.x8b = torch.empty(M * K, **u8)
         self.w8b = torch.empty(N * K, **u8)
         self.out = torch.empty(M * N, **i16)
@@ -171,7 +177,8 @@ class Layer:
         self.dw = torch.empty(N * K, **i16)
         self.db = torch.empty(N, **i16)
         self.sfwd = torch.zeros(2, dtype=torch.float32, device=dev)
-        self.sg = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.sb = torch.zeros(3, dtype=torch.float32, device=dev)  # [sg, sx, sw] of the backward
+        self.sg = self.sb[0:1]
         self.cs_ws = torch.empty(f.fp8_colsum_workspace(M, N), **u8)
         self.rx, self.rw, self.rg = f.Ring(16), f.Ring(16), f.Ring(16)
 
@@ -184,23 +191,19 @@ class Layer:
             r.initialized = True
 
     def step(self, f):
+        """One fwd + bwd of the layer through the C-ABI linear calls: the
+        forward quantizes x and w once each into E4M3 (its GEMM) and E5M2
+        (the backward's operands, same steps), folds both rings and runs the
+        NT GEMM; the backward quantizes g with its ring and its column sums
+        in one pass, then dX (NN) and dW (TN) in one paired launch.  The
+        calls advance the rings."""
         M, N, K = self.M, self.N, self.K
-        sx, sw = self.sfwd[0:1], self.sfwd[1:2]
-        # forward: x and w quantized with their rings' steps (amax folded),
-        # each in one pass that also writes the backward's E5M2 codes with
-        # the same step; NT GEMM in E4M3
-        f.fp8_quantize2(self.x, E4M3, self.rx.scale, self.x8, E5M2, self.x8b, ring=self.rx,
-                        scale_used=sx)
-        f.fp8_quantize2(self.w, E4M3, self.rw.scale, self.w8, E5M2, self.w8b, ring=self.rw,
-                        scale_used=sw)
-        self.gemm_nt_fwd(f)
-        # backward (E5M2): g with its ring, its column sum (bias gradient)
-        # from the same pass; dX (NN) and dW (TN)
-        f.fp8_quantize_colsum(self.g, M, N, E5M2, self.rg.scale, self.g8, self.db, self.cs_ws,
-                              ring=self.rg, scale_used=self.sg)
-        self.gemm_bwd_pair(f)
-        for r in (self.rx, self.rw, self.rg):
-            r.idx = (r.idx + 1) % r.len
+        f.fp8_linear_fwd(self.x, self.w, self.bias, M, N, K, E4M3, False, 0, self.rx, self.rw,
+                         self.fws, self.sfwd, self.out, fmt_bwd=E5M2, x8_bwd=self.x8b,
+                         w8_bwd=self.w8b)
+        f.fp8_linear_bwd(self.g, None, None, M, N, K, E5M2, False, 0, self.sfwd, self.rg,
+                         self.bws, self.sb, self.dx, self.dw, self.db, x8_bwd=self.x8b,
+                         w8_bwd=self.w8b)
 
     # The step's three GEMMs on its own operands (also timed on their own).
     def gemm_nt_fwd(self, f):
@@ -230,7 +233,9 @@ class Layer:
 
 
 def check_against_linear_entry_points(f, torch):
-    """The benchmark step and fp8_linear_fwd / _bwd give identical bits."""
+    """The benchmark step (the backward's x and w codes from the forward's
+    pass) and fp8_linear_fwd / _bwd quantizing x and w again in the backward
+    give identical bits."""
     ref = Layer(f, torch, 256, seed0=900)
     ref.seed(f)
     ref.step(f)

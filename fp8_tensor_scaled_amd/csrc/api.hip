@@ -135,7 +135,8 @@ fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const floa
 fp8_status_t do_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt_t fmt,
                                 const float* scale, uint8_t* out, float* ring_state,
                                 int32_t len, int32_t idx, int32_t margin, float* scale_used,
-                                uint16_t* db, void* ws, hipStream_t stream) {
+                                uint16_t* db, void* ws, hipStream_t stream,
+                                fp8lin::ColsumFinalJob* defer = nullptr) {
     fp8lin::QuantLaunch q;
     q.x = g;
     q.numel = m * n;
@@ -147,7 +148,7 @@ fp8_status_t do_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt
     q.ring_idx = idx;
     q.pow2_margin = pow2f(margin);
     q.scale_used = scale_used;
-    hipError_t e = fp8lin::launch_quantize_colsum(q, m, n, db, ws, stream);
+    hipError_t e = fp8lin::launch_quantize_colsum(q, m, n, db, ws, stream, defer);
     if (e != hipSuccess) return hip_fail(e, "quantize + colsum launch");
     return FP8_OK;
 }
@@ -192,8 +193,8 @@ fp8_status_t do_gemm_launch(const fp8lin::GemmLaunch& g, hipStream_t stream) {
 }
 
 fp8_status_t do_gemm_pair(const fp8lin::GemmLaunch& g0, const fp8lin::GemmLaunch& g1,
-                          hipStream_t stream) {
-    hipError_t e = fp8lin::launch_gemm_pair(g0, g1, stream);
+                          hipStream_t stream, const fp8lin::ColsumFinalJob* cf = nullptr) {
+    hipError_t e = fp8lin::launch_gemm_pair(g0, g1, stream, cf);
     if (e != hipSuccess) return hip_fail(e, "gemm pair launch");
     return FP8_OK;
 }
@@ -671,6 +672,10 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     uint8_t* w8 = ws + L.w8;
     // Scales used: in scales_out when given, else in the control block.
     float* sc = scales_out ? scales_out : scratch_ring(workspace, 3);
+    // With dX and dW both wanted, the bias gradient's last pass rides on
+    // their paired launch.
+    fp8lin::ColsumFinalJob cf;
+    fp8lin::ColsumFinalJob* defer = dx && dw ? &cf : nullptr;
     float* sg = sc;
     const float* sx;
     const float* sw;
@@ -685,7 +690,7 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
             return st;
         if (db) {
             if ((st = do_quantize_colsum(g, M, N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0,
-                                         margin, sg, db, ws + L.colsum, stream)))
+                                         margin, sg, db, ws + L.colsum, stream, defer)))
                 return st;
         } else if ((st = do_quantize(g, M * N, fmt, rg + kScratchRingLen, g8, nullptr, 0, 0,
                                      margin, sg, stream, nullptr, -1, fp8lin::kInBf16, nullptr, true))) {
@@ -737,7 +742,7 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         if (db) {
             if ((st = do_quantize_colsum(g, M, N, fmt, ring_g->state + ring_g->len, g8,
                                          ring_g->state, ring_g->len, ring_g->idx, margin, sg, db,
-                                         ws + L.colsum, stream)))
+                                         ws + L.colsum, stream, defer)))
                 return st;
         } else if ((st = do_quantize(g, M * N, fmt, ring_g->state + ring_g->len, g8,
                                      ring_g->state, ring_g->len, ring_g->idx, margin, sg,
@@ -769,7 +774,7 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     const fp8lin::GemmLaunch gdx = gemm_of(g8, w8u, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx);
     const fp8lin::GemmLaunch gdw = gemm_of(g8, x8u, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw);
     if (dx && dw) {
-        if ((st = do_gemm_pair(gdx, gdw, stream))) return st;
+        if ((st = do_gemm_pair(gdx, gdw, stream, &cf))) return st;
     } else if (dx) {
         if ((st = do_gemm_launch(gdx, stream))) return st;
     } else if (dw) {

@@ -105,6 +105,42 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Bias gradient, last pass: db[c] = bf16 of the sum over chunks k of the
+// partial column sums part[k][c], for the T/4 columns c0 .. c0 + T/4 - 1 of
+// one workgroup of T lanes.  Lane group q (T/4 lanes, one column each) adds
+// the q-th quarter of the chunks in chunk order; the four quarter sums are
+// then added as ((0 + 1) + 2) + 3 and rounded once (RNE).  The arithmetic
+// depends on the chunk count and the data only, not on T.  `red` is T
+// floats of LDS.  Every lane of the workgroup must call it.
+template <int T>
+__device__ __forceinline__ void colsum_final_cols(const float* part, int64_t chunks, int64_t n,
+                                                  int64_t c0, uint16_t* db, float* red) {
+    constexpr int kCols = T / 4;
+    const int col = threadIdx.x % kCols;
+    const int q = threadIdx.x / kCols;
+    const int64_t c = c0 + col;
+    float acc = 0.0f;
+    if (c < n) {
+        const int64_t per = (chunks + 3) / 4;
+        const int64_t b = q * per;
+        const int64_t e = b + per < chunks ? b + per : chunks;
+        // 8 loads in flight, then their adds in chunk order
+        for (int64_t k = b; k < e; k += 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = k + i < e ? part[(k + i) * n + c] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (k + i < e) acc += v[i];
+        }
+    }
+    red[q * kCols + col] = acc;
+    __syncthreads();
+    if (q == 0 && c < n)
+        db[c] = f32_to_bf16(((red[col] + red[kCols + col]) + red[2 * kCols + col]) +
+                            red[3 * kCols + col]);
+}
+
 // One fp8 MFMA: D(16x16, fp32) += X(16x128) . Y(16x128)^T.
 // Lane l holds row l%16 of X and of Y, bytes k = 32*(l/16) .. +31; the
 // result row 4*(l/16)+i, column l%16 sits in register i.

@@ -132,13 +132,17 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream) {
     return launch_generic(g, stream);
 }
 
-hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream) {
+hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream,
+                            const ColsumFinalJob* cf) {
+    const bool job = cf && cf->db;
     if (!gemm_skinny_supported(g0) && !gemm_skinny_supported(g1) &&
-        gemm_tiled_pair_supported(g0, g1))
-        return launch_gemm_tiled_pair(g0, g1, stream);
+        gemm_tiled_pair_supported(g0, g1) && (!job || gemm_tiled_pair_carries(g0, g1, *cf)))
+        return launch_gemm_tiled_pair(g0, g1, stream, job ? cf : nullptr);
     hipError_t e = launch_gemm(g0, stream);
     if (e != hipSuccess) return e;
-    return launch_gemm(g1, stream);
+    e = launch_gemm(g1, stream);
+    if (e != hipSuccess || !job) return e;
+    return launch_colsum_final_job(*cf, stream);
 }
 
 }  // namespace fp8lin

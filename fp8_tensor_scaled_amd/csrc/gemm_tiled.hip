@@ -823,15 +823,23 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 // the rest problem 1's.  One workgroup fits a CU, so problem 1's tiles start
 // on CUs as problem 0's finish: their prologue loads overlap problem 0's
 // output stores, and there is one launch boundary instead of two.
+// Workgroups past n0 + n1 run the bias gradient's last pass (`cf`, 128
+// columns each): the highest ids are dispatched last, so they take CUs as
+// the last tiles finish, in place of a launch of their own.  Stream order
+// makes the partials (written by an earlier launch) visible to them.
 template <int FMT>
 __global__ __launch_bounds__(512, 1) void gemm_tiled_pair_kernel(TiledParams p0, TiledParams p1,
-                                                                  int n0) {
+                                                                  int n0, int n1,
+                                                                  ColsumFinalJob cf) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<256, 256, 64, 4>()];
     const int b = blockIdx.x;
     if (b < n0)
         gemm_tile<FMT, false, true, 256, 256, 2, 4, 64, 4>(p0, b, n0, smem);
+    else if (b < n0 + n1)
+        gemm_tile<FMT, true, true, 256, 256, 2, 4, 64, 4>(p1, b - n0, n1, smem);
     else
-        gemm_tile<FMT, true, true, 256, 256, 2, 4, 64, 4>(p1, b - n0, (int)gridDim.x - n0, smem);
+        colsum_final_cols<512>(cf.part, cf.chunks, cf.n, (int64_t)(b - n0 - n1) * 128, cf.db,
+                               reinterpret_cast<float*>(smem));
 }
 
 // ---------------------------------------------------------------------------
@@ -954,19 +962,33 @@ bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1) {
     return n0 >= 256 && n1 >= 256 && (double)n0 + (double)n1 < 2147483647.0;
 }
 
+bool gemm_tiled_pair_carries(const GemmLaunch& g0, const GemmLaunch& g1,
+                             const ColsumFinalJob& cf) {
+    const int64_t extra = (cf.n + 127) / 128;
+    return cf.db && cf.n >= 1 && (double)tiles256(g0) + (double)tiles256(g1) + (double)extra <
+                                     2147483647.0;
+}
+
 hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const ColsumFinalJob* cf) {
     TiledParams p0 = tiled_params<256, 256>(g0);
     TiledParams p1 = tiled_params<256, 256>(g1);
     const int n0 = (int)tiles256(g0), n1 = (int)tiles256(g1);
     // problem 1's local ids line up with the XCDs only if n0 is a multiple of 8
     p1.xcd_remap = p1.xcd_remap && (n0 % 8) == 0;
+    ColsumFinalJob job;
+    int extra = 0;
+    if (cf && cf->db) {  // callers check gemm_tiled_pair_carries first
+        job = *cf;
+        extra = (int)((cf->n + 127) / 128);
+    }
+    const dim3 grid((unsigned)(n0 + n1 + extra));
     if (g0.fmt == 0)
-        hipLaunchKernelGGL(gemm_tiled_pair_kernel<0>, dim3((unsigned)(n0 + n1)), dim3(512), 0,
-                           stream, p0, p1, n0);
+        hipLaunchKernelGGL(gemm_tiled_pair_kernel<0>, grid, dim3(512), 0, stream, p0, p1, n0, n1,
+                           job);
     else
-        hipLaunchKernelGGL(gemm_tiled_pair_kernel<1>, dim3((unsigned)(n0 + n1)), dim3(512), 0,
-                           stream, p0, p1, n0);
+        hipLaunchKernelGGL(gemm_tiled_pair_kernel<1>, grid, dim3(512), 0, stream, p0, p1, n0, n1,
+                           job);
     return hipGetLastError();
 }
 

@@ -15,6 +15,11 @@ hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream);
 // Two independent problems in one launch: problem 0 NN and problem 1 TN,
 // same format, both large enough for 256x256 tiles.
 bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1);
-hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream);
+// Whether the paired launch of a supported pair can also run `cf` (extra
+// workgroups at the end of its grid).
+bool gemm_tiled_pair_carries(const GemmLaunch& g0, const GemmLaunch& g1,
+                             const ColsumFinalJob& cf);
+hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream,
+                                  const ColsumFinalJob* cf = nullptr);
 
 }  // namespace fp8lin

@@ -90,10 +90,24 @@ struct GemmLaunch {
     bool ext() const { return bias_scale != nullptr || out_q >= 0; }
 };
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
+
+// The bias gradient's last pass (chunk partials -> bf16 db) as a job that
+// another launch can carry; db == nullptr: no job.
+struct ColsumFinalJob {
+    const float* part = nullptr;  // [chunks][n]
+    int64_t chunks = 0;
+    int64_t n = 0;
+    uint16_t* db = nullptr;
+};
+hipError_t launch_colsum_final_job(const ColsumFinalJob& j, hipStream_t stream);
+
 // Two independent GEMMs: one launch when both take the tiled kernels' paired
 // form (the linear backward's NN dX and TN dW), else launch_gemm twice in
-// order.  Results are bit-identical to the two separate launches.
-hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream);
+// order.  Results are bit-identical to the two separate launches.  A job
+// `cf` (nullable) rides along as extra workgroups of the paired launch, or
+// runs as its own launch after the two.
+hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream,
+                            const ColsumFinalJob* cf = nullptr);
 
 // Column sum (bias gradient).
 size_t colsum_workspace(int64_t m, int64_t n);
@@ -101,8 +115,11 @@ hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, 
                          hipStream_t stream);
 // Quantize of g [m][n] (q.x = g, q.numel = m*n) fused with its column sum:
 // one read of g when the shape allows, else the two launches in sequence;
-// the column sums are the bits launch_colsum gives for the same g.
+// the column sums are the bits launch_colsum gives for the same g.  With
+// `defer`, the fused form leaves its last pass (partials -> db) to the
+// caller in *defer instead of launching it; defer->db stays nullptr when
+// nothing was left.
 hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, uint16_t* db,
-                                  void* ws, hipStream_t stream);
+                                  void* ws, hipStream_t stream, ColsumFinalJob* defer = nullptr);
 
 }  // namespace fp8lin

@@ -699,32 +699,31 @@ __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const uint1
 __global__ __launch_bounds__(kColThreads) void colsum_final_kernel(const float* part,
                                                                    int64_t chunks, int64_t n,
                                                                    uint16_t* db) {
-    __shared__ float red[4][64];
-    const int col = threadIdx.x % 64;
-    const int q = threadIdx.x / 64;
-    const int64_t c = (int64_t)blockIdx.x * 64 + col;
-    float acc = 0.0f;
-    if (c < n) {
-        const int64_t per = (chunks + 3) / 4;
-        const int64_t b = q * per;
-        const int64_t e = b + per < chunks ? b + per : chunks;
-        for (int64_t k = b; k < e; ++k) acc += part[k * n + c];
-    }
-    red[q][col] = acc;
-    __syncthreads();
-    if (q == 0 && c < n) db[c] = f32_to_bf16(((red[0][col] + red[1][col]) + red[2][col]) + red[3][col]);
+    __shared__ float red[kColThreads];
+    colsum_final_cols<kColThreads>(part, chunks, n, (int64_t)blockIdx.x * (kColThreads / 4), db,
+                                   red);
 }
 
 static bool colsum_vec(const uint16_t* g, int64_t n) {
     return (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(g) & 15) == 0);
 }
 
+hipError_t launch_colsum_final_job(const ColsumFinalJob& j, hipStream_t stream) {
+    constexpr int kCols = kColThreads / 4;
+    const dim3 grid2((unsigned)((j.n + kCols - 1) / kCols));
+    hipLaunchKernelGGL(colsum_final_kernel, grid2, dim3(kColThreads), 0, stream, j.part, j.chunks,
+                       j.n, j.db);
+    return hipGetLastError();
+}
+
 static hipError_t launch_colsum_final(float* part, int64_t m, int64_t n, uint16_t* db,
                                       hipStream_t stream) {
-    const dim3 grid2((unsigned)((n + 63) / 64));
-    hipLaunchKernelGGL(colsum_final_kernel, grid2, dim3(kColThreads), 0, stream, part,
-                       colsum_chunks(m, n), n, db);
-    return hipGetLastError();
+    ColsumFinalJob j;
+    j.part = part;
+    j.chunks = colsum_chunks(m, n);
+    j.n = n;
+    j.db = db;
+    return launch_colsum_final_job(j, stream);
 }
 
 hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, void* ws,
@@ -753,7 +752,8 @@ hipError_t launch_colsum(const uint16_t* g, int64_t m, int64_t n, uint16_t* db, 
 }
 
 hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, uint16_t* db,
-                                  void* ws, hipStream_t stream) {
+                                  void* ws, hipStream_t stream, ColsumFinalJob* defer) {
+    if (defer) *defer = ColsumFinalJob{};
     const uint16_t* gx = static_cast<const uint16_t*>(q.x);
     const bool vec = colsum_vec(gx, n) && q.out &&
                      (reinterpret_cast<uintptr_t>(q.out) & 15) == 0 && !q.out2;
@@ -793,6 +793,13 @@ hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, ui
                            p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (defer) {  // the caller's next launch carries the last pass
+        defer->part = p.part;
+        defer->chunks = colsum_chunks(m, n);
+        defer->n = n;
+        defer->db = db;
+        return hipSuccess;
+    }
     return launch_colsum_final(p.part, m, n, db, stream);
 }
 

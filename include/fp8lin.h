@@ -406,7 +406,9 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  *     scales_fwd and ring_g are ignored.
  * dx, dw, db: each NULL to skip that gradient (x8b is only made for dw,
  *     w8b only for dx).  With both dx and dw, the two products run as
- *     fp8_mm_pair (one launch when the shapes allow).
+ *     fp8_mm_pair (one launch when the shapes allow); that launch then
+ *     also runs db's last pass (the sum of the column-sum partials) in
+ *     extra workgroups, else that pass is a launch of its own.
  * workspace: fp8_linear_bwd_workspace(M, N, K) bytes, 256-byte aligned,
  *     with the forward's 6656-byte control block and zero-once contract;
  *     it receives g8 [M][N] at fp8_linear_fwd_x8_offset(M, N, K).

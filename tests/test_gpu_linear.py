@@ -320,3 +320,27 @@ def test_backward_codes_from_the_forward(lib, orc):
     for t in range(3):
         for a, b in zip(runs[0][t], runs[1][t]):
             assert torch.equal(a, b), t
+
+
+@pytest.mark.gpu
+def test_bias_gradient_in_the_pair_launch_ragged(lib):
+    """The backward's dX + dW at 4096 x 4112 x 4096 run as one paired launch
+    (both products have at least 256 tiles), which also runs db's last pass
+    in extra workgroups of 128 columns: 33 of them, the last with 16
+    columns.  db is bit-identical to fp8_colsum's (its own final launch, 64
+    columns per workgroup) and every column is written (db starts as NaN
+    bits)."""
+    M, N, K = 4096, 4112, 4096
+    gd = to_dev_bf16(wl.normal_bf16((M, N), 1e-3, 1301))
+    xd = to_dev_bf16(wl.normal_bf16((M, K), 1.0, 1302))
+    wd = to_dev_bf16(wl.normal_bf16((N, K), 0.02, 1303))
+    bws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    db = torch.full((N,), 0x7FC1, dtype=torch.int16, device="cuda")
+    lib.fp8_linear_bwd(gd, xd, wd, M, N, K, E5M2, True, 0, None, None, bws, None, dx, dw, db)
+    ref = torch.empty(N, dtype=torch.int16, device="cuda")
+    cws = torch.empty(lib.fp8_colsum_workspace(M, N), dtype=torch.uint8, device="cuda")
+    lib.fp8_colsum(gd, M, N, ref, cws)
+    torch.cuda.synchronize()
+    assert torch.equal(db, ref)

@@ -18,10 +18,11 @@ FP8TensorMeta, FP8State, fp8_autocast, fp8_linear_forward, _LinearFp8):
 
 Every number is computed in libfp8lin (``fp8_linear_fwd`` /
 ``fp8_linear_bwd`` under dynamic scaling; under delayed scaling the
-quantize, GEMM and bias-gradient entry points they are made of, in an order
-that reads x and w once per step; ``fp8_quantize`` / ``fp8_mm`` for
-pre-quantized weights); this module only keeps the rings, picks formats,
-allocates outputs and reshapes.  Inputs, weights and biases are bf16.
+forward's quantize and GEMM entry points, which read x and w once per step
+and keep the backward's codes, and ``fp8_linear_bwd`` given those codes;
+``fp8_quantize`` / ``fp8_mm`` for pre-quantized weights); this module only
+keeps the rings, picks formats, allocates outputs and reshapes.  Inputs,
+weights and biases are bf16.
 
 Pre-quantized weights: a ``torch.float8_e4m3fn`` / ``torch.float8_e5m2``
 weight is used as its codes with a step given by the caller (``w_scale``,
@@ -47,7 +48,7 @@ import torch
 
 from . import (E4M3, E5M2, OUT_BF16, Ring, fp8_colsum, fp8_colsum_workspace, fp8_linear_bwd,
                fp8_linear_bwd_workspace, fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
-               fp8_mm_ex, fp8_mm_pair, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
+               fp8_mm_ex, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
 
 __all__ = ["FP8Format", "FP8Recipe", "FP8TensorMeta", "FP8State", "fp8_state", "fp8_autocast",
            "current_config", "fp8_linear", "FP8Linear"]
@@ -210,8 +211,10 @@ class _LinearFp8(torch.autograd.Function):
     steps, so the forward writes them from its own read of x and w
     (fp8_quantize2 when the formats differ; under one format they are the
     forward codes) and keeps them -- one byte per element instead of bf16 x
-    and w.  The backward quantizes g with its ring, the bias gradient from
-    the same pass, then dX (NN) and dW (TN) in one paired launch."""
+    and w.  The backward is fp8_linear_bwd given those codes: g quantized
+    with its ring and the bias gradient's column sums from the same pass,
+    then dX (NN) and dW (TN) in one paired launch that also finishes the
+    bias gradient."""
 
     @staticmethod
     def forward(ctx, x, w, bias, cfg):
@@ -278,29 +281,13 @@ class _LinearFp8(torch.autograd.Function):
             fp8_linear_bwd(i16(g2), i16(x2), i16(w), M, N, K, fmt, True, m, scales, None,
                            _workspace("bwd", dev, M, N, K), None, i16(dx), i16(dw), i16(db))
         else:
+            # the forward kept x8b when dW is wanted and w8b when dX is; the
+            # call seeds, uses and advances the g ring
             x8b, w8b, scales = ctx.saved_tensors
-            rg, gi = ctx.meta.g, g2.view(torch.int16)
-            if not rg.initialized:
-                fp8_quantize(gi, fmt, ring=rg, margin=m)
-                rg.initialized = True
-            g8 = torch.empty(M * N, dtype=torch.uint8, device=dev)
-            sg = torch.empty(1, dtype=torch.float32, device=dev)
-            if db is not None:  # codes, fold and bias gradient from one read of g
-                cs_ws = torch.empty(fp8_colsum_workspace(M, N), dtype=torch.uint8, device=dev)
-                fp8_quantize_colsum(gi, M, N, fmt, rg.scale, g8, i16(db), cs_ws, ring=rg,
-                                    margin=m, scale_used=sg)
-            else:
-                fp8_quantize(gi, fmt, scale=rg.scale, out=g8, ring=rg, margin=m, scale_used=sg)
-            rg.idx = (rg.idx + 1) % rg.len
-            # dX[M][K] = g8[M][N] . w8b[N][K] (NN); dW[N][K] = g8^T . x8b[M][K] (TN)
-            pdx = (g8, w8b, fmt, 0, 0, M, K, N, N, K, 1, 0, 0, sg, scales[1:2], None, i16(dx))
-            pdw = (g8, x8b, fmt, 1, 0, N, K, M, N, K, 1, 0, 0, sg, scales[0:1], None, i16(dw))
-            if dx is not None and dw is not None:
-                fp8_mm_pair(pdx, pdw)
-            elif dx is not None:
-                fp8_mm(*pdx)
-            elif dw is not None:
-                fp8_mm(*pdw)
+            fp8_linear_bwd(i16(g2), None, None, M, N, K, fmt, False, m, scales, ctx.meta.g,
+                           _workspace("bwd", dev, M, N, K), None, i16(dx), i16(dw), i16(db),
+                           x8_bwd=x8b if dw is not None else None,
+                           w8_bwd=w8b if dx is not None else None)
         return (None if dx is None else dx.reshape(ctx.x_shape), dw, db, None)
 
 

@@ -399,15 +399,124 @@ def test_gemm_sampled_matches_full(orc):
     full = orc.gemm(A, B, fmt, True, False, M, N, K, 0.5, 0.5, bias, batch=batch)
     rng = np.random.default_rng(0)
     s = (rng.integers(0, batch, 50), rng.integers(0, M, 50), rng.integers(0, N, 50))
-    vals, absdot = orc.gemm_sampled(A, B, fmt, True, False, M, N, K, 0.5, 0.5, bias, s,
-                                    batch=batch)
+    vals, bound = orc.gemm_sampled(A, B, fmt, True, False, M, N, K, 0.5, 0.5, bias, s,
+                                   batch=batch)
     assert np.array_equal(vals, full[s])
+    fb = orc.gemm_bound(A, B, fmt, True, False, M, N, K, 0.5, 0.5, batch=batch)
+    assert np.array_equal(bound, fb[s])
     ad = orc.gemm_absdot(A, B, fmt, True, False, M, N, K, 0.5, 0.5, batch=batch)
-    assert np.array_equal(absdot, ad[s])
     Ad = torch_decode(A, fmt)
     Bd = torch_decode(B, fmt)
     ref = np.abs(np.einsum("bkm,bkn->bmnk", Ad, Bd)).sum(-1) * 0.25
     assert np.allclose(ad, ref, rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------
+# The GEMM tolerance's accumulation bound (reading c13: outputs that cancel
+# to near zero are accepted within the error a correct fp32-accumulating fp8
+# kernel may carry).  Tolerance tooling, pinned like the rest.
+# --------------------------------------------------------------------------
+
+def _groupmax_bruteforce(Ad, Bd, K):
+    """sum over aligned groups of 8 k of max |a_k b_k|, from decoded
+    operands Ad [M][K], Bd [K][N] (numpy, independent of the C loops)."""
+    p = np.abs(Ad[:, None, :] * Bd.T[None, :, :])  # [M][N][K]
+    pad = (-K) % 8
+    p = np.concatenate([p, np.zeros(p.shape[:2] + (pad,))], axis=2)
+    return p.reshape(p.shape[0], p.shape[1], -1, 8).max(-1).sum(-1)
+
+
+@pytest.mark.parametrize("trans_a,trans_b", [(0, 1), (0, 0), (1, 0), (1, 1)])
+def test_gemm_groupmax_bruteforce(orc, trans_a, trans_b):
+    """Group maxima against numpy on small shapes with ragged last groups,
+    batched and broadcast."""
+    for fmt in (E4M3, E5M2):
+        for (M, N, K) in ((3, 5, 1), (4, 3, 7), (5, 6, 8), (2, 7, 21), (6, 4, 64)):
+            A = wl.random_codes((M, K), fmt, M * 100 + K)
+            B = wl.random_codes((K, N), fmt, N * 100 + K + 7)
+            sa, sb = np.float32(0.5), np.float32(3.0)
+            got = orc.gemm_groupmax(_store(A, trans_a), _store(B, trans_b), fmt, bool(trans_a),
+                                    bool(trans_b), M, N, K, sa, sb)
+            ref = _groupmax_bruteforce(torch_decode(A, fmt).astype(np.float64),
+                                       torch_decode(B, fmt).astype(np.float64), K) * 1.5
+            assert np.allclose(got, ref, rtol=1e-13, atol=0), (fmt, M, N, K)
+    batch, M, N, K = 3, 4, 5, 24
+    A = wl.random_codes((batch, M, K), E4M3, 71)
+    B1 = wl.random_codes((N, K), E4M3, 72)
+    got = orc.gemm_groupmax(A, B1, E4M3, False, True, M, N, K, 1.0, 1.0, batch=batch,
+                            stride_b=0)
+    for b in range(batch):
+        ref = _groupmax_bruteforce(torch_decode(A[b], E4M3).astype(np.float64),
+                                   torch_decode(B1, E4M3).T.astype(np.float64), K)
+        assert np.allclose(got[b], ref, rtol=1e-13, atol=0)
+
+
+def _crafted_dot(orc, pairs, fmt=E4M3):
+    """A 1 x 1 NT product whose k-th terms are the value pairs given."""
+    K = len(pairs)
+    a = orc.encode_array(np.array([[x for x, _ in pairs]], np.float32), fmt)
+    b = orc.encode_array(np.array([[y for _, y in pairs]], np.float32), fmt)
+    return a, b, K
+
+
+def test_gemm_bound_closed_forms(orc):
+    """Two crafted cases by hand.  (1) +-2^10 at k = 0, 1 and 126 products of
+    2^-4: group maxima 1024 + 15 * 2^-4, |sum| 2048 + 126 * 2^-4.  (2) +2^10 at
+    k = 70 and -2^10 at k = 73, on either side of the group boundary at 72:
+    group maxima 2 * 1024 + 14 * 2^-4 (an unaligned grouping, e.g. groups
+    starting at k = 4, would give 1024 + 15 * 2^-4)."""
+    u = 2.0 ** -24
+    K = 128
+    gamma = K * u / (1 - K * u)
+    small = (0.25, 0.25)
+    pairs = [small] * K
+    pairs[0], pairs[1] = (32.0, 32.0), (-32.0, 32.0)
+    a, b, _ = _crafted_dot(orc, pairs)
+    gm = orc.gemm_groupmax(a, b, E4M3, False, True, 1, 1, K, 1.0, 1.0)[0, 0]
+    ad = orc.gemm_absdot(a, b, E4M3, False, True, 1, 1, K, 1.0, 1.0)[0, 0]
+    assert gm == 1024 + 15 * 2.0 ** -4 and ad == 2048 + 126 * 2.0 ** -4
+    bound = orc.gemm_bound(a, b, E4M3, False, True, 1, 1, K, 1.0, 1.0)[0, 0]
+    assert bound == 7 * 2.0 ** -13 * gm + gamma * ad
+    # the cut of the 6 small products beside +-1024 (6 * 2^-4) is inside it
+    assert 6 * 2.0 ** -4 <= bound
+    pairs = [small] * K
+    pairs[70], pairs[73] = (32.0, 32.0), (-32.0, 32.0)
+    a, b, _ = _crafted_dot(orc, pairs)
+    gm = orc.gemm_groupmax(a, b, E4M3, False, True, 1, 1, K, 1.0, 1.0)[0, 0]
+    assert gm == 2 * 1024 + 14 * 2.0 ** -4
+    # the scale enters as |fp32(sa * sb)|
+    gm_s = orc.gemm_groupmax(a, b, E4M3, False, True, 1, 1, K, -0.5, 0.25)[0, 0]
+    assert gm_s == gm * 0.125
+
+
+def _group_cut_model(p):
+    """Worst case of the modelled arithmetic: every product of a group except
+    its largest loses just under 2^-13 of the group's leading power of two,
+    all in the same direction."""
+    total = 0.0
+    for g in range(0, p.size, 8):
+        grp = p[g:g + 8]
+        mx = np.abs(grp).max()
+        if mx == 0:
+            continue
+        lsb = 2.0 ** (np.floor(np.log2(mx)) - 13)
+        total += (grp.size - 1) * lsb * (1 - 2.0 ** -20)
+    return total
+
+
+def test_gemm_bound_covers_the_group_model(orc):
+    """On random operands over the whole fp8 range the worst-case cut of the
+    group model stays inside the oracle's bound, output by output."""
+    for fmt in (E4M3, E5M2):
+        M, N, K = 6, 5, 200
+        A = wl.random_codes((M, K), fmt, 91 + fmt)
+        B = wl.random_codes((N, K), fmt, 92 + fmt)
+        bound = orc.gemm_bound(A, B, fmt, False, True, M, N, K, 1.0, 1.0)
+        Ad = torch_decode(A, fmt).astype(np.float64)
+        Bd = torch_decode(B, fmt).astype(np.float64)
+        for i in range(M):
+            for j in range(N):
+                assert _group_cut_model(Ad[i] * Bd[j]) <= bound[i, j]
 
 
 # --------------------------------------------------------------------------

@@ -20,7 +20,8 @@ __all__ = [
     "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_ex", "fp8_mm_pair", "fp8_colsum",
     "fp8_colsum_workspace", "fp8_quantize_colsum", "OUT_BF16", "OUT_E4M3", "OUT_E5M2",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
-    "fp8_linear_bwd_workspace", "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset",
+    "fp8_linear_bwd_workspace", "fp8_linear_bwd_workspace_codes", "fp8_linear_fwd_x8_offset",
+    "fp8_linear_fwd_w8_offset",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -38,7 +39,8 @@ EXPORTED_SYMBOLS = (
     "fp8_mm", "fp8_mm_ex", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum",
     "fp8_quantize_colsum", "fp8_linear_fwd_workspace",
     "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
-    "fp8_linear_bwd_workspace", "fp8_linear_bwd", "fp8_last_error", "fp8_version",
+    "fp8_linear_bwd_workspace", "fp8_linear_bwd_workspace_codes", "fp8_linear_bwd",
+    "fp8_last_error", "fp8_version",
 )
 
 
@@ -92,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "fp8_linear_fwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, R, R, P, S, P, P, I32, P,
                                  P, P]),
         "fp8_linear_bwd_workspace": (S, [I64, I64, I64]),
+        "fp8_linear_bwd_workspace_codes": (S, [I64, I64, I64]),
         "fp8_linear_bwd": (I32, [P, P, P, I64, I64, I64, I32, I32, I32, P, R, P, S, P, P, P, P,
                                  P, P, P]),
         "fp8_last_error": (ctypes.c_char_p, []),
@@ -130,9 +133,57 @@ def _check(status: int, what: str) -> None:
 
 
 def _ptr(t: torch.Tensor | None):
+    """Device pointer of a tensor handed to the library (None -> NULL)."""
     if t is None:
         return None
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor of shape {tuple(t.shape)} is on {t.device}, not a GPU")
     return ctypes.c_void_p(t.data_ptr())
+
+
+# Element sizes of the buffers the C entry points take: bf16 / fp16 bit
+# patterns (2 bytes), fp8 codes (1 byte), fp32 steps and amaxes (4 bytes).
+_BYTE1 = (torch.uint8, torch.int8, torch.float8_e4m3fn, torch.float8_e5m2)
+_BYTE2 = (torch.bfloat16, torch.int16, torch.float16) + (
+    (torch.uint16,) if hasattr(torch, "uint16") else ())
+_F32 = (torch.float32,)
+
+
+def _buf(t: torch.Tensor | None, what: str, numel: int, dtypes: tuple,
+         nullable: bool = True) -> None:
+    """The C side sees only a device pointer: check here that the tensor is
+    a dense tensor of one of `dtypes` holding at least `numel` elements, so a
+    short or mistyped buffer raises ValueError instead of being read or
+    written out of bounds (_ptr then refuses tensors that are not on a
+    GPU)."""
+    if t is None:
+        if nullable:
+            return
+        raise ValueError(f"{what}: required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected one of "
+                         f"{', '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{what}: {t.numel()} elements, needs at least {numel}")
+
+
+def _ws_bytes(t: torch.Tensor, what: str) -> int:
+    """Byte size of a workspace tensor (any dtype, dense, on a GPU)."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError(f"{what}: a contiguous GPU tensor is required")
+    return t.numel() * t.element_size()
+
+
+def _extent(rows: int, cols: int, ld: int, batch: int, stride: int) -> int:
+    """Elements spanned by `batch` slices of a [rows][cols] matrix with row
+    stride ld and batch stride `stride` (0 broadcasts one slice)."""
+    if rows <= 0 or cols <= 0 or batch <= 0:
+        return 0
+    return (batch - 1) * max(int(stride), 0) + (rows - 1) * int(ld) + cols
 
 
 # torch's raw accessors of the current device and its current stream: the
@@ -216,6 +267,12 @@ def fp8_quantize(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None,
                  amax_out: torch.Tensor | None = None) -> None:
     """bf16 x -> fp8 codes in ``out`` (uint8, same numel), and / or max |x|
     in ``amax_out`` (float32 [1]); see fp8lin.h."""
+    _buf(x, "x", 0, _BYTE2, nullable=False)
+    n = x.numel()
+    _buf(out, "out", n, _BYTE1)
+    _buf(scale, "scale", 1, _F32)
+    _buf(scale_used, "scale_used", 1, _F32)
+    _buf(amax_out, "amax_out", 1, _F32)
     st = _lib.fp8_quantize(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), _ptr(amax_out),
                            _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize")
@@ -227,6 +284,12 @@ def fp8_quantize_t(x: torch.Tensor, rows: int, cols: int, fmt: int, scale: torch
                    scale_used: torch.Tensor | None = None, stream=None) -> None:
     """bf16 x [rows][cols] -> codes transposed in out_t [cols][rows] (and
     row-major in ``out`` when given) from one read of x; see fp8lin.h."""
+    n = max(int(rows), 0) * max(int(cols), 0)
+    _buf(x, "x", n, _BYTE2, nullable=False)
+    _buf(out_t, "out_t", n, _BYTE1, nullable=False)
+    _buf(out, "out", n, _BYTE1)
+    _buf(scale, "scale", 1, _F32)
+    _buf(scale_used, "scale_used", 1, _F32)
     st = _lib.fp8_quantize_t(_ptr(x), rows, cols, fmt, _ptr(scale), _ptr(out), _ptr(out_t),
                              _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize_t")
@@ -247,6 +310,14 @@ def fp8_quantize_ex(x: torch.Tensor, fmt: int, scale: torch.Tensor | None = None
         if x.dtype not in _IN_OF_DTYPE:
             raise ValueError(f"fp8_quantize_ex: no input type for dtype {x.dtype}")
         in_type = _IN_OF_DTYPE[x.dtype]
+    if in_type not in (IN_BF16, IN_F16, IN_F32):
+        raise ValueError(f"fp8_quantize_ex: bad input type {in_type}")
+    _buf(x, "x", 0, _F32 if in_type == IN_F32 else _BYTE2, nullable=False)
+    n = x.numel()
+    _buf(out, "out", n, _BYTE1)
+    _buf(scale, "scale", 1, _F32)
+    _buf(scale_used, "scale_used", 1, _F32)
+    _buf(amax_out, "amax_out", 1, _F32)
     st = _lib.fp8_quantize_ex(_ptr(x), in_type, x.numel(), fmt, _ptr(scale), _ptr(out),
                               _ptr(amax_out), _ring_ref(ring), margin, _ptr(scale_used),
                               _stream(stream))
@@ -258,6 +329,12 @@ def fp8_quantize2(x: torch.Tensor, fmt: int, scale: torch.Tensor, out: torch.Ten
                   scale_used: torch.Tensor | None = None, stream=None) -> None:
     """bf16 x -> fp8 codes of format ``fmt`` in ``out`` and of ``fmt2`` in
     ``out2`` from one read of x (same step); see fp8lin.h."""
+    _buf(x, "x", 0, _BYTE2, nullable=False)
+    n = x.numel()
+    _buf(out, "out", n, _BYTE1, nullable=False)
+    _buf(out2, "out2", n, _BYTE1, nullable=False)
+    _buf(scale, "scale", 1, _F32)
+    _buf(scale_used, "scale_used", 1, _F32)
     st = _lib.fp8_quantize2(_ptr(x), x.numel(), fmt, _ptr(scale), _ptr(out), fmt2, _ptr(out2),
                             _ring_ref(ring), margin, _ptr(scale_used), _stream(stream))
     _check(st, "fp8_quantize2")
@@ -265,14 +342,36 @@ def fp8_quantize2(x: torch.Tensor, fmt: int, scale: torch.Tensor, out: torch.Ten
 
 def fp8_scale_ring_finalize(ring: Ring, fmt: int, amax: torch.Tensor, margin: int = 0,
                             stream=None) -> None:
+    _buf(amax, "amax", 1, _F32, nullable=False)
     st = _lib.fp8_scale_ring_finalize(_ring_ref(ring), fmt, _ptr(amax), margin, _stream(stream))
     _check(st, "fp8_scale_ring_finalize")
+
+
+def _check_mm(a, b, trans_a, trans_b, m, n, k, lda, ldb, batch, stride_a, stride_b, scale_a,
+              scale_b, bias, bias_dtypes, out, out_bytes) -> None:
+    """Buffer sizes of one GEMM: A stored [m][k] (or [k][m] when trans_a)
+    with row stride lda, B stored [k][n] (or [n][k] when trans_b) with row
+    stride ldb, batch slices `stride_*` apart (0 broadcasts), a bias of n
+    values and a contiguous [batch][m][n] output."""
+    m, n, k, batch = int(m), int(n), int(k), int(batch)
+    if min(m, n, k, batch) < 0:
+        raise ValueError("fp8_mm: negative size")
+    ra, ca = (k, m) if trans_a else (m, k)
+    rb, cb = (n, k) if trans_b else (k, n)
+    _buf(a, "a", _extent(ra, ca, lda, batch, stride_a), _BYTE1, nullable=False)
+    _buf(b, "b", _extent(rb, cb, ldb, batch, stride_b), _BYTE1, nullable=False)
+    _buf(scale_a, "scale_a", 1, _F32, nullable=False)
+    _buf(scale_b, "scale_b", 1, _F32, nullable=False)
+    _buf(bias, "bias", n, bias_dtypes)
+    _buf(out, "out", batch * m * n, _BYTE2 if out_bytes == 2 else _BYTE1, nullable=False)
 
 
 def fp8_mm(a: torch.Tensor, b: torch.Tensor, fmt: int, trans_a: int, trans_b: int, m: int,
            n: int, k: int, lda: int, ldb: int, batch: int, stride_a: int, stride_b: int,
            scale_a: torch.Tensor, scale_b: torch.Tensor, bias: torch.Tensor | None,
            out: torch.Tensor, stream=None) -> None:
+    _check_mm(a, b, trans_a, trans_b, m, n, k, lda, ldb, batch, stride_a, stride_b, scale_a,
+              scale_b, bias, _BYTE2, out, 2)
     st = _lib.fp8_mm(_ptr(a), _ptr(b), fmt, trans_a, trans_b, m, n, k, lda, ldb, batch,
                      stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias), _ptr(out),
                      _stream(stream))
@@ -291,6 +390,13 @@ def fp8_mm_ex(a: torch.Tensor, b: torch.Tensor, fmt: int, trans_a: int, trans_b:
     """fp8_mm with an fp8 bias (codes of ``fmt`` and their step ``bias_scale``)
     and / or an fp8 output (``out_type`` OUT_E4M3 / OUT_E5M2, step
     ``out_scale``); see fp8lin.h."""
+    if out_type not in (OUT_BF16, OUT_E4M3, OUT_E5M2):
+        raise ValueError(f"fp8_mm_ex: bad output type {out_type}")
+    _check_mm(a, b, trans_a, trans_b, m, n, k, lda, ldb, batch, stride_a, stride_b, scale_a,
+              scale_b, bias, _BYTE1 if bias_scale is not None else _BYTE2, out,
+              2 if out_type == OUT_BF16 else 1)
+    _buf(bias_scale, "bias_scale", 1, _F32)
+    _buf(out_scale, "out_scale", 1, _F32)
     st = _lib.fp8_mm_ex(_ptr(a), _ptr(b), fmt, trans_a, trans_b, m, n, k, lda, ldb, batch,
                         stride_a, stride_b, _ptr(scale_a), _ptr(scale_b), _ptr(bias),
                         _ptr(bias_scale), out_type, _ptr(out_scale), _ptr(out),
@@ -309,6 +415,11 @@ def fp8_mm_pair(p0: tuple, p1: tuple, stream=None) -> None:
     positional arguments (a, b, fmt, trans_a, trans_b, m, n, k, lda, ldb,
     batch, stride_a, stride_b, scale_a, scale_b, bias, out).  One launch when
     p0 is NN and p1 is TN and both are large; see fp8lin.h."""
+    for p in (p0, p1):
+        if len(p) != 17:
+            raise ValueError("fp8_mm_pair: each problem takes fp8_mm's 17 arguments")
+        (a, b, _fmt, ta, tb, m, n, k, lda, ldb, batch, sta, stb, sa, sb, bias, out) = p
+        _check_mm(a, b, ta, tb, m, n, k, lda, ldb, batch, sta, stb, sa, sb, bias, _BYTE2, out, 2)
     a0, a1 = _mm_args(*p0), _mm_args(*p1)
     st = _lib.fp8_mm_pair(ctypes.byref(a0), ctypes.byref(a1), _stream(stream))
     _check(st, "fp8_mm_pair")
@@ -320,8 +431,10 @@ def fp8_colsum_workspace(m: int, n: int) -> int:
 
 def fp8_colsum(g: torch.Tensor, m: int, n: int, db: torch.Tensor, workspace: torch.Tensor,
                stream=None) -> None:
-    st = _lib.fp8_colsum(_ptr(g), m, n, _ptr(db), _ptr(workspace), workspace.numel(),
-                         _stream(stream))
+    _buf(g, "g", max(int(m), 0) * max(int(n), 0), _BYTE2, nullable=False)
+    _buf(db, "db", max(int(n), 0), _BYTE2, nullable=False)
+    st = _lib.fp8_colsum(_ptr(g), m, n, _ptr(db), _ptr(workspace),
+                         _ws_bytes(workspace, "workspace"), _stream(stream))
     _check(st, "fp8_colsum")
 
 
@@ -331,9 +444,15 @@ def fp8_quantize_colsum(g: torch.Tensor, m: int, n: int, fmt: int, scale: torch.
                         scale_used: torch.Tensor | None = None, stream=None) -> None:
     """Quantize of g [m][n] and its column sum db from one read of g; the
     results equal fp8_quantize + fp8_colsum; see fp8lin.h."""
+    mn = max(int(m), 0) * max(int(n), 0)
+    _buf(g, "g", mn, _BYTE2, nullable=False)
+    _buf(out, "out", mn, _BYTE1)
+    _buf(db, "db", max(int(n), 0), _BYTE2, nullable=False)
+    _buf(scale, "scale", 1, _F32)
+    _buf(scale_used, "scale_used", 1, _F32)
     st = _lib.fp8_quantize_colsum(_ptr(g), m, n, fmt, _ptr(scale), _ptr(out), _ring_ref(ring),
                                   margin, _ptr(scale_used), _ptr(db), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream))
+                                  _ws_bytes(workspace, "workspace"), _stream(stream))
     _check(st, "fp8_quantize_colsum")
 
 
@@ -353,6 +472,10 @@ def fp8_linear_bwd_workspace(M: int, N: int, K: int) -> int:
     return int(_lib.fp8_linear_bwd_workspace(M, N, K))
 
 
+def fp8_linear_bwd_workspace_codes(M: int, N: int, K: int) -> int:
+    return int(_lib.fp8_linear_bwd_workspace_codes(M, N, K))
+
+
 def fp8_linear_fwd(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x: Ring | None,
                    ring_w: Ring | None, workspace: torch.Tensor, scales_out: torch.Tensor,
                    out: torch.Tensor, stream=None, fmt_bwd: int = E5M2,
@@ -360,9 +483,20 @@ def fp8_linear_fwd(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x: Ring | Non
     """Forward of the linear layer; with x8_bwd / w8_bwd (delayed scaling)
     the same pass also writes x's and w's codes in fmt_bwd for the backward;
     see fp8lin.h."""
+    M, N, K = int(M), int(N), int(K)
+    if min(M, N, K) < 0:
+        raise ValueError("fp8_linear_fwd: negative size")
+    _buf(x, "x", M * K, _BYTE2, nullable=False)
+    _buf(w, "w", N * K, _BYTE2, nullable=False)
+    _buf(bias, "bias", N, _BYTE2)
+    _buf(scales_out, "scales_out", 2, _F32)
+    _buf(out, "out", M * N, _BYTE2, nullable=False)
+    _buf(x8_bwd, "x8_bwd", M * K, _BYTE1)
+    _buf(w8_bwd, "w8_bwd", N * K, _BYTE1)
     st = _lib.fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, fmt, int(dynamic), margin,
                              _ring_ref(ring_x), _ring_ref(ring_w), _ptr(workspace),
-                             workspace.numel(), _ptr(scales_out), _ptr(out), fmt_bwd,
+                             _ws_bytes(workspace, "workspace"), _ptr(scales_out), _ptr(out),
+                             fmt_bwd,
                              _ptr(x8_bwd), _ptr(w8_bwd), _stream(stream))
     _check(st, "fp8_linear_fwd")
 
@@ -373,8 +507,22 @@ def fp8_linear_bwd(g, x, w, M, N, K, fmt, dynamic, margin, scales_fwd, ring_g: R
     """Gradients of the linear layer; x8_bwd / w8_bwd (delayed scaling) are
     the forward's backward-format codes, used instead of quantizing x / w;
     see fp8lin.h."""
+    M, N, K = int(M), int(N), int(K)
+    if min(M, N, K) < 0:
+        raise ValueError("fp8_linear_bwd: negative size")
+    _buf(g, "g", M * N, _BYTE2, nullable=False)
+    _buf(x, "x", M * K, _BYTE2)
+    _buf(w, "w", N * K, _BYTE2)
+    _buf(scales_fwd, "scales_fwd", 2, _F32)
+    _buf(scales_out, "scales_out", 3, _F32)
+    _buf(dx, "dx", M * K, _BYTE2)
+    _buf(dw, "dw", N * K, _BYTE2)
+    _buf(db, "db", N, _BYTE2)
+    _buf(x8_bwd, "x8_bwd", M * K, _BYTE1)
+    _buf(w8_bwd, "w8_bwd", N * K, _BYTE1)
     st = _lib.fp8_linear_bwd(_ptr(g), _ptr(x), _ptr(w), M, N, K, fmt, int(dynamic), margin,
                              _ptr(scales_fwd), _ring_ref(ring_g), _ptr(workspace),
-                             workspace.numel(), _ptr(scales_out), _ptr(dx), _ptr(dw), _ptr(db),
+                             _ws_bytes(workspace, "workspace"), _ptr(scales_out), _ptr(dx),
+                             _ptr(dw), _ptr(db),
                              _ptr(x8_bwd), _ptr(w8_bwd), _stream(stream))
     _check(st, "fp8_linear_bwd")

@@ -46,8 +46,9 @@ import weakref
 
 import torch
 
-from . import (E4M3, E5M2, OUT_BF16, Ring, fp8_colsum, fp8_colsum_workspace, fp8_linear_bwd,
-               fp8_linear_bwd_workspace, fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
+from . import (E4M3, E5M2, OUT_BF16, Ring, _stream, fp8_colsum, fp8_colsum_workspace,
+               fp8_linear_bwd, fp8_linear_bwd_workspace, fp8_linear_bwd_workspace_codes,
+               fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
                fp8_mm_ex, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
 
 __all__ = ["FP8Format", "FP8Recipe", "FP8TensorMeta", "FP8State", "fp8_state", "fp8_autocast",
@@ -175,18 +176,21 @@ class fp8_autocast:
         return False
 
 
-# Linear workspaces: their control slots start at zero and every call
-# leaves them so, so one zero-filled buffer per (device, kind, shape) is
-# reused by calls that are ordered on a stream.
+# Linear workspaces.  Their control block starts at zero and every call
+# leaves it so; the rest is scratch that a call uses only while its kernels
+# run.  So one zero-filled buffer per (device, stream) serves every linear
+# call on that stream, forward and backward, of any shape: it grows (a new
+# zero-filled buffer replaces it) when a call needs more, and never holds
+# more than the largest call on that stream asked for.  Calls on one stream
+# are ordered, so they never use it at the same time.
 _WS: dict = {}
 
 
-def _workspace(kind: str, device, M: int, N: int, K: int) -> torch.Tensor:
-    key = (str(device), kind, M, N, K)
+def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    key = (dev.index, _stream().value)  # the stream the library call will use
     ws = _WS.get(key)
-    if ws is None:
-        size = (fp8_linear_fwd_workspace if kind == "fwd" else fp8_linear_bwd_workspace)(M, N, K)
-        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
         _WS[key] = ws
     return ws
 
@@ -217,7 +221,7 @@ class _LinearFp8(torch.autograd.Function):
     bias gradient."""
 
     @staticmethod
-    def forward(ctx, x, w, bias, cfg):
+    def forward(ctx, x, w, bias, cfg, grad_enabled):
         N, K = w.shape
         x2 = x.reshape(-1, K)
         M = x2.shape[0]
@@ -231,7 +235,8 @@ class _LinearFp8(torch.autograd.Function):
         if recipe.dynamic:
             ctx.meta = None
             fp8_linear_fwd(x2.view(torch.int16), w.view(torch.int16), bias16, M, N, K, fmt, True,
-                           recipe.margin, None, None, _workspace("fwd", dev, M, N, K), scales,
+                           recipe.margin, None, None,
+                           _workspace(dev, fp8_linear_fwd_workspace(M, N, K)), scales,
                            out.view(torch.int16))
             ctx.save_for_backward(x2, w, scales)
             return out.reshape(*x.shape[:-1], N)
@@ -253,7 +258,10 @@ class _LinearFp8(torch.autograd.Function):
             fp8_quantize(t, fmt, scale=ring.scale, out=q, ring=ring, margin=m, scale_used=used)
             return q, (q if keep else None)
 
-        need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        # backward codes only when a backward can follow (grad mode on at the
+        # call, and that input's gradient wanted)
+        need_x = grad_enabled and ctx.needs_input_grad[0]
+        need_w = grad_enabled and ctx.needs_input_grad[1]
         x8, x8b = codes(xi, M * K, meta.x, scales[0:1], need_w)  # dW = g^T x
         w8, w8b = codes(wi, N * K, meta.w, scales[1:2], need_x)  # dX = g w
         fp8_mm(x8, w8, fmt, 0, 1, M, N, K, K, K, 1, 0, 0, scales[0:1], scales[1:2], bias16,
@@ -273,22 +281,24 @@ class _LinearFp8(torch.autograd.Function):
         dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if need_w else None
         db = torch.empty(N, dtype=torch.bfloat16, device=dev) if need_b and ctx.has_bias else None
         if dx is None and dw is None and db is None:
-            return None, None, None, None
+            return None, None, None, None, None
         i16 = (lambda t: None if t is None else t.view(torch.int16))
         fmt, m = ctx.fmt_bwd, ctx.recipe.margin
         if ctx.meta is None:
             x2, w, scales = ctx.saved_tensors
             fp8_linear_bwd(i16(g2), i16(x2), i16(w), M, N, K, fmt, True, m, scales, None,
-                           _workspace("bwd", dev, M, N, K), None, i16(dx), i16(dw), i16(db))
+                           _workspace(dev, fp8_linear_bwd_workspace(M, N, K)), None, i16(dx),
+                           i16(dw), i16(db))
         else:
             # the forward kept x8b when dW is wanted and w8b when dX is; the
             # call seeds, uses and advances the g ring
             x8b, w8b, scales = ctx.saved_tensors
             fp8_linear_bwd(i16(g2), None, None, M, N, K, fmt, False, m, scales, ctx.meta.g,
-                           _workspace("bwd", dev, M, N, K), None, i16(dx), i16(dw), i16(db),
+                           _workspace(dev, fp8_linear_bwd_workspace_codes(M, N, K)), None,
+                           i16(dx), i16(dw), i16(db),
                            x8_bwd=x8b if dw is not None else None,
                            w8_bwd=w8b if dx is not None else None)
-        return (None if dx is None else dx.reshape(ctx.x_shape), dw, db, None)
+        return (None if dx is None else dx.reshape(ctx.x_shape), dw, db, None, None)
 
 
 class _LinearFp8Weight(torch.autograd.Function):
@@ -396,7 +406,8 @@ def fp8_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = Non
                                       bias if bias8 else _bf16(bias, "bias"), b_scale, cfg)
     if not cfg.enabled:
         return torch.nn.functional.linear(x, w, bias)
-    return _LinearFp8.apply(_bf16(x, "x"), _bf16(w, "w"), _bf16(bias, "bias"), cfg)
+    return _LinearFp8.apply(_bf16(x, "x"), _bf16(w, "w"), _bf16(bias, "bias"), cfg,
+                            torch.is_grad_enabled())
 
 
 class FP8Linear(torch.nn.Linear):

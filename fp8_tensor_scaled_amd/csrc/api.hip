@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -35,18 +36,20 @@ fp8_status_t hip_fail(hipError_t e, const char* what) {
     return fail(FP8_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// gfx950 check, cached per device.
+// gfx950 check, cached per device.  Calls may come from several host
+// threads: each slot is an atomic (a racing first call only repeats the
+// property query and stores the same value).
 fp8_status_t check_device() {
-    static int cached[64];  // 0 unknown, 1 ok, 2 unsupported
+    static std::atomic<int> cached[64];  // 0 unknown, 1 ok, 2 unsupported
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (dev >= 0 && dev < 64 && cached[dev] == 1) return FP8_OK;
+    if (dev >= 0 && dev < 64 && cached[dev].load(std::memory_order_relaxed) == 1) return FP8_OK;
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev >= 0 && dev < 64) cached[dev] = ok ? 1 : 2;
+    if (dev >= 0 && dev < 64) cached[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
     if (!ok)
         return fail(FP8_EUNSUPPORTED, "device %d is %s; this library is built for gfx950",
                     dev, prop.gcnArchName);
@@ -92,16 +95,20 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K) {
     return l;
 }
 
+// Backward: control block, g8, the column-sum partials, then the codes of x
+// and w that the call makes itself (not needed when the caller passes them,
+// so `base` bytes suffice then).
 struct BwdLayout {
-    size_t g8, x8, w8, colsum, total;
+    size_t g8, colsum, base, x8, w8, total;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
     BwdLayout l;
     l.g8 = kCtrl;
-    l.x8 = align256(l.g8 + (size_t)M * N);
+    l.colsum = align256(l.g8 + (size_t)M * N);
+    l.base = align256(l.colsum + fp8lin::colsum_workspace(M, N));
+    l.x8 = l.base;
     l.w8 = align256(l.x8 + (size_t)M * K);
-    l.colsum = align256(l.w8 + (size_t)N * K);
-    l.total = align256(l.colsum + fp8lin::colsum_workspace(M, N));
+    l.total = align256(l.w8 + (size_t)N * K);
     return l;
 }
 
@@ -634,6 +641,11 @@ size_t fp8_linear_bwd_workspace(int64_t M, int64_t N, int64_t K) {
     return bwd_layout(M, N, K).total;
 }
 
+size_t fp8_linear_bwd_workspace_codes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return bwd_layout(M, N, K).base;
+}
+
 fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t* w, int64_t M,
                             int64_t N, int64_t K, fp8_fmt_t fmt, int32_t dynamic,
                             int32_t margin, const float* scales_fwd, fp8_ring_t* ring_g,
@@ -659,9 +671,11 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
         if (st) return st;
     }
     const BwdLayout L = bwd_layout(M, N, K);
-    if (workspace_bytes < L.total)
+    // the x / w code regions are needed only for codes made here
+    const size_t need = (dw && !x8_bwd) || (dx && !w8_bwd) ? L.total : L.base;
+    if (workspace_bytes < need)
         return fail(FP8_EINVAL, "fp8_linear_bwd: workspace %zu < %zu bytes", workspace_bytes,
-                    L.total);
+                    need);
     if ((uintptr_t)workspace & 255)
         return fail(FP8_EINVAL, "fp8_linear_bwd: workspace not 256-byte aligned");
     fp8_status_t st = check_device();

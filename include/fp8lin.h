@@ -411,7 +411,10 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  *     extra workgroups, else that pass is a launch of its own.
  * workspace: fp8_linear_bwd_workspace(M, N, K) bytes, 256-byte aligned,
  *     with the forward's 6656-byte control block and zero-once contract;
- *     it receives g8 [M][N] at fp8_linear_fwd_x8_offset(M, N, K).
+ *     it receives g8 [M][N] at fp8_linear_fwd_x8_offset(M, N, K).  When
+ *     every product made takes the caller's codes (dx only with w8_bwd, dw
+ *     only with x8_bwd), fp8_linear_bwd_workspace_codes(M, N, K) bytes
+ *     suffice: the regions for x's and w's codes come last.
  * scales_out: nullable fp32 [3] receives [sg, sx, sw]; sx is written only
  *     when dw is made from x here, sw only when dx is made from w here.
  * x8_bwd, w8_bwd: nullable, the backward-format codes of x and w with the
@@ -420,6 +423,7 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  *     scaling only (FP8_EINVAL with dynamic != 0).
  * ------------------------------------------------------------------- */
 size_t fp8_linear_bwd_workspace(int64_t M, int64_t N, int64_t K);
+size_t fp8_linear_bwd_workspace_codes(int64_t M, int64_t N, int64_t K);
 fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t* w,
                             int64_t M, int64_t N, int64_t K, fp8_fmt_t fmt,
                             int32_t dynamic, int32_t margin, const float* scales_fwd,

@@ -58,6 +58,11 @@ def test_pure_helpers(f):
     assert f.fp8_linear_fwd_x8_offset(M, N, K) % 256 == 0
     assert f.fp8_linear_fwd_w8_offset(M, N, K) >= f.fp8_linear_fwd_x8_offset(M, N, K) + M * K
     assert f.fp8_linear_bwd_workspace(M, N, K) >= 256 + M * N + M * K + N * K
+    # with the caller's codes of x and w the two code regions are not needed
+    codes = f.fp8_linear_bwd_workspace_codes(M, N, K)
+    assert codes >= 256 + M * N + f.fp8_colsum_workspace(M, N)
+    assert codes + M * K + N * K <= f.fp8_linear_bwd_workspace(M, N, K)
+    assert f.fp8_linear_bwd_workspace_codes(0, 1, 1) == 0
     assert b"gfx950" in lib.fp8_version()
 
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import check_gemm, from_dev_bf16, ring_state_equal, to_dev_bf16
+from tests.gpu_util import check_gemm, from_dev_bf16, ring_state_equal, sum_bound, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -97,16 +97,16 @@ def test_fp8_linear_dynamic_vs_oracle(lib, fa, orc):
         y.backward(bf16(gb, (M, N)))
     torch.cuda.synchronize()
     rf = orc.linear_fwd(xb, wb, None, M, N, K, E4M3, True)
-    ad = orc.gemm_absdot(rf.x8, rf.w8, E4M3, False, True, M, N, K, rf.sx, rf.sw)
+    ad = orc.gemm_bound(rf.x8, rf.w8, E4M3, False, True, M, N, K, rf.sx, rf.sw)
     check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N), rf.out,
-               ad, K, "dynamic fwd")
+               ad, "dynamic fwd")
     rb = orc.linear_bwd(gb, xb, wb, M, N, K, E5M2, True)
     w8b, x8b = orc.quantize(wb, E5M2, rb.sw), orc.quantize(xb, E5M2, rb.sx)
-    ad = orc.gemm_absdot(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
-    check_gemm(from_dev_bf16(x.grad.reshape(-1).view(torch.int16)).reshape(M, K), rb.dx, ad, N,
+    ad = orc.gemm_bound(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+    check_gemm(from_dev_bf16(x.grad.reshape(-1).view(torch.int16)).reshape(M, K), rb.dx, ad,
                "dynamic dX")
-    ad = orc.gemm_absdot(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
-    check_gemm(from_dev_bf16(w.grad.reshape(-1).view(torch.int16)).reshape(N, K), rb.dw, ad, M,
+    ad = orc.gemm_bound(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+    check_gemm(from_dev_bf16(w.grad.reshape(-1).view(torch.int16)).reshape(N, K), rb.dw, ad,
                "dynamic dW")
 
 
@@ -130,26 +130,25 @@ def test_fp8_linear_prequantized_weight_vs_oracle(lib, fa, orc):
     torch.cuda.synchronize()
     # bias gradient (fused with the g quantize here): the oracle's column sum
     absg = np.abs(wl.bf16_bits_to_f32(gb).astype(np.float64)).sum(0)
-    check_gemm(from_dev_bf16(b.grad.view(torch.int16)), orc.colsum(gb, M, N), absg, M,
+    check_gemm(from_dev_bf16(b.grad.view(torch.int16)), orc.colsum(gb, M, N), sum_bound(absg, M),
                "prequant db fused")
     sx = orc.scale_from_peak(orc.amax(xb), E4M3)
     x8 = orc.quantize(xb, E4M3, sx)
     ref = orc.gemm(x8, w8, E4M3, False, True, M, N, K, sx, sw, bb)
-    ad = orc.gemm_absdot(x8, w8, E4M3, False, True, M, N, K, sx, sw)
-    check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N), ref, ad,
-               K, "prequant fwd")
+    ad = orc.gemm_bound(x8, w8, E4M3, False, True, M, N, K, sx, sw)
+    check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N), ref, ad, "prequant fwd")
     sg = orc.scale_from_peak(orc.amax(gb), E4M3)
     g8 = orc.quantize(gb, E4M3, sg)
     ref = orc.gemm(g8, w8, E4M3, False, False, M, K, N, sg, sw)
-    ad = orc.gemm_absdot(g8, w8, E4M3, False, False, M, K, N, sg, sw)
-    check_gemm(from_dev_bf16(x.grad.reshape(-1).view(torch.int16)).reshape(M, K), ref, ad, N,
+    ad = orc.gemm_bound(g8, w8, E4M3, False, False, M, K, N, sg, sw)
+    check_gemm(from_dev_bf16(x.grad.reshape(-1).view(torch.int16)).reshape(M, K), ref, ad,
                "prequant dX")
     # bias gradient alone (x without grad: no g quantize)
     b.grad = None
     with fa.fp8_autocast(recipe=fa.FP8Recipe(dynamic=True), fp8_format=fa.FP8Format.E4M3):
         fa.fp8_linear(x.detach(), w8d, b, w_scale=swd).backward(bf16(gb, (M, N)))
     torch.cuda.synchronize()
-    check_gemm(from_dev_bf16(b.grad.view(torch.int16)), orc.colsum(gb, M, N), absg, M,
+    check_gemm(from_dev_bf16(b.grad.view(torch.int16)), orc.colsum(gb, M, N), sum_bound(absg, M),
                "prequant db alone")
     with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
         with pytest.raises(NotImplementedError):
@@ -212,7 +211,7 @@ def test_prequantized_weight_and_fp8_bias_vs_oracle(lib, fa, orc):
     x8 = orc.quantize(xb, E4M3, sx)
     ref, _, ad = orc.gemm_ex(x8, w8, E4M3, False, True, M, N, K, sx, sw, b8, sbias)
     check_gemm(from_dev_bf16(y.detach().reshape(-1).view(torch.int16)).reshape(M, N),
-               ref.reshape(M, N), ad.reshape(M, N), K, "w8/b8 fwd")
+               ref.reshape(M, N), ad.reshape(M, N), "w8/b8 fwd")
     assert x.grad is not None and x.grad.shape == (M, K)
     with fa.fp8_autocast():
         with pytest.raises(ValueError, match="fp8 bias"):
@@ -261,3 +260,60 @@ def test_backward_outside_region_and_vs_bf16(lib, fa, dynamic):
     for name, got, r in zip(("dX", "dW", "db"), outside, ref):
         cos, ratio = _cos_and_norm_ratio(got, r)
         assert cos > 0.99 and abs(ratio - 1) < 0.03, (name, cos, ratio)
+
+
+def test_no_grad_keeps_no_backward_codes(lib, fa, monkeypatch):
+    """Under torch.no_grad() / inference_mode a delayed HYBRID FP8Linear
+    with a trainable weight quantizes x and w once each in the forward
+    format only (no fp8_quantize2, no backward codes kept); with grad mode
+    on it writes both formats.  The outputs are the same bits."""
+    calls = {"q2": 0}
+    real = fa.fp8_quantize2
+
+    def counting(*a, **kw):
+        calls["q2"] += 1
+        return real(*a, **kw)
+
+    monkeypatch.setattr(fa, "fp8_quantize2", counting)
+    torch.manual_seed(3)
+    x = torch.randn(64, 256, device="cuda").to(torch.bfloat16).requires_grad_()
+    outs = []
+    for mode in ("no_grad", "inference", "grad"):
+        layer = fa.FP8Linear(256, 128).cuda().to(torch.bfloat16)
+        with torch.no_grad():
+            layer.weight.copy_(torch.linspace(-1, 1, 128 * 256, device="cuda").reshape(128, 256))
+            layer.bias.zero_()
+        fa.fp8_state().reset()
+        calls["q2"] = 0
+        with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+            if mode == "no_grad":
+                with torch.no_grad():
+                    y = layer(x)
+            elif mode == "inference":
+                with torch.inference_mode():
+                    y = layer(x)
+            else:
+                y = layer(x)
+        torch.cuda.synchronize()
+        assert calls["q2"] == (2 if mode == "grad" else 0), (mode, calls)
+        outs.append(y.detach().clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_workspace_cache_stays_bounded(lib, fa):
+    """Linear calls of many token counts on one stream share one workspace
+    that only grows to the largest call's size."""
+    fa._WS.clear()
+    layer = fa.FP8Linear(256, 384).cuda().to(torch.bfloat16)
+    sizes = []
+    with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+        for M in (64, 512, 96, 1024, 32, 700):
+            x = torch.randn(M, 256, device="cuda").to(torch.bfloat16).requires_grad_()
+            layer(x).float().sum().backward()
+            torch.cuda.synchronize()
+            assert len(fa._WS) == 1, len(fa._WS)
+            sizes.append(next(iter(fa._WS.values())).numel())
+    need = max(max(lib.fp8_linear_fwd_workspace(M, 384, 256),
+                   lib.fp8_linear_bwd_workspace_codes(M, 384, 256))
+               for M in (64, 512, 96, 1024, 32, 700))
+    assert sizes[-1] == need and sizes == sorted(sizes)

@@ -103,10 +103,10 @@ def test_mm_ex_fp8_out_full_compare(lib, orc, fmt, ta, tb, M, N, K, out_type):
     A, B = storage(a8, ta), storage(b8, tb)
     _, y, _ = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs)
     so = out_step(orc, y, out_type, headroom=0.8)
-    ref, y, absdot = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs,
+    ref, y, bound = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs,
                                  out_type, so)
     got = run_mm_ex(lib, A, B, fmt, ta, tb, M, N, K, sa, sb, bias, bs, out_type, so)
-    check_fp8_codes(orc, got, y, absdot, K, out_type, so,
+    check_fp8_codes(orc, got, y, bound, out_type, so,
                     f"{M}x{N}x{K} t{ta}{tb} f{fmt} o{out_type} bias {kind}")
     # saturation: the largest outputs (above the step's range) give +-max
     fo_max = 0x7E if out_type == OUT_E4M3 else 0x7B
@@ -123,9 +123,9 @@ def test_mm_ex_fp8_bias_bf16_out(lib, orc, fmt, ta, tb, M, N, K):
     b8, sb = prequant(orc, wl.normal_bf16((K, N), 1.0, N + 13 * K), fmt)
     bias, bs = make_bias(orc, "fp8", N, fmt, N + 17)
     A, B = storage(a8, ta), storage(b8, tb)
-    ref, _, absdot = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs)
+    ref, _, bound = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs)
     got = run_mm_ex(lib, A, B, fmt, ta, tb, M, N, K, sa, sb, bias, bs, OUT_BF16, None)
-    check_gemm(got.reshape(M, N), ref.reshape(M, N), absdot.reshape(M, N), K,
+    check_gemm(got.reshape(M, N), ref.reshape(M, N), bound.reshape(M, N),
                f"fp8 bias {M}x{N}x{K} t{ta}{tb} f{fmt}")
 
 
@@ -172,11 +172,11 @@ def test_mm_ex_misaligned_output(lib, orc, shift):
     bias, bs = make_bias(orc, "fp8", N, fmt, 73)
     _, y, _ = orc.gemm_ex(a8, b8, fmt, False, True, M, N, K, sa, sb, bias, bs)
     so = out_step(orc, y, OUT_E4M3)
-    ref, y, absdot = orc.gemm_ex(a8, b8, fmt, False, True, M, N, K, sa, sb, bias, bs,
+    ref, y, bound = orc.gemm_ex(a8, b8, fmt, False, True, M, N, K, sa, sb, bias, bs,
                                  OUT_E4M3, so)
     got = run_mm_ex(lib, a8, b8, fmt, 0, 1, M, N, K, sa, sb, bias, bs, OUT_E4M3, so,
                     out_shift=shift)
-    check_fp8_codes(orc, got, y, absdot, K, OUT_E4M3, so, f"misaligned by {shift}")
+    check_fp8_codes(orc, got, y, bound, OUT_E4M3, so, f"misaligned by {shift}")
 
 
 def test_mm_ex_batched_broadcast(lib, orc):
@@ -185,11 +185,11 @@ def test_mm_ex_batched_broadcast(lib, orc):
     b8, sb = prequant(orc, wl.normal_bf16((N, K), 1.0, 82), fmt)  # broadcast [N][K]
     _, y, _ = orc.gemm_ex(a8, b8, fmt, False, True, M, N, K, sa, sb, batch=batch, stride_b=0)
     so = out_step(orc, y, OUT_E4M3)
-    ref, y, absdot = orc.gemm_ex(a8, b8, fmt, False, True, M, N, K, sa, sb, out_type=OUT_E4M3,
+    ref, y, bound = orc.gemm_ex(a8, b8, fmt, False, True, M, N, K, sa, sb, out_type=OUT_E4M3,
                                  out_scale=so, batch=batch, stride_b=0)
     got = run_mm_ex(lib, a8, b8, fmt, 0, 1, M, N, K, sa, sb, None, None, OUT_E4M3, so,
                     batch=batch, stride_b=0)
-    check_fp8_codes(orc, got, y, absdot, K, OUT_E4M3, so, "batched broadcast")
+    check_fp8_codes(orc, got, y, bound, OUT_E4M3, so, "batched broadcast")
 
 
 @pytest.mark.parametrize("ta,tb,out_type", [(0, 1, OUT_E4M3), (0, 1, OUT_E5M2),
@@ -210,8 +210,8 @@ def test_config_square_4096_fp8_out(lib, orc, ta, tb, out_type):
     _, y, _ = orc.gemm_ex(a8, b8, E4M3, bool(ta), bool(tb), n, n, n, sa, sb, bias, bs,
                           samples=s)
     so = out_step(orc, y, out_type, headroom=1.25)
-    ref, y, absdot = orc.gemm_ex(a8, b8, E4M3, bool(ta), bool(tb), n, n, n, sa, sb, bias, bs,
+    ref, y, bound = orc.gemm_ex(a8, b8, E4M3, bool(ta), bool(tb), n, n, n, sa, sb, bias, bs,
                                  out_type, so, samples=s)
     got = run_mm_ex(lib, a8, b8, E4M3, ta, tb, n, n, n, sa, sb, bias, bs, out_type, so)
     got = got.reshape(n, n)[s[1], s[2]]
-    check_fp8_codes(orc, got, y, absdot, n, out_type, so, f"square 4096 t{ta}{tb} o{out_type}")
+    check_fp8_codes(orc, got, y, bound, out_type, so, f"square 4096 t{ta}{tb} o{out_type}")

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import (check_gemm, from_dev_bf16, from_dev_u8, ring_state_equal,
+from tests.gpu_util import (check_gemm, from_dev_bf16, from_dev_u8, ring_state_equal, sum_bound,
                             to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -59,8 +59,8 @@ def test_linear256_dynamic_forward(lib, orc):
         assert sc[0] == ref.sx and sc[1] == ref.sw, rep
         assert np.array_equal(f.x8(), ref.x8.ravel()), rep
         assert np.array_equal(f.w8(), ref.w8.ravel()), rep
-        absdot = orc.gemm_absdot(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
-        check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, f"linear256 {rep}")
+        bound = orc.gemm_bound(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
+        check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, bound, f"linear256 {rep}")
 
 
 def test_dynamic_backward_reused_workspace(lib, orc):
@@ -88,13 +88,13 @@ def test_dynamic_backward_reused_workspace(lib, orc):
         assert (s[0], s[1], s[2]) == (rb.sg, rb.sx, rb.sw), rep
         assert np.array_equal(from_dev_u8(ws[g8_off: g8_off + M * N]), rb.g8.ravel()), rep
         w8b = orc.quantize(w, E5M2, rb.sw)
-        ad = orc.gemm_absdot(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
-        check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, N, f"dx {rep}")
+        ad = orc.gemm_bound(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+        check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, f"dx {rep}")
         x8b = orc.quantize(x, E5M2, rb.sx)
-        ad = orc.gemm_absdot(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
-        check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, M, f"dw {rep}")
+        ad = orc.gemm_bound(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+        check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, f"dw {rep}")
         absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
-        check_gemm(from_dev_bf16(db), rb.db, absg, M, f"db {rep}")
+        check_gemm(from_dev_bf16(db), rb.db, sum_bound(absg, M), f"db {rep}")
 
 
 def _samples(M, N, n, seed):
@@ -140,19 +140,19 @@ def test_train_delayed_hybrid_four_steps(lib, orc):
         s = _samples(M, N, 2000, t)
         ref, ad = orc.gemm_sampled(rf.x8, rf.w8, E4M3, False, True, M, N, K, rf.sx, rf.sw,
                                    d["bias"], s)
-        check_gemm(from_dev_bf16(f.out).reshape(M, N)[s[1], s[2]], ref, ad, K, f"fwd {t}")
+        check_gemm(from_dev_bf16(f.out).reshape(M, N)[s[1], s[2]], ref, ad, f"fwd {t}")
         w8b = orc.quantize(d["w"], E5M2, rb.sw)
         x8b = orc.quantize(d["x"][t], E5M2, rb.sx)
         s = _samples(M, K, 2000, 10 + t)
         ref, ad = orc.gemm_sampled(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw, None,
                                    s)
-        check_gemm(from_dev_bf16(dx).reshape(M, K)[s[1], s[2]], ref, ad, N, f"dX {t}")
+        check_gemm(from_dev_bf16(dx).reshape(M, K)[s[1], s[2]], ref, ad, f"dX {t}")
         s = _samples(N, K, 2000, 20 + t)
         ref, ad = orc.gemm_sampled(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx, None,
                                    s)
-        check_gemm(from_dev_bf16(dw).reshape(N, K)[s[1], s[2]], ref, ad, M, f"dW {t}")
+        check_gemm(from_dev_bf16(dw).reshape(N, K)[s[1], s[2]], ref, ad, f"dW {t}")
         absg = np.abs(wl.bf16_bits_to_f32(d["g"][t]).astype(np.float64)).sum(0)
-        check_gemm(from_dev_bf16(db), rb.db, absg, M, f"db {t}")
+        check_gemm(from_dev_bf16(db), rb.db, sum_bound(absg, M), f"db {t}")
 
 
 @pytest.mark.parametrize("dynamic", [True, False])
@@ -177,15 +177,15 @@ def test_backward_masks_and_dynamic_small(lib, orc, dynamic):
                             bool(need[1]), bool(need[2]))
         if need[0]:
             w8b = orc.quantize(w, E5M2, rb.sw)
-            ad = orc.gemm_absdot(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
-            check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, N, "dx")
+            ad = orc.gemm_bound(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+            check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, "dx")
         if need[1]:
             x8b = orc.quantize(x, E5M2, rb.sx)
-            ad = orc.gemm_absdot(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
-            check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, M, "dw")
+            ad = orc.gemm_bound(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+            check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, "dw")
         if need[2]:
             absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
-            check_gemm(from_dev_bf16(db), rb.db, absg, M, "db")
+            check_gemm(from_dev_bf16(db), rb.db, sum_bound(absg, M), "db")
         if not dynamic:
             assert ring_state_equal(rg, og)
 
@@ -244,14 +244,14 @@ def test_benchmark_step_4096_vs_oracle(lib, orc):
             assert ring_state_equal(gr, orr) and gr.idx == orr.idx, t
         s = _samples(n, n, 2000, 40 + t)
         ref, ad = orc.gemm_sampled(x8, w8, E4M3, False, True, n, n, n, sx, sw, bias, s)
-        check_gemm(from_dev_bf16(L.out).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step fwd {t}")
+        check_gemm(from_dev_bf16(L.out).reshape(n, n)[s[1], s[2]], ref, ad, f"step fwd {t}")
         s = _samples(n, n, 2000, 50 + t)
         ref, ad = orc.gemm_sampled(g8, w8b, E5M2, False, False, n, n, n, sg, sw, None, s)
-        check_gemm(from_dev_bf16(L.dx).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step dX {t}")
+        check_gemm(from_dev_bf16(L.dx).reshape(n, n)[s[1], s[2]], ref, ad, f"step dX {t}")
         s = _samples(n, n, 2000, 60 + t)
         ref, ad = orc.gemm_sampled(g8, x8b, E5M2, True, False, n, n, n, sg, sx, None, s)
-        check_gemm(from_dev_bf16(L.dw).reshape(n, n)[s[1], s[2]], ref, ad, n, f"step dW {t}")
-        check_gemm(from_dev_bf16(L.db), orc.colsum(g, n, n), absg, n, f"step db {t}")
+        check_gemm(from_dev_bf16(L.dw).reshape(n, n)[s[1], s[2]], ref, ad, f"step dW {t}")
+        check_gemm(from_dev_bf16(L.db), orc.colsum(g, n, n), sum_bound(absg, n), f"step db {t}")
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 640, 384), (96, 1024, 256), (33, 17, 19)])
@@ -272,8 +272,8 @@ def test_dynamic_forward_launch_paths(lib, orc, M, N, K):
     assert sc[0] == ref.sx and sc[1] == ref.sw
     assert np.array_equal(f.x8(), ref.x8.ravel())
     assert np.array_equal(f.w8(), ref.w8.ravel())
-    absdot = orc.gemm_absdot(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
-    check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, absdot, K, f"dyn fwd {M}x{N}x{K}")
+    bound = orc.gemm_bound(ref.x8, ref.w8, E4M3, False, True, M, N, K, ref.sx, ref.sw)
+    check_gemm(from_dev_bf16(f.out).reshape(M, N), ref.out, bound, f"dyn fwd {M}x{N}x{K}")
 
 
 def test_backward_codes_from_the_forward(lib, orc):
@@ -323,24 +323,44 @@ def test_backward_codes_from_the_forward(lib, orc):
 
 
 @pytest.mark.gpu
-def test_bias_gradient_in_the_pair_launch_ragged(lib):
+def test_bias_gradient_in_the_pair_launch_ragged(lib, orc):
     """The backward's dX + dW at 4096 x 4112 x 4096 run as one paired launch
     (both products have at least 256 tiles), which also runs db's last pass
     in extra workgroups of 128 columns: 33 of them, the last with 16
-    columns.  db is bit-identical to fp8_colsum's (its own final launch, 64
-    columns per workgroup) and every column is written (db starts as NaN
-    bits)."""
+    columns.  db equals the oracle's column sums within their fp32 summation
+    bound, is bit-identical to fp8_colsum's (its own final launch, 64 columns
+    per workgroup), and every column is written (db starts as NaN bits).  dX
+    (NN, reduction over N = 4112: a k tail of 16 in every output) and dW
+    (TN, a last tile row of 16 rows) match the oracle on the E5M2 codes of
+    the dynamic steps: dW on every output of its last tile row plus samples,
+    dX on samples."""
     M, N, K = 4096, 4112, 4096
-    gd = to_dev_bf16(wl.normal_bf16((M, N), 1e-3, 1301))
-    xd = to_dev_bf16(wl.normal_bf16((M, K), 1.0, 1302))
-    wd = to_dev_bf16(wl.normal_bf16((N, K), 0.02, 1303))
+    g = wl.normal_bf16((M, N), 1e-3, 1301)
+    x = wl.normal_bf16((M, K), 1.0, 1302)
+    w = wl.normal_bf16((N, K), 0.02, 1303)
+    gd, xd, wd = to_dev_bf16(g), to_dev_bf16(x), to_dev_bf16(w)
     bws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
     dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
     dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
     db = torch.full((N,), 0x7FC1, dtype=torch.int16, device="cuda")
-    lib.fp8_linear_bwd(gd, xd, wd, M, N, K, E5M2, True, 0, None, None, bws, None, dx, dw, db)
+    sb = torch.zeros(3, dtype=torch.float32, device="cuda")
+    lib.fp8_linear_bwd(gd, xd, wd, M, N, K, E5M2, True, 0, None, None, bws, sb, dx, dw, db)
     ref = torch.empty(N, dtype=torch.int16, device="cuda")
     cws = torch.empty(lib.fp8_colsum_workspace(M, N), dtype=torch.uint8, device="cuda")
     lib.fp8_colsum(gd, M, N, ref, cws)
     torch.cuda.synchronize()
     assert torch.equal(db, ref)
+    absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+    check_gemm(from_dev_bf16(db), orc.colsum(g, M, N), sum_bound(absg, M), "pair db")
+    sg, sx, sw = (orc.scale_from_peak(orc.amax(v), E5M2) for v in (g, x, w))
+    assert tuple(sb.cpu().numpy()) == (sg, sx, sw)
+    g8, x8, w8 = orc.quantize(g, E5M2, sg), orc.quantize(x, E5M2, sx), orc.quantize(w, E5M2, sw)
+    s = _samples(M, K, 2000, 1304)
+    r, bnd = orc.gemm_sampled(g8, w8, E5M2, False, False, M, K, N, sg, sw, None, s)
+    check_gemm(from_dev_bf16(dx).reshape(M, K)[s[1], s[2]], r, bnd, "pair dX")
+    rows, cols = np.meshgrid(np.arange(4096, N), np.arange(K), indexing="ij")
+    rs = _samples(N, K, 2000, 1305)
+    s = (np.concatenate([np.zeros(rows.size, np.int64), rs[0]]),
+         np.concatenate([rows.ravel(), rs[1]]), np.concatenate([cols.ravel(), rs[2]]))
+    r, bnd = orc.gemm_sampled(g8, x8, E5M2, True, False, N, K, M, sg, sx, None, s)
+    check_gemm(from_dev_bf16(dw).reshape(N, K)[s[1], s[2]], r, bnd, "pair dW")

@@ -96,10 +96,9 @@ def test_quantize_special_values(lib, orc):
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
-def test_conversion_exhaustive_fp32(lib, orc, fmt):
-    """Every fp32 value a quantize can produce from a bf16 input times a
-    multiplier: all bf16 inputs at several multipliers, plus a dense sweep
-    of fp32 bit patterns through x * 1.0 (bf16 inputs are exact in fp32)."""
+def test_conversion_bf16_times_multipliers(lib, orc, fmt):
+    """Every bf16 input at several multipliers (fp32 products that round,
+    overflow and underflow) through the bf16 quantize."""
     allbf = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     for s in (np.float32(1.0), np.float32(1 / 3.0), np.float32(2.0 ** 20), np.float32(7e-5)):
         got, _ = gpu_quantize(lib, allbf, fmt, s)
@@ -107,6 +106,31 @@ def test_conversion_exhaustive_fp32(lib, orc, fmt):
         nan = _is_nan_code(ref, fmt)
         assert np.array_equal(got[~nan], ref[~nan])
         assert _is_nan_code(got[nan], fmt).all()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_conversion_exhaustive_fp32(lib, orc, fmt):
+    """The cast on all 2^32 fp32 bit patterns: fp32 inputs through
+    fp8_quantize_ex with step 1 (multiplier exactly 1, so the kernel converts
+    each pattern itself), in chunks of 2^27 generated on the device, against
+    the oracle's encode of the same patterns.  NaN patterns must give a NaN
+    code; every other code is bit-exact."""
+    chunk = 1 << 27
+    one = dev_f32(1.0)
+    idx = torch.arange(chunk, dtype=torch.int32, device="cuda")
+    q = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    for start in range(0, 1 << 32, chunk):
+        signed = start - (1 << 32) if start >= (1 << 31) else start
+        x = (idx + signed).view(torch.float32)
+        lib.fp8_quantize_ex(x, fmt, scale=one, out=q, in_type=2)
+        got = q.cpu().numpy()
+        ref = orc.encode_bits_range(start, chunk, fmt)
+        nan = _is_nan_code(ref, fmt)
+        ok = (got == ref) | nan
+        if not ok.all():
+            i = int(np.argmin(ok))
+            raise AssertionError(f"fmt {fmt} bits {start + i:#010x}: {got[i]:#x} vs {ref[i]:#x}")
+        assert _is_nan_code(got[nan], fmt).all(), f"fmt {fmt} chunk {start:#x}: NaN codes"
 
 
 def test_ring_fold_measure_and_quantize(lib, orc):
@@ -200,7 +224,7 @@ def test_scale_ring_finalize(lib, orc):
 
 @pytest.mark.parametrize("M,N", [(2048, 4096), (1, 7), (33, 8), (300, 1000), (70000, 16)])
 def test_colsum(lib, orc, M, N):
-    from tests.gpu_util import check_gemm
+    from tests.gpu_util import check_gemm, sum_bound
     g = wl.normal_bf16((M, N), 1e-3, 77 + M)
     ws = torch.empty(lib.fp8_colsum_workspace(M, N), dtype=torch.uint8, device="cuda")
     db = torch.empty(N, dtype=torch.int16, device="cuda")
@@ -208,8 +232,8 @@ def test_colsum(lib, orc, M, N):
     torch.cuda.synchronize()
     got = from_dev_bf16(db)
     ref = orc.colsum(g, M, N)
-    absdot = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
-    check_gemm(got, ref, absdot=absdot, K=M, what="colsum")
+    absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+    check_gemm(got, ref, sum_bound(absg, M), what="colsum")
     # deterministic
     db2 = torch.empty_like(db)
     lib.fp8_colsum(to_dev_bf16(g), M, N, db2, ws)
@@ -288,8 +312,8 @@ def test_quantize_colsum_matches_separate_calls(lib, orc, fmt, M, N, offset):
     assert torch.equal(r1.state, r2.state) and torch.equal(u1, u2)
     assert np.array_equal(from_dev_u8(q1), orc.quantize(g.ravel(), fmt, s))
     ref = orc.colsum(g.ravel(), M, N)
-    absdot = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
-    check_gemm(from_dev_bf16(db1), ref, absdot=absdot, K=M, what=f"colsum {M}x{N}")
+    absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+    check_gemm(from_dev_bf16(db1), ref, sum_bound(absg, M), what=f"colsum {M}x{N}")
 
 
 # ---------------------------------------------------------------------------
@@ -450,11 +474,11 @@ def test_backward_nt_only_route(lib, orc):
     g8r, x8r, w8r = orc.quantize(g, fmt, sg), orc.quantize(x, fmt, sx), orc.quantize(w, fmt, sw)
     assert np.array_equal(from_dev_u8(g8), g8r.ravel())
     ref_dx = orc.gemm(g8r, w8r, fmt, False, False, M, K, N, sg, sw)
-    ad_dx = orc.gemm_absdot(g8r, w8r, fmt, False, False, M, K, N, sg, sw)
-    check_gemm(from_dev_bf16(dx).reshape(M, K), ref_dx, ad_dx, N, "nt-route dX")
+    ad_dx = orc.gemm_bound(g8r, w8r, fmt, False, False, M, K, N, sg, sw)
+    check_gemm(from_dev_bf16(dx).reshape(M, K), ref_dx, ad_dx, "nt-route dX")
     ref_dw = orc.gemm(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
-    ad_dw = orc.gemm_absdot(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
-    check_gemm(from_dev_bf16(dw).reshape(N, K), ref_dw, ad_dw, M, "nt-route dW")
+    ad_dw = orc.gemm_bound(g8r, x8r, fmt, True, False, N, K, M, sg, sx)
+    check_gemm(from_dev_bf16(dw).reshape(N, K), ref_dw, ad_dw, "nt-route dW")
 
 
 # ---------------------------------------------------------------------------

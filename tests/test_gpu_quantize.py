@@ -12,7 +12,7 @@ import torch
 
 import workloads as wl
 from tests.gpu_util import (check_gemm, dev_f32, from_dev_bf16, from_dev_u8, ring_state_equal,
-                            to_dev_bf16)
+                            sum_bound, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 

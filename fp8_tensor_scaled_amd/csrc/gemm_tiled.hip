@@ -819,27 +819,33 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 }
 
 // Two independent problems in one launch (the linear backward's dX, NN, and
-// dW, TN, at 256x256 tiles): workgroups [0, n0) take problem 0's tiles and
-// the rest problem 1's.  One workgroup fits a CU, so problem 1's tiles start
-// on CUs as problem 0's finish: their prologue loads overlap problem 0's
-// output stores, and there is one launch boundary instead of two.
-// Workgroups past n0 + n1 run the bias gradient's last pass (`cf`, 128
+// dW, TN), both on one tile configuration: workgroups [0, n0) take problem
+// 0's tiles and the rest problem 1's.  One workgroup fits a CU, so problem
+// 1's tiles start on CUs as problem 0's finish: their prologue loads overlap
+// problem 0's output stores, and there is one launch boundary instead of
+// two.  When problem 0's tiles are the longer ones (dX walks the layer's N,
+// dW its M), the CUs that finish a short tile early take the next one, so
+// the two problems balance over the machine.  Workgroups past n0 + n1 run
+// the bias gradient's last pass (`cf`, a quarter of the workgroup's lanes in
 // columns each): the highest ids are dispatched last, so they take CUs as
 // the last tiles finish, in place of a launch of their own.  Stream order
 // makes the partials (written by an earlier launch) visible to them.
-template <int FMT>
-__global__ __launch_bounds__(512, 1) void gemm_tiled_pair_kernel(TiledParams p0, TiledParams p1,
-                                                                  int n0, int n1,
-                                                                  ColsumFinalJob cf) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<256, 256, 64, 4>()];
+template <int FMT, int BM, int BN, int WM, int WN, int BK, int ST>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_pair_kernel(TiledParams p0,
+                                                                         TiledParams p1, int n0,
+                                                                         int n1,
+                                                                         ColsumFinalJob cf) {
+    constexpr int T = WM * WN * 64;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<BM, BN, BK, ST>()];
+    static_assert(tiled_lds_bytes<BM, BN, BK, ST>() >= T * 4, "column-sum scratch fits");
     const int b = blockIdx.x;
     if (b < n0)
-        gemm_tile<FMT, false, true, 256, 256, 2, 4, 64, 4>(p0, b, n0, smem);
+        gemm_tile<FMT, false, true, BM, BN, WM, WN, BK, ST>(p0, b, n0, smem);
     else if (b < n0 + n1)
-        gemm_tile<FMT, true, true, 256, 256, 2, 4, 64, 4>(p1, b - n0, n1, smem);
+        gemm_tile<FMT, true, true, BM, BN, WM, WN, BK, ST>(p1, b - n0, n1, smem);
     else
-        colsum_final_cols<512>(cf.part, cf.chunks, cf.n, (int64_t)(b - n0 - n1) * 128, cf.db,
-                               reinterpret_cast<float*>(smem));
+        colsum_final_cols<T>(cf.part, cf.chunks, cf.n, (int64_t)(b - n0 - n1) * (T / 4), cf.db,
+                             reinterpret_cast<float*>(smem));
 }
 
 // ---------------------------------------------------------------------------
@@ -917,21 +923,52 @@ static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
     return hipGetLastError();
 }
 
+static int64_t tiles_of(const GemmLaunch& g, int bm, int bn) {
+    return ((g.m + bm - 1) / bm) * ((g.n + bn - 1) / bn) * g.batch;
+}
+
+// Tile configuration by output-tile count.  Every configuration runs one
+// workgroup per CU (its LDS ring takes most of the 160 KB), so a launch with
+// fewer tiles than the 256 CUs leaves CUs idle, and the largest tile that
+// still gives every CU one is the most efficient (fewest operand bytes per
+// flop, longest time per stage to cover load latency).  Measured on MI355X
+// (µs, fp8 operands; the sweep is in the design notes):
+//   kBig    256 x 256, 8 waves of 128 x 64       at >= 256 tiles of 256 x 256
+//   kWide   128 x 256, 8 waves of  64 x 64       at >= 256 tiles of 128 x 256
+//   kTall   256 x 128, 8 waves of  64 x 64       at >= 256 tiles of 256 x 128
+//   kMid    128 x 128, 8 waves of  32 x 64       otherwise
+//   kSmall   64 x  64, 4 waves of  32 x 32       m <= 64 below 256 tiles of 128 x 128
+// (2048 x 4096 x 1024 NT: 13.9 wide against 18.8 for 4-wave 128 x 128 tiles;
+// 2048 x 1024 x 4096 NN: 16.8 mid against 21.6; 4096 x 1024 x 2048 TN: 12.1
+// mid against 14.9.)  All configurations sum every output's k range in the
+// same order, so the choice never changes a result bit.
+enum TileCfg { kBig, kWide, kTall, kMid, kSmall };
+
+static TileCfg tile_cfg(const GemmLaunch& g) {
+    if (tiles_of(g, 256, 256) >= 256) return kBig;
+    const int64_t wide = tiles_of(g, 128, 256), tall = tiles_of(g, 256, 128);
+    if (wide >= 256 && (g.n >= g.m || tall < 256)) return kWide;
+    if (tall >= 256) return kTall;
+    if (g.m <= 64 && tiles_of(g, 128, 128) < 256) return kSmall;
+    return kMid;
+}
+
 template <int FMT, bool AMN, bool BMN>
 static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
-    // Pick the largest tile that still gives every CU at least one tile.
-    const int64_t t256 = ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
-    const int64_t t128 = ((g.m + 127) / 128) * ((g.n + 127) / 128) * g.batch;
-    // Both operands k-contiguous: 128-byte stages (every row segment a whole
-    // line), double-buffered.  Otherwise 64-byte stages, four deep: the
-    // m/n-contiguous operand reads whole lines anyway and the deeper ring
-    // hides more latency.
+    // Both operands k-contiguous: 256 x 256 tiles take 128-byte stages
+    // (every row segment a whole line), double-buffered.  Otherwise 64-byte
+    // stages, four deep: the m/n-contiguous operand reads whole lines anyway
+    // and the deeper ring hides more latency.
     constexpr bool kBoth = !AMN && !BMN;
-    if (t256 >= 256) {
-        if constexpr (kBoth) return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
-        else return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 64, 4>(g, stream);
+    switch (tile_cfg(g)) {
+        case kBig:
+            if constexpr (kBoth) return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
+            else return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 64, 4>(g, stream);
+        case kWide: return launch_cfg<FMT, AMN, BMN, 128, 256, 2, 4, 128, 3>(g, stream);
+        case kTall: return launch_cfg<FMT, AMN, BMN, 256, 128, 4, 2, 128, 3>(g, stream);
+        case kMid: return launch_cfg<FMT, AMN, BMN, 128, 128, 4, 2, 128, 4>(g, stream);
+        case kSmall: break;
     }
-    if (t128 >= 256 || g.m > 64) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 2, 128, 4>(g, stream);
     return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 128, 4>(g, stream);
 }
 
@@ -948,48 +985,69 @@ hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream) {
     return g.fmt == 0 ? launch_fmt<0>(g, stream) : launch_fmt<1>(g, stream);
 }
 
-static int64_t tiles256(const GemmLaunch& g) {
-    return ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
+// Paired configuration: the 256 x 256 one when both problems fill the CUs
+// with it, else 128 x 128 tiles (8 waves) when the two together give at
+// least one tile per CU; kSmall: no paired launch.
+static TileCfg pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1) {
+    if (tiles_of(g0, 256, 256) >= 256 && tiles_of(g1, 256, 256) >= 256) return kBig;
+    if (tiles_of(g0, 128, 128) + tiles_of(g1, 128, 128) >= 256) return kMid;
+    return kSmall;
 }
+
+static int pair_tile(TileCfg c) { return c == kBig ? 256 : 128; }
 
 bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1) {
     if (!gemm_tiled_supported(g0) || !gemm_tiled_supported(g1) || g0.fmt != g1.fmt) return false;
     if (g0.ext() || g1.ext()) return false;  // the paired kernel has the plain epilogue
     // problem 0 NN (A k-contiguous, B n-contiguous), problem 1 TN (both
-    // m/n-contiguous), each big enough for the 256x256 configuration
+    // m/n-contiguous)
     if (g0.trans_a != 0 || g0.trans_b != 0 || g1.trans_a != 1 || g1.trans_b != 0) return false;
-    const int64_t n0 = tiles256(g0), n1 = tiles256(g1);
-    return n0 >= 256 && n1 >= 256 && (double)n0 + (double)n1 < 2147483647.0;
+    const TileCfg c = pair_cfg(g0, g1);
+    if (c == kSmall) return false;
+    const int t = pair_tile(c);
+    return (double)tiles_of(g0, t, t) + (double)tiles_of(g1, t, t) < 2147483647.0;
 }
 
 bool gemm_tiled_pair_carries(const GemmLaunch& g0, const GemmLaunch& g1,
                              const ColsumFinalJob& cf) {
+    const int t = pair_tile(pair_cfg(g0, g1));
     const int64_t extra = (cf.n + 127) / 128;
-    return cf.db && cf.n >= 1 && (double)tiles256(g0) + (double)tiles256(g1) + (double)extra <
-                                     2147483647.0;
+    return cf.db && cf.n >= 1 &&
+           (double)tiles_of(g0, t, t) + (double)tiles_of(g1, t, t) + (double)extra <
+               2147483647.0;
 }
 
-hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
+template <int BM, int BN, int WM, int WN, int BK, int ST>
+static hipError_t launch_pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1,
                                   hipStream_t stream, const ColsumFinalJob* cf) {
-    TiledParams p0 = tiled_params<256, 256>(g0);
-    TiledParams p1 = tiled_params<256, 256>(g1);
-    const int n0 = (int)tiles256(g0), n1 = (int)tiles256(g1);
+    TiledParams p0 = tiled_params<BM, BN>(g0);
+    TiledParams p1 = tiled_params<BM, BN>(g1);
+    const int n0 = (int)tiles_of(g0, BM, BN), n1 = (int)tiles_of(g1, BM, BN);
     // problem 1's local ids line up with the XCDs only if n0 is a multiple of 8
     p1.xcd_remap = p1.xcd_remap && (n0 % 8) == 0;
     ColsumFinalJob job;
     int extra = 0;
+    constexpr int kCols = WM * WN * 64 / 4;  // bias-gradient columns per extra workgroup
     if (cf && cf->db) {  // callers check gemm_tiled_pair_carries first
         job = *cf;
-        extra = (int)((cf->n + 127) / 128);
+        extra = (int)((cf->n + kCols - 1) / kCols);
     }
     const dim3 grid((unsigned)(n0 + n1 + extra));
+    const dim3 block(WM * WN * 64);
     if (g0.fmt == 0)
-        hipLaunchKernelGGL(gemm_tiled_pair_kernel<0>, grid, dim3(512), 0, stream, p0, p1, n0, n1,
-                           job);
+        hipLaunchKernelGGL((gemm_tiled_pair_kernel<0, BM, BN, WM, WN, BK, ST>), grid, block, 0,
+                           stream, p0, p1, n0, n1, job);
     else
-        hipLaunchKernelGGL(gemm_tiled_pair_kernel<1>, grid, dim3(512), 0, stream, p0, p1, n0, n1,
-                           job);
+        hipLaunchKernelGGL((gemm_tiled_pair_kernel<1, BM, BN, WM, WN, BK, ST>), grid, block, 0,
+                           stream, p0, p1, n0, n1, job);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
+                                  hipStream_t stream, const ColsumFinalJob* cf) {
+    if (pair_cfg(g0, g1) == kBig)
+        return launch_pair_cfg<256, 256, 2, 4, 64, 4>(g0, g1, stream, cf);
+    return launch_pair_cfg<128, 128, 4, 2, 128, 4>(g0, g1, stream, cf);
 }
 
 }  // namespace fp8lin

@@ -288,11 +288,12 @@ fp8_status_t fp8_mm_ex(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int32_
  *
  * p0, p1: host pointers to the two problems' fp8_mm arguments (the struct
  *     below; fields as in fp8_mm).  When p0 is NN (trans_a 0, trans_b 0)
- *     and p1 is TN (trans_a 1, trans_b 0) in the same format and both are
- *     large enough for the 256 x 256 tiles (at least 256 tiles each), one
- *     kernel runs both, problem 0's tiles first; otherwise the two products
- *     are enqueued one after the other.  Either way each output is
- *     bit-identical to fp8_mm with the same arguments.
+ *     and p1 is TN (trans_a 1, trans_b 0) in the same format and together
+ *     they fill the GPU (at least 256 tiles of 256 x 256 each, or 256 tiles
+ *     of 128 x 128 between them), one kernel runs both, problem 0's tiles
+ *     first; otherwise the two products are enqueued one after the other.
+ *     Either way each output is bit-identical to fp8_mm with the same
+ *     arguments.
  * The problems must be independent: neither output may overlap the other
  * problem's operands (checked: the two outputs must not overlap).
  * Validation is fp8_mm's for each problem; on FP8_EINVAL nothing is

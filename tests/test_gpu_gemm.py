@@ -236,26 +236,48 @@ def test_epilogue_rounding_ties(lib, orc, lay, M):
             f"{int((got != ref).sum())} outputs differ"
 
 
-# Shapes that take the 256 x 256 tile configurations (at least 256 output
-# tiles of 256 x 256): every output compared, both formats, with ragged m, n
-# and k tails (for an m- or n-contiguous operand the tiled kernels need that
-# extent in multiples of 16, so its tail is 16).
-TILE256_SHAPES = {
-    "NT": [(4096, 4096, 256), (4100, 4120, 272)],
-    "NN": [(4096, 4096, 256), (4100, 4112, 272)],
-    "TN": [(4096, 4096, 256), (4112, 4112, 272)],
-    "TT": [(4096, 4096, 256), (4112, 4120, 272)],
+# Shapes that take each large tile configuration (the library picks the
+# largest tile that still gives every one of the 256 CUs a tile): every
+# output compared, both formats, with ragged m, n and k tails (for an m- or
+# n-contiguous operand the tiled kernels need that extent in multiples of 16,
+# so its tail is 16).
+#   big:  >= 256 tiles of 256 x 256
+#   wide: fewer, but >= 256 tiles of 128 x 256 (n >= m)
+#   tall: fewer of 256 x 256, >= 256 tiles of 256 x 128 (m > n)
+TILE_SHAPES = {
+    ("big", "NT"): [(4096, 4096, 256), (4100, 4120, 272)],
+    ("big", "NN"): [(4096, 4096, 256), (4100, 4112, 272)],
+    ("big", "TN"): [(4096, 4096, 256), (4112, 4112, 272)],
+    ("big", "TT"): [(4096, 4096, 256), (4112, 4120, 272)],
+    ("wide", "NT"): [(2048, 4096, 256), (2060, 4120, 272)],
+    ("wide", "NN"): [(2048, 4096, 256), (2060, 4112, 272)],
+    ("wide", "TN"): [(2048, 4096, 256), (2064, 4112, 272)],
+    ("wide", "TT"): [(2048, 4096, 256), (2064, 4120, 272)],
+    ("tall", "NT"): [(4096, 2048, 256), (4100, 2056, 272)],
+    ("tall", "NN"): [(4096, 2048, 256), (4100, 2064, 272)],
+    ("tall", "TN"): [(4096, 2048, 256), (4112, 2064, 272)],
+    ("tall", "TT"): [(4096, 2048, 256), (4112, 2056, 272)],
 }
 
 
+def _tiles(M, N, bm, bn):
+    return ((M + bm - 1) // bm) * ((N + bn - 1) // bn)
+
+
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
-@pytest.mark.parametrize("lay", ["NT", "NN", "TN", "TT"])
+@pytest.mark.parametrize("cfg,lay", list(TILE_SHAPES), ids=[f"{c}-{l}" for c, l in TILE_SHAPES])
 @pytest.mark.parametrize("ragged", [False, True], ids=["whole", "ragged"])
-def test_tile256_full_compare(lib, orc, fmt, lay, ragged):
+def test_tile_configs_full_compare(lib, orc, fmt, cfg, lay, ragged):
     ta, tb = dict(zip(["NT", "NN", "TN", "TT"], LAYOUTS))[lay]
-    M, N, K = TILE256_SHAPES[lay][int(ragged)]
-    assert ((M + 255) // 256) * ((N + 255) // 256) >= 256
-    seed = 900 + 10 * ta + 20 * tb + int(ragged)
+    M, N, K = TILE_SHAPES[(cfg, lay)][int(ragged)]
+    big = _tiles(M, N, 256, 256) >= 256
+    if cfg == "big":
+        assert big
+    elif cfg == "wide":
+        assert not big and _tiles(M, N, 128, 256) >= 256 and N >= M
+    else:
+        assert not big and _tiles(M, N, 256, 128) >= 256 and M > N
+    seed = 900 + 10 * ta + 20 * tb + int(ragged) + 100 * ["big", "wide", "tall"].index(cfg)
     a8, sa = prequant(orc, wl.normal_bf16((M, K), 1.0, seed), fmt)
     b8, sb = prequant(orc, wl.normal_bf16((K, N), 1.0, seed + 1), fmt)
     bias = wl.normal_bf16((N,), 0.1, seed + 2) if lay == "NT" else None
@@ -263,9 +285,9 @@ def test_tile256_full_compare(lib, orc, fmt, lay, ragged):
     got = run_mm(lib, A, B, fmt, ta, tb, M, N, K, sa, sb, bias)
     ref = orc.gemm(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias)
     bound = orc.gemm_bound(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb)
-    st = check_gemm(got, ref, bound, f"tile256 {lay} {M}x{N}x{K} f{fmt}")
-    print(f"[tile256 {lay} {M}x{N}x{K} f{fmt}] outside 1e-2|r|+ulp: {st['outside_rel_tol']} "
-          f"of {st['n']}")
+    what = f"tiles {cfg} {lay} {M}x{N}x{K} f{fmt}"
+    st = check_gemm(got, ref, bound, what)
+    print(f"[{what}] outside 1e-2|r|+ulp: {st['outside_rel_tol']} of {st['n']}")
 
 
 def test_config_smallm(lib, orc):
@@ -382,13 +404,15 @@ def test_mfma_group_model(lib, orc, fmt, ta, tb, M):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
-@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (4144, 4176, 272), (256, 512, 320)])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (4144, 4176, 272), (2064, 1040, 272),
+                                   (256, 512, 320)])
 def test_mm_pair_matches_two_calls(lib, orc, fmt, M, N, K):
     """fp8_mm_pair of an NN and a TN product gives the bits of two fp8_mm
-    calls: through the paired kernel when both have at least 256 tiles of
-    256 x 256 (the first two shapes, the second with ragged m, n and k
-    tails), as two launches otherwise; and every output of both matches the
-    oracle."""
+    calls: through the paired kernel on 256 x 256 tiles when both have at
+    least 256 of them (the first two shapes, the second with ragged m, n and
+    k tails), on 128 x 128 tiles when the two have at least 256 of those
+    between them (the third, ragged), as two launches otherwise; and every
+    output of both matches the oracle."""
     # problem 0, NN: A [M][K], B [K][N]; problem 1, TN: A stored [K][M], B [K][N]
     a0, sa0 = prequant(orc, wl.normal_bf16((M, K), 1.0, 700 + K), fmt)
     b0, sb0 = prequant(orc, wl.normal_bf16((K, N), 0.02, 701 + K), fmt)

@@ -830,19 +830,36 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 // columns each): the highest ids are dispatched last, so they take CUs as
 // the last tiles finish, in place of a launch of their own.  Stream order
 // makes the partials (written by an earlier launch) visible to them.
-template <int FMT, int BM, int BN, int WM, int WN, int BK, int ST>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_pair_kernel(TiledParams p0,
-                                                                         TiledParams p1, int n0,
-                                                                         int n1,
-                                                                         ColsumFinalJob cf) {
-    constexpr int T = WM * WN * 64;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<BM, BN, BK, ST>()];
-    static_assert(tiled_lds_bytes<BM, BN, BK, ST>() >= T * 4, "column-sum scratch fits");
+// A tile configuration as a type: BM x BN tile, WM x WN waves, BK k per
+// stage, ST stages.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_>
+struct TileShape {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, ST = ST_;
+    static constexpr int kThreads = WM * WN * 64;
+    static constexpr int kLds = tiled_lds_bytes<BM, BN, BK, ST>();
+};
+using ShapeBig64 = TileShape<256, 256, 2, 4, 64, 4>;  // 256 x 256, 64-k stages
+using ShapeWide = TileShape<128, 256, 2, 4, 128, 3>;
+using ShapeTall = TileShape<256, 128, 4, 2, 128, 3>;
+using ShapeMid = TileShape<128, 128, 4, 2, 128, 4>;
+
+template <int FMT, class S0, class S1>
+__global__ __launch_bounds__(S0::kThreads, 1) void gemm_tiled_pair_kernel(TiledParams p0,
+                                                                          TiledParams p1, int n0,
+                                                                          int n1,
+                                                                          ColsumFinalJob cf) {
+    static_assert(S0::kThreads == S1::kThreads, "one workgroup size");
+    constexpr int T = S0::kThreads;
+    constexpr int kLds = S0::kLds > S1::kLds ? S0::kLds : S1::kLds;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+    static_assert(kLds >= T * 4, "column-sum scratch fits");
     const int b = blockIdx.x;
     if (b < n0)
-        gemm_tile<FMT, false, true, BM, BN, WM, WN, BK, ST>(p0, b, n0, smem);
+        gemm_tile<FMT, false, true, S0::BM, S0::BN, S0::WM, S0::WN, S0::BK, S0::ST>(p0, b, n0,
+                                                                                  smem);
     else if (b < n0 + n1)
-        gemm_tile<FMT, true, true, BM, BN, WM, WN, BK, ST>(p1, b - n0, n1, smem);
+        gemm_tile<FMT, true, true, S1::BM, S1::BN, S1::WM, S1::WN, S1::BK, S1::ST>(p1, b - n0,
+                                                                                 n1, smem);
     else
         colsum_final_cols<T>(cf.part, cf.chunks, cf.n, (int64_t)(b - n0 - n1) * (T / 4), cf.db,
                              reinterpret_cast<float*>(smem));
@@ -985,16 +1002,40 @@ hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream) {
     return g.fmt == 0 ? launch_fmt<0>(g, stream) : launch_fmt<1>(g, stream);
 }
 
-// Paired configuration: the 256 x 256 one when both problems fill the CUs
-// with it, else 128 x 128 tiles (8 waves) when the two together give at
-// least one tile per CU; kSmall: no paired launch.
-static TileCfg pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1) {
-    if (tiles_of(g0, 256, 256) >= 256 && tiles_of(g1, 256, 256) >= 256) return kBig;
-    if (tiles_of(g0, 128, 128) + tiles_of(g1, 128, 128) >= 256) return kMid;
-    return kSmall;
+// Paired configurations.  Both problems on 256 x 256 tiles when each fills
+// the CUs with them.  Otherwise the tiles are sized so that one tile of
+// either problem is about the same work: the problem with the longer k
+// (the backward's dX walks the layer's N, dW its M) takes 128 x 128 tiles
+// and the other, when its k is a third to two thirds of that, tiles twice
+// that area (256 x 128 when its m >= n, else 128 x 256); and the two must
+// give at least one tile per CU.  Then the CUs finish together instead of
+// some taking two short tiles while others run one long tile (training
+// step at 2048 x 4096 x 1024: dX 2048 x 1024 x 4096 + dW 4096 x 1024 x 2048).
+struct PairCfg {
+    TileCfg c0 = kSmall, c1 = kSmall;  // kSmall: no paired launch
+};
+
+static int cfg_bm(TileCfg c) { return c == kBig || c == kTall ? 256 : 128; }
+static int cfg_bn(TileCfg c) { return c == kBig || c == kWide ? 256 : 128; }
+
+static PairCfg pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1) {
+    PairCfg r;
+    if (tiles_of(g0, 256, 256) >= 256 && tiles_of(g1, 256, 256) >= 256) {
+        r.c0 = r.c1 = kBig;
+        return r;
+    }
+    auto larger = [](const GemmLaunch& g) { return g.m >= g.n ? kTall : kWide; };
+    r.c0 = r.c1 = kMid;
+    if (2 * g1.k <= g0.k * 4 / 3 && 2 * g1.k >= g0.k * 2 / 3) r.c1 = larger(g1);  // k1 ~ k0/2
+    else if (2 * g0.k <= g1.k * 4 / 3 && 2 * g0.k >= g1.k * 2 / 3) r.c0 = larger(g0);
+    if (tiles_of(g0, cfg_bm(r.c0), cfg_bn(r.c0)) + tiles_of(g1, cfg_bm(r.c1), cfg_bn(r.c1)) < 256)
+        r.c0 = r.c1 = kSmall;
+    return r;
 }
 
-static int pair_tile(TileCfg c) { return c == kBig ? 256 : 128; }
+static int64_t pair_tiles(const GemmLaunch& g0, const GemmLaunch& g1, const PairCfg& c) {
+    return tiles_of(g0, cfg_bm(c.c0), cfg_bn(c.c0)) + tiles_of(g1, cfg_bm(c.c1), cfg_bn(c.c1));
+}
 
 bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1) {
     if (!gemm_tiled_supported(g0) || !gemm_tiled_supported(g1) || g0.fmt != g1.fmt) return false;
@@ -1002,52 +1043,53 @@ bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1) {
     // problem 0 NN (A k-contiguous, B n-contiguous), problem 1 TN (both
     // m/n-contiguous)
     if (g0.trans_a != 0 || g0.trans_b != 0 || g1.trans_a != 1 || g1.trans_b != 0) return false;
-    const TileCfg c = pair_cfg(g0, g1);
-    if (c == kSmall) return false;
-    const int t = pair_tile(c);
-    return (double)tiles_of(g0, t, t) + (double)tiles_of(g1, t, t) < 2147483647.0;
+    const PairCfg c = pair_cfg(g0, g1);
+    if (c.c0 == kSmall) return false;
+    return (double)pair_tiles(g0, g1, c) < 2147483647.0;
 }
 
 bool gemm_tiled_pair_carries(const GemmLaunch& g0, const GemmLaunch& g1,
                              const ColsumFinalJob& cf) {
-    const int t = pair_tile(pair_cfg(g0, g1));
     const int64_t extra = (cf.n + 127) / 128;
     return cf.db && cf.n >= 1 &&
-           (double)tiles_of(g0, t, t) + (double)tiles_of(g1, t, t) + (double)extra <
-               2147483647.0;
+           (double)pair_tiles(g0, g1, pair_cfg(g0, g1)) + (double)extra < 2147483647.0;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int ST>
+template <class S0, class S1>
 static hipError_t launch_pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1,
                                   hipStream_t stream, const ColsumFinalJob* cf) {
-    TiledParams p0 = tiled_params<BM, BN>(g0);
-    TiledParams p1 = tiled_params<BM, BN>(g1);
-    const int n0 = (int)tiles_of(g0, BM, BN), n1 = (int)tiles_of(g1, BM, BN);
+    TiledParams p0 = tiled_params<S0::BM, S0::BN>(g0);
+    TiledParams p1 = tiled_params<S1::BM, S1::BN>(g1);
+    const int n0 = (int)tiles_of(g0, S0::BM, S0::BN), n1 = (int)tiles_of(g1, S1::BM, S1::BN);
     // problem 1's local ids line up with the XCDs only if n0 is a multiple of 8
     p1.xcd_remap = p1.xcd_remap && (n0 % 8) == 0;
     ColsumFinalJob job;
     int extra = 0;
-    constexpr int kCols = WM * WN * 64 / 4;  // bias-gradient columns per extra workgroup
+    constexpr int kCols = S0::kThreads / 4;  // bias-gradient columns per extra workgroup
     if (cf && cf->db) {  // callers check gemm_tiled_pair_carries first
         job = *cf;
         extra = (int)((cf->n + kCols - 1) / kCols);
     }
     const dim3 grid((unsigned)(n0 + n1 + extra));
-    const dim3 block(WM * WN * 64);
+    const dim3 block(S0::kThreads);
     if (g0.fmt == 0)
-        hipLaunchKernelGGL((gemm_tiled_pair_kernel<0, BM, BN, WM, WN, BK, ST>), grid, block, 0,
-                           stream, p0, p1, n0, n1, job);
+        hipLaunchKernelGGL((gemm_tiled_pair_kernel<0, S0, S1>), grid, block, 0, stream, p0, p1, n0,
+                           n1, job);
     else
-        hipLaunchKernelGGL((gemm_tiled_pair_kernel<1, BM, BN, WM, WN, BK, ST>), grid, block, 0,
-                           stream, p0, p1, n0, n1, job);
+        hipLaunchKernelGGL((gemm_tiled_pair_kernel<1, S0, S1>), grid, block, 0, stream, p0, p1, n0,
+                           n1, job);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
                                   hipStream_t stream, const ColsumFinalJob* cf) {
-    if (pair_cfg(g0, g1) == kBig)
-        return launch_pair_cfg<256, 256, 2, 4, 64, 4>(g0, g1, stream, cf);
-    return launch_pair_cfg<128, 128, 4, 2, 128, 4>(g0, g1, stream, cf);
+    const PairCfg c = pair_cfg(g0, g1);
+    if (c.c0 == kBig) return launch_pair_cfg<ShapeBig64, ShapeBig64>(g0, g1, stream, cf);
+    if (c.c0 == kMid && c.c1 == kTall) return launch_pair_cfg<ShapeMid, ShapeTall>(g0, g1, stream, cf);
+    if (c.c0 == kMid && c.c1 == kWide) return launch_pair_cfg<ShapeMid, ShapeWide>(g0, g1, stream, cf);
+    if (c.c0 == kTall) return launch_pair_cfg<ShapeTall, ShapeMid>(g0, g1, stream, cf);
+    if (c.c0 == kWide) return launch_pair_cfg<ShapeWide, ShapeMid>(g0, g1, stream, cf);
+    return launch_pair_cfg<ShapeMid, ShapeMid>(g0, g1, stream, cf);
 }
 
 }  // namespace fp8lin

@@ -436,3 +436,38 @@ def test_mm_pair_matches_two_calls(lib, orc, fmt, M, N, K):
                         f"pair {'TN' if ta else 'NN'} {M}x{N}x{K}")
         print(f"[pair {'TN' if ta else 'NN'} {M}x{N}x{K} f{fmt}] outside 1e-2|r|+ulp: "
               f"{st['outside_rel_tol']} of {st['n']}")
+
+
+@pytest.mark.parametrize("shapes", [((2048, 1024, 4096), (4096, 1024, 2048)),
+                                    ((2064, 1040, 4112), (4112, 1040, 2064))],
+                         ids=["train2048", "ragged"])
+def test_mm_pair_unequal_k(lib, orc, shapes):
+    """The paired launch with tiles of unequal area: NN problem 0 with twice
+    the k of TN problem 1 (the training layer's dX and dW) runs on 128 x 128
+    tiles for problem 0 and 256 x 128 tiles for problem 1; the bits equal two
+    fp8_mm calls and every output matches the oracle (E5M2, the backward
+    format)."""
+    fmt = E5M2
+    (M0, N0, K0), (M1, N1, K1) = shapes
+    a0, sa0 = prequant(orc, wl.normal_bf16((M0, K0), 1e-3, 1400), fmt)
+    b0, sb0 = prequant(orc, wl.normal_bf16((K0, N0), 0.02, 1401), fmt)
+    a1, sa1 = prequant(orc, wl.normal_bf16((K1, M1), 1e-3, 1402), fmt)
+    b1, sb1 = prequant(orc, wl.normal_bf16((K1, N1), 1.0, 1403), fmt)
+    d = [to_dev_u8(v.ravel()) for v in (a0, b0, a1, b1)]
+    s = [dev_f32(v) for v in (sa0, sb0, sa1, sb1)]
+    outs = [torch.full((M * N,), 0x7FC1, dtype=torch.int16, device="cuda")
+            for M, N in ((M0, N0), (M1, N1), (M0, N0), (M1, N1))]
+    p0 = (d[0], d[1], fmt, 0, 0, M0, N0, K0, K0, N0, 1, 0, 0, s[0], s[1], None)
+    p1 = (d[2], d[3], fmt, 1, 0, M1, N1, K1, M1, N1, 1, 0, 0, s[2], s[3], None)
+    lib.fp8_mm_pair(p0 + (outs[0],), p1 + (outs[1],))
+    lib.fp8_mm(*(p0 + (outs[2],)))
+    lib.fp8_mm(*(p1 + (outs[3],)))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
+    for o, (a, b, ta, M, N, K, sa, sb) in ((outs[0], (a0, b0, False, M0, N0, K0, sa0, sb0)),
+                                           (outs[1], (a1, b1, True, M1, N1, K1, sa1, sb1))):
+        ref = orc.gemm(a, b, fmt, ta, False, M, N, K, sa, sb)
+        bound = orc.gemm_bound(a, b, fmt, ta, False, M, N, K, sa, sb)
+        what = f"pair {'TN' if ta else 'NN'} {M}x{N}x{K}"
+        st = check_gemm(from_dev_bf16(o).reshape(M, N), ref, bound, what)
+        print(f"[{what}] outside 1e-2|r|+ulp: {st['outside_rel_tol']} of {st['n']}")

@@ -49,7 +49,7 @@ import torch
 from . import (E4M3, E5M2, OUT_BF16, Ring, _stream, fp8_colsum, fp8_colsum_workspace,
                fp8_linear_bwd, fp8_linear_bwd_workspace, fp8_linear_bwd_workspace_codes,
                fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
-               fp8_mm_ex, fp8_quantize, fp8_quantize2, fp8_quantize_colsum)
+               fp8_mm_ex, fp8_quantize, fp8_quantize_colsum)
 
 __all__ = ["FP8Format", "FP8Recipe", "FP8TensorMeta", "FP8State", "fp8_state", "fp8_autocast",
            "current_config", "fp8_linear", "FP8Linear"]
@@ -213,9 +213,11 @@ class _LinearFp8(torch.autograd.Function):
     Delayed scaling: the same operations as those two entry points, bit for
     bit, in fewer passes.  The backward's x and w codes use the forward's
     steps, so the forward writes them from its own read of x and w
-    (fp8_quantize2 when the formats differ; under one format they are the
-    forward codes) and keeps them -- one byte per element instead of bf16 x
-    and w.  The backward is fp8_linear_bwd given those codes: g quantized
+    (fp8_linear_fwd with x8_bwd / w8_bwd when the formats differ: x and w in
+    one launch; under one format they are the forward codes) and keeps them
+    -- one byte per element instead of bf16 x and w -- only when a gradient
+    that needs them can follow.  The backward is fp8_linear_bwd given those
+    codes: g quantized
     with its ring and the bias gradient's column sums from the same pass,
     then dX (NN) and dW (TN) in one paired launch that also finishes the
     bias gradient."""
@@ -243,32 +245,37 @@ class _LinearFp8(torch.autograd.Function):
         meta = ctx.meta = _STATE.get_weight_meta(w, recipe)
         m = recipe.margin
         xi, wi = x2.view(torch.int16), w.view(torch.int16)
-        for ring, t in ((meta.x, xi), (meta.w, wi)):
-            if not ring.initialized:  # first use: the ring starts from this tensor's amax
-                fp8_quantize(t, fmt, ring=ring, margin=m)
-                ring.initialized = True
-
-        def codes(t, numel, ring, used, keep):
-            q = torch.empty(numel, dtype=torch.uint8, device=dev)
-            if keep and ctx.fmt_bwd != fmt:
-                qb = torch.empty(numel, dtype=torch.uint8, device=dev)
-                fp8_quantize2(t, fmt, ring.scale, q, ctx.fmt_bwd, qb, ring=ring, margin=m,
-                              scale_used=used)
-                return q, qb
-            fp8_quantize(t, fmt, scale=ring.scale, out=q, ring=ring, margin=m, scale_used=used)
-            return q, (q if keep else None)
-
         # backward codes only when a backward can follow (grad mode on at the
         # call, and that input's gradient wanted)
         need_x = grad_enabled and ctx.needs_input_grad[0]
         need_w = grad_enabled and ctx.needs_input_grad[1]
-        x8, x8b = codes(xi, M * K, meta.x, scales[0:1], need_w)  # dW = g^T x
-        w8, w8b = codes(wi, N * K, meta.w, scales[1:2], need_x)  # dX = g w
+        if ctx.fmt_bwd != fmt:
+            # fp8_linear_fwd: x and w quantized in one launch, each writing
+            # its backward codes (other format, same step) when they are
+            # wanted; it seeds, folds and advances the rings
+            x8b = torch.empty(M * K, dtype=torch.uint8, device=dev) if need_w else None
+            w8b = torch.empty(N * K, dtype=torch.uint8, device=dev) if need_x else None
+            fp8_linear_fwd(xi, wi, bias16, M, N, K, fmt, False, m, meta.x, meta.w,
+                           _workspace(dev, fp8_linear_fwd_workspace(M, N, K)), scales,
+                           out.view(torch.int16), fmt_bwd=ctx.fmt_bwd, x8_bwd=x8b, w8_bwd=w8b)
+            ctx.save_for_backward(x8b, w8b, scales)
+            return out.reshape(*x.shape[:-1], N)
+        # one format both ways: the forward's codes are the backward's
+        for ring, t in ((meta.x, xi), (meta.w, wi)):
+            if not ring.initialized:  # first use: the ring starts from this tensor's amax
+                fp8_quantize(t, fmt, ring=ring, margin=m)
+                ring.initialized = True
+        x8 = torch.empty(M * K, dtype=torch.uint8, device=dev)
+        w8 = torch.empty(N * K, dtype=torch.uint8, device=dev)
+        fp8_quantize(xi, fmt, scale=meta.x.scale, out=x8, ring=meta.x, margin=m,
+                     scale_used=scales[0:1])
+        fp8_quantize(wi, fmt, scale=meta.w.scale, out=w8, ring=meta.w, margin=m,
+                     scale_used=scales[1:2])
         fp8_mm(x8, w8, fmt, 0, 1, M, N, K, K, K, 1, 0, 0, scales[0:1], scales[1:2], bias16,
                out.view(torch.int16))
         for ring in (meta.x, meta.w):
             ring.idx = (ring.idx + 1) % ring.len
-        ctx.save_for_backward(x8b, w8b, scales)
+        ctx.save_for_backward(x8 if need_w else None, w8 if need_x else None, scales)
         return out.reshape(*x.shape[:-1], N)
 
     @staticmethod

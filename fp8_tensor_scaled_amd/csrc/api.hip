@@ -112,12 +112,11 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
     return l;
 }
 
-fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
-                         uint8_t* out, float* ring_state, int32_t len, int32_t idx,
-                         int32_t margin, float* scale_used, hipStream_t stream,
-                         uint8_t* out2 = nullptr, int fmt2 = -1,
-                         int in_type = fp8lin::kInBf16, float* amax_out = nullptr,
-                         bool cached_input = false) {
+fp8lin::QuantLaunch make_quant(const void* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+                               uint8_t* out, float* ring_state, int32_t len, int32_t idx,
+                               int32_t margin, float* scale_used, uint8_t* out2 = nullptr,
+                               int fmt2 = -1, int in_type = fp8lin::kInBf16,
+                               float* amax_out = nullptr, bool cached_input = false) {
     fp8lin::QuantLaunch q;
     q.x = x;
     q.in_type = in_type;
@@ -134,6 +133,18 @@ fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const floa
     q.scale_used = scale_used;
     q.amax_out = amax_out;
     q.cached_input = cached_input;
+    return q;
+}
+
+fp8_status_t do_quantize(const void* x, int64_t numel, fp8_fmt_t fmt, const float* scale,
+                         uint8_t* out, float* ring_state, int32_t len, int32_t idx,
+                         int32_t margin, float* scale_used, hipStream_t stream,
+                         uint8_t* out2 = nullptr, int fmt2 = -1,
+                         int in_type = fp8lin::kInBf16, float* amax_out = nullptr,
+                         bool cached_input = false) {
+    const fp8lin::QuantLaunch q = make_quant(x, numel, fmt, scale, out, ring_state, len, idx,
+                                             margin, scale_used, out2, fmt2, in_type, amax_out,
+                                             cached_input);
     hipError_t e = fp8lin::launch_quantize(q, stream);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return FP8_OK;
@@ -619,14 +630,21 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
         // to scales_out) before its own last workgroup folds the new amax.
         // With x8_bwd / w8_bwd the same pass also writes the backward's
         // codes: the same scaled values in fmt_bwd.
-        if ((st = do_quantize(x, M * K, fmt, ring_x->state + ring_x->len, x8, ring_x->state,
-                              ring_x->len, ring_x->idx, margin, sx, stream, x8_bwd,
-                              x8_bwd ? (int)fmt_bwd : -1)))
-            return st;
-        if ((st = do_quantize(w, N * K, fmt, ring_w->state + ring_w->len, w8, ring_w->state,
-                              ring_w->len, ring_w->idx, margin, sw, stream, w8_bwd,
-                              w8_bwd ? (int)fmt_bwd : -1)))
-            return st;
+        // x and w go in one launch when both or neither write backward codes.
+        const fp8lin::QuantLaunch qx =
+            make_quant(x, M * K, fmt, ring_x->state + ring_x->len, x8, ring_x->state,
+                       ring_x->len, ring_x->idx, margin, sx, x8_bwd, x8_bwd ? (int)fmt_bwd : -1);
+        const fp8lin::QuantLaunch qw =
+            make_quant(w, N * K, fmt, ring_w->state + ring_w->len, w8, ring_w->state,
+                       ring_w->len, ring_w->idx, margin, sw, w8_bwd, w8_bwd ? (int)fmt_bwd : -1);
+        if (fp8lin::quantize_two_supported(qx, qw)) {
+            hipError_t e = fp8lin::launch_quantize_two(qx, qw, stream);
+            if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        } else {
+            hipError_t e = fp8lin::launch_quantize(qx, stream);
+            if (e == hipSuccess) e = fp8lin::launch_quantize(qw, stream);
+            if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        }
     }
     if ((st = do_gemm(x8, w8, fmt, 0, 1, M, N, K, K, K, sx, sw, bias, out, stream))) return st;
     if (!dynamic) {

@@ -44,6 +44,12 @@ struct QuantLaunch {
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
 
+// Two bf16 quantizes with codes (same format, same second format or none, no
+// amax_out) in one launch, each with its own fold; results are those of two
+// launch_quantize calls.
+bool quantize_two_supported(const QuantLaunch& q0, const QuantLaunch& q1);
+hipError_t launch_quantize_two(const QuantLaunch& q0, const QuantLaunch& q1, hipStream_t stream);
+
 // Dynamic (current-amax) quantize of up to two small bf16 tensors in one
 // launch, one workgroup each: measure max |x|, derive the step, cast.  The
 // codes and steps equal those of a measure-only pass into a length-1 ring

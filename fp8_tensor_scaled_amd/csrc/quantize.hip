@@ -271,8 +271,11 @@ __device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, ui
 // and before the stores, so the fold's atomics overlap the store drain
 // instead of following it.  Scalar path (unaligned bases): grid-stride
 // elements, then the publish.
+// Workgroup b of the nb that process p (the whole grid, or one tensor's
+// share of a two-tensor launch).
 template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) {
+__device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32_t b,
+                                              const uint32_t nb) {
     constexpr int kL = In<IN>::kLoads;
     float m = 0.0f, s_read = 0.0f;
     if constexpr (!MEASURE_ONLY) {
@@ -287,10 +290,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
     uint32_t ticket = ~0u;  // publish_amax's result (thread 0)
     if (p.vec) {
         const int64_t nvec = p.numel / kVecElems;
-        const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
-        const int64_t lo = (int64_t)blockIdx.x * per;
+        const int64_t per = (nvec + nb - 1) / nb;
+        const int64_t lo = (int64_t)b * per;
         const int64_t hi = lo + per < nvec ? lo + per : nvec;
-        if (blockIdx.x == 0) {
+        if (b == 0) {
             const int64_t e = nvec * kVecElems + t;
             if (e < p.numel) {
                 const float f = In<IN>::one(p.x, e);
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
                 if (c0 + u * kQuantThreads < hi) amax = absmax16<IN>(r[u], amax);
-            if (p.hist && rd == nr - 1) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
+            if (p.hist && rd == nr - 1) ticket = publish_amax(p, amax, nb, b);
             if constexpr (!MEASURE_ONLY) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
@@ -345,10 +348,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
                 }
             }
         }
-        if (p.hist && nr == 0) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
+        if (p.hist && nr == 0) ticket = publish_amax(p, amax, nb, b);
     } else {
-        const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-        for (int64_t e = (int64_t)blockIdx.x * kQuantThreads + t; e < p.numel; e += stride) {
+        const int64_t stride = (int64_t)nb * kQuantThreads;
+        for (int64_t e = (int64_t)b * kQuantThreads + t; e < p.numel; e += stride) {
             const float f = In<IN>::one(p.x, e);
             amax = fmaxf(amax, fabsf(f));
             if constexpr (!MEASURE_ONLY) {
@@ -356,16 +359,34 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) 
                 if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
             }
         }
-        if (p.hist) ticket = publish_amax(p, amax, gridDim.x, blockIdx.x);
+        if (p.hist) ticket = publish_amax(p, amax, nb, b);
     }
     if (p.hist) {
-        finish_fold(p, ticket, s_read, win, gridDim.x);
+        finish_fold(p, ticket, s_read, win, nb);
     } else {
         if constexpr (!MEASURE_ONLY) {
-            if (p.scale_used && blockIdx.x == 0 && t == 0) *p.scale_used = s_read;
+            if (p.scale_used && b == 0 && t == 0) *p.scale_used = s_read;
         }
         if (p.amax_out) publish_amax_out(p, amax);
     }
+}
+
+template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(QuantParams p) {
+    quantize_body<IN, FMT, FMT2, MEASURE_ONLY>(p, blockIdx.x, gridDim.x);
+}
+
+// Two bf16 tensors in one launch (the forward's x and w): workgroups
+// [0, nb0) quantize p0, the rest p1, each with its own fold; one launch and
+// one latency chain (first loads, fold, last stores) instead of two.
+template <int FMT, int FMT2>
+__global__ __launch_bounds__(kQuantThreads) void quantize_two_kernel(QuantParams p0,
+                                                                     QuantParams p1,
+                                                                     uint32_t nb0) {
+    if (blockIdx.x < nb0)
+        quantize_body<kInBf16, FMT, FMT2, false>(p0, blockIdx.x, nb0);
+    else
+        quantize_body<kInBf16, FMT, FMT2, false>(p1, blockIdx.x - nb0, gridDim.x - nb0);
 }
 
 static int quant_grid(int64_t numel, int vec) {
@@ -403,8 +424,7 @@ static void launch_quantize_in(const QuantLaunch& q, const QuantParams& p, dim3 
 #undef FP8_Q
 }
 
-hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
-    if (q.out2 && q.in_type != kInBf16) return hipErrorInvalidValue;
+static QuantParams quant_params(const QuantLaunch& q) {
     QuantParams p{};
     p.x = q.x;
     p.numel = q.numel;
@@ -428,12 +448,56 @@ hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
                          reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;
+    return p;
+}
+
+hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
+    if (q.out2 && q.in_type != kInBf16) return hipErrorInvalidValue;
+    const QuantParams p = quant_params(q);
     const dim3 grid(quant_grid(q.numel, p.vec));
     if (q.amax_out && !q.ring_state)
         hipLaunchKernelGGL(arm_amax_kernel, dim3(1), dim3(1), 0, stream, q.amax_out);
     if (q.in_type == kInF16) launch_quantize_in<kInF16>(q, p, grid, stream);
     else if (q.in_type == kInF32) launch_quantize_in<kInF32>(q, p, grid, stream);
     else launch_quantize_in<kInBf16>(q, p, grid, stream);
+    return hipGetLastError();
+}
+
+bool quantize_two_supported(const QuantLaunch& q0, const QuantLaunch& q1) {
+    auto ok = [](const QuantLaunch& q) {
+        return q.in_type == kInBf16 && q.out && !q.amax_out && q.numel > 0;
+    };
+    return ok(q0) && ok(q1) && q0.fmt == q1.fmt && (q0.out2 ? q0.fmt2 : -1) ==
+                                                       (q1.out2 ? q1.fmt2 : -1);
+}
+
+hipError_t launch_quantize_two(const QuantLaunch& q0, const QuantLaunch& q1,
+                               hipStream_t stream) {
+    if (!quantize_two_supported(q0, q1)) return hipErrorInvalidValue;
+    const QuantParams p0 = quant_params(q0), p1 = quant_params(q1);
+    // Each tensor's own grid, scaled down to 256 workgroups in all (one per
+    // CU), split in proportion to the tensors' sizes.
+    int64_t b0 = quant_grid(q0.numel, p0.vec), b1 = quant_grid(q1.numel, p1.vec);
+    if (b0 + b1 > 256) {
+        const double f0 = (double)q0.numel / ((double)q0.numel + (double)q1.numel);
+        b0 = (int64_t)(256.0 * f0 + 0.5);
+        b0 = b0 < 1 ? 1 : (b0 > 255 ? 255 : b0);
+        b1 = 256 - b0;
+    }
+    const dim3 grid((unsigned)(b0 + b1)), block(kQuantThreads);
+    const int dual = q0.out2 ? q0.fmt2 : -1;
+#define FP8_Q2(F, F2) \
+    hipLaunchKernelGGL((quantize_two_kernel<F, F2>), grid, block, 0, stream, p0, p1, (uint32_t)b0)
+    if (q0.fmt == 0) {
+        if (dual < 0) FP8_Q2(0, -1);
+        else if (dual == 0) FP8_Q2(0, 0);
+        else FP8_Q2(0, 1);
+    } else {
+        if (dual < 0) FP8_Q2(1, -1);
+        else if (dual == 0) FP8_Q2(1, 0);
+        else FP8_Q2(1, 1);
+    }
+#undef FP8_Q2
     return hipGetLastError();
 }
 

@@ -18,7 +18,9 @@ __all__ = [
     "E4M3", "E5M2", "FMT_MAX", "IN_BF16", "IN_F16", "IN_F32", "Ring", "library_path",
     "fp8_quantize", "fp8_quantize_ex", "fp8_quantize_t", "fp8_quantize2",
     "fp8_scale_ring_finalize", "fp8_mm", "fp8_mm_ex", "fp8_mm_pair", "fp8_colsum",
-    "fp8_colsum_workspace", "fp8_quantize_colsum", "OUT_BF16", "OUT_E4M3", "OUT_E5M2",
+    "fp8_colsum_workspace", "fp8_quantize_colsum", "fp8_quantize_colsum_noalloc",
+    "fp8_quantize_colsum_noalloc_max_bytes",
+    "OUT_BF16", "OUT_E4M3", "OUT_E5M2",
     "fp8_linear_fwd", "fp8_linear_bwd", "fp8_linear_fwd_workspace",
     "fp8_linear_bwd_workspace", "fp8_linear_bwd_workspace_codes", "fp8_linear_fwd_x8_offset",
     "fp8_linear_fwd_w8_offset",
@@ -37,7 +39,8 @@ EXPORTED_SYMBOLS = (
     "fp8_quantize_t", "fp8_quantize2",
     "fp8_scale_ring_finalize",
     "fp8_mm", "fp8_mm_ex", "fp8_mm_pair", "fp8_colsum_workspace", "fp8_colsum",
-    "fp8_quantize_colsum", "fp8_linear_fwd_workspace",
+    "fp8_quantize_colsum", "fp8_quantize_colsum_noalloc_max_bytes",
+    "fp8_quantize_colsum_noalloc", "fp8_linear_fwd_workspace",
     "fp8_linear_fwd_x8_offset", "fp8_linear_fwd_w8_offset", "fp8_linear_fwd",
     "fp8_linear_bwd_workspace", "fp8_linear_bwd_workspace_codes", "fp8_linear_bwd",
     "fp8_last_error", "fp8_version",
@@ -88,6 +91,8 @@ def _load() -> ctypes.CDLL:
         "fp8_colsum_workspace": (S, [I64, I64]),
         "fp8_colsum": (I32, [P, I64, I64, P, P, S, P]),
         "fp8_quantize_colsum": (I32, [P, I64, I64, I32, P, P, R, I32, P, P, P, S, P]),
+        "fp8_quantize_colsum_noalloc_max_bytes": (S, []),
+        "fp8_quantize_colsum_noalloc": (I32, [P, I64, I64, I32, P, P, R, I32, P, P, P]),
         "fp8_linear_fwd_workspace": (S, [I64, I64, I64]),
         "fp8_linear_fwd_x8_offset": (S, [I64, I64, I64]),
         "fp8_linear_fwd_w8_offset": (S, [I64, I64, I64]),
@@ -454,6 +459,28 @@ def fp8_quantize_colsum(g: torch.Tensor, m: int, n: int, fmt: int, scale: torch.
                                   margin, _ptr(scale_used), _ptr(db), _ptr(workspace),
                                   _ws_bytes(workspace, "workspace"), _stream(stream))
     _check(st, "fp8_quantize_colsum")
+
+
+def fp8_quantize_colsum_noalloc_max_bytes() -> int:
+    return int(_lib.fp8_quantize_colsum_noalloc_max_bytes())
+
+
+def fp8_quantize_colsum_noalloc(g: torch.Tensor, m: int, n: int, fmt: int,
+                                scale: torch.Tensor, out: torch.Tensor, db: torch.Tensor,
+                                ring: Ring | None = None, margin: int = 0,
+                                scale_used: torch.Tensor | None = None, stream=None) -> None:
+    """fp8_quantize_colsum with its partials in the library's static scratch
+    (no workspace, no allocation); see fp8lin.h."""
+    mn = max(int(m), 0) * max(int(n), 0)
+    _buf(g, "g", mn, _BYTE2, nullable=False)
+    _buf(out, "out", mn, _BYTE1, nullable=False)
+    _buf(db, "db", max(int(n), 0), _BYTE2, nullable=False)
+    _buf(scale, "scale", 1, _F32, nullable=False)
+    _buf(scale_used, "scale_used", 1, _F32)
+    st = _lib.fp8_quantize_colsum_noalloc(_ptr(g), m, n, fmt, _ptr(scale), _ptr(out),
+                                          _ring_ref(ring), margin, _ptr(scale_used), _ptr(db),
+                                          _stream(stream))
+    _check(st, "fp8_quantize_colsum_noalloc")
 
 
 def fp8_linear_fwd_workspace(M: int, N: int, K: int) -> int:

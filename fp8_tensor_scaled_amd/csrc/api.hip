@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -529,6 +530,77 @@ fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fm
     return do_quantize_colsum(g, m, n, fmt, scale, out, ring ? ring->state : nullptr,
                               ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, db,
                               workspace, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of fp8_quantize_colsum_noalloc: the column-sum partials live in
+// this file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` only names the variable; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(1) << 20;  // the partials' maximum
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device, under g_scratch_mu
+
+fp8_status_t scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(FP8_EUNSUPPORTED, "device index %d above 63", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(FP8_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8_quantize_colsum_noalloc_max_bytes(void) { return kScratchBytes; }
+
+fp8_status_t fp8_quantize_colsum_noalloc(const uint16_t* g, int64_t m, int64_t n, fp8_fmt_t fmt,
+                                         const float* scale, uint8_t* out,
+                                         const fp8_ring_t* ring, int32_t margin,
+                                         float* scale_used, uint16_t* db, hipStream_t stream) {
+    g_err[0] = 0;
+    if (!fmt_ok(fmt))
+        return fail(FP8_EINVAL, "fp8_quantize_colsum_noalloc: unsupported fp8 format %d", fmt);
+    if (m < 1 || n < 1) return fail(FP8_EINVAL, "fp8_quantize_colsum_noalloc: m, n must be >= 1");
+    if (!g || !out || !db || !scale)
+        return fail(FP8_EINVAL, "fp8_quantize_colsum_noalloc: NULL pointer");
+    const size_t need = fp8lin::colsum_workspace(m, n);
+    if (need > kScratchBytes)
+        return fail(FP8_EINVAL,
+                    "fp8_quantize_colsum_noalloc: %lld x %lld needs %zu bytes of column-sum "
+                    "partials, above the static scratch of %zu bytes; use "
+                    "fp8_quantize_colsum with a workspace",
+                    (long long)m, (long long)n, need, kScratchBytes);
+    if (ring) {
+        fp8_status_t st = check_ring(ring, "fp8_quantize_colsum_noalloc");
+        if (st) return st;
+    }
+    if (margin < 0 || margin > 64)
+        return fail(FP8_EINVAL, "fp8_quantize_colsum_noalloc: margin %d outside [0, 64]",
+                    margin);
+    fp8_status_t st = check_device();
+    if (st) return st;
+    void* ws = nullptr;
+    if ((st = scratch_for_current_device(&ws))) return st;
+    return do_quantize_colsum(g, m, n, fmt, scale, out, ring ? ring->state : nullptr,
+                              ring ? ring->len : 0, ring ? ring->idx : 0, margin, scale_used, db,
+                              ws, stream);
 }
 
 size_t fp8_linear_fwd_workspace(int64_t M, int64_t N, int64_t K) {

@@ -344,6 +344,28 @@ fp8_status_t fp8_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fm
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * fp8_quantize_colsum_noalloc -- fp8_quantize_colsum for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, serving loops, harnesses that forbid allocation): the same
+ * arguments without the workspace, the same results bit for bit.
+ *
+ * The column-sum partials go to a static scratch array inside the library
+ * (one per GPU, kept until the process ends): no hipMalloc, hipFree or
+ * other allocation happens in the call.  Its size bounds the shapes:
+ * fp8_colsum_workspace(m, n) must be at most
+ * fp8_quantize_colsum_noalloc_max_bytes() (1 MiB: every m for n up to
+ * 262144 columns), else FP8_EINVAL and nothing is enqueued.  Every call on
+ * one GPU shares that GPU's scratch: calls that may overlap on one GPU
+ * (unordered streams) race and must not be made; calls ordered on one
+ * stream are safe (each writes the partials before reading them).
+ * ------------------------------------------------------------------- */
+size_t fp8_quantize_colsum_noalloc_max_bytes(void);
+fp8_status_t fp8_quantize_colsum_noalloc(const uint16_t* g, int64_t m, int64_t n,
+                                         fp8_fmt_t fmt, const float* scale, uint8_t* out,
+                                         const fp8_ring_t* ring, int32_t margin,
+                                         float* scale_used, uint16_t* db, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * fp8_linear_fwd -- out[M][N] = x[M][K] w[N][K]^T * (sx*sw) + bias
  * (compare view: astrai/extension/fp8.py fp8_linear_forward)
  *

@@ -477,8 +477,8 @@ def components(f, torch):
     # fp8_autocast, delayed HYBRID): what the policy layer costs over the
     # step's own launch sequence
     res.update(autograd_layer(f, torch))
-    # reference for the quantize's practical ceiling: torch's copy of 1 GiB
-    # (read + write, 2 GiB moved)
+    res.update(ceilings(torch))
+    # torch's copy of 1 GiB (read + write, 2 GiB moved), for comparison
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     ms = time_kernel(torch, lambda i: dst.copy_(src), 10)
@@ -486,6 +486,60 @@ def components(f, torch):
                                           gbs=round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
                                           hbm_frac=round(2 * (1 << 30) / (ms * 1e-3) / 1e9
                                                          / PEAK_HBM_GBS, 3))
+    return res
+
+
+def ceilings(torch):
+    """Practical ceilings of the bandwidth-bound kernels on this GPU, from
+    the reference kernels of libfp8bench.so (same bytes, no arithmetic):
+    the per-launch floor (an empty 256-workgroup launch in a graph), a read
+    of the short-A GEMM's 16.8 MB weight (graph of 64 launches over 64
+    rotated copies, 1.07 GB, so it comes from HBM), and the quantize's 2:1
+    read/write stream in the quantize's launch shape at the workloads'
+    largest and smallest quantize shapes (rotated over >= 1 GB)."""
+    import ctypes
+    dev = "cuda"
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                   "fp8_tensor_scaled_amd", "libfp8bench.so"))
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.fp8bench_empty.argtypes = [I, I, P]
+    lib.fp8bench_read.argtypes = [P, I64, P, I, I, P]
+    lib.fp8bench_stream21.argtypes = [P, I64, P, I, P]
+    for fn in (lib.fp8bench_empty, lib.fp8bench_read, lib.fp8bench_stream21):
+        fn.restype = I
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def ok(rc):
+        if rc != 0:
+            raise SystemExit(f"reference kernel launch failed: {rc}")
+    res = {}
+    ms = time_graph(torch, lambda i: ok(lib.fp8bench_empty(256, 512, stream())), 64)
+    res["ceiling_launch_floor_256wg"] = dict(us=round(ms * 1e3, 2))
+    nbytes, rot = 8192 * 2048, 64
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(rot)]
+    sink = torch.empty(512, dtype=torch.int32, device=dev)
+    for nt in (1, 0):
+        ms = time_graph(torch, lambda i: ok(lib.fp8bench_read(bufs[i % rot].data_ptr(), nbytes,
+                                                              sink.data_ptr(), 256, nt,
+                                                              stream())), rot)
+        res[f"ceiling_read_16.8MB{'_nt' if nt else ''}"] = dict(
+            us=round(ms * 1e3, 2), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+            hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+    del bufs
+    for name, numel in (("ceiling_stream21_8192x8192", 8192 * 8192),
+                        ("ceiling_stream21_2048x4096", 2048 * 4096)):
+        nrot = (1 << 30) // (3 * numel) + 1
+        xs = [torch.empty(numel, dtype=torch.int16, device=dev) for _ in range(nrot)]
+        qs = [torch.empty(numel, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+        grid = min(256, max(1, numel // (1024 * 16)))
+        ms = time_graph(torch, lambda i: ok(lib.fp8bench_stream21(
+            xs[i % nrot].data_ptr(), numel, qs[i % nrot].data_ptr(), grid, stream())),
+            max(2 * nrot, 8))
+        res[name] = dict(us=round(ms * 1e3, 2), gbs=round(3 * numel / (ms * 1e-3) / 1e9, 1),
+                         hbm_frac=round(3 * numel / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+        del xs, qs
     return res
 
 

@@ -15,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8lin.so")
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_tiled.hip", "gemm_skinny.hip"]
+# the benchmark's ceiling kernels, a library of their own that only bench.py loads
+BENCH_LIB = os.path.join(HERE, "libfp8bench.so")
+BENCH_SOURCES = ["bench_ref.hip"]
 ARCH = "gfx950"
 
 
@@ -41,7 +44,9 @@ def _flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libfp8lin.so; returns its path."""
+    """Compile every source for gfx950 and link libfp8lin.so (and the
+    benchmark's reference kernels, libfp8bench.so); returns the library's
+    path."""
     hipcc = _hipcc()
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -58,14 +63,15 @@ def build(verbose: bool = False) -> str:
             print(msgs, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES) + len(BENCH_SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES + BENCH_SOURCES))
+    for lib, parts in ((LIB, objs[:len(SOURCES)]), (BENCH_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp, lib)
     return LIB
 
 

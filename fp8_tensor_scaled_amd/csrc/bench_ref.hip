@@ -1,0 +1,128 @@
+// Reference kernels for the benchmark's HBM ceilings (not part of the fp8
+// library's interface; built into libfp8bench.so, which only bench.py
+// loads).  They move the same bytes as the library's bandwidth-bound kernels
+// with no arithmetic, so their rates are the practical ceilings those kernels
+// are judged against on this GPU:
+//   * fp8bench_empty: a launch that does nothing (the per-launch floor);
+//   * fp8bench_read: every byte of a buffer read once, 256 workgroups each
+//     streaming a contiguous slab (the short-A GEMM's weight stream);
+//   * fp8bench_stream21: the quantize's access pattern without the
+//     conversion (read 2 bytes, write 1 byte per element: the high byte of
+//     each bf16), in the quantize's launch shape.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__global__ void empty_kernel() {}
+
+// Each lane keeps kU 16-byte loads in flight; a contiguous slab per
+// workgroup.  The xor of everything read is stored only in the (never
+// taken) case that it equals a fixed pattern, so the loads cannot be
+// dropped and nothing is written.
+template <int kU, bool NT>
+__global__ __launch_bounds__(512) void read_kernel(const uint4* b, int64_t nvec, uint32_t* sink) {
+    const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < nvec ? lo + per : nvec;
+    uint32_t acc = 0;
+    for (int64_t c0 = lo + threadIdx.x; c0 < hi; c0 += (int64_t)kU * blockDim.x) {
+        uint4 r[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t c = c0 + (int64_t)u * blockDim.x;
+            const int64_t cl = c < hi ? c : lo;
+            if constexpr (NT) {
+                typedef int v4i __attribute__((ext_vector_type(4)));
+                const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(b + cl));
+                r[u] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2], (uint32_t)t[3]);
+            } else {
+                r[u] = b[cl];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+    }
+    if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
+}
+
+// 16 bf16 -> their 16 high bytes.
+__device__ __forceinline__ uint32_t hi_bytes(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07050301u);
+}
+
+constexpr int kThreads = 1024;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void stream21_kernel(const uint4* x, int64_t nvec,
+                                                            uint4* out) {
+    const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < nvec ? lo + per : nvec;
+    constexpr int kRound = kThreads * kUnroll;
+    const int64_t nr = hi > lo ? (hi - lo + kRound - 1) / kRound : 0;
+    for (int64_t rd = 0; rd < nr; ++rd) {
+        const int64_t c0 = lo + rd * kRound + threadIdx.x;
+        uint4 r[kUnroll][2];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t c = c0 + u * kThreads;
+            const int64_t cl = c < hi ? c : lo;
+            typedef int v4i __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(x + 2 * cl + i));
+                r[u][i] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2], (uint32_t)t[3]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t c = c0 + u * kThreads;
+            if (c < hi)
+                out[c] = make_uint4(hi_bytes(r[u][0].x, r[u][0].y), hi_bytes(r[u][0].z, r[u][0].w),
+                                    hi_bytes(r[u][1].x, r[u][1].y), hi_bytes(r[u][1].z, r[u][1].w));
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Returns 0 on success, else the HIP error code of the launch.
+int fp8bench_empty(int grid, int threads, hipStream_t stream) {
+    if (grid < 1 || threads < 1 || threads > 1024) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(empty_kernel, dim3(grid), dim3(threads), 0, stream);
+    return (int)hipGetLastError();
+}
+
+// bytes: a multiple of 16; b 16-byte aligned; sink: 512 uint32 (never
+// written in practice).
+int fp8bench_read(const void* b, int64_t bytes, uint32_t* sink, int grid, int nontemporal,
+                  hipStream_t stream) {
+    if (!b || !sink || bytes < 16 || (bytes % 16) || grid < 1 ||
+        (reinterpret_cast<uintptr_t>(b) & 15))
+        return (int)hipErrorInvalidValue;
+    const int64_t nvec = bytes / 16;
+    if (nontemporal)
+        hipLaunchKernelGGL((read_kernel<8, true>), dim3(grid), dim3(512), 0, stream,
+                           static_cast<const uint4*>(b), nvec, sink);
+    else
+        hipLaunchKernelGGL((read_kernel<8, false>), dim3(grid), dim3(512), 0, stream,
+                           static_cast<const uint4*>(b), nvec, sink);
+    return (int)hipGetLastError();
+}
+
+// numel: a multiple of 16; x, out 16-byte aligned.
+int fp8bench_stream21(const uint16_t* x, int64_t numel, uint8_t* out, int grid,
+                      hipStream_t stream) {
+    if (!x || !out || numel < 16 || (numel % 16) || grid < 1 ||
+        ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) & 15))
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream21_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(x), numel / 16, reinterpret_cast<uint4*>(out));
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -41,9 +41,6 @@ struct QuantLaunch {
     // the cast): ordinary loads.  Otherwise 2-byte inputs are loaded
     // non-temporally, which skips the MALL for data read once.
     bool cached_input = false;
-    // The codes are not read soon (a standalone quantize of a large tensor):
-    // non-temporal stores, which stream past the MALL.
-    bool stream_out = false;
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
 

@@ -71,9 +71,8 @@ struct QuantParams {
     float* scale_used;
     float* amax_out;  // optional max |x| output: written by the fold, or (no
                       // ring) an atomic max over workgroups after an arming launch
-    int vec;     // 1: x and out are 16-byte aligned
-    int nt;      // 1: non-temporal input loads (vector path, 2-byte inputs)
-    int nt_out;  // 1: non-temporal code stores
+    int vec;  // 1: x and out are 16-byte aligned
+    int nt;   // 1: non-temporal input loads (vector path, 2-byte inputs)
 };
 
 // Last-workgroup fold (wave 0): hist[idx] = amax;
@@ -251,8 +250,7 @@ __device__ __forceinline__ float absmax16(const uint4* r, float amax) {
 // 16 codes of x * m into dst; FMT2 >= 0: the same scaled values in the
 // second format into dst2 (one read of x feeds both encodings).
 template <int IN, int FMT, int FMT2>
-__device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, uint4* dst2,
-                                         bool nt = false) {
+__device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, uint4* dst2) {
     float f[16];
     In<IN>::unpack(r, f);
 #pragma unroll
@@ -262,22 +260,14 @@ __device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, ui
     o.y = cvt4<FMT>(f[4], f[5], f[6], f[7]);
     o.z = cvt4<FMT>(f[8], f[9], f[10], f[11]);
     o.w = cvt4<FMT>(f[12], f[13], f[14], f[15]);
-    auto put = [nt](uint4* d, const uint4& v) {
-        if (nt) {
-            const v4i t = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-            __builtin_nontemporal_store(t, reinterpret_cast<v4i*>(d));
-        } else {
-            *d = v;
-        }
-    };
-    put(dst, o);
+    *dst = o;
     if constexpr (FMT2 >= 0) {
         uint4 o2;
         o2.x = cvt4<FMT2>(f[0], f[1], f[2], f[3]);
         o2.y = cvt4<FMT2>(f[4], f[5], f[6], f[7]);
         o2.z = cvt4<FMT2>(f[8], f[9], f[10], f[11]);
         o2.w = cvt4<FMT2>(f[12], f[13], f[14], f[15]);
-        put(dst2, o2);
+        *dst2 = o2;
     }
 }
 
@@ -364,7 +354,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int64_t c = c0 + u * slot;
-                    if (c < nvec) encode16<IN, FMT, FMT2>(r[u], m, ov + c, ov2 + c, p.nt_out);
+                    if (c < nvec) encode16<IN, FMT, FMT2>(r[u], m, ov + c, ov2 + c);
                 }
             }
         }
@@ -464,7 +454,6 @@ static QuantParams quant_params(const QuantLaunch& q) {
     p.scale_used = q.scale_used;
     p.amax_out = q.amax_out;
     p.nt = q.cached_input ? 0 : 1;
-    p.nt_out = q.stream_out ? 1 : 0;
     const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
                          reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;

@@ -52,7 +52,8 @@ from . import (E4M3, E5M2, OUT_BF16, Ring, _stream, fp8_colsum, fp8_colsum_works
                fp8_mm_ex, fp8_quantize, fp8_quantize_colsum)
 
 __all__ = ["FP8Format", "FP8Recipe", "FP8TensorMeta", "FP8State", "fp8_state", "fp8_autocast",
-           "current_config", "fp8_linear", "FP8Linear"]
+           "current_config", "fp8_linear", "FP8Linear", "fp8_linear_enable",
+           "fp8_linear_enabled"]
 
 _FP8_DTYPES = {torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
 
@@ -422,3 +423,60 @@ class FP8Linear(torch.nn.Linear):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return fp8_linear(x, self.weight, self.bias)
+
+
+# --------------------------------------------------------------------------
+# Routing of torch's own linear (nn.Linear, F.linear) -- opt in
+# --------------------------------------------------------------------------
+#
+# The pages register their fp8 linear as the aten::linear kernel of CUDA
+# tensors, on the autograd key (training and no_grad) and on the CUDA key
+# (inference_mode, where the autograd keys are skipped), so that existing
+# models need no module swap (compare view 3e57cc8...main, commit log of
+# astrai/extension: the _LinearFp8 registration).  fp8_linear_enable() does
+# the same with torch.library, as an explicit switch: while it is on, every
+# aten::linear call on CUDA tensors comes here; the fp8 path runs when an
+# fp8_autocast region (or the default switch) enables it and the operands are
+# bf16, and every other call runs torch's own decomposition of linear.
+
+_ROUTE_LIB = None
+
+
+def _plain_linear(x, w, b):
+    """torch's decomposition of aten::linear (addmm for 2-D inputs, and for
+    contiguous 3-D inputs with a bias; else matmul, then the bias)."""
+    if b is not None and x.dim() == 2:
+        return torch.addmm(b, x, w.t())
+    if b is not None and x.dim() == 3 and x.is_contiguous():
+        out = torch.addmm(b, x.reshape(-1, x.shape[-1]), w.t())
+        return out.view(*x.shape[:-1], w.shape[0])
+    out = torch.matmul(x, w.t())
+    return out if b is None else out + b
+
+
+def _routed_linear(x, w, b=None):
+    if (current_config().enabled and x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16
+            and (b is None or b.dtype == torch.bfloat16) and x.dim() >= 1 and w.dim() == 2):
+        return fp8_linear(x, w, b)
+    return _plain_linear(x, w, b)
+
+
+def fp8_linear_enable(enabled: bool = True) -> None:
+    """Route torch's linear on CUDA tensors (nn.Linear, F.linear) through
+    fp8_linear (True), or give it back to torch (False).  With the routing on,
+    a stock nn.Linear takes the fp8 path inside fp8_autocast exactly as
+    FP8Linear does, and torch's own computation outside it."""
+    global _ROUTE_LIB
+    if enabled and _ROUTE_LIB is None:
+        lib = torch.library.Library("aten", "IMPL")
+        lib.impl("linear", _routed_linear, "AutogradCUDA")
+        lib.impl("linear", _routed_linear, "CUDA")
+        _ROUTE_LIB = lib
+    elif not enabled and _ROUTE_LIB is not None:
+        _ROUTE_LIB._destroy()
+        _ROUTE_LIB = None
+
+
+def fp8_linear_enabled() -> bool:
+    """Whether torch's linear is routed here (fp8_linear_enable)."""
+    return _ROUTE_LIB is not None

@@ -98,3 +98,21 @@ def test_weight_meta_lifetime():
     del w
     gc.collect()
     assert len(st._metas) == n - 1
+
+
+def test_linear_routing_switch_host():
+    """fp8_linear_enable registers and removes the aten::linear kernels of
+    CUDA tensors; CPU calls never change."""
+    x, lin = torch.randn(4, 8), torch.nn.Linear(8, 3)
+    want = lin(x)
+    fa.fp8_linear_enable(True)
+    try:
+        assert fa.fp8_linear_enabled()
+        fa.fp8_linear_enable(True)  # idempotent
+        with fa.fp8_autocast():
+            assert torch.equal(lin(x), want)
+    finally:
+        fa.fp8_linear_enable(False)
+    assert not fa.fp8_linear_enabled()
+    fa.fp8_linear_enable(False)
+    assert torch.equal(lin(x), want)

@@ -317,3 +317,52 @@ def test_workspace_cache_stays_bounded(lib, fa):
                    lib.fp8_linear_bwd_workspace_codes(M, 384, 256))
                for M in (64, 512, 96, 1024, 32, 700))
     assert sizes[-1] == need and sizes == sorted(sizes)
+
+
+def test_stock_linear_routed_under_autocast(lib, fa):
+    """fp8_linear_enable(): a stock torch.nn.Linear inside fp8_autocast gives
+    the bits of FP8Linear with the same weights (forward, input and weight
+    gradients, bias gradient, over two delayed steps, also under
+    inference_mode), and outside the region the bits of torch's own linear;
+    switched off, nothing is routed."""
+    torch.manual_seed(7)
+    K, N = 512, 384
+    xs = [torch.randn(3, 64, K, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    gs = [torch.randn(3, 64, N, device="cuda").to(torch.bfloat16) * 1e-3 for _ in range(2)]
+
+    def run(layer):
+        fa.fp8_state().reset()
+        res = []
+        for x0, g in zip(xs, gs):
+            x = x0.clone().requires_grad_()
+            layer.zero_grad()
+            with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+                y = layer(x)
+            y.backward(g)
+            res += [y.detach(), x.grad, layer.weight.grad.clone(), layer.bias.grad.clone()]
+        with torch.inference_mode(), fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+            res.append(layer(xs[0]).clone())
+        return res
+
+    ref_layer = fa.FP8Linear(K, N).cuda().to(torch.bfloat16)
+    stock = torch.nn.Linear(K, N).cuda().to(torch.bfloat16)
+    with torch.no_grad():
+        stock.weight.copy_(ref_layer.weight)
+        stock.bias.copy_(ref_layer.bias)
+    want = run(ref_layer)
+    plain = stock(xs[0]).detach()  # before routing: torch's own linear
+    fa.fp8_linear_enable(True)
+    try:
+        assert fa.fp8_linear_enabled()
+        got = run(stock)
+        outside = stock(xs[0]).detach()
+        f_out = torch.nn.functional.linear(xs[0], stock.weight, stock.bias).detach()
+    finally:
+        fa.fp8_linear_enable(False)
+    assert not fa.fp8_linear_enabled()
+    for a, b in zip(got, want):
+        assert torch.equal(a, b)
+    assert torch.equal(outside, plain) and torch.equal(f_out, plain)
+    # off again: inside a region a stock layer no longer takes the fp8 path
+    with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+        assert torch.equal(stock(xs[0]).detach(), plain)

@@ -263,23 +263,30 @@ def check_against_linear_entry_points(f, torch):
 # HBM traffic of the step's GEMMs from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch, one counter per run, `bench.py --kernel NAME`), scaled by
 # what the same counters read for a 192 MiB copy (FETCH_SIZE x 2.0, WRITE_SIZE
-# x 1.0).  Valid only for the kernel sources they were taken on: PMC_SRC is
-# the sha256 of gemm_tiled.hip + common.hpp then; any other source gives null.
+# x 1.0).  Valid only for the kernel code they were taken on: PMC_SRC is the
+# sha256 of gemm_tiled.hip + common.hpp with comments and blank lines left out
+# (gemm_source_hash); any other code gives null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 PMC_TRAFFIC = {
     "gemm_nt_fwd": {"FETCH_SIZE": 49228.0, "WRITE_SIZE": 32768.0},
     "gemm_bwd_pair": {"FETCH_SIZE": 98479.5, "WRITE_SIZE": 65536.0},
 }
-PMC_SRC = "9a2ea2981ab5b359b70fd3d85157f7cf50087bb182f6d893b5135490dabbd3b9"
+PMC_SRC = "88c9b17a2b96dae94f99198790ee6f6f6f03dfc588533d784948c18e9514e931"
 
 
 def gemm_source_hash():
+    """sha256 of the GEMM kernels' code: gemm_tiled.hip and common.hpp, each
+    line cut at `//` and stripped, blank lines dropped (the sources have no
+    block comments and no `//` inside literals)."""
     import hashlib
     h = hashlib.sha256()
     for part in ("gemm_tiled.hip", "common.hpp"):
         with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "fp8_tensor_scaled_amd",
-                               "csrc", part), "rb") as fh:
-            h.update(fh.read())
+                               "csrc", part), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
@@ -538,7 +545,7 @@ def ceilings(torch):
         nrot = (1 << 30) // (3 * numel) + 1
         xs = [torch.empty(numel, dtype=torch.int16, device=dev) for _ in range(nrot)]
         qs = [torch.empty(numel, dtype=torch.uint8, device=dev) for _ in range(nrot)]
-        grid = min(256, max(1, numel // (1024 * 16)))
+        grid = min(512, max(1, (numel + 256 * 16 - 1) // (256 * 16)))  # the quantize's grid
         ms = time_graph(torch, lambda i: ok(lib.fp8bench_stream21(
             xs[i % nrot].data_ptr(), numel, qs[i % nrot].data_ptr(), grid, stream())),
             max(2 * nrot, 8))

@@ -7,8 +7,9 @@
 //   * fp8bench_read: every byte of a buffer read once, 256 workgroups each
 //     streaming a contiguous slab (the short-A GEMM's weight stream);
 //   * fp8bench_stream21: the quantize's access pattern without the
-//     conversion (read 2 bytes, write 1 byte per element: the high byte of
-//     each bf16), in the quantize's launch shape.
+//     conversion, the amax or the fold (read 2 bytes, write 1 byte per
+//     element: the high byte of each bf16), in the quantize's launch shape
+//     and chunk order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,24 +53,26 @@ __device__ __forceinline__ uint32_t hi_bytes(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07050301u);
 }
 
-constexpr int kThreads = 1024;
+// The quantize's launch shape and sweep: 256-lane workgroups (at most 512,
+// two per CU), the grid's lanes taking consecutive 16-element chunks in each
+// round, four chunks in flight per lane.
+constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
 __global__ __launch_bounds__(kThreads) void stream21_kernel(const uint4* x, int64_t nvec,
-                                                            uint4* out) {
-    const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
-    const int64_t lo = (int64_t)blockIdx.x * per;
-    const int64_t hi = lo + per < nvec ? lo + per : nvec;
-    constexpr int kRound = kThreads * kUnroll;
-    const int64_t nr = hi > lo ? (hi - lo + kRound - 1) / kRound : 0;
+                                                           uint4* out) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const int64_t slot = (int64_t)gridDim.x * kThreads;  // chunks per slot of a round
+    const int64_t round = slot * kUnroll;
+    const int64_t nr = (nvec + round - 1) / round;
+    const int64_t mine = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     for (int64_t rd = 0; rd < nr; ++rd) {
-        const int64_t c0 = lo + rd * kRound + threadIdx.x;
+        const int64_t c0 = rd * round + mine;
         uint4 r[kUnroll][2];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t c = c0 + u * kThreads;
-            const int64_t cl = c < hi ? c : lo;
-            typedef int v4i __attribute__((ext_vector_type(4)));
+            const int64_t c = c0 + u * slot;
+            const int64_t cl = c < nvec ? c : 0;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(x + 2 * cl + i));
@@ -78,8 +81,8 @@ __global__ __launch_bounds__(kThreads) void stream21_kernel(const uint4* x, int6
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t c = c0 + u * kThreads;
-            if (c < hi)
+            const int64_t c = c0 + u * slot;
+            if (c < nvec)
                 out[c] = make_uint4(hi_bytes(r[u][0].x, r[u][0].y), hi_bytes(r[u][0].z, r[u][0].w),
                                     hi_bytes(r[u][1].x, r[u][1].y), hi_bytes(r[u][1].z, r[u][1].w));
         }

@@ -28,10 +28,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 }
 
 // fp32 -> bf16 bit patterns, round to nearest even, by gfx950's
-// v_cvt_pk_bf16_f32 (two values per instruction).  Checked against the
-// integer formulation (add 0x7fff plus the kept lsb, truncate) on all 2^32
-// fp32 patterns on the device: identical for every non-NaN input, NaN stays
-// NaN.
+// v_cvt_pk_bf16_f32 (two values per instruction).  The GEMM parity tests
+// check its results against the oracle's single rounding, among them
+// outputs whose low 16 bits are an exact tie, a near tie either way, zero
+// and the largest cut, at 18 exponents, on the short-A, 128 x 128 and
+// 256 x 256 kernels.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {

@@ -948,8 +948,8 @@ static int64_t tiles_of(const GemmLaunch& g, int bm, int bn) {
 // workgroup per CU (its LDS ring takes most of the 160 KB), so a launch with
 // fewer tiles than the 256 CUs leaves CUs idle, and the largest tile that
 // still gives every CU one is the most efficient (fewest operand bytes per
-// flop, longest time per stage to cover load latency).  Measured on MI355X
-// (µs, fp8 operands; the sweep is in the design notes):
+// flop, longest time per stage to cover load latency).  The configurations,
+// with what they measured on MI355X (µs, fp8 operands, alternating bursts):
 //   kBig    256 x 256, 8 waves of 128 x 64       at >= 256 tiles of 256 x 256
 //   kWide   128 x 256, 8 waves of  64 x 64       at >= 256 tiles of 128 x 256
 //   kTall   256 x 128, 8 waves of  64 x 64       at >= 256 tiles of 256 x 128

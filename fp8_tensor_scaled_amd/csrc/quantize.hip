@@ -12,25 +12,27 @@
 // update costs no extra launch.
 //
 // gfx950 design:
-//  * HBM streaming: one workgroup of 16 waves per CU (at most 256
-//    workgroups), every lane keeping four 32-byte loads in flight per
-//    round (16 bf16 each, two 16-byte loads) and storing 16 fp8 codes
-//    with one 16-byte store.  Plain (cached) accesses: the codes feed the
-//    GEMM that follows and the bf16 input is read again by the backward's
-//    quantizes, and in the layer's step non-temporal hints measured slower
-//    (they only win on a stream of cold, never-reused buffers).
-//    Conversions are v_cvt_pk_{fp8,bf8}_f32 after a med3 clamp to +-max
-//    (satfinite).
+//  * HBM streaming (quantize_kernel, quantize_two_kernel): workgroups of 256
+//    lanes, two per CU (at most 512), sweeping the tensor in rounds: in a
+//    round the grid's lanes take consecutive 16-element chunks, each lane
+//    keeping four chunks (four 32-byte loads) in flight and storing 16 codes
+//    per chunk with one 16-byte store.  An input read once is loaded
+//    non-temporally, so it neither displaces lines the next kernel reads
+//    nor, when cold, loses anything; the library's measure-then-cast
+//    sequences and fp32 inputs use ordinary loads.  The codes' stores are
+//    ordinary (they feed the GEMM that follows).  Conversions are
+//    v_cvt_pk_{fp8,bf8}_f32 after a med3 clamp to +-max (satfinite).
 //  * The fold's cost is its atomics: same-address atomics serialize at the
 //    coherence point (about 11 ns each, measured), and a returning atomic
-//    waits for every store its wave issued before it.  So there is one
-//    workgroup per CU, the maxima meet in two levels (16 groups, then the
-//    ring's words), each workgroup owns a contiguous range and publishes in
-//    its last round after the loads and before the stores (the round trips
-//    overlap the store drain), and the window is read at kernel start so
-//    the last workgroup does not wait for it.  The single-lane atomics are
-//    kept as written (the build turns off the compiler's atomic optimizer,
-//    whose wave-wide form would wait for the result at once).
+//    waits for every store its wave issued before it.  So the maxima meet
+//    in two levels (16 groups, then the ring's words), each workgroup
+//    publishes in its last round after the loads and before the stores (the
+//    round trips overlap the store drain), and the window is read at kernel
+//    start so the last workgroup does not wait for it.  The single-lane
+//    atomics are kept as written (the build turns off the compiler's atomic
+//    optimizer, whose wave-wide form would wait for the result at once).
+//  * The fused column-sum, transposed and small-tensor kernels keep
+//    1024-lane workgroups (one per CU).
 //  * The fold uses relaxed agent-scope atomics only.  Release/acquire at
 //    agent scope write back / invalidate the per-XCD L2s and cost tens of ns
 //    per workgroup when every workgroup issues them; instead each level

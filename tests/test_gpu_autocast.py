@@ -322,7 +322,7 @@ def test_workspace_cache_stays_bounded(lib, fa):
 def test_stock_linear_routed_under_autocast(lib, fa):
     """fp8_linear_enable(): a stock torch.nn.Linear inside fp8_autocast gives
     the bits of FP8Linear with the same weights (forward, input and weight
-    gradients, bias gradient, over two delayed steps, also under
+    gradients, bias gradient, over two delayed steps, then under no_grad and
     inference_mode), and outside the region the bits of torch's own linear;
     switched off, nothing is routed."""
     torch.manual_seed(7)
@@ -340,6 +340,8 @@ def test_stock_linear_routed_under_autocast(lib, fa):
                 y = layer(x)
             y.backward(g)
             res += [y.detach(), x.grad, layer.weight.grad.clone(), layer.bias.grad.clone()]
+        with torch.no_grad(), fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
+            res.append(layer(xs[1]).clone())
         with torch.inference_mode(), fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
             res.append(layer(xs[0]).clone())
         return res

@@ -13,7 +13,8 @@
 //
 // gfx950 design:
 //  * HBM streaming (quantize_kernel, quantize_two_kernel): workgroups of 256
-//    lanes, two per CU (at most 512), sweeping the tensor in rounds: in a
+//    data lanes and one publisher wave, two per CU (at most 512), sweeping
+//    the tensor in rounds: in a
 //    round the grid's lanes take consecutive 16-element chunks, each lane
 //    keeping four chunks (four 32-byte loads) in flight and storing 16 codes
 //    per chunk with one 16-byte store.  An input read once is loaded
@@ -26,9 +27,10 @@
 //    coherence point (about 11 ns each, measured), and a returning atomic
 //    waits for every store its wave issued before it.  So the maxima meet
 //    in two levels (16 groups, then the ring's words), each workgroup
-//    publishes in its last round after the loads and before the stores (the
-//    round trips overlap the store drain), and the window is read at kernel
-//    start so the last workgroup does not wait for it.  The single-lane
+//    publishes in its last round after the loads and before the stores, from
+//    a wave with no stores of its own (the publisher; in the 1024-lane
+//    kernels, wave 0), and the window is read at kernel start so the last
+//    workgroup does not wait for it.  The single-lane
 //    atomics are kept as written (the build turns off the compiler's atomic
 //    optimizer, whose wave-wide form would wait for the result at once).
 //  * The fused column-sum, transposed and small-tensor kernels keep
@@ -77,12 +79,12 @@ struct QuantParams {
     int nt;   // 1: non-temporal input loads (vector path, 2-byte inputs)
 };
 
-// Last-workgroup fold (wave 0): hist[idx] = amax;
+// Last-workgroup fold (one wave): hist[idx] = amax;
 // scale = max(peak / fmax / 2^margin, 1e-12).  `win` = this lane's share of
 // the window's other slots, loaded at kernel start (only the fold writes the
 // window, and the previous launch's fold finished before this kernel began).
 __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, float win) {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave;
     float amax = 0.0f;
     if (lane == 0)
         amax = __uint_as_float(
@@ -104,18 +106,18 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, fl
     }
 }
 
-// Workgroup max of v, published by thread 0 in two levels: workgroup b is
+// Workgroup max of v, published by thread PUB in two levels: workgroup b is
 // in group b % G (G = min(workgroups, kRingGroups)); it takes the group's
 // atomic max and then, once that has been performed (the increment depends
 // on the returned value), the group's counter.  The group's last workgroup
 // reads the group max, re-arms the group's line, and does the same on the
 // ring's amax / done words.  Same-address atomics serialize (about 11 ns
 // each, measured), so 16 x 16 contenders cost far less than 256 on one
-// word.  Returns, at thread 0, nblocks - 1 if this workgroup drew the last
+// word.  Returns, at thread PUB, nblocks - 1 if this workgroup drew the last
 // top-level ticket (it folds), else ~0u.  The whole chain runs before the
 // caller's last stores, which go out while it is in flight.  Every thread
 // of the workgroup must call it once.
-template <int T = kQuantThreads>
+template <int T = kQuantThreads, int PUB = 0>
 __device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, uint32_t nblocks,
                                                  uint32_t b) {
     constexpr int kW = T / kWave;
@@ -124,7 +126,8 @@ __device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, 
     if ((threadIdx.x % kWave) == 0) slots[threadIdx.x / kWave] = v;
     __syncthreads();
     uint32_t ticket = ~0u;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == PUB) {
+        v = slots[0];
 #pragma unroll
         for (int w = 1; w < kW; ++w) v = fmaxf(v, slots[w]);
         const uint32_t ng = nblocks < kRingGroups ? nblocks : kRingGroups;
@@ -154,14 +157,15 @@ __device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, 
 // Without a ring: the workgroup max goes into *amax_out (armed to +0 by the
 // launch before) by one atomic max; non-negative floats order as their bits.
 // Every thread of the workgroup must call it once.
-template <int T>
+template <int T, int PUB = 0>
 __device__ __forceinline__ void publish_amax_out(const QuantParams& p, float v) {
     constexpr int kW = T / kWave;
     __shared__ float slots[kW];
     v = wave_max(v);
     if ((threadIdx.x % kWave) == 0) slots[threadIdx.x / kWave] = v;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == PUB) {
+        v = slots[0];
 #pragma unroll
         for (int w = 1; w < kW; ++w) v = fmaxf(v, slots[w]);
         __hip_atomic_fetch_max(reinterpret_cast<uint32_t*>(p.amax_out), __float_as_uint(v),
@@ -171,11 +175,12 @@ __device__ __forceinline__ void publish_amax_out(const QuantParams& p, float v) 
 
 __global__ void arm_amax_kernel(float* amax_out) { *amax_out = 0.0f; }
 
-// The workgroup that drew the last ticket folds, on its wave 0.
+// The workgroup that drew the last ticket folds, on the wave of thread PUB.
+template <int PUB = 0>
 __device__ __forceinline__ void finish_fold(const QuantParams& p, uint32_t ticket, float s_read,
                                             float win, uint32_t nblocks) {
-    if (threadIdx.x >= kWave) return;
-    const int last = threadIdx.x == 0 && ticket == nblocks - 1u;
+    if (threadIdx.x / kWave != PUB / kWave) return;
+    const int last = threadIdx.x == PUB && ticket == nblocks - 1u;
     if (__shfl(last, 0, kWave)) fold_ring(p, s_read, win);
 }
 
@@ -273,17 +278,22 @@ __device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, ui
     }
 }
 
-// Vector path (x, out, out2 16-byte aligned): the grid sweeps the 16-element
-// chunks in rounds; in round rd, slot u, workgroup b's lanes take the kQT
-// consecutive chunks ((rd * kUnroll + u) * nb + b) * kQT + lane, so at any
-// time the whole grid streams one narrow window of the tensor (measured
-// faster than a contiguous range per workgroup: 37 against 40.6 us for the
-// bare read-2 / write-1 stream at 8192 x 8192, with 256-lane workgroups two
-// to a CU).  The numel % 16 leftover elements go to workgroup 0 first.  With
-// a ring, the workgroup's max is published in its last round after the
-// loads and before the stores, so the fold's atomics overlap the store drain
-// instead of following it.  Scalar path (unaligned bases): grid-stride
-// elements, then the publish.
+// A workgroup is kQT data lanes plus one publisher wave.  Vector path (x,
+// out, out2 16-byte aligned): the grid sweeps the 16-element chunks in
+// rounds; in round rd, slot u, workgroup b's lanes take the kQT consecutive
+// chunks ((rd * kUnroll + u) * nb + b) * kQT + lane, so at any time the
+// whole grid streams one narrow window of the tensor (measured faster than a
+// contiguous range per workgroup: 37 against 40.6 us for the bare read-2 /
+// write-1 stream at 8192 x 8192).  A round's loads all go out before any of
+// its data is used (round 0's before the step's reciprocal is taken, so the
+// wait for the step overlaps them), and the non-temporal choice is made
+// once, outside the loop, so the waits count the loads one by one.  The
+// numel % 16 leftover elements go to workgroup 0.  With a ring, the data
+// waves hand their max to the publisher wave at one barrier in their last
+// round, before their stores; the publisher runs the fold's atomics while
+// the data waves store (a data wave that ran them would hold its own stores
+// back for the whole chain: 1 us more per launch, measured at every size).
+// Scalar path (unaligned bases): grid-stride elements, then the publish.
 // Workgroup b of the nb that process p (the whole grid, or one tensor's
 // share of a two-tensor launch).
 template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
@@ -291,19 +301,28 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
                                               const uint32_t nb) {
     constexpr int kL = In<IN>::kLoads;
     float m = 0.0f, s_read = 0.0f;
-    if constexpr (!MEASURE_ONLY) {
-        s_read = *p.scale;
-        m = __fdiv_rn(1.0f, s_read);
-    }
-    // the window slot of this lane (wave 0), loaded now so that its latency
-    // hides under the streaming loop
+    if constexpr (!MEASURE_ONLY) s_read = *p.scale;
     const int t = threadIdx.x;
-    const float win = (p.hist && t < p.len && t < kWave && t != p.idx) ? p.hist[t] : 0.0f;
+    if (t >= kQT) {
+        // The publisher wave: no data of its own; it takes the workgroup's
+        // max at the publish barrier and runs the atomics (and the fold), so
+        // that no data wave waits for them before its stores.
+        if (p.hist) {
+            const int wl = t - kQT;
+            const float win = (wl < p.len && wl != p.idx) ? p.hist[wl] : 0.0f;
+            const uint32_t tk = publish_amax<kQT + kWave, kQT>(p, 0.0f, nb, b);
+            finish_fold<kQT>(p, tk, s_read, win, nb);
+        } else if (p.amax_out) {
+            publish_amax_out<kQT + kWave, kQT>(p, 0.0f);
+        }
+        return;
+    }
     float amax = 0.0f;
-    uint32_t ticket = ~0u;  // publish_amax's result (thread 0)
     if (p.vec) {
         const int64_t nvec = p.numel / kVecElems;
-        if (b == 0) {
+        // the numel % 16 leftover elements (workgroup 0)
+        auto leftover = [&]() __attribute__((always_inline)) {
+            if (b != 0) return;
             const int64_t e = nvec * kVecElems + t;
             if (e < p.numel) {
                 const float f = In<IN>::one(p.x, e);
@@ -313,7 +332,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
                     if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
                 }
             }
-        }
+        };
         const uint4* xv = reinterpret_cast<const uint4*>(p.x);
         uint4* ov = reinterpret_cast<uint4*>(p.out);
         uint4* ov2 = reinterpret_cast<uint4*>(p.out2);
@@ -321,47 +340,71 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
         const int64_t round = slot * kUnroll;     // chunks per round
         const int64_t nr = (nvec + round - 1) / round;  // uniform
         const int64_t mine = (int64_t)b * kQT + t;
-        for (int64_t rd = 0; rd < nr; ++rd) {
-            const int64_t c0 = rd * round + mine;
+        // An input read once is loaded non-temporally (p.nt): it then skips
+        // the MALL, neither displacing lines the next kernel reads nor, when
+        // cold, losing anything.  An input that a measure pass just read is
+        // cached, and fp32 inputs measured slower with the hint: ordinary
+        // loads.  Loads are unconditional (a chunk past the end re-reads
+        // chunk 0 and is ignored).
+        auto sweep = [&](auto nt_tag) __attribute__((always_inline)) {
             uint4 r[kUnroll][kL];
-            // Loads are unconditional (a chunk past the end re-reads chunk 0
-            // and is ignored), so their waits stay counted one by one instead
-            // of collapsing into a wait for all of them.  An input read once
-            // is loaded non-temporally (p.nt): it then skips the MALL,
-            // neither displacing lines the next kernel reads nor, when cold,
-            // losing anything.  An input that a measure pass just read is
-            // cached, and fp32 inputs measured slower with the hint: ordinary
-            // loads.
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t c = c0 + u * slot;
-                const int64_t cl = c < nvec ? c : 0;
-#pragma unroll
-                for (int i = 0; i < kL; ++i) {
-                    if (IN != kInF32 && p.nt) {
-                        const v4i t = __builtin_nontemporal_load(
-                            reinterpret_cast<const v4i*>(xv + kL * cl + i));
-                        r[u][i] = make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2],
-                                             (uint32_t)t[3]);
-                    } else {
-                        r[u][i] = xv[kL * cl + i];
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if (c0 + u * slot < nvec) amax = absmax16<IN>(r[u], amax);
-            if (p.hist && rd == nr - 1) ticket = publish_amax<kQT>(p, amax, nb, b);
-            if constexpr (!MEASURE_ONLY) {
+            auto issue = [&](int64_t rd) __attribute__((always_inline)) {
+                const int64_t c0 = rd * round + mine;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int64_t c = c0 + u * slot;
-                    if (c < nvec) encode16<IN, FMT, FMT2>(r[u], m, ov + c, ov2 + c);
+                    const int64_t cl = c < nvec ? c : 0;
+#pragma unroll
+                    for (int i = 0; i < kL; ++i) {
+                        if constexpr (decltype(nt_tag)::value) {
+                            const v4i v = __builtin_nontemporal_load(
+                                reinterpret_cast<const v4i*>(xv + kL * cl + i));
+                            r[u][i] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2],
+                                                 (uint32_t)v[3]);
+                        } else {
+                            r[u][i] = xv[kL * cl + i];
+                        }
+                    }
                 }
+                // every load of the round goes out before any of its data is used
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto process = [&](int64_t rd) __attribute__((always_inline)) {
+                const int64_t c0 = rd * round + mine;
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (c0 + u * slot < nvec) amax = absmax16<IN>(r[u], amax);
+                if (p.hist && rd == nr - 1) publish_amax<kQT + kWave, kQT>(p, amax, nb, b);
+                if constexpr (!MEASURE_ONLY) {
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) {
+                        const int64_t c = c0 + u * slot;
+                        if (c < nvec) encode16<IN, FMT, FMT2>(r[u], m, ov + c, ov2 + c);
+                    }
+                }
+            };
+            // Round 0's loads go out before the step's reciprocal is taken,
+            // so the wait for the step overlaps them.
+            issue(0);
+            if constexpr (!MEASURE_ONLY) m = __fdiv_rn(1.0f, s_read);
+            leftover();
+            process(0);
+            for (int64_t rd = 1; rd < nr; ++rd) {
+                issue(rd);
+                process(rd);
             }
+        };
+        if (nr == 0) {
+            if constexpr (!MEASURE_ONLY) m = __fdiv_rn(1.0f, s_read);
+            leftover();
+            if (p.hist) publish_amax<kQT + kWave, kQT>(p, amax, nb, b);
+        } else if (IN != kInF32 && p.nt) {
+            sweep(std::true_type{});
+        } else {
+            sweep(std::false_type{});
         }
-        if (p.hist && nr == 0) ticket = publish_amax<kQT>(p, amax, nb, b);
     } else {
+        if constexpr (!MEASURE_ONLY) m = __fdiv_rn(1.0f, s_read);
         const int64_t stride = (int64_t)nb * kQT;
         for (int64_t e = (int64_t)b * kQT + t; e < p.numel; e += stride) {
             const float f = In<IN>::one(p.x, e);
@@ -371,20 +414,18 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
                 if constexpr (FMT2 >= 0) p.out2[e] = cvt1<FMT2>(f * m);
             }
         }
-        if (p.hist) ticket = publish_amax<kQT>(p, amax, nb, b);
+        if (p.hist) publish_amax<kQT + kWave, kQT>(p, amax, nb, b);
     }
-    if (p.hist) {
-        finish_fold(p, ticket, s_read, win, nb);
-    } else {
+    if (!p.hist) {
         if constexpr (!MEASURE_ONLY) {
             if (p.scale_used && b == 0 && t == 0) *p.scale_used = s_read;
         }
-        if (p.amax_out) publish_amax_out<kQT>(p, amax);
+        if (p.amax_out) publish_amax_out<kQT + kWave, kQT>(p, amax);
     }
 }
 
 template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
-__global__ __launch_bounds__(kQT) void quantize_kernel(QuantParams p) {
+__global__ __launch_bounds__(kQT + kWave) void quantize_kernel(QuantParams p) {
     quantize_body<IN, FMT, FMT2, MEASURE_ONLY>(p, blockIdx.x, gridDim.x);
 }
 
@@ -392,7 +433,7 @@ __global__ __launch_bounds__(kQT) void quantize_kernel(QuantParams p) {
 // [0, nb0) quantize p0, the rest p1, each with its own fold; one launch and
 // one latency chain (first loads, fold, last stores) instead of two.
 template <int FMT, int FMT2>
-__global__ __launch_bounds__(kQT) void quantize_two_kernel(QuantParams p0,
+__global__ __launch_bounds__(kQT + kWave) void quantize_two_kernel(QuantParams p0,
                                                                      QuantParams p1,
                                                                      uint32_t nb0) {
     if (blockIdx.x < nb0)
@@ -412,7 +453,7 @@ static int quant_grid(int64_t numel, int vec) {
 template <int IN>
 static void launch_quantize_in(const QuantLaunch& q, const QuantParams& p, dim3 grid,
                                hipStream_t stream) {
-    const dim3 block(kQT);
+    const dim3 block(kQT + kWave);
     const bool measure = q.out == nullptr;
     const int dual = q.out2 ? q.fmt2 : -1;
 #define FP8_Q(F, F2, M) \
@@ -495,7 +536,7 @@ hipError_t launch_quantize_two(const QuantLaunch& q0, const QuantLaunch& q1,
         b0 = b0 < 1 ? 1 : (b0 > kQGridMax - 1 ? kQGridMax - 1 : b0);
         b1 = kQGridMax - b0;
     }
-    const dim3 grid((unsigned)(b0 + b1)), block(kQT);
+    const dim3 grid((unsigned)(b0 + b1)), block(kQT + kWave);
     const int dual = q0.out2 ? q0.fmt2 : -1;
 #define FP8_Q2(F, F2) \
     hipLaunchKernelGGL((quantize_two_kernel<F, F2>), grid, block, 0, stream, p0, p1, (uint32_t)b0)

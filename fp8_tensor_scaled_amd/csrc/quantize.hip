@@ -702,10 +702,7 @@ struct QCParams {
 template <int FMT, bool QUANT>
 __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p) {
     float mul = 0.0f, s_read = 0.0f;
-    if constexpr (QUANT) {
-        s_read = *p.q.scale;
-        mul = __fdiv_rn(1.0f, s_read);
-    }
+    if constexpr (QUANT) s_read = *p.q.scale;
     const int wl = threadIdx.x;
     const float win = (QUANT && p.q.hist && wl < p.q.len && wl < kWave && wl != p.q.idx)
                           ? p.q.hist[wl] : 0.0f;
@@ -736,6 +733,12 @@ __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p)
             const int64_t r = rb + u * kQCPhases;
             const int64_t rl = r < r1 ? r : r0;
             v[u] = *reinterpret_cast<const uint4*>(p.g + rl * p.n + (colok ? c0 : 0));
+        }
+        // the round's loads all go out first; the step's reciprocal is
+        // taken after round 0's, so the wait for the step overlaps them
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (QUANT) {
+            if (rd == 0) mul = __fdiv_rn(1.0f, s_read);
         }
 #pragma unroll
         for (int u = 0; u < kRows; ++u) {

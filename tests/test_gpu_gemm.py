@@ -244,6 +244,7 @@ def test_epilogue_rounding_ties(lib, orc, lay, M):
 #   big:  >= 256 tiles of 256 x 256
 #   wide: fewer, but >= 256 tiles of 128 x 256 (n >= m)
 #   tall: fewer of 256 x 256, >= 256 tiles of 256 x 128 (m > n)
+#   mid:  fewer than 256 tiles of each of those, m > 64 (128 x 128 tiles)
 TILE_SHAPES = {
     ("big", "NT"): [(4096, 4096, 256), (4100, 4120, 272)],
     ("big", "NN"): [(4096, 4096, 256), (4100, 4112, 272)],
@@ -257,6 +258,10 @@ TILE_SHAPES = {
     ("tall", "NN"): [(4096, 2048, 256), (4100, 2064, 272)],
     ("tall", "TN"): [(4096, 2048, 256), (4112, 2064, 272)],
     ("tall", "TT"): [(4096, 2048, 256), (4112, 2056, 272)],
+    ("mid", "NT"): [(1024, 1024, 256), (1036, 1032, 272)],
+    ("mid", "NN"): [(1024, 1024, 256), (1036, 1040, 272)],
+    ("mid", "TN"): [(1024, 1024, 256), (1040, 1040, 272)],
+    ("mid", "TT"): [(1024, 1024, 256), (1040, 1032, 272)],
 }
 
 
@@ -275,9 +280,12 @@ def test_tile_configs_full_compare(lib, orc, fmt, cfg, lay, ragged):
         assert big
     elif cfg == "wide":
         assert not big and _tiles(M, N, 128, 256) >= 256 and N >= M
-    else:
+    elif cfg == "tall":
         assert not big and _tiles(M, N, 256, 128) >= 256 and M > N
-    seed = 900 + 10 * ta + 20 * tb + int(ragged) + 100 * ["big", "wide", "tall"].index(cfg)
+    else:
+        assert (not big and _tiles(M, N, 128, 256) < 256 and _tiles(M, N, 256, 128) < 256
+                and M > 64)
+    seed = 900 + 10 * ta + 20 * tb + int(ragged) + 100 * ["big", "wide", "tall", "mid"].index(cfg)
     a8, sa = prequant(orc, wl.normal_bf16((M, K), 1.0, seed), fmt)
     b8, sb = prequant(orc, wl.normal_bf16((K, N), 1.0, seed + 1), fmt)
     bias = wl.normal_bf16((N,), 0.1, seed + 2) if lay == "NT" else None

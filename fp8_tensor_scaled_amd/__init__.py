@@ -520,6 +520,16 @@ def fp8_linear_fwd(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x: Ring | Non
     _buf(out, "out", M * N, _BYTE2, nullable=False)
     _buf(x8_bwd, "x8_bwd", M * K, _BYTE1)
     _buf(w8_bwd, "w8_bwd", N * K, _BYTE1)
+    _linear_fwd_call(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x, ring_w, workspace,
+                     scales_out, out, stream, fmt_bwd, x8_bwd, w8_bwd)
+
+
+def _linear_fwd_call(x, w, bias, M, N, K, fmt, dynamic, margin, ring_x, ring_w, workspace,
+                     scales_out, out, stream, fmt_bwd, x8_bwd, w8_bwd) -> None:
+    """fp8_linear_fwd's call itself, for callers whose buffers are sized and
+    typed for (M, N, K) by construction (the autograd layer allocates them
+    from the operands' own shapes): no per-buffer checks beyond the device
+    one."""
     st = _lib.fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, fmt, int(dynamic), margin,
                              _ring_ref(ring_x), _ring_ref(ring_w), _ptr(workspace),
                              _ws_bytes(workspace, "workspace"), _ptr(scales_out), _ptr(out),
@@ -547,6 +557,13 @@ def fp8_linear_bwd(g, x, w, M, N, K, fmt, dynamic, margin, scales_fwd, ring_g: R
     _buf(db, "db", N, _BYTE2)
     _buf(x8_bwd, "x8_bwd", M * K, _BYTE1)
     _buf(w8_bwd, "w8_bwd", N * K, _BYTE1)
+    _linear_bwd_call(g, x, w, M, N, K, fmt, dynamic, margin, scales_fwd, ring_g, workspace,
+                     scales_out, dx, dw, db, stream, x8_bwd, w8_bwd)
+
+
+def _linear_bwd_call(g, x, w, M, N, K, fmt, dynamic, margin, scales_fwd, ring_g, workspace,
+                     scales_out, dx, dw, db, stream, x8_bwd, w8_bwd) -> None:
+    """fp8_linear_bwd's call itself (see _linear_fwd_call)."""
     st = _lib.fp8_linear_bwd(_ptr(g), _ptr(x), _ptr(w), M, N, K, fmt, int(dynamic), margin,
                              _ptr(scales_fwd), _ring_ref(ring_g), _ptr(workspace),
                              _ws_bytes(workspace, "workspace"), _ptr(scales_out), _ptr(dx),

@@ -42,11 +42,13 @@ from __future__ import annotations
 import contextvars
 import dataclasses
 import enum
+import functools
 import weakref
 
 import torch
 
-from . import (E4M3, E5M2, OUT_BF16, Ring, _stream, fp8_colsum, fp8_colsum_workspace,
+from . import (E4M3, E5M2, OUT_BF16, Ring, _linear_bwd_call, _linear_fwd_call, _stream,
+               fp8_colsum, fp8_colsum_workspace,
                fp8_linear_bwd, fp8_linear_bwd_workspace, fp8_linear_bwd_workspace_codes,
                fp8_linear_fwd, fp8_linear_fwd_workspace, fp8_mm,
                fp8_mm_ex, fp8_quantize, fp8_quantize_colsum)
@@ -187,6 +189,14 @@ class fp8_autocast:
 _WS: dict = {}
 
 
+@functools.lru_cache(maxsize=256)
+def _ws_sizes(M: int, N: int, K: int) -> tuple:
+    """(forward, backward, backward given the forward's codes) workspace
+    bytes of a linear call shape."""
+    return (fp8_linear_fwd_workspace(M, N, K), fp8_linear_bwd_workspace(M, N, K),
+            fp8_linear_bwd_workspace_codes(M, N, K))
+
+
 def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
     key = (dev.index, _stream().value)  # the stream the library call will use
     ws = _WS.get(key)
@@ -237,10 +247,11 @@ class _LinearFp8(torch.autograd.Function):
         bias16 = None if bias is None else bias.view(torch.int16)
         if recipe.dynamic:
             ctx.meta = None
-            fp8_linear_fwd(x2.view(torch.int16), w.view(torch.int16), bias16, M, N, K, fmt, True,
-                           recipe.margin, None, None,
-                           _workspace(dev, fp8_linear_fwd_workspace(M, N, K)), scales,
-                           out.view(torch.int16))
+            # buffers sized from the operands here, so the unchecked call
+            _linear_fwd_call(x2.view(torch.int16), w.view(torch.int16), bias16, M, N, K, fmt,
+                             True, recipe.margin, None, None,
+                             _workspace(dev, _ws_sizes(M, N, K)[0]), scales,
+                             out.view(torch.int16), None, E5M2, None, None)
             ctx.save_for_backward(x2, w, scales)
             return out.reshape(*x.shape[:-1], N)
         meta = ctx.meta = _STATE.get_weight_meta(w, recipe)
@@ -256,9 +267,9 @@ class _LinearFp8(torch.autograd.Function):
             # wanted; it seeds, folds and advances the rings
             x8b = torch.empty(M * K, dtype=torch.uint8, device=dev) if need_w else None
             w8b = torch.empty(N * K, dtype=torch.uint8, device=dev) if need_x else None
-            fp8_linear_fwd(xi, wi, bias16, M, N, K, fmt, False, m, meta.x, meta.w,
-                           _workspace(dev, fp8_linear_fwd_workspace(M, N, K)), scales,
-                           out.view(torch.int16), fmt_bwd=ctx.fmt_bwd, x8_bwd=x8b, w8_bwd=w8b)
+            _linear_fwd_call(xi, wi, bias16, M, N, K, fmt, False, m, meta.x, meta.w,
+                             _workspace(dev, _ws_sizes(M, N, K)[0]), scales,
+                             out.view(torch.int16), None, ctx.fmt_bwd, x8b, w8b)
             ctx.save_for_backward(x8b, w8b, scales)
             return out.reshape(*x.shape[:-1], N)
         # one format both ways: the forward's codes are the backward's
@@ -294,18 +305,18 @@ class _LinearFp8(torch.autograd.Function):
         fmt, m = ctx.fmt_bwd, ctx.recipe.margin
         if ctx.meta is None:
             x2, w, scales = ctx.saved_tensors
-            fp8_linear_bwd(i16(g2), i16(x2), i16(w), M, N, K, fmt, True, m, scales, None,
-                           _workspace(dev, fp8_linear_bwd_workspace(M, N, K)), None, i16(dx),
-                           i16(dw), i16(db))
+            _linear_bwd_call(i16(g2), i16(x2), i16(w), M, N, K, fmt, True, m, scales, None,
+                             _workspace(dev, _ws_sizes(M, N, K)[1]), None, i16(dx), i16(dw),
+                             i16(db), None, None, None)
         else:
             # the forward kept x8b when dW is wanted and w8b when dX is; the
             # call seeds, uses and advances the g ring
             x8b, w8b, scales = ctx.saved_tensors
-            fp8_linear_bwd(i16(g2), None, None, M, N, K, fmt, False, m, scales, ctx.meta.g,
-                           _workspace(dev, fp8_linear_bwd_workspace_codes(M, N, K)), None,
-                           i16(dx), i16(dw), i16(db),
-                           x8_bwd=x8b if dw is not None else None,
-                           w8_bwd=w8b if dx is not None else None)
+            _linear_bwd_call(i16(g2), None, None, M, N, K, fmt, False, m, scales, ctx.meta.g,
+                             _workspace(dev, _ws_sizes(M, N, K)[2]), None,
+                             i16(dx), i16(dw), i16(db), None,
+                             x8b if dw is not None else None,
+                             w8b if dx is not None else None)
         return (None if dx is None else dx.reshape(ctx.x_shape), dw, db, None, None)
 
 
@@ -402,6 +413,12 @@ def fp8_linear(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = Non
     bias may be fp8 codes [N] of the same format with their step
     ``b_scale`` ([LOG1] bias_scale), dequantized in the GEMM's epilogue."""
     cfg = current_config()
+    if w.dim() != 2 or x.dim() < 1 or x.shape[-1] != w.shape[1]:
+        raise ValueError(f"fp8_linear: input of shape {tuple(x.shape)} and weight of shape "
+                         f"{tuple(w.shape)} do not match")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != w.shape[0]):
+        raise ValueError(f"fp8_linear: bias of shape {tuple(bias.shape)} for {w.shape[0]} "
+                         "outputs")
     bias8 = bias is not None and bias.dtype in _FP8_DTYPES
     if bias8 and (w.dtype not in _FP8_DTYPES or b_scale is None):
         raise ValueError("fp8_linear: an fp8 bias needs fp8 weight codes and b_scale")

@@ -85,6 +85,18 @@ def test_enabled_path_checks_dtypes():
             fa.fp8_linear(torch.randn(2, 8).bfloat16(), torch.zeros(4, 8).to(torch.float8_e4m3fn))
 
 
+def test_enabled_path_checks_shapes():
+    """The shapes are checked before anything reaches the library: the
+    input's last dimension against the weight's, the bias against the
+    weight's outputs."""
+    with fa.fp8_autocast():
+        with pytest.raises(ValueError, match="do not match"):
+            fa.fp8_linear(torch.randn(2, 6).bfloat16(), torch.randn(4, 8).bfloat16())
+        with pytest.raises(ValueError, match="bias of shape"):
+            fa.fp8_linear(torch.randn(2, 8).bfloat16(), torch.randn(4, 8).bfloat16(),
+                          torch.randn(3).bfloat16())
+
+
 def test_weight_meta_lifetime():
     st = fa.fp8_state()
     st.reset()

@@ -838,7 +838,7 @@ struct TileShape {
     static constexpr int kThreads = WM * WN * 64;
     static constexpr int kLds = tiled_lds_bytes<BM, BN, BK, ST>();
 };
-using ShapeBig64 = TileShape<256, 256, 2, 4, 64, 4>;  // 256 x 256, 64-k stages
+using ShapeBig = TileShape<256, 256, 2, 4, 128, 2>;
 using ShapeWide = TileShape<128, 256, 2, 4, 128, 3>;
 using ShapeTall = TileShape<256, 128, 4, 2, 128, 3>;
 using ShapeMid = TileShape<128, 128, 4, 2, 128, 4>;
@@ -972,15 +972,15 @@ static TileCfg tile_cfg(const GemmLaunch& g) {
 
 template <int FMT, bool AMN, bool BMN>
 static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
-    // Both operands k-contiguous: 256 x 256 tiles take 128-byte stages
-    // (every row segment a whole line), double-buffered.  Otherwise 64-byte
-    // stages, four deep: the m/n-contiguous operand reads whole lines anyway
-    // and the deeper ring hides more latency.
-    constexpr bool kBoth = !AMN && !BMN;
+    // 256 x 256 tiles take 128-k stages, double-buffered, in every layout:
+    // a k-contiguous row segment is then a whole 128-byte line, and for NN /
+    // TN they measured as fast as four 64-k stages refilled in pairs alone
+    // (54.5 / 53.0 against 54.6 / 53.5 us at 4096^3) and 2.5 us faster in
+    // the backward pair (103.4 against 106.1 us).  The 64-k stage code
+    // (kSubs == 1, refills in pairs) is kept for configurations that want a
+    // deeper ring of smaller stages; none of the shipped ones does.
     switch (tile_cfg(g)) {
-        case kBig:
-            if constexpr (kBoth) return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
-            else return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 64, 4>(g, stream);
+        case kBig: return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
         case kWide: return launch_cfg<FMT, AMN, BMN, 128, 256, 2, 4, 128, 3>(g, stream);
         case kTall: return launch_cfg<FMT, AMN, BMN, 256, 128, 4, 2, 128, 3>(g, stream);
         case kMid: return launch_cfg<FMT, AMN, BMN, 128, 128, 4, 2, 128, 4>(g, stream);
@@ -1084,7 +1084,7 @@ static hipError_t launch_pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1,
 hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
                                   hipStream_t stream, const ColsumFinalJob* cf) {
     const PairCfg c = pair_cfg(g0, g1);
-    if (c.c0 == kBig) return launch_pair_cfg<ShapeBig64, ShapeBig64>(g0, g1, stream, cf);
+    if (c.c0 == kBig) return launch_pair_cfg<ShapeBig, ShapeBig>(g0, g1, stream, cf);
     if (c.c0 == kMid && c.c1 == kTall) return launch_pair_cfg<ShapeMid, ShapeTall>(g0, g1, stream, cf);
     if (c.c0 == kMid && c.c1 == kWide) return launch_pair_cfg<ShapeMid, ShapeWide>(g0, g1, stream, cf);
     if (c.c0 == kTall) return launch_pair_cfg<ShapeTall, ShapeMid>(g0, g1, stream, cf);

@@ -53,7 +53,10 @@ hipError_t launch_quantize_two(const QuantLaunch& q0, const QuantLaunch& q1, hip
 // Dynamic (current-amax) quantize of up to two small bf16 tensors in one
 // launch, one workgroup each: measure max |x|, derive the step, cast.  The
 // codes and steps equal those of a measure-only pass into a length-1 ring
-// followed by the cast with its step.  For numel <= kSmallDynamicNumel.
+// followed by the cast with its step.  For numel <= kSmallDynamicNumel: the
+// dynamic forward at M = N = K = n took 7.8 / 11.7 / 26.0 us this way against
+// 17.2 / 18.5 / 19.4 us through the general path's launches at 2^14 / 2^16 /
+// 2^18 elements per tensor, so the paths cross near 2^17.
 constexpr int64_t kSmallDynamicNumel = int64_t(1) << 17;
 struct SmallDynamicJob {
     const uint16_t* x = nullptr;

@@ -2,7 +2,7 @@
 // library's interface; built into libfp8bench.so, which only bench.py
 // loads).  They move the same bytes as the library's bandwidth-bound kernels
 // with no arithmetic, so their rates are the practical ceilings those kernels
-// are judged against on this GPU:
+// are measured against on this GPU:
 //   * fp8bench_empty: a launch that does nothing (the per-launch floor);
 //   * fp8bench_read: every byte of a buffer read once, 256 workgroups each
 //     streaming a contiguous slab (the short-A GEMM's weight stream);

@@ -1,4 +1,4 @@
-"""Python driver of the CPU oracle of the FP8 linear layer.
+"""Python side of the CPU oracle of the FP8 linear layer.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
 CPU-baseline leg of the benchmark may import this module.  It shares no code

@@ -13,8 +13,10 @@ bool gemm_tiled_supported(const GemmLaunch& g);
 hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream);
 
 // Two independent problems in one launch: problem 0 NN and problem 1 TN,
-// same format, together filling the CUs (256 x 256 tiles when each has at
-// least 256 of them, else 128 x 128 tiles, at least 256 between the two).
+// same format, together filling the CUs: 256 x 256 tiles when each has at
+// least 256 of them; else 128 x 128 tiles, the problem with about half the
+// other's k taking 256 x 128 or 128 x 256 ones, at least 256 between the
+// two.
 bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1);
 // Whether the paired launch of a supported pair can also run `cf` (extra
 // workgroups at the end of its grid).

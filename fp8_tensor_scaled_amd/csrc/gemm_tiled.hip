@@ -842,6 +842,7 @@ using ShapeBig = TileShape<256, 256, 2, 4, 128, 2>;
 using ShapeWide = TileShape<128, 256, 2, 4, 128, 3>;
 using ShapeTall = TileShape<256, 128, 4, 2, 128, 3>;
 using ShapeMid = TileShape<128, 128, 4, 2, 128, 4>;
+using ShapeMidNN = TileShape<128, 128, 2, 4, 128, 4>;  // the NN problem (dX) on 128 x 128
 
 template <int FMT, class S0, class S1>
 __global__ __launch_bounds__(S0::kThreads, 1) void gemm_tiled_pair_kernel(TiledParams p0,
@@ -953,12 +954,18 @@ static int64_t tiles_of(const GemmLaunch& g, int bm, int bn) {
 //   kBig    256 x 256, 8 waves of 128 x 64       at >= 256 tiles of 256 x 256
 //   kWide   128 x 256, 8 waves of  64 x 64       at >= 256 tiles of 128 x 256
 //   kTall   256 x 128, 8 waves of  64 x 64       at >= 256 tiles of 256 x 128
-//   kMid    128 x 128, 8 waves of  32 x 64       otherwise
+//   kMid    128 x 128, 8 waves of  32 x 64       otherwise (NN: 64 x 32)
 //   kSmall   64 x  64, 4 waves of  32 x 32       m <= 64 below 256 tiles of 128 x 128
 // (2048 x 4096 x 1024 NT: 13.9 wide against 18.8 for 4-wave 128 x 128 tiles;
 // 2048 x 1024 x 4096 NN: 16.8 mid against 21.6; 4096 x 1024 x 2048 TN: 12.1
-// mid against 14.9.)  All configurations sum every output's k range in the
-// same order, so the choice never changes a result bit.
+// mid against 14.9.)  For NN, B is n-contiguous and goes through the
+// transposing LDS read (about 180 B/clk per CU against 250 for ds_read_b128),
+// so kMid arranges its waves 2 x 4 there: each B fragment is read by two
+// waves instead of four (per 64-k substep 16 KB of transposing reads and
+// 32 KB of plain ones, instead of 32 and 16); 2048 x 1024 x 4096 NN 16.37 against 16.50, 1024 x 1024 x 8192 NN
+// 27.5 against 27.9, the training step's paired dX + dW 19.54 against
+// 19.74.  All configurations sum every output's k range in the same order,
+// so the choice never changes a result bit.
 enum TileCfg { kBig, kWide, kTall, kMid, kSmall };
 
 static TileCfg tile_cfg(const GemmLaunch& g) {
@@ -983,7 +990,9 @@ static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
         case kBig: return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
         case kWide: return launch_cfg<FMT, AMN, BMN, 128, 256, 2, 4, 128, 3>(g, stream);
         case kTall: return launch_cfg<FMT, AMN, BMN, 256, 128, 4, 2, 128, 3>(g, stream);
-        case kMid: return launch_cfg<FMT, AMN, BMN, 128, 128, 4, 2, 128, 4>(g, stream);
+        case kMid:
+            if constexpr (!AMN && BMN) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 4, 128, 4>(g, stream);
+            else return launch_cfg<FMT, AMN, BMN, 128, 128, 4, 2, 128, 4>(g, stream);
         case kSmall: break;
     }
     return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 128, 4>(g, stream);
@@ -1085,11 +1094,11 @@ hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
                                   hipStream_t stream, const ColsumFinalJob* cf) {
     const PairCfg c = pair_cfg(g0, g1);
     if (c.c0 == kBig) return launch_pair_cfg<ShapeBig, ShapeBig>(g0, g1, stream, cf);
-    if (c.c0 == kMid && c.c1 == kTall) return launch_pair_cfg<ShapeMid, ShapeTall>(g0, g1, stream, cf);
-    if (c.c0 == kMid && c.c1 == kWide) return launch_pair_cfg<ShapeMid, ShapeWide>(g0, g1, stream, cf);
+    if (c.c0 == kMid && c.c1 == kTall) return launch_pair_cfg<ShapeMidNN, ShapeTall>(g0, g1, stream, cf);
+    if (c.c0 == kMid && c.c1 == kWide) return launch_pair_cfg<ShapeMidNN, ShapeWide>(g0, g1, stream, cf);
     if (c.c0 == kTall) return launch_pair_cfg<ShapeTall, ShapeMid>(g0, g1, stream, cf);
     if (c.c0 == kWide) return launch_pair_cfg<ShapeWide, ShapeMid>(g0, g1, stream, cf);
-    return launch_pair_cfg<ShapeMid, ShapeMid>(g0, g1, stream, cf);
+    return launch_pair_cfg<ShapeMidNN, ShapeMid>(g0, g1, stream, cf);
 }
 
 }  // namespace fp8lin

@@ -155,7 +155,8 @@ fp8_status_t do_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt
                                 const float* scale, uint8_t* out, float* ring_state,
                                 int32_t len, int32_t idx, int32_t margin, float* scale_used,
                                 uint16_t* db, void* ws, hipStream_t stream,
-                                fp8lin::ColsumFinalJob* defer = nullptr) {
+                                fp8lin::ColsumFinalJob* defer = nullptr,
+                                fp8lin::FoldJob* fold = nullptr) {
     fp8lin::QuantLaunch q;
     q.x = g;
     q.numel = m * n;
@@ -167,6 +168,10 @@ fp8_status_t do_quantize_colsum(const uint16_t* g, int64_t m, int64_t n, fp8_fmt
     q.ring_idx = idx;
     q.pow2_margin = pow2f(margin);
     q.scale_used = scale_used;
+    if (fold && ring_state) {  // the ring's fold held back for a later launch
+        q.defer_fold = true;
+        fp8lin::fold_job_add(*fold, q);
+    }
     hipError_t e = fp8lin::launch_quantize_colsum(q, m, n, db, ws, stream, defer);
     if (e != hipSuccess) return hip_fail(e, "quantize + colsum launch");
     return FP8_OK;
@@ -198,22 +203,24 @@ fp8lin::GemmLaunch gemm_of(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, in
 fp8_status_t do_gemm(const uint8_t* a, const uint8_t* b, fp8_fmt_t fmt, int ta, int tb,
                      int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb,
                      const float* sa, const float* sb, const uint16_t* bias, uint16_t* out,
-                     hipStream_t stream) {
+                     hipStream_t stream, fp8lin::FoldJob* fold = nullptr) {
     hipError_t e = fp8lin::launch_gemm(
-        gemm_of(a, b, fmt, ta, tb, m, n, k, lda, ldb, sa, sb, bias, out), stream);
+        gemm_of(a, b, fmt, ta, tb, m, n, k, lda, ldb, sa, sb, bias, out), stream, fold);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return FP8_OK;
 }
 
-fp8_status_t do_gemm_launch(const fp8lin::GemmLaunch& g, hipStream_t stream) {
-    hipError_t e = fp8lin::launch_gemm(g, stream);
+fp8_status_t do_gemm_launch(const fp8lin::GemmLaunch& g, hipStream_t stream,
+                            fp8lin::FoldJob* fold = nullptr) {
+    hipError_t e = fp8lin::launch_gemm(g, stream, fold);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return FP8_OK;
 }
 
 fp8_status_t do_gemm_pair(const fp8lin::GemmLaunch& g0, const fp8lin::GemmLaunch& g1,
-                          hipStream_t stream, const fp8lin::ColsumFinalJob* cf = nullptr) {
-    hipError_t e = fp8lin::launch_gemm_pair(g0, g1, stream, cf);
+                          hipStream_t stream, const fp8lin::ColsumFinalJob* cf = nullptr,
+                          fp8lin::FoldJob* fold = nullptr) {
+    hipError_t e = fp8lin::launch_gemm_pair(g0, g1, stream, cf, fold);
     if (e != hipSuccess) return hip_fail(e, "gemm pair launch");
     return FP8_OK;
 }
@@ -656,6 +663,7 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
     uint8_t* w8 = ws + L.w8;
     float* sx = scales_out;
     float* sw = scales_out + 1;
+    fp8lin::FoldJob fold;  // delayed: the rings' folds, held back for the GEMM's launch
     if (dynamic) {
         // Current-amax scaling: measure into a length-1 scratch ring, then
         // quantize with the scale it published.
@@ -699,16 +707,22 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
             ring_x->initialized = 1;
         }
         // Each quantize reads the ring's published step (its snapshot goes
-        // to scales_out) before its own last workgroup folds the new amax.
+        // to scales_out) and takes its amax into the ring's group lines; the
+        // fold of both rings is held back and runs as the GEMM launch's
+        // last workgroup (the GEMM reads the snapshots, not the rings), so
+        // no chain of dependent atomics ends the quantize.
         // With x8_bwd / w8_bwd the same pass also writes the backward's
         // codes: the same scaled values in fmt_bwd.
         // x and w go in one launch when both or neither write backward codes.
-        const fp8lin::QuantLaunch qx =
+        fp8lin::QuantLaunch qx =
             make_quant(x, M * K, fmt, ring_x->state + ring_x->len, x8, ring_x->state,
                        ring_x->len, ring_x->idx, margin, sx, x8_bwd, x8_bwd ? (int)fmt_bwd : -1);
-        const fp8lin::QuantLaunch qw =
+        fp8lin::QuantLaunch qw =
             make_quant(w, N * K, fmt, ring_w->state + ring_w->len, w8, ring_w->state,
                        ring_w->len, ring_w->idx, margin, sw, w8_bwd, w8_bwd ? (int)fmt_bwd : -1);
+        qx.defer_fold = qw.defer_fold = true;
+        fp8lin::fold_job_add(fold, qx);
+        fp8lin::fold_job_add(fold, qw);
         if (fp8lin::quantize_two_supported(qx, qw)) {
             hipError_t e = fp8lin::launch_quantize_two(qx, qw, stream);
             if (e != hipSuccess) return hip_fail(e, "quantize launch");
@@ -718,7 +732,8 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
             if (e != hipSuccess) return hip_fail(e, "quantize launch");
         }
     }
-    if ((st = do_gemm(x8, w8, fmt, 0, 1, M, N, K, K, K, sx, sw, bias, out, stream))) return st;
+    if ((st = do_gemm(x8, w8, fmt, 0, 1, M, N, K, K, K, sx, sw, bias, out, stream, &fold)))
+        return st;
     if (!dynamic) {
         ring_x->idx = (ring_x->idx + 1) % ring_x->len;
         ring_w->idx = (ring_w->idx + 1) % ring_w->len;
@@ -784,6 +799,7 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     const float* sx;
     const float* sw;
     bool xw_cast = false;  // x8 / w8 already made (small dynamic path)
+    fp8lin::FoldJob fold;  // delayed: g's ring fold, held back for the GEMM's launch
     if (dynamic) {
         float* rg = scratch_ring(workspace, 0);
         float* rx = scratch_ring(workspace, 1);
@@ -843,15 +859,21 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
                 return st;
             ring_g->initialized = 1;
         }
+        // g's amax goes into its ring's group lines; the fold runs as the
+        // GEMM launch's last workgroup (or a launch of its own)
         if (db) {
             if ((st = do_quantize_colsum(g, M, N, fmt, ring_g->state + ring_g->len, g8,
                                          ring_g->state, ring_g->len, ring_g->idx, margin, sg, db,
-                                         ws + L.colsum, stream, defer)))
+                                         ws + L.colsum, stream, defer, &fold)))
                 return st;
-        } else if ((st = do_quantize(g, M * N, fmt, ring_g->state + ring_g->len, g8,
-                                     ring_g->state, ring_g->len, ring_g->idx, margin, sg,
-                                     stream))) {
-            return st;
+        } else {
+            fp8lin::QuantLaunch q = make_quant(g, M * N, fmt, ring_g->state + ring_g->len, g8,
+                                               ring_g->state, ring_g->len, ring_g->idx, margin,
+                                               sg);
+            q.defer_fold = true;
+            fp8lin::fold_job_add(fold, q);
+            hipError_t e = fp8lin::launch_quantize(q, stream);
+            if (e != hipSuccess) return hip_fail(e, "quantize launch");
         }
         sx = scales_fwd;
         sw = scales_fwd + 1;
@@ -878,11 +900,15 @@ fp8_status_t fp8_linear_bwd(const uint16_t* g, const uint16_t* x, const uint16_t
     const fp8lin::GemmLaunch gdx = gemm_of(g8, w8u, fmt, 0, 0, M, K, N, N, K, sg, sw, nullptr, dx);
     const fp8lin::GemmLaunch gdw = gemm_of(g8, x8u, fmt, 1, 0, N, K, M, N, K, sg, sx, nullptr, dw);
     if (dx && dw) {
-        if ((st = do_gemm_pair(gdx, gdw, stream, &cf))) return st;
+        if ((st = do_gemm_pair(gdx, gdw, stream, &cf, &fold))) return st;
     } else if (dx) {
-        if ((st = do_gemm_launch(gdx, stream))) return st;
+        if ((st = do_gemm_launch(gdx, stream, &fold))) return st;
     } else if (dw) {
-        if ((st = do_gemm_launch(gdw, stream))) return st;
+        if ((st = do_gemm_launch(gdw, stream, &fold))) return st;
+    }
+    if (fold.n > 0) {  // no GEMM carried it (only the bias gradient wanted)
+        hipError_t e = fp8lin::launch_fold_job(fold, stream);
+        if (e != hipSuccess) return hip_fail(e, "fold launch");
     }
     if (!dynamic) ring_g->idx = (ring_g->idx + 1) % ring_g->len;
     return FP8_OK;

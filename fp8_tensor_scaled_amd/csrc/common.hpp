@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.hpp"
+
 namespace fp8lin {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -104,6 +106,44 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
+}
+
+// A held-back ring fold (one wave; every lane calls it).  The new amax is
+// the largest of the group lines' maxima, taken by atomics of an earlier
+// launch (non-negative floats order as their bits); hist[idx] = amax; the
+// step max(peak / fmax / 2^margin, 1e-12) from the window's peak, with the
+// quantize's own fold's two IEEE divisions; the lines back to zero for the
+// next launch.
+__device__ __forceinline__ void fold_ring_lines(const RingFold& f) {
+    // the lane from the hardware's lane count, not from threadIdx: a GEMM
+    // kernel that carries the fold must not keep a value shared with its
+    // tile code alive across the tile loop
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    float* hist = f.state;
+    uint32_t* lines = reinterpret_cast<uint32_t*>(f.state + ring_groups_offset(f.len));
+    uint32_t m = 0;
+    if (lane < kRingGroups)
+        m = __hip_atomic_load(lines + kRingGroupWords * lane, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    float w = 0.0f;
+    for (int i = lane; i < f.len; i += kWave)
+        if (i != f.idx) w = fmaxf(w, hist[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = __shfl_xor(m, off, kWave);
+        m = o > m ? o : m;
+    }
+    const float amax = __uint_as_float(m);
+    const float peak = fmaxf(wave_max(w), amax);
+    if (lane < kRingGroups)
+        __hip_atomic_store(lines + kRingGroupWords * lane, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+        hist[f.idx] = amax;
+        const float t = __fdiv_rn(peak, f.fmax);
+        const float s = __fdiv_rn(t, f.pow2_margin);
+        hist[f.len] = fmaxf(s, 1e-12f);
+    }
 }
 
 // Bias gradient, last pass: db[c] = bf16 of the sum over chunks k of the

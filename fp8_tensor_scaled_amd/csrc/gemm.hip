@@ -126,19 +126,39 @@ static hipError_t launch_generic(const GemmLaunch& g, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream) {
-    if (gemm_skinny_supported(g)) return launch_gemm_skinny(g, stream);
-    if (gemm_tiled_supported(g)) return launch_gemm_tiled(g, stream);
-    return launch_generic(g, stream);
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream, FoldJob* fold) {
+    const FoldJob none;
+    const FoldJob& fj = fold ? *fold : none;
+    hipError_t e;
+    if (gemm_skinny_supported(g)) {
+        e = launch_gemm_skinny(g, stream);
+    } else if (fj.n > 0 && gemm_tiled_carries_fold(g)) {
+        e = launch_gemm_tiled(g, stream, fj);  // the fold rides along
+        if (e == hipSuccess) fold->n = 0;
+        return e;
+    } else if (gemm_tiled_supported(g)) {
+        e = launch_gemm_tiled(g, stream);
+    } else {
+        e = launch_generic(g, stream);
+    }
+    if (e != hipSuccess || fj.n <= 0) return e;
+    e = launch_fold_job(fj, stream);
+    if (e == hipSuccess) fold->n = 0;
+    return e;
 }
 
 hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream,
-                            const ColsumFinalJob* cf) {
+                            const ColsumFinalJob* cf, FoldJob* fold) {
     const bool job = cf && cf->db;
     if (!gemm_skinny_supported(g0) && !gemm_skinny_supported(g1) &&
-        gemm_tiled_pair_supported(g0, g1) && (!job || gemm_tiled_pair_carries(g0, g1, *cf)))
-        return launch_gemm_tiled_pair(g0, g1, stream, job ? cf : nullptr);
-    hipError_t e = launch_gemm(g0, stream);
+        gemm_tiled_pair_supported(g0, g1) && (!job || gemm_tiled_pair_carries(g0, g1, *cf))) {
+        const FoldJob none;
+        hipError_t e = launch_gemm_tiled_pair(g0, g1, stream, job ? cf : nullptr,
+                                              fold ? *fold : none);
+        if (e == hipSuccess && fold) fold->n = 0;
+        return e;
+    }
+    hipError_t e = launch_gemm(g0, stream, fold);
     if (e != hipSuccess) return e;
     e = launch_gemm(g1, stream);
     if (e != hipSuccess || !job) return e;

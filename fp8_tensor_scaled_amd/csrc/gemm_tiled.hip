@@ -353,6 +353,14 @@ constexpr int tiled_lds_bytes() {
     return STAGES * (BM + BN) * BK;
 }
 
+// A held-back fold carried by a GEMM launch: waves 0 and 1 of its extra
+// workgroup fold one ring each.
+__device__ __forceinline__ void fold_waves(const FoldJob& fold) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+    if (wave == 0) fold_ring_lines(fold.r[0]);
+    else if (wave == 1 && fold.n > 1) fold_ring_lines(fold.r[1]);
+}
+
 // One output tile: workgroup `bid` of a grid of G workgroups over problem p,
 // with `smem` the workgroup's LDS ring of tiled_lds_bytes<...>() bytes.
 // Four bias values of columns gn .. gn+3 (zero past n) for the extended
@@ -811,11 +819,26 @@ __device__ __forceinline__ void gemm_tile(const TiledParams& p, int bid, const i
     }
 }
 
+// FOLD: the grid's last workgroup runs a held-back ring fold instead of a
+// tile.  Only the plain NT kernels that the linear forward launches are
+// built with it; every other kernel is the same code with or without the
+// job argument (a branch ahead of the tile code costs the 256 x 256 tiles a
+// register at their limit).
 template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int STAGES,
-          bool EXT>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p) {
+          bool EXT, bool FOLD>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams p, FoldJob fold) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[tiled_lds_bytes<BM, BN, BK, STAGES>()];
-    gemm_tile<FMT, AMN, BMN, BM, BN, WM, WN, BK, STAGES, EXT>(p, blockIdx.x, gridDim.x, smem);
+    if constexpr (FOLD) {
+        // (this form of the test keeps the 256 x 256 tiles free of spills)
+        const int tiles = (int)gridDim.x - 1;
+        if ((int)blockIdx.x == tiles) {  // the last workgroup, dispatched after
+            fold_waves(fold);            // every tile: the held-back fold(s)
+            return;
+        }
+        gemm_tile<FMT, AMN, BMN, BM, BN, WM, WN, BK, STAGES, EXT>(p, blockIdx.x, tiles, smem);
+    } else {
+        gemm_tile<FMT, AMN, BMN, BM, BN, WM, WN, BK, STAGES, EXT>(p, blockIdx.x, gridDim.x, smem);
+    }
 }
 
 // Two independent problems in one launch (the linear backward's dX, NN, and
@@ -828,8 +851,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tiled_kernel(TiledParams 
 // the two problems balance over the machine.  Workgroups past n0 + n1 run
 // the bias gradient's last pass (`cf`, a quarter of the workgroup's lanes in
 // columns each): the highest ids are dispatched last, so they take CUs as
-// the last tiles finish, in place of a launch of their own.  Stream order
-// makes the partials (written by an earlier launch) visible to them.
+// the first tiles finish, in place of a launch of their own.  A held-back
+// ring fold (`fold`) takes one more workgroup, id fold_at, ahead of the
+// tiles and workgroups after it.  Stream order makes the partials and the
+// group lines (written by earlier launches) visible to them.
 // A tile configuration as a type: BM x BN tile, WM x WN waves, BK k per
 // stage, ST stages.
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_>
@@ -848,13 +873,19 @@ template <int FMT, class S0, class S1>
 __global__ __launch_bounds__(S0::kThreads, 1) void gemm_tiled_pair_kernel(TiledParams p0,
                                                                           TiledParams p1, int n0,
                                                                           int n1,
-                                                                          ColsumFinalJob cf) {
+                                                                          ColsumFinalJob cf,
+                                                                          FoldJob fold,
+                                                                          int fold_at) {
     static_assert(S0::kThreads == S1::kThreads, "one workgroup size");
     constexpr int T = S0::kThreads;
     constexpr int kLds = S0::kLds > S1::kLds ? S0::kLds : S1::kLds;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
     static_assert(kLds >= T * 4, "column-sum scratch fits");
-    const int b = blockIdx.x;
+    if (fold.n > 0 && (int)blockIdx.x == fold_at) {
+        fold_waves(fold);
+        return;
+    }
+    const int b = (int)blockIdx.x - (fold.n > 0 && (int)blockIdx.x > fold_at ? 1 : 0);
     if (b < n0)
         gemm_tile<FMT, false, true, S0::BM, S0::BN, S0::WM, S0::WN, S0::BK, S0::ST>(p0, b, n0,
                                                                                   smem);
@@ -929,16 +960,31 @@ static TiledParams tiled_params(const GemmLaunch& g) {
 }
 
 template <int FMT, bool AMN, bool BMN, int BM, int BN, int WM, int WN, int BK, int ST>
-static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream) {
+static hipError_t launch_cfg(const GemmLaunch& g, hipStream_t stream, const FoldJob& fold) {
     const TiledParams p = tiled_params<BM, BN>(g);
     const int64_t total = (int64_t)p.tiles_per_batch * g.batch;
+    const dim3 block(WM * WN * 64);
+    if constexpr (!AMN && !BMN) {  // NT: the linear forward's GEMM may carry a fold
+        if (fold.n > 0) {
+            if (g.ext()) return hipErrorInvalidValue;  // callers check gemm_tiled_carries_fold
+            hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, false, true>),
+                               dim3((unsigned)(total + 1)), block, 0, stream, p, fold);
+            return hipGetLastError();
+        }
+    } else {
+        if (fold.n > 0) return hipErrorInvalidValue;
+    }
     if (g.ext())
-        hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, true>),
-                           dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
+        hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, true, false>),
+                           dim3((unsigned)total), block, 0, stream, p, fold);
     else
-        hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, false>),
-                           dim3((unsigned)total), dim3(WM * WN * 64), 0, stream, p);
+        hipLaunchKernelGGL((gemm_tiled_kernel<FMT, AMN, BMN, BM, BN, WM, WN, BK, ST, false, false>),
+                           dim3((unsigned)total), block, 0, stream, p, fold);
     return hipGetLastError();
+}
+
+bool gemm_tiled_carries_fold(const GemmLaunch& g) {
+    return gemm_tiled_supported(g) && g.trans_a == 0 && g.trans_b != 0 && !g.ext();
 }
 
 static int64_t tiles_of(const GemmLaunch& g, int bm, int bn) {
@@ -978,7 +1024,7 @@ static TileCfg tile_cfg(const GemmLaunch& g) {
 }
 
 template <int FMT, bool AMN, bool BMN>
-static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
+static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream, const FoldJob& fold) {
     // 256 x 256 tiles take 128-k stages, double-buffered, in every layout:
     // a k-contiguous row segment is then a whole 128-byte line, and for NN /
     // TN they measured as fast as four 64-k stages refilled in pairs alone
@@ -987,28 +1033,28 @@ static hipError_t launch_layout(const GemmLaunch& g, hipStream_t stream) {
     // (kSubs == 1, refills in pairs) is kept for configurations that want a
     // deeper ring of smaller stages; none of the shipped ones does.
     switch (tile_cfg(g)) {
-        case kBig: return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream);
-        case kWide: return launch_cfg<FMT, AMN, BMN, 128, 256, 2, 4, 128, 3>(g, stream);
-        case kTall: return launch_cfg<FMT, AMN, BMN, 256, 128, 4, 2, 128, 3>(g, stream);
+        case kBig: return launch_cfg<FMT, AMN, BMN, 256, 256, 2, 4, 128, 2>(g, stream, fold);
+        case kWide: return launch_cfg<FMT, AMN, BMN, 128, 256, 2, 4, 128, 3>(g, stream, fold);
+        case kTall: return launch_cfg<FMT, AMN, BMN, 256, 128, 4, 2, 128, 3>(g, stream, fold);
         case kMid:
-            if constexpr (!AMN && BMN) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 4, 128, 4>(g, stream);
-            else return launch_cfg<FMT, AMN, BMN, 128, 128, 4, 2, 128, 4>(g, stream);
+            if constexpr (!AMN && BMN) return launch_cfg<FMT, AMN, BMN, 128, 128, 2, 4, 128, 4>(g, stream, fold);
+            else return launch_cfg<FMT, AMN, BMN, 128, 128, 4, 2, 128, 4>(g, stream, fold);
         case kSmall: break;
     }
-    return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 128, 4>(g, stream);
+    return launch_cfg<FMT, AMN, BMN, 64, 64, 2, 2, 128, 4>(g, stream, fold);
 }
 
 template <int FMT>
-static hipError_t launch_fmt(const GemmLaunch& g, hipStream_t stream) {
+static hipError_t launch_fmt(const GemmLaunch& g, hipStream_t stream, const FoldJob& fold) {
     const bool a_mn = g.trans_a != 0, b_mn = g.trans_b == 0;
-    if (!a_mn && !b_mn) return launch_layout<FMT, false, false>(g, stream);
-    if (!a_mn && b_mn) return launch_layout<FMT, false, true>(g, stream);
-    if (a_mn && !b_mn) return launch_layout<FMT, true, false>(g, stream);
-    return launch_layout<FMT, true, true>(g, stream);
+    if (!a_mn && !b_mn) return launch_layout<FMT, false, false>(g, stream, fold);
+    if (!a_mn && b_mn) return launch_layout<FMT, false, true>(g, stream, fold);
+    if (a_mn && !b_mn) return launch_layout<FMT, true, false>(g, stream, fold);
+    return launch_layout<FMT, true, true>(g, stream, fold);
 }
 
-hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream) {
-    return g.fmt == 0 ? launch_fmt<0>(g, stream) : launch_fmt<1>(g, stream);
+hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream, const FoldJob& fold) {
+    return g.fmt == 0 ? launch_fmt<0>(g, stream, fold) : launch_fmt<1>(g, stream, fold);
 }
 
 // Paired configurations.  Both problems on 256 x 256 tiles when each fills
@@ -1066,7 +1112,8 @@ bool gemm_tiled_pair_carries(const GemmLaunch& g0, const GemmLaunch& g1,
 
 template <class S0, class S1>
 static hipError_t launch_pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1,
-                                  hipStream_t stream, const ColsumFinalJob* cf) {
+                                  hipStream_t stream, const ColsumFinalJob* cf,
+                                  const FoldJob& fold) {
     TiledParams p0 = tiled_params<S0::BM, S0::BN>(g0);
     TiledParams p1 = tiled_params<S1::BM, S1::BN>(g1);
     const int n0 = (int)tiles_of(g0, S0::BM, S0::BN), n1 = (int)tiles_of(g1, S1::BM, S1::BN);
@@ -1079,26 +1126,32 @@ static hipError_t launch_pair_cfg(const GemmLaunch& g0, const GemmLaunch& g1,
         job = *cf;
         extra = (int)((cf->n + kCols - 1) / kCols);
     }
-    const dim3 grid((unsigned)(n0 + n1 + extra));
+    // A held-back fold goes to the first CU that frees up: right after
+    // problem 0's tiles when those alone fill the 256 CUs (the CU that
+    // folds then takes one of problem 1's tiles a moment later, while others
+    // still run problem 0), else right after all the tiles.
+    const int fold_at = n0 >= 256 ? n0 : n0 + n1;
+    const dim3 grid((unsigned)(n0 + n1 + extra + (fold.n > 0 ? 1 : 0)));
     const dim3 block(S0::kThreads);
     if (g0.fmt == 0)
         hipLaunchKernelGGL((gemm_tiled_pair_kernel<0, S0, S1>), grid, block, 0, stream, p0, p1, n0,
-                           n1, job);
+                           n1, job, fold, fold_at);
     else
         hipLaunchKernelGGL((gemm_tiled_pair_kernel<1, S0, S1>), grid, block, 0, stream, p0, p1, n0,
-                           n1, job);
+                           n1, job, fold, fold_at);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1,
-                                  hipStream_t stream, const ColsumFinalJob* cf) {
+                                  hipStream_t stream, const ColsumFinalJob* cf,
+                                  const FoldJob& fold) {
     const PairCfg c = pair_cfg(g0, g1);
-    if (c.c0 == kBig) return launch_pair_cfg<ShapeBig, ShapeBig>(g0, g1, stream, cf);
-    if (c.c0 == kMid && c.c1 == kTall) return launch_pair_cfg<ShapeMidNN, ShapeTall>(g0, g1, stream, cf);
-    if (c.c0 == kMid && c.c1 == kWide) return launch_pair_cfg<ShapeMidNN, ShapeWide>(g0, g1, stream, cf);
-    if (c.c0 == kTall) return launch_pair_cfg<ShapeTall, ShapeMid>(g0, g1, stream, cf);
-    if (c.c0 == kWide) return launch_pair_cfg<ShapeWide, ShapeMid>(g0, g1, stream, cf);
-    return launch_pair_cfg<ShapeMidNN, ShapeMid>(g0, g1, stream, cf);
+    if (c.c0 == kBig) return launch_pair_cfg<ShapeBig, ShapeBig>(g0, g1, stream, cf, fold);
+    if (c.c0 == kMid && c.c1 == kTall) return launch_pair_cfg<ShapeMidNN, ShapeTall>(g0, g1, stream, cf, fold);
+    if (c.c0 == kMid && c.c1 == kWide) return launch_pair_cfg<ShapeMidNN, ShapeWide>(g0, g1, stream, cf, fold);
+    if (c.c0 == kTall) return launch_pair_cfg<ShapeTall, ShapeMid>(g0, g1, stream, cf, fold);
+    if (c.c0 == kWide) return launch_pair_cfg<ShapeWide, ShapeMid>(g0, g1, stream, cf, fold);
+    return launch_pair_cfg<ShapeMidNN, ShapeMid>(g0, g1, stream, cf, fold);
 }
 
 }  // namespace fp8lin

@@ -10,7 +10,11 @@ namespace fp8lin {
 // k-contiguous operand; m (n) a multiple of 16 for an m- (n-) contiguous
 // A (B).  Everything else runs on the general kernel.
 bool gemm_tiled_supported(const GemmLaunch& g);
-hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream);
+// A held-back ring fold (fold.n > 0) runs as one extra workgroup at the end
+// of the grid; only plain NT problems take one (gemm_tiled_carries_fold).
+bool gemm_tiled_carries_fold(const GemmLaunch& g);
+hipError_t launch_gemm_tiled(const GemmLaunch& g, hipStream_t stream,
+                             const FoldJob& fold = FoldJob{});
 
 // Two independent problems in one launch: problem 0 NN and problem 1 TN,
 // same format, together filling the CUs: 256 x 256 tiles when each has at
@@ -23,6 +27,7 @@ bool gemm_tiled_pair_supported(const GemmLaunch& g0, const GemmLaunch& g1);
 bool gemm_tiled_pair_carries(const GemmLaunch& g0, const GemmLaunch& g1,
                              const ColsumFinalJob& cf);
 hipError_t launch_gemm_tiled_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream,
-                                  const ColsumFinalJob* cf = nullptr);
+                                  const ColsumFinalJob* cf = nullptr,
+                                  const FoldJob& fold = FoldJob{});
 
 }  // namespace fp8lin

@@ -41,8 +41,33 @@ struct QuantLaunch {
     // the cast): ordinary loads.  Otherwise 2-byte inputs are loaded
     // non-temporally, which skips the MALL for data read once.
     bool cached_input = false;
+    // With a ring: hold the fold back (FoldJob below); the kernel then
+    // writes the step snapshot to scale_used itself.  Not with amax_out.
+    bool defer_fold = false;
 };
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream);
+
+// A ring fold held back from quantize launches made with defer_fold: their
+// workgroups only take the atomic max of their |x| maxima into the ring's
+// group lines (no counters, no dependent round trips), and the fold --
+// hist[idx] = the largest line, the next step from the window's peak, the
+// lines back to zero -- runs later in stream order: as one extra workgroup
+// of the GEMM launch that follows (which reads the step snapshot, never the
+// ring), or as a launch of its own.  It leaves the ring state the
+// quantize's own fold leaves, bit for bit.
+struct RingFold {
+    float* state = nullptr;  // ring state words (layout above)
+    int32_t len = 0, idx = 0;
+    float fmax = 448.0f;
+    float pow2_margin = 1.0f;
+};
+struct FoldJob {
+    RingFold r[2];
+    int n = 0;  // rings held, 0..2
+};
+// Appends q's ring (q.ring_state set) to j.
+void fold_job_add(FoldJob& j, const QuantLaunch& q);
+hipError_t launch_fold_job(const FoldJob& j, hipStream_t stream);
 
 // Two bf16 quantizes with codes (same format, same second format or none, no
 // amax_out) in one launch, each with its own fold; results are those of two
@@ -98,7 +123,10 @@ struct GemmLaunch {
     // Needs the extended epilogue (fp8 bias or fp8 output).
     bool ext() const { return bias_scale != nullptr || out_q >= 0; }
 };
-hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
+// A held-back fold (nullable; consumed: n is 0 on success) rides along as
+// an extra workgroup of the tiled kernels' launch, or runs as a launch of
+// its own after the GEMM.
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream, FoldJob* fold = nullptr);
 
 // The bias gradient's last pass (chunk partials -> bf16 db) as a job that
 // another launch can carry; db == nullptr: no job.
@@ -114,9 +142,9 @@ hipError_t launch_colsum_final_job(const ColsumFinalJob& j, hipStream_t stream);
 // form (the linear backward's NN dX and TN dW), else launch_gemm twice in
 // order.  Results are bit-identical to the two separate launches.  A job
 // `cf` (nullable) rides along as extra workgroups of the paired launch, or
-// runs as its own launch after the two.
+// runs as its own launch after the two; a held-back fold as launch_gemm.
 hipError_t launch_gemm_pair(const GemmLaunch& g0, const GemmLaunch& g1, hipStream_t stream,
-                            const ColsumFinalJob* cf = nullptr);
+                            const ColsumFinalJob* cf = nullptr, FoldJob* fold = nullptr);
 
 // Column sum (bias gradient).
 size_t colsum_workspace(int64_t m, int64_t n);

@@ -75,8 +75,9 @@ struct QuantParams {
     float* scale_used;
     float* amax_out;  // optional max |x| output: written by the fold, or (no
                       // ring) an atomic max over workgroups after an arming launch
-    int vec;  // 1: x and out are 16-byte aligned
-    int nt;   // 1: non-temporal input loads (vector path, 2-byte inputs)
+    int vec;    // 1: x and out are 16-byte aligned
+    int nt;     // 1: non-temporal input loads (vector path, 2-byte inputs)
+    int defer;  // 1: with a ring, only the group lines' maxima (held-back fold)
 };
 
 // Last-workgroup fold (one wave): hist[idx] = amax;
@@ -115,8 +116,10 @@ __device__ __forceinline__ void fold_ring(const QuantParams& p, float s_read, fl
 // each, measured), so 16 x 16 contenders cost far less than 256 on one
 // word.  Returns, at thread PUB, nblocks - 1 if this workgroup drew the last
 // top-level ticket (it folds), else ~0u.  The whole chain runs before the
-// caller's last stores, which go out while it is in flight.  Every thread
-// of the workgroup must call it once.
+// caller's last stores, which go out while it is in flight.  With p.defer
+// (a held-back fold) the workgroup only takes the max into line b % 16 and
+// returns ~0u: nothing waits on it.  Every thread of the workgroup must
+// call it once.
 template <int T = kQuantThreads, int PUB = 0>
 __device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, uint32_t nblocks,
                                                  uint32_t b) {
@@ -130,6 +133,12 @@ __device__ __forceinline__ uint32_t publish_amax(const QuantParams& p, float v, 
         v = slots[0];
 #pragma unroll
         for (int w = 1; w < kW; ++w) v = fmaxf(v, slots[w]);
+        if (p.defer) {
+            __hip_atomic_fetch_max(p.groups + kRingGroupWords * (b % kRingGroups),
+                                   __float_as_uint(v), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            return ticket;
+        }
         const uint32_t ng = nblocks < kRingGroups ? nblocks : kRingGroups;
         const uint32_t g = b % ng;
         const uint32_t members = (nblocks - g + ng - 1) / ng;
@@ -309,9 +318,9 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
         // that no data wave waits for them before its stores.
         if (p.hist) {
             const int wl = t - kQT;
-            const float win = (wl < p.len && wl != p.idx) ? p.hist[wl] : 0.0f;
+            const float win = (!p.defer && wl < p.len && wl != p.idx) ? p.hist[wl] : 0.0f;
             const uint32_t tk = publish_amax<kQT + kWave, kQT>(p, 0.0f, nb, b);
-            finish_fold<kQT>(p, tk, s_read, win, nb);
+            finish_fold<kQT>(p, tk, s_read, win, nb);  // no ticket when deferred
         } else if (p.amax_out) {
             publish_amax_out<kQT + kWave, kQT>(p, 0.0f);
         }
@@ -416,12 +425,12 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
         }
         if (p.hist) publish_amax<kQT + kWave, kQT>(p, amax, nb, b);
     }
-    if (!p.hist) {
+    if (!p.hist || p.defer) {
         if constexpr (!MEASURE_ONLY) {
             if (p.scale_used && b == 0 && t == 0) *p.scale_used = s_read;
         }
-        if (p.amax_out) publish_amax_out<kQT + kWave, kQT>(p, amax);
     }
+    if (!p.hist && p.amax_out) publish_amax_out<kQT + kWave, kQT>(p, amax);
 }
 
 template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
@@ -497,6 +506,7 @@ static QuantParams quant_params(const QuantLaunch& q) {
     p.scale_used = q.scale_used;
     p.amax_out = q.amax_out;
     p.nt = q.cached_input ? 0 : 1;
+    p.defer = q.defer_fold && q.ring_state ? 1 : 0;
     const uintptr_t al = reinterpret_cast<uintptr_t>(q.x) | reinterpret_cast<uintptr_t>(q.out) |
                          reinterpret_cast<uintptr_t>(q.out2);
     p.vec = (al & 15) == 0;
@@ -641,6 +651,29 @@ __global__ __launch_bounds__(kWave) void ring_finalize_kernel(float* state, int3
     }
 }
 
+// A held-back fold as a launch of its own: one workgroup, a wave per ring.
+__global__ __launch_bounds__(2 * kWave) void fold_job_kernel(FoldJob j) {
+    const int wave = threadIdx.x / kWave;
+    if (wave == 0) fold_ring_lines(j.r[0]);
+    else if (j.n > 1) fold_ring_lines(j.r[1]);
+}
+
+void fold_job_add(FoldJob& j, const QuantLaunch& q) {
+    if (j.n >= 2 || !q.ring_state) return;
+    RingFold& r = j.r[j.n++];
+    r.state = q.ring_state;
+    r.len = q.ring_len;
+    r.idx = q.ring_idx;
+    r.fmax = q.fmt ? 57344.0f : 448.0f;
+    r.pow2_margin = q.pow2_margin;
+}
+
+hipError_t launch_fold_job(const FoldJob& j, hipStream_t stream) {
+    if (j.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fold_job_kernel, dim3(1), dim3(2 * kWave), 0, stream, j);
+    return hipGetLastError();
+}
+
 hipError_t launch_ring_finalize(float* state, int32_t len, int32_t idx, int fmt,
                                 float pow2_margin, const float* amax, hipStream_t stream) {
     hipLaunchKernelGGL(ring_finalize_kernel, dim3(1), dim3(kWave), 0, stream, state, len, idx,
@@ -704,7 +737,8 @@ __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p)
     float mul = 0.0f, s_read = 0.0f;
     if constexpr (QUANT) s_read = *p.q.scale;
     const int wl = threadIdx.x;
-    const float win = (QUANT && p.q.hist && wl < p.q.len && wl < kWave && wl != p.q.idx)
+    const float win = (QUANT && p.q.hist && !p.q.defer && wl < p.q.len && wl < kWave &&
+                       wl != p.q.idx)
                           ? p.q.hist[wl] : 0.0f;
     const int cg = threadIdx.x % 32;   // column group
     const int ph = threadIdx.x / 32;   // row phase
@@ -793,7 +827,7 @@ __global__ __launch_bounds__(kQCThreads) void quantize_colsum_kernel(QCParams p)
         }
     }
     if constexpr (QUANT) {
-        if (p.q.hist) {
+        if (p.q.hist && !p.q.defer) {
             finish_fold(p.q, ticket, s_read, win, gridDim.x * gridDim.y);
         } else if (p.q.scale_used && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
             *p.q.scale_used = s_read;
@@ -898,6 +932,7 @@ hipError_t launch_quantize_colsum(const QuantLaunch& q, int64_t m, int64_t n, ui
     p.q.fmax = q.fmt ? 57344.0f : 448.0f;
     p.q.pow2_margin = q.pow2_margin;
     p.q.scale_used = q.scale_used;
+    p.q.defer = q.defer_fold && q.ring_state ? 1 : 0;
     p.g = gx;
     p.m = m;
     p.n = n;
@@ -1020,6 +1055,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_t_kernel(QTParams p) {
 
 hipError_t launch_quantize_t(const QuantLaunch& q, int64_t rows, int64_t cols, uint8_t* out_t,
                              hipStream_t stream) {
+    if (q.defer_fold) return hipErrorInvalidValue;  // folds itself only
     QTParams p{};
     p.q.x = q.x;
     p.q.numel = rows * cols;

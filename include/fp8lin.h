@@ -69,7 +69,9 @@ typedef enum {
  *        uint32 bits) that every fold leaves at zero again;
  * pad, groups: more kernel scratch, also left at zero by every fold: from
  *        the first 128-byte boundary after `done`, 16 lines of 32 words
- *        (the first level of the quantize kernels' amax reduction).
+ *        (the first level of the quantize kernels' amax reduction; the
+ *        linear calls' quantizes leave their maxima there for the fold
+ *        that their GEMM launch runs).
  * Only the first len + 4 words have a meaning for callers.
  * The caller zero-fills `state` once when the ring is created.
  * `len`, `idx`, `initialized` live on the host: `idx` is the slot the next
@@ -376,9 +378,12 @@ fp8_status_t fp8_quantize_colsum_noalloc(const uint16_t* g, int64_t m, int64_t n
  *     ring_x / ring_w are ignored (may be NULL).
  * dynamic == 0 (delayed): ring_x and ring_w (host pointers, required) are
  *     seeded from the current tensors when not initialized; the scale in
- *     each ring is snapshotted by the quantize that reads it, the quantize
- *     folds the current amax and publishes the next scale, the GEMM
- *     dequantizes with the snapshots, and both rings advance.
+ *     each ring is snapshotted by the quantize that reads it, the GEMM
+ *     dequantizes with the snapshots, the current amax is folded and the
+ *     next scale published (by one extra workgroup of the GEMM's launch,
+ *     or a small launch after it: the quantize only gathers the amax), and
+ *     both rings advance.  When the call's work has run, each ring holds
+ *     what a quantize with its own fold would have left.
  * workspace: device scratch of fp8_linear_fwd_workspace(M, N, K) bytes,
  *     256-byte aligned; its first fp8_linear_fwd_x8_offset(M, N, K) bytes
  *     (6656, whatever the shape) are control slots (scratch rings for the
@@ -422,8 +427,9 @@ fp8_status_t fp8_linear_fwd(const uint16_t* x, const uint16_t* w, const uint16_t
  * quantized in `fmt` (the backward format, E5M2 under HYBRID).
  *
  * dynamic == 0 (delayed): sg is ring_g's scale (seeded from g when not
- *     initialized), snapshotted while the g quantize folds amax(g) and
- *     publishes the next scale; ring_g advances.  sx, sw are the forward's
+ *     initialized), snapshotted by the g quantize; amax(g) is folded and
+ *     the next scale published within the call (by an extra workgroup of
+ *     the GEMM launch, or a small launch of its own); ring_g advances.  sx, sw are the forward's
  *     steps, scales_fwd = [sx, sw] (device fp32 [2], required).
  * dynamic != 0: sg, sx, sw are measured now from g, x, w in `fmt`;
  *     scales_fwd and ring_g are ignored.

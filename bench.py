@@ -487,7 +487,7 @@ def components(f, torch):
     res.update(backward_routes(f, torch))
     # the same layer step through the autograd layer (FP8Linear under
     # fp8_autocast, delayed HYBRID): what the policy layer costs over the
-    # step's own launch sequence
+    # step's own launch sequence (the C-ABI step timed in turn with it)
     res.update(autograd_layer(f, torch))
     res.update(ceilings(torch))
     # torch's copy of 1 GiB (read + write, 2 GiB moved), for comparison
@@ -666,7 +666,24 @@ def autograd_layer(f, torch, n=4096):
         with fa.fp8_autocast(fp8_format=fa.FP8Format.HYBRID):
             layer(x).backward(g)
 
-    ms = time_kernel(torch, lambda i: step(), 20)
+    # steady state first: the first steps seed the rings, allocate the
+    # layer's workspace and size torch's allocator cache for the step's
+    # tensors (in a process that has cached the components' buffers)
+    for _ in range(30):
+        step()
+    # the C-ABI step of the same size, timed in turn with it (same clock
+    # state: this runs after the long component bursts)
+    ref = Layer(f, torch, n, seed0=900)
+    ref.seed(f)
+    for _ in range(30):
+        ref.step(f)
+    t_ag, t_ref = [], []
+    for _ in range(3):
+        t_ag.append(time_kernel(torch, lambda i: step(), 20))
+        t_ref.append(time_kernel(torch, lambda i: ref.step(f), 20))
+    ms = float(np.median(t_ag))
+    ms_ref = float(np.median(t_ref))
+    del ref
     # host time per step (Python, autograd, launches): the median over 20
     # steps, each timed on its own (a stray garbage collection or allocator
     # call then moves one sample, not the figure), the GPU kept busy by
@@ -688,7 +705,7 @@ def autograd_layer(f, torch, n=4096):
     torch.cuda.synchronize()
     return {"autograd_fp8linear_step_4096": dict(
         us=round(ms * 1e3, 2), tflops=round(3 * 2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1),
-        host_us=round(host_us, 1))}
+        c_abi_step_us=round(ms_ref * 1e3, 2), host_us=round(host_us, 1))}
 
 
 def cpu_baseline(size, rows=1024):

@@ -190,6 +190,59 @@ def test_backward_masks_and_dynamic_small(lib, orc, dynamic):
             assert ring_state_equal(rg, og)
 
 
+@pytest.mark.parametrize("M,N,K", [(48, 256, 128), (80, 96, 40), (300, 136, 272)])
+def test_delayed_steps_on_every_gemm_kernel(lib, orc, M, N, K):
+    """Delayed scaling over three steps (the input rescaled each step, so
+    every fold changes the window) on shapes whose forward GEMM takes each
+    kernel family: short-A (M <= 64), the general kernel (K not a multiple
+    of 16) and the tiled one with ragged tiles.  The linear calls gather
+    each ring's amax in their quantize and fold it in a later launch (an
+    extra workgroup of the tiled forward GEMM or of the paired backward,
+    else a launch of its own): every step's steps, rings, codes and
+    outputs against the oracle."""
+    x0 = wl.normal_bf16((M, K), 1.0, 41)
+    w = wl.normal_bf16((N, K), 0.02, 42)
+    bias = wl.normal_bf16((N,), 0.1, 43)
+    f = Fwd(lib, M, N, K)
+    bws = torch.zeros(lib.fp8_linear_bwd_workspace(M, N, K), dtype=torch.uint8, device="cuda")
+    rx, rw, rg = lib.Ring(16), lib.Ring(16), lib.Ring(16)
+    ox, ow, og = orc.Ring(16), orc.Ring(16), orc.Ring(16)
+    dx = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    dw = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    db = torch.empty(N, dtype=torch.int16, device="cuda")
+    sb = torch.zeros(3, dtype=torch.float32, device="cuda")
+    wd, bd = to_dev_bf16(w), to_dev_bf16(bias)
+    for t, s in enumerate((1.0, 8.0, 0.125)):
+        x = wl.scaled_bf16(x0, s)
+        g = wl.normal_bf16((M, N), 1e-3 * (t + 1), 44 + t)
+        xd, gd = to_dev_bf16(x), to_dev_bf16(g)
+        lib.fp8_linear_fwd(xd, wd, bd, M, N, K, E4M3, False, 0, rx, rw, f.ws, f.scales, f.out)
+        lib.fp8_linear_bwd(gd, xd, wd, M, N, K, E5M2, False, 0, f.scales, rg, bws, sb, dx, dw,
+                           db)
+        torch.cuda.synchronize()
+        rf = orc.linear_fwd(x, w, bias, M, N, K, E4M3, False, ox, ow)
+        rb = orc.linear_bwd(g, x, w, M, N, K, E5M2, False, rf.sx, rf.sw, og)
+        sc = f.scales.cpu().numpy()
+        assert (sc[0], sc[1]) == (rf.sx, rf.sw), t
+        sbh = sb.cpu().numpy()
+        assert (sbh[0], sbh[1], sbh[2]) == (rb.sg, rb.sx, rb.sw), t
+        for gr, orr in ((rx, ox), (rw, ow), (rg, og)):
+            assert ring_state_equal(gr, orr), t
+            assert gr.idx == orr.idx
+        assert np.array_equal(f.x8(), rf.x8.ravel()), t
+        assert np.array_equal(f.w8(), rf.w8.ravel()), t
+        bound = orc.gemm_bound(rf.x8, rf.w8, E4M3, False, True, M, N, K, rf.sx, rf.sw)
+        check_gemm(from_dev_bf16(f.out).reshape(M, N), rf.out, bound, f"fwd {t}")
+        w8b = orc.quantize(w, E5M2, rb.sw)
+        x8b = orc.quantize(x, E5M2, rb.sx)
+        ad = orc.gemm_bound(rb.g8, w8b, E5M2, False, False, M, K, N, rb.sg, rb.sw)
+        check_gemm(from_dev_bf16(dx).reshape(M, K), rb.dx, ad, f"dx {t}")
+        ad = orc.gemm_bound(rb.g8, x8b, E5M2, True, False, N, K, M, rb.sg, rb.sx)
+        check_gemm(from_dev_bf16(dw).reshape(N, K), rb.dw, ad, f"dw {t}")
+        absg = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64)).sum(0)
+        check_gemm(from_dev_bf16(db), rb.db, sum_bound(absg, M), f"db {t}")
+
+
 def test_linear_invalid_arguments(lib):
     M, N, K = 32, 32, 32
     ws = torch.zeros(16, dtype=torch.uint8, device="cuda")

@@ -516,7 +516,7 @@ def ceilings(torch):
     P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.fp8bench_empty.argtypes = [I, I, P]
     lib.fp8bench_read.argtypes = [P, I64, P, I, I, P]
-    lib.fp8bench_stream21.argtypes = [P, I64, P, I, P]
+    lib.fp8bench_stream21.argtypes = [P, I64, P, I, I, P]
     for fn in (lib.fp8bench_empty, lib.fp8bench_read, lib.fp8bench_stream21):
         fn.restype = I
 
@@ -545,9 +545,13 @@ def ceilings(torch):
         nrot = (1 << 30) // (3 * numel) + 1
         xs = [torch.empty(numel, dtype=torch.int16, device=dev) for _ in range(nrot)]
         qs = [torch.empty(numel, dtype=torch.uint8, device=dev) for _ in range(nrot)]
-        grid = min(512, max(1, (numel + 256 * 16 - 1) // (256 * 16)))  # the quantize's grid
+        # the quantize's launch shape: up to 512 workgroups with 4 chunks per
+        # lane per round, from 2^25 elements up to 1024 with 1
+        large = numel >= (1 << 25)
+        grid = min(1024 if large else 512, max(1, (numel + 256 * 16 - 1) // (256 * 16)))
+        unroll = 1 if large else 4
         ms = time_graph(torch, lambda i: ok(lib.fp8bench_stream21(
-            xs[i % nrot].data_ptr(), numel, qs[i % nrot].data_ptr(), grid, stream())),
+            xs[i % nrot].data_ptr(), numel, qs[i % nrot].data_ptr(), grid, unroll, stream())),
             max(2 * nrot, 8))
         res[name] = dict(us=round(ms * 1e3, 2), gbs=round(3 * numel / (ms * 1e-3) / 1e9, 1),
                          hbm_frac=round(3 * numel / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))

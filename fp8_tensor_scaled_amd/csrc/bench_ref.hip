@@ -9,7 +9,7 @@
 //   * fp8bench_stream21: the quantize's access pattern without the
 //     conversion, the amax or the fold (read 2 bytes, write 1 byte per
 //     element: the high byte of each bf16), in the quantize's launch shape
-//     and chunk order.
+//     (grid, chunks per lane per round) and chunk order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -53,12 +53,13 @@ __device__ __forceinline__ uint32_t hi_bytes(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07050301u);
 }
 
-// The quantize's launch shape and sweep: 256-lane workgroups (at most 512,
-// two per CU), the grid's lanes taking consecutive 16-element chunks in each
-// round, four chunks in flight per lane.
+// The quantize's sweep: 256-lane workgroups, the grid's lanes taking
+// consecutive 16-element chunks in each round, kUnroll chunks in flight per
+// lane (4 below 2^25 elements, 1 from there, with the grid the caller
+// passes).
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 
+template <int kUnroll>
 __global__ __launch_bounds__(kThreads) void stream21_kernel(const uint4* x, int64_t nvec,
                                                            uint4* out) {
     typedef int v4i __attribute__((ext_vector_type(4)));
@@ -117,14 +118,22 @@ int fp8bench_read(const void* b, int64_t bytes, uint32_t* sink, int grid, int no
     return (int)hipGetLastError();
 }
 
-// numel: a multiple of 16; x, out 16-byte aligned.
-int fp8bench_stream21(const uint16_t* x, int64_t numel, uint8_t* out, int grid,
+// numel: a multiple of 16; x, out 16-byte aligned; unroll: 1 or 4 chunks
+// per lane per round.
+int fp8bench_stream21(const uint16_t* x, int64_t numel, uint8_t* out, int grid, int unroll,
                       hipStream_t stream) {
     if (!x || !out || numel < 16 || (numel % 16) || grid < 1 ||
+        (unroll != 1 && unroll != 4) ||
         ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out)) & 15))
         return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(stream21_kernel, dim3(grid), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(x), numel / 16, reinterpret_cast<uint4*>(out));
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    uint4* ov = reinterpret_cast<uint4*>(out);
+    if (unroll == 1)
+        hipLaunchKernelGGL(stream21_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, xv,
+                           numel / 16, ov);
+    else
+        hipLaunchKernelGGL(stream21_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, xv,
+                           numel / 16, ov);
     return (int)hipGetLastError();
 }
 

@@ -17,7 +17,8 @@
 //    the tensor in rounds: in a
 //    round the grid's lanes take consecutive 16-element chunks, each lane
 //    keeping four chunks (four 32-byte loads) in flight and storing 16 codes
-//    per chunk with one 16-byte store.  An input read once is loaded
+//    per chunk with one 16-byte store.  From 2^25 elements, one chunk per
+//    lane per round and up to 1024 workgroups (four per CU).  An input read once is loaded
 //    non-temporally, so it neither displaces lines the next kernel reads
 //    nor, when cold, loses anything; the library's measure-then-cast
 //    sequences and fp32 inputs use ordinary loads.  The codes' stores are
@@ -56,6 +57,13 @@ constexpr int kUnroll = 4;     // slots in flight per lane
 // The streaming quantize: workgroups of 256 lanes, two per CU.
 constexpr int kQT = 256;
 constexpr int kQGridMax = 512;
+// From 2^25 elements: one slot per lane per round and up to 1024
+// workgroups (four per CU), the shape the bare 2:1 stream runs fastest in
+// there (8192^2 with fold 41.0 against 44.1 us; below it the narrower,
+// deeper shape wins: 4096^2 13.9 against 14.0, 2048 x 4096 9.6 against 9.8).
+constexpr int kUnrollLarge = 1;
+constexpr int kQGridMaxLarge = 1024;
+constexpr int64_t kLargeNumel = int64_t(1) << 25;
 
 struct QuantParams {
     const void* x;        // elements of the kernel's input type
@@ -290,7 +298,7 @@ __device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, ui
 // A workgroup is kQT data lanes plus one publisher wave.  Vector path (x,
 // out, out2 16-byte aligned): the grid sweeps the 16-element chunks in
 // rounds; in round rd, slot u, workgroup b's lanes take the kQT consecutive
-// chunks ((rd * kUnroll + u) * nb + b) * kQT + lane, so at any time the
+// chunks ((rd * U + u) * nb + b) * kQT + lane, so at any time the
 // whole grid streams one narrow window of the tensor (measured faster than a
 // contiguous range per workgroup: 37 against 40.6 us for the bare read-2 /
 // write-1 stream at 8192 x 8192).  A round's loads all go out before any of
@@ -305,7 +313,7 @@ __device__ __forceinline__ void encode16(const uint4* r, float m, uint4* dst, ui
 // Scalar path (unaligned bases): grid-stride elements, then the publish.
 // Workgroup b of the nb that process p (the whole grid, or one tensor's
 // share of a two-tensor launch).
-template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
+template <int IN, int FMT, int FMT2, bool MEASURE_ONLY, int U = kUnroll>
 __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32_t b,
                                               const uint32_t nb) {
     constexpr int kL = In<IN>::kLoads;
@@ -346,7 +354,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
         uint4* ov = reinterpret_cast<uint4*>(p.out);
         uint4* ov2 = reinterpret_cast<uint4*>(p.out2);
         const int64_t slot = (int64_t)nb * kQT;   // chunks per slot of a round
-        const int64_t round = slot * kUnroll;     // chunks per round
+        const int64_t round = slot * U;     // chunks per round
         const int64_t nr = (nvec + round - 1) / round;  // uniform
         const int64_t mine = (int64_t)b * kQT + t;
         // An input read once is loaded non-temporally (p.nt): it then skips
@@ -356,11 +364,11 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
         // loads.  Loads are unconditional (a chunk past the end re-reads
         // chunk 0 and is ignored).
         auto sweep = [&](auto nt_tag) __attribute__((always_inline)) {
-            uint4 r[kUnroll][kL];
+            uint4 r[U][kL];
             auto issue = [&](int64_t rd) __attribute__((always_inline)) {
                 const int64_t c0 = rd * round + mine;
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < U; ++u) {
                     const int64_t c = c0 + u * slot;
                     const int64_t cl = c < nvec ? c : 0;
 #pragma unroll
@@ -381,12 +389,12 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
             auto process = [&](int64_t rd) __attribute__((always_inline)) {
                 const int64_t c0 = rd * round + mine;
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
+                for (int u = 0; u < U; ++u)
                     if (c0 + u * slot < nvec) amax = absmax16<IN>(r[u], amax);
                 if (p.hist && rd == nr - 1) publish_amax<kQT + kWave, kQT>(p, amax, nb, b);
                 if constexpr (!MEASURE_ONLY) {
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) {
+                    for (int u = 0; u < U; ++u) {
                         const int64_t c = c0 + u * slot;
                         if (c < nvec) encode16<IN, FMT, FMT2>(r[u], m, ov + c, ov2 + c);
                     }
@@ -433,9 +441,9 @@ __device__ __forceinline__ void quantize_body(const QuantParams& p, const uint32
     if (!p.hist && p.amax_out) publish_amax_out<kQT + kWave, kQT>(p, amax);
 }
 
-template <int IN, int FMT, int FMT2, bool MEASURE_ONLY>
+template <int IN, int FMT, int FMT2, bool MEASURE_ONLY, int U>
 __global__ __launch_bounds__(kQT + kWave) void quantize_kernel(QuantParams p) {
-    quantize_body<IN, FMT, FMT2, MEASURE_ONLY>(p, blockIdx.x, gridDim.x);
+    quantize_body<IN, FMT, FMT2, MEASURE_ONLY, U>(p, blockIdx.x, gridDim.x);
 }
 
 // Two bf16 tensors in one launch (the forward's x and w): workgroups
@@ -451,22 +459,23 @@ __global__ __launch_bounds__(kQT + kWave) void quantize_two_kernel(QuantParams p
         quantize_body<kInBf16, FMT, FMT2, false>(p1, blockIdx.x - nb0, gridDim.x - nb0);
 }
 
-static int quant_grid(int64_t numel, int vec) {
+static int quant_grid(int64_t numel, int vec, bool large = false) {
     const int64_t per_block = (int64_t)kQT * (vec ? kVecElems : 1);
     int64_t blocks = (numel + per_block - 1) / per_block;
-    if (blocks > kQGridMax) blocks = kQGridMax;  // two workgroups per CU
+    const int64_t cap = large ? kQGridMaxLarge : kQGridMax;  // four / two per CU
+    if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     return (int)blocks;
 }
 
-template <int IN>
+template <int IN, int U>
 static void launch_quantize_in(const QuantLaunch& q, const QuantParams& p, dim3 grid,
                                hipStream_t stream) {
     const dim3 block(kQT + kWave);
     const bool measure = q.out == nullptr;
     const int dual = q.out2 ? q.fmt2 : -1;
 #define FP8_Q(F, F2, M) \
-    hipLaunchKernelGGL((quantize_kernel<IN, F, F2, M>), grid, block, 0, stream, p)
+    hipLaunchKernelGGL((quantize_kernel<IN, F, F2, M, U>), grid, block, 0, stream, p)
     if (measure) {
         if (q.fmt == 0) FP8_Q(0, -1, true);
         else FP8_Q(1, -1, true);
@@ -516,12 +525,19 @@ static QuantParams quant_params(const QuantLaunch& q) {
 hipError_t launch_quantize(const QuantLaunch& q, hipStream_t stream) {
     if (q.out2 && q.in_type != kInBf16) return hipErrorInvalidValue;
     const QuantParams p = quant_params(q);
-    const dim3 grid(quant_grid(q.numel, p.vec));
+    const bool large = p.vec && q.numel >= kLargeNumel;
+    const dim3 grid(quant_grid(q.numel, p.vec, large));
     if (q.amax_out && !q.ring_state)
         hipLaunchKernelGGL(arm_amax_kernel, dim3(1), dim3(1), 0, stream, q.amax_out);
-    if (q.in_type == kInF16) launch_quantize_in<kInF16>(q, p, grid, stream);
-    else if (q.in_type == kInF32) launch_quantize_in<kInF32>(q, p, grid, stream);
-    else launch_quantize_in<kInBf16>(q, p, grid, stream);
+    if (large) {
+        if (q.in_type == kInF16) launch_quantize_in<kInF16, kUnrollLarge>(q, p, grid, stream);
+        else if (q.in_type == kInF32) launch_quantize_in<kInF32, kUnrollLarge>(q, p, grid, stream);
+        else launch_quantize_in<kInBf16, kUnrollLarge>(q, p, grid, stream);
+    } else {
+        if (q.in_type == kInF16) launch_quantize_in<kInF16, kUnroll>(q, p, grid, stream);
+        else if (q.in_type == kInF32) launch_quantize_in<kInF32, kUnroll>(q, p, grid, stream);
+        else launch_quantize_in<kInBf16, kUnroll>(q, p, grid, stream);
+    }
     return hipGetLastError();
 }
 

@@ -254,6 +254,43 @@ def test_invalid_arguments_raise(lib):
         lib.fp8_quantize(x, 0, ring=r)
 
 
+def test_quantize_large_tensor_shape(lib, orc):
+    """From 2^25 elements the quantize sweeps in another launch shape (one
+    16-element chunk per lane per round, up to 1024 workgroups).  At
+    2^25 + 40 elements (a ragged tail): a ring seeded by a measure-only
+    pass, then two steps that quantize with the published step while the
+    kernel folds, then the dual-format pass and a max-only pass, all against
+    the oracle bit for bit."""
+    n = (1 << 25) + 40
+    x = wl.normal_bf16((n,), 2.0, 4242)
+    xd = to_dev_bf16(x)
+    ring, oring = lib.Ring(16), orc.Ring(16)
+    fmt = E4M3
+    lib.fp8_quantize(xd, fmt, ring=ring)
+    oring.seed(x, fmt)
+    out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    used = dev_f32(0.0)
+    for t in range(2):
+        lib.fp8_quantize(xd, fmt, scale=ring.scale, out=out, ring=ring, scale_used=used)
+        s_snap = np.float32(oring.scale)
+        oring.fold(orc.amax(x), fmt)
+        torch.cuda.synchronize()
+        assert float(used.cpu()[0]) == s_snap, t
+        assert np.array_equal(from_dev_u8(out), orc.quantize(x, fmt, s_snap)), t
+        assert ring_state_equal(ring, oring), t
+        ring.idx = (ring.idx + 1) % 16
+        oring.advance()
+    s = np.float32(0.0123)
+    q2 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    lib.fp8_quantize2(xd, E4M3, dev_f32(s), out, E5M2, q2)
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lib.fp8_quantize(xd, fmt, amax_out=am)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_u8(out), orc.quantize(x, E4M3, s))
+    assert np.array_equal(from_dev_u8(q2), orc.quantize(x, E5M2, s))
+    assert float(am.cpu()[0]) == orc.amax(x)
+
+
 @pytest.mark.parametrize("fmt,fmt2", [(E4M3, E5M2), (E5M2, E4M3), (E4M3, E4M3)])
 @pytest.mark.parametrize("numel,offset", [(4096 * 1024, 0), (100003, 0), (5000, 1)])
 def test_quantize2_matches_two_single_quantizes(lib, orc, fmt, fmt2, numel, offset):

@@ -448,15 +448,16 @@ __global__ __launch_bounds__(kQT + kWave) void quantize_kernel(QuantParams p) {
 
 // Two bf16 tensors in one launch (the forward's x and w): workgroups
 // [0, nb0) quantize p0, the rest p1, each with its own fold; one launch and
-// one latency chain (first loads, fold, last stores) instead of two.
-template <int FMT, int FMT2>
+// one latency chain (first loads, fold, last stores) instead of two.  U as
+// in quantize_kernel, chosen from the two tensors' total size.
+template <int FMT, int FMT2, int U>
 __global__ __launch_bounds__(kQT + kWave) void quantize_two_kernel(QuantParams p0,
                                                                      QuantParams p1,
                                                                      uint32_t nb0) {
     if (blockIdx.x < nb0)
-        quantize_body<kInBf16, FMT, FMT2, false>(p0, blockIdx.x, nb0);
+        quantize_body<kInBf16, FMT, FMT2, false, U>(p0, blockIdx.x, nb0);
     else
-        quantize_body<kInBf16, FMT, FMT2, false>(p1, blockIdx.x - nb0, gridDim.x - nb0);
+        quantize_body<kInBf16, FMT, FMT2, false, U>(p1, blockIdx.x - nb0, gridDim.x - nb0);
 }
 
 static int quant_grid(int64_t numel, int vec, bool large = false) {
@@ -553,19 +554,31 @@ hipError_t launch_quantize_two(const QuantLaunch& q0, const QuantLaunch& q1,
                                hipStream_t stream) {
     if (!quantize_two_supported(q0, q1)) return hipErrorInvalidValue;
     const QuantParams p0 = quant_params(q0), p1 = quant_params(q1);
+    // From 2^25 elements in all (both tensors aligned for the vector path):
+    // the large-tensor shape of quantize_kernel (one slot per lane per
+    // round, a cap of four workgroups per CU).
+    const bool large = p0.vec && p1.vec && q0.numel + q1.numel >= kLargeNumel;
+    const int64_t cap = large ? kQGridMaxLarge : kQGridMax;
     // Each tensor's own grid, scaled down to the single launch's cap in all,
     // split in proportion to the tensors' sizes.
-    int64_t b0 = quant_grid(q0.numel, p0.vec), b1 = quant_grid(q1.numel, p1.vec);
-    if (b0 + b1 > kQGridMax) {
+    int64_t b0 = quant_grid(q0.numel, p0.vec, large), b1 = quant_grid(q1.numel, p1.vec, large);
+    if (b0 + b1 > cap) {
         const double f0 = (double)q0.numel / ((double)q0.numel + (double)q1.numel);
-        b0 = (int64_t)(kQGridMax * f0 + 0.5);
-        b0 = b0 < 1 ? 1 : (b0 > kQGridMax - 1 ? kQGridMax - 1 : b0);
-        b1 = kQGridMax - b0;
+        b0 = (int64_t)(cap * f0 + 0.5);
+        b0 = b0 < 1 ? 1 : (b0 > cap - 1 ? cap - 1 : b0);
+        b1 = cap - b0;
     }
     const dim3 grid((unsigned)(b0 + b1)), block(kQT + kWave);
     const int dual = q0.out2 ? q0.fmt2 : -1;
-#define FP8_Q2(F, F2) \
-    hipLaunchKernelGGL((quantize_two_kernel<F, F2>), grid, block, 0, stream, p0, p1, (uint32_t)b0)
+#define FP8_Q2(F, F2)                                                                         \
+    do {                                                                                      \
+        if (large)                                                                            \
+            hipLaunchKernelGGL((quantize_two_kernel<F, F2, kUnrollLarge>), grid, block, 0,     \
+                               stream, p0, p1, (uint32_t)b0);                                 \
+        else                                                                                  \
+            hipLaunchKernelGGL((quantize_two_kernel<F, F2, kUnroll>), grid, block, 0, stream,  \
+                               p0, p1, (uint32_t)b0);                                         \
+    } while (0)
     if (q0.fmt == 0) {
         if (dual < 0) FP8_Q2(0, -1);
         else if (dual == 0) FP8_Q2(0, 0);

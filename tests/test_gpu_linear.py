@@ -307,6 +307,53 @@ def test_benchmark_step_4096_vs_oracle(lib, orc):
         check_gemm(from_dev_bf16(L.db), orc.colsum(g, n, n), sum_bound(absg, n), f"step db {t}")
 
 
+def test_delayed_forward_two_tensor_quantize_large_shape(lib, orc):
+    """x [3001, 4200] and w [5003, 4200]: 2^25 elements and more in all, so
+    the forward's one-launch quantize of x and w takes its large-tensor
+    shape (one chunk per lane per round, up to 1024 workgroups split in
+    proportion to the sizes), with ragged tensor ends.  Three delayed steps
+    with the backward's codes written by the same pass: every code array,
+    step and ring bit-exact against the oracle, the output sampled."""
+    M, N, K = 3001, 5003, 4200
+    assert M * K + N * K >= 1 << 25
+    x = wl.normal_bf16((M, K), 1.0, 91)
+    w = wl.normal_bf16((N, K), 0.02, 92)
+    bias = wl.normal_bf16((N,), 0.1, 93)
+    xd, wd, bd = to_dev_bf16(x), to_dev_bf16(w), to_dev_bf16(bias)
+    f = Fwd(lib, M, N, K)
+    rx, rw = lib.Ring(16), lib.Ring(16)
+    ox, ow = orc.Ring(16), orc.Ring(16)
+    lib.fp8_quantize(wd, E4M3, ring=rw)
+    lib.fp8_quantize(xd, E4M3, ring=rx)
+    rx.initialized = rw.initialized = True
+    ow.seed(w, E4M3)
+    ox.seed(x, E4M3)
+    amax_x, amax_w = orc.amax(x), orc.amax(w)
+    x8b = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+    w8b = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+    for t in range(3):
+        lib.fp8_linear_fwd(xd, wd, bd, M, N, K, E4M3, False, 0, rx, rw, f.ws, f.scales, f.out,
+                           fmt_bwd=E5M2, x8_bwd=x8b, w8_bwd=w8b)
+        torch.cuda.synchronize()
+        sx, sw = np.float32(ox.scale), np.float32(ow.scale)
+        x8, w8 = orc.quantize(x, E4M3, sx), orc.quantize(w, E4M3, sw)
+        ox.fold(amax_x, E4M3)
+        ow.fold(amax_w, E4M3)
+        for r in (ox, ow):
+            r.advance()
+        sc = f.scales.cpu().numpy()
+        assert (sc[0], sc[1]) == (sx, sw), t
+        assert np.array_equal(f.x8(), x8.ravel()), t
+        assert np.array_equal(f.w8(), w8.ravel()), t
+        assert np.array_equal(from_dev_u8(x8b), orc.quantize(x, E5M2, sx).ravel()), t
+        assert np.array_equal(from_dev_u8(w8b), orc.quantize(w, E5M2, sw).ravel()), t
+        for gr, orr in ((rx, ox), (rw, ow)):
+            assert ring_state_equal(gr, orr) and gr.idx == orr.idx, t
+        s = _samples(M, N, 2000, 70 + t)
+        ref, ad = orc.gemm_sampled(x8, w8, E4M3, False, True, M, N, K, sx, sw, bias, s)
+        check_gemm(from_dev_bf16(f.out).reshape(M, N)[s[1], s[2]], ref, ad, f"large fwd {t}")
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 640, 384), (96, 1024, 256), (33, 17, 19)])
 def test_dynamic_forward_launch_paths(lib, orc, M, N, K):
     """Dynamic forward with x and w both above the one-launch size (measure

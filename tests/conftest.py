@@ -20,3 +20,15 @@ def orc():
     from oracle import oracle as o
     o._load()
     return o
+
+
+def pytest_terminal_summary(terminalreporter):
+    """GEMM comparisons of the session: how many outputs were checked
+    against the oracle and how many passed only through the fp8 MFMA
+    accumulation bound (never hidden)."""
+    from tests.gpu_util import STATS
+    if STATS["comparisons"]:
+        terminalreporter.write_line(
+            f"GEMM parity: {STATS['comparisons']} comparisons, {STATS['compared']} outputs "
+            f"compared; {STATS['with_outside']} comparisons had outputs outside 1e-2|r|+ulp, "
+            f"{STATS['outside']} outputs in all, each within the accumulation bound")

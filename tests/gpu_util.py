@@ -66,6 +66,12 @@ def sum_bound(absg: np.ndarray, n: int) -> np.ndarray:
     return n * u / (1 - n * u) * np.asarray(absg, np.float64)
 
 
+# Totals over every check_gemm call of a test session (reported at its end by
+# conftest.py): comparisons made, those with outputs outside the primary
+# tolerance, outputs compared, and outputs accepted only through the bound.
+STATS = {"comparisons": 0, "with_outside": 0, "compared": 0, "outside": 0}
+
+
 def check_gemm(y_bits: np.ndarray, r_bits: np.ndarray, bound: np.ndarray | None = None,
                what: str = "", max_frac: float = 2e-3) -> dict:
     """Assert the GEMM tolerance element-wise; `bound` is the oracle's
@@ -79,7 +85,11 @@ def check_gemm(y_bits: np.ndarray, r_bits: np.ndarray, bound: np.ndarray | None 
     tol = 1e-2 * np.abs(r) + bf16_ulp(r)
     bad = ~(err <= tol)
     n_bad = int(bad.sum())
+    STATS["comparisons"] += 1
+    STATS["compared"] += int(y.size)
     if n_bad:
+        STATS["with_outside"] += 1
+        STATS["outside"] += n_bad
         assert bound is not None, (
             f"{what}: {n_bad} elements outside 1e-2|r| + ulp; worst err {err[bad].max()}")
         bound = np.broadcast_to(np.asarray(bound, np.float64), y.shape)

@@ -309,9 +309,9 @@ def test_benchmark_step_4096_vs_oracle(lib, orc):
 
 def test_delayed_forward_two_tensor_quantize_large_shape(lib, orc):
     """x [3001, 4200] and w [5003, 4200]: 2^25 elements and more in all, so
-    the forward's one-launch quantize of x and w takes its large-tensor
-    shape (one chunk per lane per round, up to 1024 workgroups split in
-    proportion to the sizes), with ragged tensor ends.  Three delayed steps
+    the forward's one-launch quantize of x and w (one chunk per lane per
+    round) runs at its grid cap, 1024 workgroups split in proportion to the
+    sizes, several rounds each, with ragged tensor ends.  Three delayed steps
     with the backward's codes written by the same pass: every code array,
     step and ring bit-exact against the oracle, the output sampled."""
     M, N, K = 3001, 5003, 4200

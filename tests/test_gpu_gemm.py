@@ -298,6 +298,43 @@ def test_tile_configs_full_compare(lib, orc, fmt, cfg, lay, ragged):
     print(f"[{what}] outside 1e-2|r|+ulp: {st['outside_rel_tol']} of {st['n']}")
 
 
+# Batched problems on the 256 x 256 tiles (at least 256 of them over the
+# batch), ragged in m, n and k inside every batch slice, every output
+# compared: tiles of one XCD's range then span batch slices (the remapped
+# order at 360 tiles, the plain order at 324), and a stride-0 operand is
+# shared by all of them.
+BATCHED_BIG = [
+    # layout, batch, M, N, K, batch stride of A / B (None: M*K / K*N; 0: broadcast)
+    ("NT", 8, 1040, 2064, 144, None, None),
+    ("NT", 4, 2064, 2080, 144, None, 0),
+    ("NN", 8, 1040, 2064, 144, 0, None),
+]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("lay,batch,M,N,K,stra,strb", BATCHED_BIG,
+                         ids=[f"{c[0]}-b{c[1]}-{c[2]}x{c[3]}x{c[4]}" for c in BATCHED_BIG])
+def test_batched_big_tiles_ragged_full_compare(lib, orc, fmt, lay, batch, M, N, K, stra, strb):
+    ta, tb = dict(zip(["NT", "NN", "TN", "TT"], LAYOUTS))[lay]
+    assert _tiles(M, N, 256, 256) * batch >= 256
+    seed = 1500 + 7 * batch + fmt
+    ash = (M, K) if stra == 0 else (batch, M, K)
+    bsh = (K, N) if strb == 0 else (batch, K, N)
+    a8, sa = prequant(orc, wl.normal_bf16(ash, 1.0, seed), fmt)
+    b8, sb = prequant(orc, wl.normal_bf16(bsh, 1.0, seed + 1), fmt)
+    bias = wl.normal_bf16((N,), 0.1, seed + 2) if lay == "NT" else None
+    A, B = storage(a8, ta), storage(b8, tb)
+    sta = M * K if stra is None else stra
+    stb = K * N if strb is None else strb
+    got = run_mm(lib, A, B, fmt, ta, tb, M, N, K, sa, sb, bias, batch=batch, stride_a=sta,
+                 stride_b=stb)
+    ref = orc.gemm(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, batch=batch,
+                   stride_a=sta, stride_b=stb)
+    bound = orc.gemm_bound(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, batch=batch,
+                           stride_a=sta, stride_b=stb)
+    check_gemm(got, ref, bound, f"batched big {lay} b{batch} {M}x{N}x{K} f{fmt} {sta} {stb}")
+
+
 def test_config_smallm(lib, orc):
     d = wl.smallm()
     full_size_case(lib, orc, d["x"], d["w"], E4M3, 64, 8192, 2048)

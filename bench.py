@@ -61,7 +61,7 @@ def parse():
 
 KERNELS = ("gemm_nt_4096", "gemm_nn_4096", "gemm_tn_4096", "gemm_bwd_pair_4096",
            "gemm_nt_64x8192x2048", "gemm_nt_8192", "gemm_nt_4096x4096x256", "quantize_8192x8192",
-           "copy_192MB")
+           "gemm_nt_2048x4096x1024", "gemm_bwd_pair_2048x4096x1024", "copy_192MB")
 
 
 def fp8_codes(f, torch, numel, seed, fmt=E4M3):
@@ -82,17 +82,21 @@ def single_kernel(f, torch, name, reps):
     operands, for rocprofv3 counter and trace runs."""
     dev = "cuda"
     s = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
-    if name == "gemm_bwd_pair_4096":
-        # the step's backward: dX (NN) and dW (TN) at M = N = K = 4096, one launch
-        n = 4096
-        g8, w8, x8 = (fp8_codes(f, torch, n * n, 800 + i, E5M2) for i in range(3))
-        dx = torch.empty(n * n, dtype=torch.int16, device=dev)
-        dw = torch.empty(n * n, dtype=torch.int16, device=dev)
+    if name in ("gemm_bwd_pair_4096", "gemm_bwd_pair_2048x4096x1024"):
+        # a layer step's backward, dX (NN) and dW (TN) in one launch: at
+        # M = N = K = 4096, or at the training configuration M, N, K =
+        # 2048, 4096, 1024 (dX 2048 x 1024 x 4096, dW 4096 x 1024 x 2048)
+        M, N, K = (4096, 4096, 4096) if name.endswith("4096") else (2048, 4096, 1024)
+        g8 = fp8_codes(f, torch, M * N, 800, E5M2)
+        w8 = fp8_codes(f, torch, N * K, 801, E5M2)
+        x8 = fp8_codes(f, torch, M * K, 802, E5M2)
+        dx = torch.empty(M * K, dtype=torch.int16, device=dev)
+        dw = torch.empty(N * K, dtype=torch.int16, device=dev)
 
         def launch():
-            f.fp8_mm_pair((g8, w8, E5M2, 0, 0, n, n, n, n, n, 1, 0, 0, s, s, None, dx),
-                          (g8, x8, E5M2, 1, 0, n, n, n, n, n, 1, 0, 0, s, s, None, dw))
-        work = dict(flop=2 * 2.0 * n ** 3, bytes=2 * (2 * n * n + 2 * n * n))
+            f.fp8_mm_pair((g8, w8, E5M2, 0, 0, M, K, N, N, K, 1, 0, 0, s, s, None, dx),
+                          (g8, x8, E5M2, 1, 0, N, K, M, N, K, 1, 0, 0, s, s, None, dw))
+        work = dict(flop=2 * 2.0 * M * N * K, bytes=2 * M * N + 3 * (M * K + N * K))
     elif name.startswith("gemm"):
         shapes = {"gemm_nt_4096": (4096, 4096, 4096, 0, 1), "gemm_nn_4096": (4096, 4096, 4096, 0, 0),
                   "gemm_tn_4096": (4096, 4096, 4096, 1, 0),
@@ -100,7 +104,9 @@ def single_kernel(f, torch, name, reps):
                   "gemm_nt_8192": (8192, 8192, 8192, 0, 1),
                   # the 4096^2 output tiles with a short k: what the epilogue
                   # and prologue count apart from the k loop
-                  "gemm_nt_4096x4096x256": (4096, 4096, 256, 0, 1)}
+                  "gemm_nt_4096x4096x256": (4096, 4096, 256, 0, 1),
+                  # the training configuration's forward
+                  "gemm_nt_2048x4096x1024": (2048, 4096, 1024, 0, 1)}
         M, N, K, ta, tb = shapes[name]
         fmt = E4M3 if (ta, tb) == (0, 1) else E5M2
         a = fp8_codes(f, torch, M * K, 810, fmt)

@@ -1021,35 +1021,56 @@ static int64_t tiles_of(const GemmLaunch& g, int bm, int bn) {
 }
 
 // Tile configuration by output-tile count.  Every configuration runs one
-// workgroup per CU (its LDS ring takes most of the 160 KB), so a launch with
-// fewer tiles than the 256 CUs leaves CUs idle, and the largest tile that
-// still gives every CU one is the most efficient (fewest operand bytes per
-// flop, longest time per stage to cover load latency).  The configurations,
-// with what they measured on MI355X (µs, fp8 operands, alternating bursts):
-//   kBig    256 x 256, 8 waves of 128 x 64       at >= 256 tiles of 256 x 256
-//   kWide   128 x 256, 8 waves of  64 x 64       at >= 256 tiles of 128 x 256
-//   kTall   256 x 128, 8 waves of  64 x 64       at >= 256 tiles of 256 x 128
-//   kMid    128 x 128, 8 waves of  32 x 64       otherwise (NN: 64 x 32)
-//   kSmall   64 x  64, 4 waves of  32 x 32       m <= 64 below 256 tiles of 128 x 128
-// (2048 x 4096 x 1024 NT: 13.9 wide against 18.8 for 4-wave 128 x 128 tiles;
-// 2048 x 1024 x 4096 NN: 16.8 mid against 21.6; 4096 x 1024 x 2048 TN: 12.1
-// mid against 14.9.)  For NN, B is n-contiguous and goes through the
-// transposing LDS read (about 180 B/clk per CU against 250 for ds_read_b128),
-// so kMid arranges its waves 2 x 4 there: each B fragment is read by two
-// waves instead of four (per 64-k substep 16 KB of transposing reads and
-// 32 KB of plain ones, instead of 32 and 16); 2048 x 1024 x 4096 NN 16.37 against 16.50, 1024 x 1024 x 8192 NN
-// 27.5 against 27.9, the training step's paired dX + dW 19.54 against
-// 19.74.  All configurations sum every output's k range in the same order,
-// so the choice never changes a result bit.
+// workgroup per CU (its LDS ring takes most of the 160 KB), so the tiles go
+// in rounds of 256 (one per CU), each round as long as one tile: the
+// launch costs rounds x tile time.  A larger tile reads fewer operand bytes
+// per flop, but fewer of them leave CUs idle or a last round nearly empty.
+// The configurations, with the tile time in units of a 256 x 256 tile's
+// (per-unit-area cost measured on MI355X over k = 272 .. 4112, graph
+// bursts, every configuration forced in turn on the same operands):
+//   kBig    256 x 256, 8 waves of 128 x 64                   1000
+//   kWide   128 x 256, 8 waves of  64 x 64   (1.35 per area)  675
+//   kTall   256 x 128, 8 waves of  64 x 64   (1.35 per area)  675
+//   kMid    128 x 128, 8 waves of  32 x 64   (1.9 per area)   475  (NN: 64 x 32)
+//   kSmall   64 x  64, 4 waves of  32 x 32   m <= 64 below 256 tiles of 128 x 128
+// The cheapest wins; ties go to the larger tile, and between 128 x 256 and
+// 256 x 128 to the one whose long side lies along the longer output side.
+// Measured (us): 2048 x 4096 x 1024 NT 13.9 wide (big 18.0, mid 15.1);
+// 2048 x 1024 x 4096 NN 16.4 mid (wide 25.7); 4096 x 1024 x 2048 TN 12.3 mid
+// (wide 15.8); 4112 x 1040 x 2064 TN 18.8 wide against 25.6 for 297 mid
+// tiles in two rounds; 3000 x 3000 x 2048 NT 28.6 big (144 tiles, one
+// round) against 31.2 wide (288 tiles, two rounds); 4096^3 57 big (wide
+// 69, mid 77).  For NN, B is n-contiguous and goes through the transposing
+// LDS read (about 180 B/clk per CU against 250 for ds_read_b128), so kMid
+// arranges its waves 2 x 4 there: each B fragment is read by two waves
+// instead of four (per 64-k substep 16 KB of transposing reads and 32 KB of
+// plain ones, instead of 32 and 16); 2048 x 1024 x 4096 NN 16.37 against
+// 16.50, 1024 x 1024 x 8192 NN 27.5 against 27.9, the training step's
+// paired dX + dW 19.54 against 19.74.  All configurations sum every
+// output's k range in the same order, so the choice never changes a result
+// bit.
 enum TileCfg { kBig, kWide, kTall, kMid, kSmall };
 
 static TileCfg tile_cfg(const GemmLaunch& g) {
-    if (tiles_of(g, 256, 256) >= 256) return kBig;
-    const int64_t wide = tiles_of(g, 128, 256), tall = tiles_of(g, 256, 128);
-    if (wide >= 256 && (g.n >= g.m || tall < 256)) return kWide;
-    if (tall >= 256) return kTall;
     if (g.m <= 64 && tiles_of(g, 128, 128) < 256) return kSmall;
-    return kMid;
+    struct Opt {
+        TileCfg c;
+        int bm, bn;
+        int64_t w;  // tile time, 1/1000 of a 256 x 256 tile's
+    };
+    const Opt wide{kWide, 128, 256, 675}, tall{kTall, 256, 128, 675};
+    const Opt order[4] = {{kBig, 256, 256, 1000}, g.n >= g.m ? wide : tall,
+                          g.n >= g.m ? tall : wide, {kMid, 128, 128, 475}};
+    TileCfg best = kBig;
+    int64_t best_cost = -1;
+    for (const Opt& o : order) {
+        const int64_t cost = (tiles_of(g, o.bm, o.bn) + 255) / 256 * o.w;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = o.c;
+        }
+    }
+    return best;
 }
 
 template <int FMT, bool AMN, bool BMN>

@@ -275,9 +275,9 @@ def check_against_linear_entry_points(f, torch):
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 PMC_TRAFFIC = {
     "gemm_nt_fwd": {"FETCH_SIZE": 49228.5, "WRITE_SIZE": 32768.0},
-    "gemm_bwd_pair": {"FETCH_SIZE": 98498.3, "WRITE_SIZE": 65536.0},
+    "gemm_bwd_pair": {"FETCH_SIZE": 98498.1, "WRITE_SIZE": 65536.0},
 }
-PMC_SRC = "cbb04673021c724677f2f93aa826a174bda29bef56bcae7cb8459f371946c587"
+PMC_SRC = "70574c763432b02f895235d5f95f35dbc6d9445aa733830adb213d21d350d7fd"
 
 
 def gemm_source_hash():

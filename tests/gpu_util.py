@@ -139,3 +139,26 @@ def check_fp8_codes(orc, got: np.ndarray, y: np.ndarray, bound: np.ndarray,
         print(f"[{what}] {n_diff} of {got.size} codes differ from the oracle's, each within "
               "the accumulation bound")
     return dict(n=int(got.size), differ=n_diff)
+
+
+def tile_count(M, N, bm, bn):
+    return ((M + bm - 1) // bm) * ((N + bn - 1) // bn)
+
+
+def chosen_tile_config(M, N, batch=1):
+    """The tile configuration the library's rule gives a batch of M x N outputs:
+    least (rounds of 256 tiles) x (tile time: 1000, 675, 675, 475 per
+    mille of a 256 x 256 tile's); ties to the larger tile, and between the
+    two halves to the one long along the longer side."""
+    if M <= 64 and tile_count(M, N, 128, 128) * batch < 256:
+        return "small"
+    halves = [("wide", 128, 256), ("tall", 256, 128)]
+    if N < M:
+        halves.reverse()
+    best = None
+    for (name, bm, bn), w in zip([("big", 256, 256)] + halves + [("mid", 128, 128)],
+                                 (1000, 675, 675, 475)):
+        cost = -(-tile_count(M, N, bm, bn) * batch // 256) * w
+        if best is None or cost < best[0]:
+            best = (cost, name)
+    return best[1]

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import check_gemm, dev_f32, from_dev_bf16, to_dev_bf16, to_dev_u8
+from tests.gpu_util import (check_gemm, chosen_tile_config as _chosen, dev_f32, from_dev_bf16,
+                            to_dev_bf16, to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -262,27 +263,6 @@ TILE_SHAPES = {
 }
 
 
-def _tiles(M, N, bm, bn):
-    return ((M + bm - 1) // bm) * ((N + bn - 1) // bn)
-
-
-def _chosen(M, N, batch=1):
-    """The tile configuration the library's rule gives a batch of M x N outputs:
-    least (rounds of 256 tiles) x (tile time: 1000, 675, 675, 475 per
-    mille of a 256 x 256 tile's); ties to the larger tile, and between the
-    two halves to the one long along the longer side."""
-    if M <= 64 and _tiles(M, N, 128, 128) * batch < 256:
-        return "small"
-    halves = [("wide", 128, 256), ("tall", 256, 128)]
-    if N < M:
-        halves.reverse()
-    best = None
-    for (name, bm, bn), w in zip([("big", 256, 256)] + halves + [("mid", 128, 128)],
-                                 (1000, 675, 675, 475)):
-        cost = -(-_tiles(M, N, bm, bn) * batch // 256) * w
-        if best is None or cost < best[0]:
-            best = (cost, name)
-    return best[1]
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])

@@ -15,8 +15,8 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import (check_fp8_codes, check_gemm, dev_f32, from_dev_bf16, from_dev_u8,
-                            to_dev_bf16, to_dev_u8)
+from tests.gpu_util import (check_fp8_codes, check_gemm, chosen_tile_config, dev_f32,
+                            from_dev_bf16, from_dev_u8, to_dev_bf16, to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +190,35 @@ def test_mm_ex_batched_broadcast(lib, orc):
     got = run_mm_ex(lib, a8, b8, fmt, 0, 1, M, N, K, sa, sb, None, None, OUT_E4M3, so,
                     batch=batch, stride_b=0)
     check_fp8_codes(orc, got, y, bound, OUT_E4M3, so, "batched broadcast")
+
+
+# The extended epilogue on the 128 x 256 and 256 x 128 tiles, ragged in m, n
+# and k (these shapes take those configurations: least rounds of 256 tiles
+# x tile time), every output: fp8 codes out with an fp8 bias, and bf16 out
+# with an fp8 bias.
+HALF_TILES = [("wide", 0, 1, 2032, 4080, 272), ("tall", 0, 0, 4084, 2032, 272),
+              ("wide", 1, 0, 2032, 4080, 272), ("tall", 0, 1, 4084, 2036, 272)]
+
+
+@pytest.mark.parametrize("cfg,ta,tb,M,N,K", HALF_TILES,
+                         ids=[f"{c[0]}-t{c[1]}{c[2]}" for c in HALF_TILES])
+def test_mm_ex_half_tiles_full_compare(lib, orc, cfg, ta, tb, M, N, K):
+    assert chosen_tile_config(M, N) == cfg
+    fmt = E4M3 if (ta, tb) == (0, 1) else E5M2
+    a8, sa = prequant(orc, wl.normal_bf16((M, K), 1.0, 61 + ta), fmt)
+    b8, sb = prequant(orc, wl.normal_bf16((K, N), 1.0, 62 + tb), fmt)
+    bias, bs = make_bias(orc, "fp8", N, fmt, 63)
+    A, B = storage(a8, ta), storage(b8, tb)
+    ref, y, bound = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs)
+    got = run_mm_ex(lib, A, B, fmt, ta, tb, M, N, K, sa, sb, bias, bs, OUT_BF16, None)
+    check_gemm(got.reshape(M, N), ref.reshape(M, N), bound.reshape(M, N),
+               f"{cfg} fp8 bias {M}x{N}x{K} t{ta}{tb}")
+    out_type = OUT_E4M3 if ta == 0 else OUT_E5M2
+    so = out_step(orc, y, out_type, headroom=0.8)
+    ref, y, bound = orc.gemm_ex(A, B, fmt, bool(ta), bool(tb), M, N, K, sa, sb, bias, bs,
+                                 out_type, so)
+    got = run_mm_ex(lib, A, B, fmt, ta, tb, M, N, K, sa, sb, bias, bs, out_type, so)
+    check_fp8_codes(orc, got, y, bound, out_type, so, f"{cfg} {M}x{N}x{K} t{ta}{tb} o{out_type}")
 
 
 @pytest.mark.parametrize("ta,tb,out_type", [(0, 1, OUT_E4M3), (0, 1, OUT_E5M2),

@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import workloads as wl
-from tests.gpu_util import (check_gemm, chosen_tile_config as _chosen, dev_f32, from_dev_bf16,
-                            to_dev_bf16, to_dev_u8)
+from tests.gpu_util import (check_gemm, chosen_tile_config, chosen_tile_config as _chosen,
+                            dev_f32, from_dev_bf16, to_dev_bf16, to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,29 @@ def test_mm_batched_and_broadcast_small(lib, orc, fmt):
         bound = orc.gemm_bound(a, b, fmt, False, True, M, N, K, sa, sb, batch=batch,
                                  stride_a=stra, stride_b=strb)
         check_gemm(got, ref, bound, f"batched {stra} {strb}", max_frac=1e-2)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (1, 1)], ids=["NN", "TN", "TT"])
+def test_mm_small_m_batched_and_broadcast(lib, orc, fmt, ta, tb):
+    """m <= 64 outside the NT short-A kernel: the 64 x 64 tiles, batched,
+    with either operand broadcast (batch stride 0), ragged m and k, every
+    output against the oracle."""
+    batch, M, N, K = 3, 48, 208, 400
+    assert chosen_tile_config(M, N, batch) == "small"
+    a3 = storage(wl.random_codes((batch, M, K), fmt, 21), ta)
+    b3 = storage(wl.random_codes((batch, K, N), fmt, 22), tb)
+    a1 = storage(wl.random_codes((M, K), fmt, 23), ta)
+    b1 = storage(wl.random_codes((K, N), fmt, 24), tb)
+    sa, sb = np.float32(1e-3), np.float32(2e-3)
+    for a, b, stra, strb in ((a3, b3, M * K, K * N), (a3, b1, M * K, 0), (a1, b3, 0, K * N)):
+        got = run_mm(lib, a, b, fmt, ta, tb, M, N, K, sa, sb, batch=batch, stride_a=stra,
+                     stride_b=strb)
+        ref = orc.gemm(a, b, fmt, bool(ta), bool(tb), M, N, K, sa, sb, batch=batch,
+                       stride_a=stra, stride_b=strb)
+        bound = orc.gemm_bound(a, b, fmt, bool(ta), bool(tb), M, N, K, sa, sb, batch=batch,
+                               stride_a=stra, stride_b=strb)
+        check_gemm(got, ref, bound, f"small m t{ta}{tb} {stra} {strb}", max_frac=1e-2)
 
 
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
